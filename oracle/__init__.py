@@ -1,0 +1,167 @@
+"""ctypes front end of the double-precision CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE.  Only tests/, the smoke check and the bench's CPU
+baseline import this package.  The GPU library never loads it and it never
+loads the GPU library.
+
+All array arguments are numpy float64, C-contiguous, in the layouts below
+(row-major, channel fastest):
+  u, x, r, i, y, dy, du : [B][T][D]
+  hist                  : [B][3][D]   (pre-conv inputs t-3, t-2, t-1)
+  h0, h_last, dh_last   : [B][D]
+  conv_w                : [D][4]      (tap k multiplies u[t-3+k])
+  W_a, W_x              : [H][K][K]   (W[h][o][j]: input hK+j -> output hK+o)
+  b_a, b_x, conv_b, Lambda : [D]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "oracle.c")
+
+_lib = None
+
+
+def build() -> str:
+    """Compile oracle.c with gcc (IEEE double, no fast-math, no FMA contraction)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+           "-fno-fast-math", "-ffp-contract=off", SRC_PATH, "-o", LIB_PATH + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(LIB_PATH + ".tmp", LIB_PATH)
+    return LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SRC_PATH):
+            build()
+        _lib = ctypes.CDLL(LIB_PATH)
+        _lib.oracle_num_threads.restype = ctypes.c_int
+    return _lib
+
+
+def _p(a):
+    if a is None:
+        return None
+    assert a.dtype == np.float64 and a.flags["C_CONTIGUOUS"], "oracle wants contiguous float64"
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _f64(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
+
+
+def set_threads(n: int) -> None:
+    lib().oracle_set_threads(ctypes.c_int(n))
+
+
+def conv1d(u, conv_w, conv_b=None, hist_in=None):
+    u, conv_w, conv_b, hist_in = map(_f64, (u, conv_w, conv_b, hist_in))
+    B, T, D = u.shape
+    x = np.empty_like(u)
+    hist_out = np.empty((B, 3, D))
+    lib().oracle_conv1d(B, T, D, _p(u), _p(conv_w), _p(conv_b), _p(hist_in), _p(x), _p(hist_out))
+    return x, hist_out
+
+
+def gates(x, W_a, b_a, W_x, b_x):
+    x, W_a, b_a, W_x, b_x = map(_f64, (x, W_a, b_a, W_x, b_x))
+    B, T, D = x.shape
+    H = W_a.shape[0]
+    r = np.empty_like(x)
+    i = np.empty_like(x)
+    lib().oracle_gates(B, T, D, H, _p(x), _p(W_a), _p(b_a), _p(W_x), _p(b_x), _p(r), _p(i))
+    return r, i
+
+
+def decay(r, Lambda, c=8.0):
+    r, Lambda = _f64(r), _f64(Lambda)
+    D = r.shape[-1]
+    N = r.size // D
+    a = np.empty_like(r)
+    beta = np.empty_like(r)
+    lib().oracle_decay(ctypes.c_long(N), D, ctypes.c_double(c), _p(r), _p(Lambda), _p(a), _p(beta))
+    return a, beta
+
+
+def scan(x, r, i, Lambda, h0=None, c=8.0):
+    x, r, i, Lambda, h0 = map(_f64, (x, r, i, Lambda, h0))
+    B, T, D = x.shape
+    y = np.empty_like(x)
+    h_last = np.empty((B, D))
+    lib().oracle_scan(B, T, D, ctypes.c_double(c), _p(x), _p(r), _p(i), _p(Lambda), _p(h0),
+                      _p(y), _p(h_last))
+    return y, h_last
+
+
+def fwd(u, conv_w, conv_b, W_a, b_a, W_x, b_x, Lambda, h0=None, hist_in=None, c=8.0):
+    """Whole forward u -> (y, h_last, hist_out).  conv_w None means no conv (x = u)."""
+    u, conv_w, conv_b, W_a, b_a, W_x, b_x, Lambda, h0, hist_in = map(
+        _f64, (u, conv_w, conv_b, W_a, b_a, W_x, b_x, Lambda, h0, hist_in))
+    B, T, D = u.shape
+    H = W_a.shape[0]
+    y = np.empty_like(u)
+    h_last = np.empty((B, D))
+    hist_out = np.empty((B, 3, D))
+    lib().oracle_fwd(B, T, D, H, ctypes.c_double(c), _p(u), _p(conv_w), _p(conv_b), _p(hist_in),
+                     _p(W_a), _p(b_a), _p(W_x), _p(b_x), _p(Lambda), _p(h0),
+                     _p(y), _p(h_last), _p(hist_out))
+    if conv_w is None:
+        hist_out = None
+    return y, h_last, hist_out
+
+
+def step(u_t, conv_w, conv_b, W_a, b_a, W_x, b_x, Lambda, hist, h, c=8.0):
+    """One decode step.  Returns (y_t, hist_new, h_new); inputs are not modified."""
+    u_t, conv_w, conv_b, W_a, b_a, W_x, b_x, Lambda = map(
+        _f64, (u_t, conv_w, conv_b, W_a, b_a, W_x, b_x, Lambda))
+    hist = np.array(hist, dtype=np.float64, order="C", copy=True)
+    h = np.array(h, dtype=np.float64, order="C", copy=True)
+    B, D = u_t.shape
+    H = W_a.shape[0]
+    y_t = np.empty((B, D))
+    lib().oracle_step(B, D, H, ctypes.c_double(c), _p(u_t), _p(conv_w), _p(conv_b), _p(W_a),
+                      _p(b_a), _p(W_x), _p(b_x), _p(Lambda), _p(hist), _p(h), _p(y_t))
+    return y_t, hist, h
+
+
+def bwd(u, conv_w, conv_b, W_a, b_a, W_x, b_x, Lambda, dy, h0=None, hist_in=None,
+        dh_last=None, c=8.0):
+    """Gradients of L = <dy, y> + <dh_last, h_last> w.r.t. every input.
+
+    Returns a dict: du, dconv_w, dconv_b, dW_a, db_a, dW_x, db_x, dLambda, dh0."""
+    u, conv_w, conv_b, W_a, b_a, W_x, b_x, Lambda, dy, h0, hist_in, dh_last = map(
+        _f64, (u, conv_w, conv_b, W_a, b_a, W_x, b_x, Lambda, dy, h0, hist_in, dh_last))
+    B, T, D = u.shape
+    H, K, _ = W_a.shape
+    g = dict(du=np.empty_like(u), dconv_w=np.empty((D, 4)), dconv_b=np.empty(D),
+             dW_a=np.empty((H, K, K)), db_a=np.empty(D), dW_x=np.empty((H, K, K)),
+             db_x=np.empty(D), dLambda=np.empty(D), dh0=np.empty((B, D)))
+    lib().oracle_bwd(B, T, D, H, ctypes.c_double(c), _p(u), _p(conv_w), _p(conv_b), _p(hist_in),
+                     _p(W_a), _p(b_a), _p(W_x), _p(b_x), _p(Lambda), _p(h0), _p(dy), _p(dh_last),
+                     _p(g["du"]), _p(g["dconv_w"]), _p(g["dconv_b"]), _p(g["dW_a"]), _p(g["db_a"]),
+                     _p(g["dW_x"]), _p(g["db_x"]), _p(g["dLambda"]), _p(g["dh0"]))
+    return g
+
+
+def rel_err(got, ref) -> float:
+    """max_i |g_i - o_i| / max(|o_i|, RMS(o)): elementwise relative error with
+    an RMS floor, so that outputs crossing zero are judged against the
+    tensor's scale rather than against a vanishing denominator."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    den = np.maximum(np.abs(ref), rms)
+    den = np.where(den == 0.0, 1.0, den)
+    return float(np.max(np.abs(got - ref) / den)) if ref.size else 0.0

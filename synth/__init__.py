@@ -1,0 +1,201 @@
+"""Seeded synthetic inputs for the RG-LRU hot path.
+
+This module is shared by the CPU oracle's tests, the GPU parity tests, the
+bench and the smoke check.  It holds no arithmetic of the method itself: only
+random-number generation, the parameter-initialisation recipe, storage
+rounding (fp32 -> bf16) and the table of workload shapes.
+
+Generator
+---------
+SplitMix64 (Steele, Lea & Flood, "Fast splittable pseudorandom number
+generators", OOPSLA 2014), used counter-style: the n-th draw (n >= 1) of the
+stream with seed s is mix(s + n * 0x9E3779B97F4A7C15), where mix is the
+published 64-bit finaliser.  Because every draw is a pure function of its
+index, any sub-range of a tensor can be generated on its own (the decode
+workload generates one step at a time, the oracle slices one sequence).
+
+Uniforms are (z >> 11) * 2^-53 in [0, 1).  Normals come from the Box-Muller
+transform (Box & Muller, 1958): element k uses draws 2k+1 and 2k+2,
+u1 = ((z1 >> 11) + 1) * 2^-53 in (0, 1], u2 = (z2 >> 11) * 2^-53,
+n = sqrt(-2 ln u1) * cos(2 pi u2).
+
+Streams: seed = 0x52474C5500000000 ^ (config << 16) ^ tensor_id.
+
+Initialisation recipe (RG-LRU page, section "Formulation of the RG-LRU
+Gating Mechanism" and the module's Lambda initialiser): the decay base
+a = sigmoid(Lambda) is drawn so that a^c is uniform on [0.9, 0.999], i.e.
+u ~ U[0.9, 0.999], a = u^(1/c), Lambda = log(a / (1 - a)); c = 8.  Gate
+weights are N(0, 1/K) (variance; std 1/sqrt(K)), conv weights N(0, 1/4)
+(std 0.5), biases 0, activations N(0, 1).
+
+Rounding: values are generated in float64, rounded to float32 (IEEE
+round-to-nearest-even) and, for bf16 storage, from float32 to bf16 with
+round-to-nearest-even on the bit pattern.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+GOLDEN = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+SEED_BASE = 0x52474C5500000000
+_BLOCK = 1 << 22
+
+# tensor ids of the per-tensor streams
+TID = dict(u=0, conv_w=1, conv_b=2, W_a=3, W_x=4, lam_u=5, dy=6, h0=7,
+           b_a=8, b_x=9, hist=10, dh_last=11)
+
+C_CONST = 8.0
+
+
+def seed_for(cfg: int, tensor: str) -> int:
+    return (SEED_BASE ^ (int(cfg) << 16) ^ TID[tensor]) & 0xFFFFFFFFFFFFFFFF
+
+
+def _mix(z: np.ndarray) -> np.ndarray:
+    z = (z ^ (z >> np.uint64(30))) * _M1
+    z = (z ^ (z >> np.uint64(27))) * _M2
+    return z ^ (z >> np.uint64(31))
+
+
+def raw_u64(seed: int, start: int, count: int) -> np.ndarray:
+    """Draws number start+1 .. start+count of the SplitMix64 stream `seed`."""
+    n = np.arange(start + 1, start + count + 1, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        return _mix(np.uint64(seed) + n * GOLDEN)
+
+
+def uniform(seed: int, start: int, count: int) -> np.ndarray:
+    """Uniform float64 in [0, 1): element k of the tensor is draw start+k+1."""
+    out = np.empty(count, dtype=np.float64)
+    for b0 in range(0, count, _BLOCK):
+        n = min(_BLOCK, count - b0)
+        z = raw_u64(seed, start + b0, n)
+        out[b0:b0 + n] = (z >> np.uint64(11)).astype(np.float64) * 2.0 ** -53
+    return out
+
+
+def normal(seed: int, start: int, count: int) -> np.ndarray:
+    """Standard normal float64; element k of the tensor uses draws 2k+1, 2k+2."""
+    out = np.empty(count, dtype=np.float64)
+    for b0 in range(0, count, _BLOCK):
+        n = min(_BLOCK, count - b0)
+        z = raw_u64(seed, 2 * (start + b0), 2 * n)
+        u1 = ((z[0::2] >> np.uint64(11)).astype(np.float64) + 1.0) * 2.0 ** -53
+        u2 = (z[1::2] >> np.uint64(11)).astype(np.float64) * 2.0 ** -53
+        out[b0:b0 + n] = np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * math.pi * u2)
+    return out
+
+
+# ---------------------------------------------------------------- bf16 storage
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """float32 -> bf16 bit pattern (uint16), round to nearest even."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    nan = (b & 0x7FFFFFFF) > 0x7F800000
+    r = ((b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16))
+    r = np.where(nan, (b >> np.uint32(16)) | np.uint32(0x40), r)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def store(x64: np.ndarray, io: str) -> np.ndarray:
+    """Round float64 values to the storage dtype.
+
+    Returns float32 for io='f32' and uint16 bf16 bit patterns for io='bf16'."""
+    f = np.asarray(x64, dtype=np.float64).astype(np.float32)
+    return f if io == "f32" else f32_to_bf16_bits(f)
+
+
+def widen(stored: np.ndarray) -> np.ndarray:
+    """Stored values (float32, or uint16 bf16 bits) as exact float64."""
+    if stored.dtype == np.uint16:
+        return bf16_bits_to_f32(stored).astype(np.float64)
+    return np.asarray(stored, dtype=np.float32).astype(np.float64)
+
+
+# ------------------------------------------------------------- workload table
+@dataclasses.dataclass(frozen=True)
+class Config:
+    idx: int
+    name: str
+    B: int
+    T: int
+    D: int
+    H: int
+    io: str          # storage dtype of activations and gate weights
+    steps: int = 0   # decode workload: number of one-token calls
+
+    @property
+    def K(self) -> int:
+        return self.D // self.H
+
+
+CONFIGS = [
+    Config(0, "tiny fp32 forward", 1, 256, 256, 1, "f32"),
+    Config(1, "2B-width prefill", 8, 2048, 2560, 10, "bf16"),
+    Config(2, "long-sequence prefill", 1, 32768, 2560, 10, "bf16"),
+    Config(3, "decode step", 256, 1, 2560, 10, "bf16", steps=512),
+    Config(4, "9B-width forward+backward", 4, 8192, 4096, 16, "bf16"),
+]
+
+
+def lambda_from_uniform(u01: np.ndarray, c: float = C_CONST) -> np.ndarray:
+    """Lambda = logit(u^(1/c)) with u = 0.9 + 0.099 * u01 (float64)."""
+    u = 0.9 + (0.999 - 0.9) * u01
+    a = u ** (1.0 / c)
+    return np.log(a / (1.0 - a))
+
+
+@dataclasses.dataclass
+class Params:
+    """Stored parameters: float32 arrays, gate weights in the io storage form."""
+    conv_w: np.ndarray   # [D][4] f32
+    conv_b: np.ndarray   # [D] f32
+    W_a: np.ndarray      # [H][K][K] io
+    b_a: np.ndarray      # [D] f32
+    W_x: np.ndarray      # [H][K][K] io
+    b_x: np.ndarray      # [D] f32
+    Lambda: np.ndarray   # [D] f32
+    lam_u: np.ndarray    # [D] float64: the a^c draw each Lambda came from
+
+
+def make_params(cfg: int, D: int, H: int, io: str, c: float = C_CONST) -> Params:
+    K = D // H
+    cw = store(0.5 * normal(seed_for(cfg, "conv_w"), 0, D * 4), "f32").reshape(D, 4)
+    wstd = 1.0 / math.sqrt(K)
+    Wa = store(wstd * normal(seed_for(cfg, "W_a"), 0, H * K * K), io).reshape(H, K, K)
+    Wx = store(wstd * normal(seed_for(cfg, "W_x"), 0, H * K * K), io).reshape(H, K, K)
+    u01 = uniform(seed_for(cfg, "lam_u"), 0, D)
+    lam = store(lambda_from_uniform(u01, c), "f32")
+    zeros = np.zeros(D, dtype=np.float32)
+    return Params(cw, zeros.copy(), Wa, zeros.copy(), Wx, zeros.copy(), lam,
+                  0.9 + (0.999 - 0.9) * u01)
+
+
+def make_activation(cfg: int, tensor: str, shape, io: str, start: int = 0,
+                    scale: float = 1.0) -> np.ndarray:
+    n = int(np.prod(shape))
+    return store(scale * normal(seed_for(cfg, tensor), start, n), io).reshape(shape)
+
+
+def make_u(cfg: Config, B=None, T=None) -> np.ndarray:
+    B = cfg.B if B is None else B
+    T = cfg.T if T is None else T
+    return make_activation(cfg.idx, "u", (B, T, cfg.D), cfg.io)
+
+
+def make_decode_u(cfg: Config, step: int) -> np.ndarray:
+    """Input of decode call `step` ([B][D]); the decode stream is [steps][B][D]."""
+    n = cfg.B * cfg.D
+    return make_activation(cfg.idx, "u", (cfg.B, cfg.D), cfg.io, start=step * n)
+
+
+def make_dy(cfg: Config) -> np.ndarray:
+    return make_activation(cfg.idx, "dy", (cfg.B, cfg.T, cfg.D), cfg.io)
