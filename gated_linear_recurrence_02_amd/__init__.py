@@ -1,0 +1,281 @@
+"""Python binding of librglru.so, the MI355X RG-LRU hot-path library.
+
+Argument marshalling only: each function checks its torch tensors (device,
+dtype, contiguity, shape), allocates outputs with torch, and calls the C entry
+point of the same name (declared in include/rglru.h) on the current HIP
+stream.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback: if the library is missing, importing works but every
+call raises.
+
+Layouts (row-major, channel fastest): activations [B][T][D], conv history
+[B][3][D], state [B][D] fp32, conv_w [D][4] fp32, W_a / W_x [H][K][K] in the
+activation dtype with K = 256, b_a / b_x / conv_b / Lambda [D] fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librglru.so")
+
+F32, BF16 = 0, 1
+OP_SCAN_FWD, OP_SCAN_BWD = 0, 1
+_IO = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+class RGLRUError(RuntimeError):
+    """A non-zero status from the C library."""
+
+
+class _Desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("D", ctypes.c_int64),
+                ("H", ctypes.c_int64), ("io", ctypes.c_int32), ("c", ctypes.c_float)]
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [("conv_w", ctypes.c_void_p), ("conv_b", ctypes.c_void_p),
+                ("W_a", ctypes.c_void_p), ("b_a", ctypes.c_void_p),
+                ("W_x", ctypes.c_void_p), ("b_x", ctypes.c_void_p),
+                ("Lambda", ctypes.c_void_p)]
+
+
+_lib = None
+SYMBOLS = ("rglru_workspace_size", "rglru_conv1d", "rglru_gates", "rglru_scan_fwd",
+           "rglru_step", "rglru_scan_bwd", "rglru_status_string")
+
+
+def lib():
+    """Load librglru.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RGLRUError(f"{LIB_PATH} is not built; run gated_linear_recurrence_02_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        D, W = ctypes.POINTER(_Desc), ctypes.POINTER(_Weights)
+        L.rglru_status_string.restype = ctypes.c_char_p
+        L.rglru_status_string.argtypes = [ctypes.c_int]
+        L.rglru_workspace_size.argtypes = [D, ctypes.c_int, ctypes.POINTER(sz)]
+        L.rglru_conv1d.argtypes = [D, vp, vp, vp, vp, vp, vp, vp]
+        L.rglru_gates.argtypes = [D, W, vp, vp, vp, vp]
+        L.rglru_scan_fwd.argtypes = [D, W, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.rglru_step.argtypes = [D, W, vp, vp, vp, vp, vp]
+        L.rglru_scan_bwd.argtypes = [D, W, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        for s in SYMBOLS:
+            if s != "rglru_status_string":
+                getattr(L, s).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        msg = lib().rglru_status_string(rc).decode()
+        raise RGLRUError(f"{what} failed with status {rc}: {msg}")
+
+
+@dataclasses.dataclass
+class Weights:
+    """Device tensors of one RG-LRU layer's parameters (conv_b, b_a, b_x optional)."""
+    conv_w: torch.Tensor
+    W_a: torch.Tensor
+    W_x: torch.Tensor
+    Lambda: torch.Tensor
+    conv_b: Optional[torch.Tensor] = None
+    b_a: Optional[torch.Tensor] = None
+    b_x: Optional[torch.Tensor] = None
+    c: float = 8.0
+
+    @property
+    def H(self) -> int:
+        return int(self.W_a.shape[0])
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, device, dtype=None, shape=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _io(t: torch.Tensor) -> int:
+    if t.dtype not in _IO:
+        raise ValueError(f"activations must be float32 or bfloat16, got {t.dtype}")
+    return _IO[t.dtype]
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _weights_struct(w: Weights, D: int, dtype, device, conv: bool, gates: bool):
+    if gates:
+        H = w.H
+        _need(w.W_a, "W_a", device, dtype, (H, D // H, D // H))
+        _need(w.W_x, "W_x", device, dtype, (H, D // H, D // H))
+        _need(w.b_a, "b_a", device, torch.float32, (D,))
+        _need(w.b_x, "b_x", device, torch.float32, (D,))
+    if conv:
+        _need(w.conv_w, "conv_w", device, torch.float32, (D, 4))
+        _need(w.conv_b, "conv_b", device, torch.float32, (D,))
+    _need(w.Lambda, "Lambda", device, torch.float32, (D,))
+    return _Weights(_ptr(w.conv_w) if conv else None, _ptr(w.conv_b) if conv else None,
+                    _ptr(w.W_a) if gates else None, _ptr(w.b_a) if gates else None,
+                    _ptr(w.W_x) if gates else None, _ptr(w.b_x) if gates else None,
+                    _ptr(w.Lambda))
+
+
+# ------------------------------------------------------------------ workspace
+_ws_cache = {}
+
+
+def workspace_size(B, T, D, H, io=BF16, op=OP_SCAN_FWD, c=8.0) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().rglru_workspace_size(ctypes.byref(_Desc(B, T, D, H, io, c)), op, ctypes.byref(n)),
+           "rglru_workspace_size")
+    return int(n.value)
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-filled workspace of at least nbytes, cached per device.
+
+    The library restores the workspace header at the end of every call, so the
+    cached buffer can be reused by calls that run one after another (one
+    stream).  Calls that may overlap need workspaces of their own."""
+    device = torch.device(device)
+    buf = _ws_cache.get(device)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[device] = buf
+    return buf
+
+
+# ----------------------------------------------------------------- entry points
+def conv1d(u: torch.Tensor, conv_w: torch.Tensor, conv_b=None, hist_in=None, H: int = 1):
+    """x = causal depthwise conv of u (width 4).  Returns (x, hist_out)."""
+    dev = u.device
+    _need(u, "u", dev)
+    B, T, D = u.shape
+    _need(conv_w, "conv_w", dev, torch.float32, (D, 4))
+    _need(conv_b, "conv_b", dev, torch.float32, (D,))
+    _need(hist_in, "hist_in", dev, u.dtype, (B, 3, D))
+    x = torch.empty_like(u)
+    hist_out = torch.empty((B, 3, D), dtype=u.dtype, device=dev)
+    d = _Desc(B, T, D, H, _io(u), 8.0)
+    _check(lib().rglru_conv1d(ctypes.byref(d), _ptr(conv_w), _ptr(conv_b), _ptr(u), _ptr(hist_in),
+                              _ptr(x), _ptr(hist_out), _stream(dev)), "rglru_conv1d")
+    return x, hist_out
+
+
+def gates(x: torch.Tensor, w: Weights):
+    """(r, i) = (sigmoid(W_a x + b_a), sigmoid(W_x x + b_x)), block-diagonal."""
+    dev = x.device
+    _need(x, "x", dev)
+    B, T, D = x.shape
+    ws = _weights_struct(w, D, x.dtype, dev, conv=False, gates=True)
+    r = torch.empty_like(x)
+    i = torch.empty_like(x)
+    d = _Desc(B, T, D, w.H, _io(x), w.c)
+    _check(lib().rglru_gates(ctypes.byref(d), ctypes.byref(ws), _ptr(x), _ptr(r), _ptr(i),
+                             _stream(dev)), "rglru_gates")
+    return r, i
+
+
+def scan_fwd(inp: torch.Tensor, w: Weights, *, r=None, i=None, h0=None, hist_in=None,
+             conv: bool = True, want_hist: bool = True, out=None, h_last_out=None,
+             hist_out_buf=None):
+    """Forward scan.  Mode A (conv=True, no r/i): inp is pre-conv u.  Mode B
+    (conv=False, no r/i): inp is x.  Mode C (r and i given): inp is x, scan only.
+    Returns (y, h_last, hist_out or None)."""
+    dev = inp.device
+    _need(inp, "in", dev)
+    B, T, D = inp.shape
+    mode_c = r is not None or i is not None
+    if mode_c and (r is None or i is None):
+        raise ValueError("r and i go together")
+    use_conv = conv and not mode_c
+    _need(r, "r", dev, inp.dtype, (B, T, D))
+    _need(i, "i", dev, inp.dtype, (B, T, D))
+    _need(h0, "h0", dev, torch.float32, (B, D))
+    _need(hist_in, "hist_in", dev, inp.dtype, (B, 3, D))
+    H = 1 if mode_c else w.H
+    ws_ = _weights_struct(w, D, inp.dtype, dev, conv=use_conv, gates=not mode_c)
+    y = torch.empty_like(inp) if out is None else out
+    h_last = torch.empty((B, D), dtype=torch.float32, device=dev) if h_last_out is None else h_last_out
+    hist_out = None
+    if use_conv and want_hist:
+        hist_out = hist_out_buf if hist_out_buf is not None else torch.empty((B, 3, D), dtype=inp.dtype, device=dev)
+    _need(y, "out", dev, inp.dtype, (B, T, D))
+    _need(h_last, "h_last_out", dev, torch.float32, (B, D))
+    _need(hist_out, "hist_out_buf", dev, inp.dtype, (B, 3, D))
+    d = _Desc(B, T, D, H, _io(inp), w.c)
+    nbytes = workspace_size(B, T, D, H, _io(inp), OP_SCAN_FWD, w.c)
+    wsb = workspace(nbytes, dev)
+    _check(lib().rglru_scan_fwd(ctypes.byref(d), ctypes.byref(ws_), _ptr(inp), _ptr(r), _ptr(i),
+                                _ptr(hist_in) if use_conv else None, _ptr(h0), _ptr(y),
+                                _ptr(h_last), _ptr(hist_out), _ptr(wsb), wsb.numel(), _stream(dev)),
+           "rglru_scan_fwd")
+    return y, h_last, hist_out
+
+
+def step(u_t: torch.Tensor, w: Weights, hist: torch.Tensor, h: torch.Tensor, y_out=None):
+    """One decode step; hist [B][3][D] and h [B][D] are updated in place.  Returns y_t."""
+    dev = u_t.device
+    _need(u_t, "u_t", dev)
+    B, D = u_t.shape
+    _need(hist, "hist", dev, u_t.dtype, (B, 3, D))
+    _need(h, "h", dev, torch.float32, (B, D))
+    ws_ = _weights_struct(w, D, u_t.dtype, dev, conv=True, gates=True)
+    y_t = torch.empty_like(u_t) if y_out is None else y_out
+    d = _Desc(B, 1, D, w.H, _io(u_t), w.c)
+    _check(lib().rglru_step(ctypes.byref(d), ctypes.byref(ws_), _ptr(u_t), _ptr(hist), _ptr(h),
+                            _ptr(y_t), _stream(dev)), "rglru_step")
+    return y_t
+
+
+def scan_bwd(u: torch.Tensor, w: Weights, dy: torch.Tensor, *, h0=None, hist_in=None,
+             dh_last=None, want_dh0: bool = True):
+    """Gradients of <dy, y> + <dh_last, h_last> for the mode-A forward.
+
+    Returns a dict: du, dconv_w, dconv_b, dW_a, db_a, dW_x, db_x, dLambda, dh0."""
+    dev = u.device
+    _need(u, "u", dev)
+    B, T, D = u.shape
+    _need(dy, "dy", dev, u.dtype, (B, T, D))
+    _need(h0, "h0", dev, torch.float32, (B, D))
+    _need(hist_in, "hist_in", dev, u.dtype, (B, 3, D))
+    _need(dh_last, "dh_last", dev, torch.float32, (B, D))
+    ws_ = _weights_struct(w, D, u.dtype, dev, conv=True, gates=True)
+    H, K = w.H, D // w.H
+    f = dict(dtype=torch.float32, device=dev)
+    g = dict(du=torch.empty_like(u), dconv_w=torch.empty((D, 4), **f), dconv_b=torch.empty(D, **f),
+             dW_a=torch.empty((H, K, K), **f), db_a=torch.empty(D, **f),
+             dW_x=torch.empty((H, K, K), **f), db_x=torch.empty(D, **f),
+             dLambda=torch.empty(D, **f),
+             dh0=torch.empty((B, D), **f) if want_dh0 else None)
+    d = _Desc(B, T, D, H, _io(u), w.c)
+    nbytes = workspace_size(B, T, D, H, _io(u), OP_SCAN_BWD, w.c)
+    wsb = workspace(nbytes, dev)
+    _check(lib().rglru_scan_bwd(ctypes.byref(d), ctypes.byref(ws_), _ptr(u), _ptr(hist_in), _ptr(h0),
+                                _ptr(dy), _ptr(dh_last), _ptr(g["du"]), _ptr(g["dconv_w"]),
+                                _ptr(g["dconv_b"]), _ptr(g["dW_a"]), _ptr(g["db_a"]), _ptr(g["dW_x"]),
+                                _ptr(g["db_x"]), _ptr(g["dLambda"]), _ptr(g["dh0"]), _ptr(wsb),
+                                wsb.numel(), _stream(dev)), "rglru_scan_bwd")
+    return g

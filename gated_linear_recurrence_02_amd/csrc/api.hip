@@ -1,0 +1,219 @@
+// api.hip -- the extern "C" entry points of librglru.so (declared and
+// documented in include/rglru.h).  Every check runs here, on the host, before
+// anything is enqueued; the launchers behind them assume valid arguments.
+#include <math.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+using namespace rglru;
+
+namespace {
+
+constexpr int64_t MAX_DIM = (int64_t)1 << 30;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t esize(const rglru_desc &d) { return d.io == RGLRU_BF16 ? 2 : 4; }
+
+int check_desc(const rglru_desc *d, bool need_k256)
+{
+    if (!d) return RGLRU_ERR_NULL;
+    if (d->io != RGLRU_F32 && d->io != RGLRU_BF16) return RGLRU_ERR_DTYPE;
+    if (d->B < 1 || d->T < 1 || d->D < 1 || d->H < 1) return RGLRU_ERR_SHAPE;
+    if (d->B > MAX_DIM || d->T > MAX_DIM || d->D > MAX_DIM || d->D % d->H != 0) return RGLRU_ERR_SHAPE;
+    if ((double)d->B * (double)d->T * (double)d->D > 9.0e15) return RGLRU_ERR_SHAPE;
+    const int64_t NC = (d->T + 31) / 32, G = (d->D + 255) / 256;
+    if ((double)d->B * NC * G >= 2147483647.0) return RGLRU_ERR_SHAPE;   // work units fit a grid
+    if (need_k256 && d->D / d->H != 256) return RGLRU_ERR_SHAPE;
+    if (!isfinite(d->c)) return RGLRU_ERR_ARG;
+    return RGLRU_OK;
+}
+
+struct Range {
+    const void *p;
+    size_t bytes;
+};
+
+bool overlap(Range a, Range b)
+{
+    if (!a.p || !b.p || !a.bytes || !b.bytes) return false;
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// any output range overlapping any input range (or another output)
+bool any_alias(const Range *outs, int nout, const Range *ins, int nin)
+{
+    for (int o = 0; o < nout; ++o) {
+        for (int k = 0; k < nin; ++k)
+            if (overlap(outs[o], ins[k])) return true;
+        for (int k = o + 1; k < nout; ++k)
+            if (overlap(outs[o], outs[k])) return true;
+    }
+    return false;
+}
+
+int launch_status()
+{
+    return hipGetLastError() == hipSuccess ? RGLRU_OK : RGLRU_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *rglru_status_string(int status)
+{
+    switch (status) {
+    case RGLRU_OK: return "ok";
+    case RGLRU_ERR_NULL: return "a required pointer is NULL";
+    case RGLRU_ERR_SHAPE: return "bad shape (B, T, D, H, block width K = D/H must be 256, T must be 1 for a step)";
+    case RGLRU_ERR_DTYPE: return "unknown io dtype";
+    case RGLRU_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case RGLRU_ERR_WORKSPACE: return "workspace missing or too small";
+    case RGLRU_ERR_LAUNCH: return "HIP launch error";
+    case RGLRU_ERR_ARG: return "inconsistent arguments";
+    default: return "unknown status";
+    }
+}
+
+int rglru_workspace_size(const rglru_desc *desc, int op, size_t *bytes)
+{
+    if (!bytes) return RGLRU_ERR_NULL;
+    int st = check_desc(desc, false);
+    if (st) return st;
+    if (op == RGLRU_OP_SCAN_FWD) *bytes = fwd_workspace_bytes(desc->B, desc->T, desc->D);
+    else if (op == RGLRU_OP_SCAN_BWD) {
+        if (desc->D / desc->H != 256) return RGLRU_ERR_SHAPE;
+        *bytes = bwd_workspace_bytes(desc->B, desc->T, desc->D, desc->H);
+    } else return RGLRU_ERR_ARG;
+    return RGLRU_OK;
+}
+
+int rglru_conv1d(const rglru_desc *desc, const float *conv_w, const float *conv_b, const void *u,
+                 const void *hist_in, void *x, void *hist_out, hipStream_t stream)
+{
+    int st = check_desc(desc, false);
+    if (st) return st;
+    if (!conv_w || !u || !x) return RGLRU_ERR_NULL;
+    const void *all[] = {conv_w, conv_b, u, hist_in, x, hist_out};
+    for (const void *p : all)
+        if (p && !aligned16(p)) return RGLRU_ERR_ALIGN;
+    const rglru_desc &d = *desc;
+    const size_t act = d.B * d.T * d.D * esize(d), hist = d.B * 3 * d.D * esize(d);
+    const Range outs[] = {{x, act}, {hist_out, hist}};
+    const Range ins[] = {{conv_w, (size_t)d.D * 16}, {conv_b, (size_t)d.D * 4}, {u, act}, {hist_in, hist}};
+    if (any_alias(outs, 2, ins, 4)) return RGLRU_ERR_ARG;
+    launch_conv1d(d, conv_w, conv_b, u, hist_in, x, hist_out, stream);
+    return launch_status();
+}
+
+int rglru_gates(const rglru_desc *desc, const rglru_weights *w, const void *x, void *r, void *i,
+                hipStream_t stream)
+{
+    int st = check_desc(desc, true);
+    if (st) return st;
+    if (!w || !w->W_a || !w->W_x || !x || !r || !i) return RGLRU_ERR_NULL;
+    const void *all[] = {w->W_a, w->W_x, w->b_a, w->b_x, x, r, i};
+    for (const void *p : all)
+        if (p && !aligned16(p)) return RGLRU_ERR_ALIGN;
+    const rglru_desc &d = *desc;
+    const size_t act = d.B * d.T * d.D * esize(d), wb = d.H * 65536 * esize(d);
+    const Range outs[] = {{r, act}, {i, act}};
+    const Range ins[] = {{x, act}, {w->W_a, wb}, {w->W_x, wb}, {w->b_a, (size_t)d.D * 4}, {w->b_x, (size_t)d.D * 4}};
+    if (any_alias(outs, 2, ins, 5)) return RGLRU_ERR_ARG;
+    launch_gates(d, *w, x, r, i, stream);
+    return launch_status();
+}
+
+int rglru_scan_fwd(const rglru_desc *desc, const rglru_weights *w, const void *in, const void *r,
+                   const void *i, const void *hist_in, const float *h0, void *y, float *h_last,
+                   void *hist_out, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (!desc || !w) return RGLRU_ERR_NULL;
+    if ((r == nullptr) != (i == nullptr)) return RGLRU_ERR_ARG;
+    const int mode = r ? 2 : (w->conv_w ? 0 : 1);
+    if (mode == 2 && w->conv_w) return RGLRU_ERR_ARG;
+    if (mode != 0 && (hist_in || hist_out)) return RGLRU_ERR_ARG;
+    int st = check_desc(desc, mode != 2);
+    if (st) return st;
+    if (!in || !y || !w->Lambda) return RGLRU_ERR_NULL;
+    if (mode != 2 && (!w->W_a || !w->W_x)) return RGLRU_ERR_NULL;
+    if (!ws) return RGLRU_ERR_WORKSPACE;
+    const void *all[] = {in, r, i, hist_in, h0, y, h_last, hist_out, ws, w->conv_w, w->conv_b,
+                         w->W_a, w->b_a, w->W_x, w->b_x, w->Lambda};
+    for (const void *p : all)
+        if (p && !aligned16(p)) return RGLRU_ERR_ALIGN;
+    const rglru_desc &d = *desc;
+    const size_t need = fwd_workspace_bytes(d.B, d.T, d.D);
+    if (ws_bytes < need) return RGLRU_ERR_WORKSPACE;
+    const size_t act = d.B * d.T * d.D * esize(d), hist = d.B * 3 * d.D * esize(d);
+    const size_t st_b = d.B * d.D * 4, vec = d.D * 4;
+    const size_t wb = mode == 2 ? 0 : d.H * 65536 * esize(d);
+    const Range outs[] = {{y, act}, {h_last, st_b}, {hist_out, hist}, {ws, need}};
+    const Range ins[] = {{in, act}, {r, act}, {i, act}, {hist_in, hist}, {h0, st_b},
+                         {w->conv_w, mode == 0 ? vec * 4 : 0}, {w->conv_b, mode == 0 ? vec : 0},
+                         {w->W_a, wb}, {w->W_x, wb}, {w->b_a, mode == 2 ? 0 : vec},
+                         {w->b_x, mode == 2 ? 0 : vec}, {w->Lambda, vec}};
+    if (any_alias(outs, 4, ins, 12)) return RGLRU_ERR_ARG;
+    launch_scan_fwd(d, *w, mode, in, r, i, hist_in, h0, y, h_last, hist_out, ws, stream);
+    return launch_status();
+}
+
+int rglru_step(const rglru_desc *desc, const rglru_weights *w, const void *u_t, void *hist, float *h,
+               void *y_t, hipStream_t stream)
+{
+    int st = check_desc(desc, true);
+    if (st) return st;
+    if (desc->T != 1) return RGLRU_ERR_SHAPE;
+    if (!w || !w->conv_w || !w->W_a || !w->W_x || !w->Lambda || !u_t || !hist || !h || !y_t)
+        return RGLRU_ERR_NULL;
+    const void *all[] = {u_t, hist, h, y_t, w->conv_w, w->conv_b, w->W_a, w->b_a, w->W_x, w->b_x, w->Lambda};
+    for (const void *p : all)
+        if (p && !aligned16(p)) return RGLRU_ERR_ALIGN;
+    const rglru_desc &d = *desc;
+    const size_t row = d.B * d.D * esize(d), hb = d.B * 3 * d.D * esize(d), sb = d.B * d.D * 4;
+    const size_t vec = d.D * 4, wb = d.H * 65536 * esize(d);
+    // hist and h are in/out by design; they must not overlap each other, y_t or any input
+    const Range outs[] = {{y_t, row}, {hist, hb}, {h, sb}};
+    const Range ins[] = {{u_t, row}, {w->conv_w, vec * 4}, {w->conv_b, vec}, {w->W_a, wb},
+                         {w->b_a, vec}, {w->W_x, wb}, {w->b_x, vec}, {w->Lambda, vec}};
+    if (any_alias(outs, 3, ins, 8)) return RGLRU_ERR_ARG;
+    launch_step(d, *w, u_t, hist, h, y_t, stream);
+    return launch_status();
+}
+
+int rglru_scan_bwd(const rglru_desc *desc, const rglru_weights *w, const void *u, const void *hist_in,
+                   const float *h0, const void *dy, const float *dh_last, void *du, float *dconv_w,
+                   float *dconv_b, float *dW_a, float *db_a, float *dW_x, float *db_x, float *dLambda,
+                   float *dh0, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int st = check_desc(desc, true);
+    if (st) return st;
+    if (!w || !w->conv_w || !w->W_a || !w->W_x || !w->Lambda || !u || !dy || !du || !dconv_w ||
+        !dconv_b || !dW_a || !db_a || !dW_x || !db_x || !dLambda)
+        return RGLRU_ERR_NULL;
+    if (!ws) return RGLRU_ERR_WORKSPACE;
+    const void *all[] = {u, hist_in, h0, dy, dh_last, du, dconv_w, dconv_b, dW_a, db_a, dW_x,
+                         db_x, dLambda, dh0, ws, w->conv_w, w->conv_b, w->W_a, w->b_a,
+                         w->W_x, w->b_x, w->Lambda};
+    for (const void *p : all)
+        if (p && !aligned16(p)) return RGLRU_ERR_ALIGN;
+    const rglru_desc &d = *desc;
+    const size_t need = bwd_workspace_bytes(d.B, d.T, d.D, d.H);
+    if (ws_bytes < need) return RGLRU_ERR_WORKSPACE;
+    const size_t act = d.B * d.T * d.D * esize(d), hist = d.B * 3 * d.D * esize(d);
+    const size_t sb = d.B * d.D * 4, vec = d.D * 4, wb = d.H * 65536 * esize(d), wf = d.H * 65536 * 4;
+    const Range outs[] = {{du, act}, {dconv_w, vec * 4}, {dconv_b, vec}, {dW_a, wf}, {db_a, vec},
+                          {dW_x, wf}, {db_x, vec}, {dLambda, vec}, {dh0, sb}, {ws, need}};
+    const Range ins[] = {{u, act}, {hist_in, hist}, {h0, sb}, {dy, act}, {dh_last, sb},
+                         {w->conv_w, vec * 4}, {w->conv_b, vec}, {w->W_a, wb}, {w->b_a, vec},
+                         {w->W_x, wb}, {w->b_x, vec}, {w->Lambda, vec}};
+    if (any_alias(outs, 10, ins, 12)) return RGLRU_ERR_ARG;
+    launch_scan_bwd(d, *w, u, hist_in, h0, dy, dh_last, du, dconv_w, dconv_b, dW_a, db_a, dW_x, db_x,
+                    dLambda, dh0, ws, stream);
+    return launch_status();
+}
+
+}  // extern "C"

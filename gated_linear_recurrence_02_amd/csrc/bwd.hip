@@ -1,0 +1,566 @@
+// bwd.hip -- a7: backward of the fused forward (conv + block-diagonal gates +
+// log-space decay + scan), i.e. the vector-Jacobian product of
+// L = <dy, y> + <dh_last, h_last>.
+//
+// The pages give the forward only (page "Griffin Guide: RecurrentGemma, RG-LRU
+// & Hybrid Attention", "Formulation of the RG-LRU Gating Mechanism" and
+// "Temporal Filtering via Separable 1D Convolutions"); this is its exact
+// derivative.  With delta_t = dL/dh_t (total) and eps_t = a_t delta_t:
+//     delta_t = dy_t + eps_{t+1},  eps_T = dh_last,  dh0 = eps_0
+//     eps_t   = a_t eps_{t+1} + a_t dy_t            (reverse affine scan)
+//     dl_t    = delta_t (a_t h_{t-1} - (a_t^2 / beta_t) i_t x_t)
+//     dz^a    = -c s dl r (1 - r),   dz^x = delta beta x i (1 - i)
+//     dx_t    = delta beta i + W_a^T dz^a + W_x^T dz^x
+//     dLambda = sum c r sigma(-Lambda) dl,   db = sum dz,   dW = sum dz x^T
+//     du_t    = sum_k cw[k] dx_{t+3-k},   dcw[k] = sum dx_t u_{t-3+k},   dcb = sum dx
+//
+// Passes (all on the caller's stream):
+//   1. forward states: the mode-A forward kernel keeps only the state before
+//      each 32-token chunk;
+//   2. transposed gate weights Wt[h][j][o'] (o' < 256: W_a, else W_x);
+//   3. the chunk kernel, one (stream, chunk, 256-channel block) per workgroup,
+//      chunks handed out from the END of the sequence: recompute conv, gates
+//      (MFMA), decay and the states inside the chunk; reverse scan whose
+//      chunk carries eps go through the same decoupled look-back as the
+//      forward (chunks numbered from the end); local gradients; dx through
+//      the gates on the matrix cores; conv backward, whose last 3 tokens need
+//      the first 3 dx of the next chunk (published as tagged words); per-chunk
+//      partial sums; dz and x written channel-major for pass 4;
+//   4. dW = sum over rows of dz x^T on the matrix cores, split over row
+//      ranges into partials;
+//   5. deterministic reductions of the partials (fixed order, no atomics).
+#include "common.h"
+#include "gatemath.h"
+#include "internal.h"
+
+namespace rglru {
+
+namespace {
+
+constexpr int NSUM = 8;   // per-chunk partial sums: dcw[4], dcb, db_a, db_x, dLambda
+
+struct BwdLayout {
+    size_t fwd_words, bwd_words, hstart, Wt, dZt, Xt, psum, dWpart, total;
+    int S;   // row-range splits of the dW products
+};
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+BwdLayout bwd_layout(int64_t B, int64_t T, int64_t D, int64_t H, size_t esz)
+{
+    BwdLayout L;
+    const int64_t NC = (T + CHUNK - 1) / CHUNK;
+    const size_t NW = (size_t)B * NC * D;
+    int S = (int)((256 + 2 * H - 1) / (2 * H));
+    if (S < 1) S = 1;
+    if ((int64_t)S > B * NC) S = (int)(B * NC);
+    L.S = S;
+    size_t off = sizeof(WsHeader);
+    L.fwd_words = off;  off = align256(off + 3 * NW * 8);
+    L.bwd_words = off;  off = align256(off + 6 * NW * 8);
+    L.hstart = off;     off = align256(off + NW * 4);
+    L.Wt = off;         off = align256(off + (size_t)H * 256 * 512 * esz);
+    L.dZt = off;        off = align256(off + NW * 64 * esz);
+    L.Xt = off;         off = align256(off + NW * 32 * esz);
+    L.psum = off;       off = align256(off + NW * NSUM * 4);
+    L.dWpart = off;     off = align256(off + (size_t)S * H * 2 * 65536 * 4);
+    L.total = off;
+    return L;
+}
+
+// ------------------------------------------------------------------ pass 2
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_w_kernel(const T *Wa, const T *Wx, T *Wt)
+{
+    // tile of 32 (o) x 32 (j); grid (256/32 j-tiles, 512/32 o'-tiles, H)
+    __shared__ T tile[32][33];
+    const int h = blockIdx.z, j0 = blockIdx.x * 32, o0 = blockIdx.y * 32;
+    const T *src = (o0 < 256 ? Wa : Wx) + (size_t)h * 65536;
+    const int ob = o0 & 255;
+    for (int e = threadIdx.x; e < 1024; e += 256) {
+        const int oo = e >> 5, jj = e & 31;
+        tile[oo][jj] = src[(size_t)(ob + oo) * 256 + j0 + jj];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 1024; e += 256) {
+        const int jj = e >> 5, oo = e & 31;
+        Wt[(size_t)h * 131072 + (size_t)(j0 + jj) * 512 + o0 + oo] = tile[oo][jj];
+    }
+}
+
+// dx[k] += sum_o Zs[16h+k][o] * Wt_part[j][o] for the lane's channel j = 32w + n
+// (Zs: 32 x 256 tile in the XTile layout; Wt_part rows have stride 512)
+__device__ __forceinline__ void dx_tile(const bf16 *Zs, const bf16 *Wt_part, int wave, int lane,
+                                        float dx[16])
+{
+    constexpr int S = XTile<bf16>::STRIDE;
+    const int r = lane & 31, kg = lane >> 5;
+    const bf16 *zrow = Zs + tile_row_token(r) * S + 8 * kg;
+    const bf16 *wrow = Wt_part + (size_t)(32 * wave + r) * 512 + 8 * kg;
+    f32x16 C = {};
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+        const bf16x8 av = *(const bf16x8 *)(zrow + 16 * s);
+        const bf16x8 bv = *(const bf16x8 *)(wrow + 16 * s);
+        C = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, C, 0, 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) dx[k] += C[k];
+}
+
+__device__ __forceinline__ void dx_tile(const float *Zs, const float *Wt_part, int wave, int lane,
+                                        float dx[16])
+{
+    constexpr int S = XTile<float>::STRIDE;
+    const int n = lane & 31, half = lane >> 5;
+    const float *wrow = Wt_part + (size_t)(32 * wave + n) * 512;
+    const float *zs = Zs + 16 * half * S;
+    for (int o = 0; o < 256; ++o) {
+        const float wv = wrow[o];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) dx[k] = fmaf(zs[k * S + o], wv, dx[k]);
+    }
+}
+
+__device__ __forceinline__ float wait_word(const uint64_t *p, uint32_t tag, WsHeader *hdr)
+{
+    float v;
+    uint32_t spins = 0;
+    while (!get_word(p, tag, v)) {
+        if (++spins > SPIN_LIMIT) {
+            __hip_atomic_store(&hdr->error, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return __builtin_nanf("");
+        }
+        __builtin_amdgcn_s_sleep(4);
+    }
+    return v;
+}
+
+struct BwdParams {
+    int B, T, D, NC, G;
+    float c;
+    const void *u, *hist_in, *dy;
+    const float *h0, *dh_last;
+    const float *cw, *cb, *ba, *bx, *Lambda;
+    const void *Wa, *Wx, *Wt;
+    const float *hstart;
+    void *du;
+    float *dh0;
+    void *dZt, *Xt;
+    float *psum;
+    WsHeader *hdr;
+    uint64_t *aggA, *aggX, *incl, *halo;   // halo: 3 consecutive arrays of [B][NC][D]
+};
+
+// ------------------------------------------------------------------ pass 3
+template <typename T>
+__global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p)
+{
+    constexpr int S = XTile<T>::STRIDE;
+    __shared__ __attribute__((aligned(16))) T Xs[32 * S];   // x tile, then dz^a, then dz^x
+    __shared__ uint32_t s_unit, s_tag;
+    claim_unit(p.hdr, &s_unit, &s_tag, &p.hdr->counter);
+    const uint32_t unit = s_unit, tag = s_tag;
+    if (unit >= (uint32_t)p.B * p.NC * p.G) {
+        __syncthreads();
+        finish_launch(p.hdr, gridDim.x);
+        return;
+    }
+    const int g = (int)(unit % p.G);
+    const uint32_t cb_ = unit / p.G;       // chunk-major, from the end of the sequence
+    const int b = (int)(cb_ % p.B);
+    const int cr = (int)(cb_ / p.B);       // chunk index counted from the end
+    const int c = p.NC - 1 - cr;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 31, half = lane >> 5;
+    const int ch = wave * 32 + n;          // channel inside the block
+    const int d = g * 256 + ch;
+    const int tb = c * CHUNK + 16 * half;
+    const T *u = (const T *)p.u;
+    const long row_b = (long)b * p.T;
+    const long cidx = ((long)b * p.NC + c) * p.D + d;   // [B][NC][D] index of this chunk
+
+    // conv recompute (window kept for dcw)
+    const float w0 = p.cw[4 * (long)d + 0], w1 = p.cw[4 * (long)d + 1];
+    const float w2 = p.cw[4 * (long)d + 2], w3 = p.cw[4 * (long)d + 3];
+    const float bias = p.cb ? p.cb[d] : 0.0f;
+    float win[19];
+#pragma unroll
+    for (int m = 0; m < 19; ++m) {
+        const int tau = tb - 3 + m;
+        float v = 0.0f;
+        if (tau < p.T) {
+            if (tau >= 0) v = ldf(u + (row_b + tau) * p.D + d);
+            else if (p.hist_in) v = ldf((const T *)p.hist_in + ((long)b * 3 + 3 + tau) * p.D + d);
+        }
+        win[m] = v;
+    }
+    float x[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+        x[k] = fmaf(w3, win[k + 3], fmaf(w2, win[k + 2], fmaf(w1, win[k + 1], fmaf(w0, win[k], bias))));
+
+    // gates
+#pragma unroll
+    for (int k = 0; k < 16; ++k) Xs[(16 * half + k) * S + ch] = from_f32<T>(x[k]);
+    {   // x, channel-major per chunk, for the dW products
+        T *xt = (T *)p.Xt + ((((long)b * p.NC + c) * p.G + g) * 256 + ch) * 32 + 16 * half;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) xt[k] = from_f32<T>(x[k]);
+    }
+    __syncthreads();
+    float za[16], zx[16];
+    gate_tile(Xs, (const T *)p.Wa + (size_t)g * 65536, (const T *)p.Wx + (size_t)g * 65536, wave, lane,
+              za, zx);
+
+    // decay, normalisation and the forward states inside the chunk
+    const float lam = p.Lambda[d];
+    const float ncs = -p.c * softplus_acc(-lam);
+    const float sgm = sigmoid_acc(-lam);
+    const float bav = p.ba ? p.ba[d] : 0.0f, bxv = p.bx ? p.bx[d] : 0.0f;
+    float a[16], hl[16], P[16];
+    float h = 0.0f, pr = 1.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        za[k] = sigmoid_acc(za[k] + bav);   // r
+        zx[k] = sigmoid_acc(zx[k] + bxv);   // i
+        float ak = expf(ncs * za[k]);
+        float bb = sqrtf(-expm1f(2.0f * ncs * za[k])) * zx[k] * x[k];
+        if (tb + k >= p.T) {
+            ak = 1.0f;
+            bb = 0.0f;
+        }
+        a[k] = ak;
+        h = fmaf(ak, h, bb);
+        pr *= ak;
+        hl[k] = h;
+        P[k] = pr;
+    }
+    const float A0 = __shfl_xor(P[15], 32), X0 = __shfl_xor(hl[15], 32);
+    const float hs_chunk = p.hstart[cidx];
+    const float hs_lane = half == 0 ? hs_chunk : fmaf(A0, hs_chunk, X0);
+
+    // reverse scan inside the lane (eps entering the lane's last token = 0)
+    const T *dyp = (const T *)p.dy;
+    float dl[16], R[16];
+    float e = 0.0f, Rrun = 1.0f;
+#pragma unroll
+    for (int k = 15; k >= 0; --k) {
+        const float gk = (tb + k < p.T) ? ldf(dyp + (row_b + tb + k) * p.D + d) : 0.0f;
+        dl[k] = gk + e;
+        R[k] = Rrun;
+        e = a[k] * dl[k];
+        Rrun *= a[k];
+    }
+    // chunk carry: half 1 is first in reverse order
+    const float A1 = __shfl_xor(Rrun, 32), X1 = __shfl_xor(e, 32);
+    float ein_chunk = 0.0f;
+    if (half == 0) {
+        const float Ach = Rrun * A1;
+        const float Xch = fmaf(Rrun, X1, e);
+        const long base = (long)b * p.NC * p.D + d;
+        const long widx = base + (long)cr * p.D;
+        const float ebefore = p.dh_last ? p.dh_last[(long)b * p.D + d] : 0.0f;
+        put_word(p.aggA + widx, Ach, tag);
+        put_word(p.aggX + widx, Xch, tag);
+        if (cr == 0) {
+            ein_chunk = ebefore;
+        } else {
+            ein_chunk = look_back(p.aggA + base, p.aggX + base, p.incl + base, cr - 1, p.D, ebefore,
+                                  tag, p.hdr);
+        }
+        const float eout = fmaf(Ach, ein_chunk, Xch);
+        put_word(p.incl + widx, eout, tag);
+        if (c == 0 && p.dh0) p.dh0[(long)b * p.D + d] = eout;
+    }
+    const float eother = __shfl_xor(ein_chunk, 32);
+    const float ein_lane = half == 1 ? eother : fmaf(A1, ein_chunk, X1);
+
+    // local gradients
+    float dxv[16];
+    float s_ba = 0.0f, s_bx = 0.0f, s_rl = 0.0f;
+    float hprev = hs_lane;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const float delta = fmaf(R[k], ein_lane, dl[k]);
+        const float hk = fmaf(P[k], hs_lane, hl[k]);
+        const float r = za[k], ii = zx[k];
+        float dza = 0.0f, dzx = 0.0f, dxd = 0.0f;
+        if (tb + k < p.T) {
+            const float l = ncs * r;
+            const float beta = sqrtf(-expm1f(2.0f * l));
+            const float dlk = delta * (a[k] * hprev - (a[k] * a[k] / beta) * ii * x[k]);
+            const float di = delta * beta * x[k];
+            dxd = delta * beta * ii;
+            dza = ncs * dlk * r * (1.0f - r);
+            dzx = di * ii * (1.0f - ii);
+            s_rl = fmaf(r, dlk, s_rl);
+        }
+        s_ba += dza;
+        s_bx += dzx;
+        dxv[k] = dxd;
+        za[k] = dza;   // reuse: dz^a
+        zx[k] = dzx;   // reuse: dz^x
+        hprev = hk;
+    }
+    {   // dz, channel-major per chunk, for the dW products
+        T *zt = (T *)p.dZt + (((((long)b * p.NC + c) * p.G + g) * 2) * 256 + ch) * 32 + 16 * half;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            zt[k] = from_f32<T>(za[k]);
+            zt[256 * 32 + k] = from_f32<T>(zx[k]);
+        }
+    }
+
+    // dx through the gates: two passes over the LDS tile (dz^a, then dz^x)
+    const T *Wt_h = (const T *)p.Wt + (size_t)g * 131072;
+    __syncthreads();   // every wave is done with the x tile
+#pragma unroll
+    for (int k = 0; k < 16; ++k) Xs[(16 * half + k) * S + ch] = from_f32<T>(za[k]);
+    __syncthreads();
+    dx_tile(Xs, Wt_h, wave, lane, dxv);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16; ++k) Xs[(16 * half + k) * S + ch] = from_f32<T>(zx[k]);
+    __syncthreads();
+    dx_tile(Xs, Wt_h + 256, wave, lane, dxv);
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+        if (tb + k >= p.T) dxv[k] = 0.0f;
+
+    // conv backward: publish this chunk's first 3 dx before waiting for the next chunk's
+    const long NW = (long)p.B * p.NC * p.D;
+    if (half == 0) {
+        put_word(p.halo + cidx, dxv[0], tag);
+        put_word(p.halo + NW + cidx, dxv[1], tag);
+        put_word(p.halo + 2 * NW + cidx, dxv[2], tag);
+    }
+    const float o0 = __shfl_xor(dxv[0], 32), o1 = __shfl_xor(dxv[1], 32), o2 = __shfl_xor(dxv[2], 32);
+    float n0 = 0.0f, n1 = 0.0f, n2 = 0.0f;   // dx of the 3 tokens after the lane's 16
+    if (half == 0) {
+        n0 = o0;
+        n1 = o1;
+        n2 = o2;
+    } else if (c + 1 < p.NC) {
+        const long nidx = cidx + p.D;        // chunk c+1
+        n0 = wait_word(p.halo + nidx, tag, p.hdr);
+        n1 = wait_word(p.halo + NW + nidx, tag, p.hdr);
+        n2 = wait_word(p.halo + 2 * NW + nidx, tag, p.hdr);
+    }
+    float ext[19];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) ext[k] = dxv[k];
+    ext[16] = n0;
+    ext[17] = n1;
+    ext[18] = n2;
+    T *du = (T *)p.du;
+    float s_cb = 0.0f, s_w0 = 0.0f, s_w1 = 0.0f, s_w2 = 0.0f, s_w3 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        if (tb + k < p.T) {
+            const float duk = fmaf(w0, ext[k + 3], fmaf(w1, ext[k + 2], fmaf(w2, ext[k + 1], w3 * ext[k])));
+            du[(row_b + tb + k) * p.D + d] = from_f32<T>(duk);
+        }
+        s_cb += ext[k];
+        s_w0 = fmaf(ext[k], win[k + 0], s_w0);
+        s_w1 = fmaf(ext[k], win[k + 1], s_w1);
+        s_w2 = fmaf(ext[k], win[k + 2], s_w2);
+        s_w3 = fmaf(ext[k], win[k + 3], s_w3);
+    }
+
+    // per-chunk partial sums (half 0 + half 1), written by half 0
+    float v[NSUM] = {s_w0, s_w1, s_w2, s_w3, s_cb, s_ba, s_bx, s_rl};
+#pragma unroll
+    for (int q = 0; q < NSUM; ++q) v[q] += __shfl_xor(v[q], 32);
+    if (half == 0) {
+        v[7] *= p.c * sgm;
+        float4 *dst = (float4 *)(p.psum + cidx * NSUM);
+        dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+        dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    __syncthreads();
+    finish_launch(p.hdr, gridDim.x);
+}
+
+// ------------------------------------------------------------------ pass 4
+// dW[q][o][j] over the row range of split s: sum_{units, t} dz_q[o][t] x[j][t].
+// bf16: wave w owns rows o = 32w..32w+31 and all 256 columns (8 MFMA tiles).
+__global__ __launch_bounds__(512) void dw_kernel_bf16(int units, int G, int S, const bf16 *dZt,
+                                                      const bf16 *Xt, float *dWpart)
+{
+    const int g = blockIdx.x / 2, q = blockIdx.x % 2, s = blockIdx.y;
+    const int u0 = (int)((long)units * s / S), u1 = (int)((long)units * (s + 1) / S);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 31, kg = lane >> 5;
+    f32x16 acc[8];
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt) acc[jt] = f32x16{};
+    for (int un = u0; un < u1; ++un) {
+        const bf16 *zt = dZt + (((long)un * G + g) * 2 + q) * 256 * 32 + (32 * wave + r) * 32 + 8 * kg;
+        const bf16 *xt = Xt + ((long)un * G + g) * 256 * 32 + r * 32 + 8 * kg;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 av = *(const bf16x8 *)(zt + 16 * ks);
+#pragma unroll
+            for (int jt = 0; jt < 8; ++jt) {
+                const bf16x8 bv = *(const bf16x8 *)(xt + jt * 32 * 32 + 16 * ks);
+                acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[jt], 0, 0, 0);
+            }
+        }
+    }
+    float *dst = dWpart + (((long)s * G + g) * 2 + q) * 65536;
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int o = 32 * wave + 8 * (k >> 2) + 4 * kg + (k & 3);
+            dst[o * 256 + jt * 32 + r] = acc[jt][k];
+        }
+}
+
+// fp32: one thread per (o, j), rows in order
+__global__ __launch_bounds__(256) void dw_kernel_f32(int units, int G, int S, const float *dZt,
+                                                     const float *Xt, float *dWpart)
+{
+    const int gq = blockIdx.x / 256, o = blockIdx.x % 256, s = blockIdx.y;
+    const int g = gq / 2, q = gq % 2, j = threadIdx.x;
+    const int u0 = (int)((long)units * s / S), u1 = (int)((long)units * (s + 1) / S);
+    float acc = 0.0f;
+    for (int un = u0; un < u1; ++un) {
+        const float *zt = dZt + (((long)un * G + g) * 2 + q) * 256 * 32 + o * 32;
+        const float *xt = Xt + ((long)un * G + g) * 256 * 32 + j * 32;
+        for (int t = 0; t < 32; ++t) acc = fmaf(zt[t], xt[t], acc);
+    }
+    dWpart[(((long)s * G + g) * 2 + q) * 65536 + o * 256 + j] = acc;
+}
+
+// ------------------------------------------------------------------ pass 5
+__global__ __launch_bounds__(256) void dw_reduce_kernel(int G, int S, const float *dWpart, float *dWa,
+                                                        float *dWx)
+{
+    const long e = (long)blockIdx.x * 256 + threadIdx.x;   // over G * 2 * 65536
+    if (e >= (long)G * 2 * 65536) return;
+    const int g = (int)(e / 131072), rem = (int)(e % 131072), q = rem / 65536, oj = rem % 65536;
+    float acc = 0.0f;
+    for (int s = 0; s < S; ++s) acc += dWpart[(((long)s * G + g) * 2 + q) * 65536 + oj];
+    (q == 0 ? dWa : dWx)[(long)g * 65536 + oj] = acc;
+}
+
+__global__ __launch_bounds__(256) void psum_reduce_kernel(int units, int D, const float *psum,
+                                                          float *dcw, float *dcb, float *dba,
+                                                          float *dbx, float *dLambda)
+{
+    const int d = blockIdx.x * 256 + threadIdx.x;
+    if (d >= D) return;
+    float acc[NSUM] = {};
+    for (int un = 0; un < units; ++un) {
+        const float4 *src = (const float4 *)(psum + ((long)un * D + d) * NSUM);
+        const float4 v0 = src[0], v1 = src[1];
+        acc[0] += v0.x; acc[1] += v0.y; acc[2] += v0.z; acc[3] += v0.w;
+        acc[4] += v1.x; acc[5] += v1.y; acc[6] += v1.z; acc[7] += v1.w;
+    }
+    dcw[4 * (long)d + 0] = acc[0];
+    dcw[4 * (long)d + 1] = acc[1];
+    dcw[4 * (long)d + 2] = acc[2];
+    dcw[4 * (long)d + 3] = acc[3];
+    dcb[d] = acc[4];
+    dba[d] = acc[5];
+    dbx[d] = acc[6];
+    dLambda[d] = acc[7];
+}
+
+template <typename T>
+void run_bwd(const rglru_desc &d, const rglru_weights &w, const void *u, const void *hist_in,
+             const float *h0, const void *dy, const float *dh_last, void *du, float *dcw, float *dcb,
+             float *dWa, float *dba, float *dWx, float *dbx, float *dLambda, float *dh0, void *ws,
+             hipStream_t s)
+{
+    const BwdLayout L = bwd_layout(d.B, d.T, d.D, d.H, sizeof(T));
+    char *base = (char *)ws;
+    const int NC = (int)((d.T + CHUNK - 1) / CHUNK);
+    const int G = (int)d.H;
+    const size_t NW = (size_t)d.B * NC * d.D;
+
+    // pass 1: states before each chunk (the forward kernel shares the header)
+    float *hstart = (float *)(base + L.hstart);
+    launch_fwd_states(d, w, u, hist_in, h0, hstart, ws, s);
+
+    // pass 2
+    T *Wt = (T *)(base + L.Wt);
+    hipLaunchKernelGGL((transpose_w_kernel<T>), dim3(8, 16, G), dim3(256), 0, s, (const T *)w.W_a,
+                       (const T *)w.W_x, Wt);
+
+    // pass 3
+    BwdParams p;
+    p.B = (int)d.B;
+    p.T = (int)d.T;
+    p.D = (int)d.D;
+    p.NC = NC;
+    p.G = G;
+    p.c = d.c;
+    p.u = u;
+    p.hist_in = hist_in;
+    p.dy = dy;
+    p.h0 = h0;
+    p.dh_last = dh_last;
+    p.cw = w.conv_w;
+    p.cb = w.conv_b;
+    p.ba = w.b_a;
+    p.bx = w.b_x;
+    p.Lambda = w.Lambda;
+    p.Wa = w.W_a;
+    p.Wx = w.W_x;
+    p.Wt = Wt;
+    p.hstart = hstart;
+    p.du = du;
+    p.dh0 = dh0;
+    p.dZt = base + L.dZt;
+    p.Xt = base + L.Xt;
+    p.psum = (float *)(base + L.psum);
+    p.hdr = (WsHeader *)ws;
+    p.aggA = (uint64_t *)(base + L.bwd_words);
+    p.aggX = p.aggA + NW;
+    p.incl = p.aggX + NW;
+    p.halo = p.incl + NW;
+    const unsigned units = (unsigned)((size_t)d.B * NC * G);
+    hipLaunchKernelGGL((bwd_chunk_kernel<T>), dim3(units), dim3(512), 0, s, p);
+
+    // pass 4
+    const int chunks = (int)(d.B * NC);
+    float *dWpart = (float *)(base + L.dWpart);
+    if (sizeof(T) == 2)
+        hipLaunchKernelGGL(dw_kernel_bf16, dim3(2 * G, L.S), dim3(512), 0, s, chunks, G, L.S,
+                           (const bf16 *)p.dZt, (const bf16 *)p.Xt, dWpart);
+    else
+        hipLaunchKernelGGL(dw_kernel_f32, dim3(2 * G * 256, L.S), dim3(256), 0, s, chunks, G, L.S,
+                           (const float *)p.dZt, (const float *)p.Xt, dWpart);
+
+    // pass 5
+    hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((G * 2 * 65536 + 255) / 256)), dim3(256), 0, s,
+                       G, L.S, (const float *)dWpart, dWa, dWx);
+    hipLaunchKernelGGL(psum_reduce_kernel, dim3((unsigned)((d.D + 255) / 256)), dim3(256), 0, s, chunks,
+                       (int)d.D, (const float *)p.psum, dcw, dcb, dba, dbx, dLambda);
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int64_t H)
+{
+    return bwd_layout(B, T, D, H, 4).total;   // sized for fp32 I/O, enough for bf16 too
+}
+
+void launch_scan_bwd(const rglru_desc &d, const rglru_weights &w, const void *u, const void *hist_in,
+                     const float *h0, const void *dy, const float *dh_last, void *du, float *dcw,
+                     float *dcb, float *dWa, float *dba, float *dWx, float *dbx, float *dLambda,
+                     float *dh0, void *ws, hipStream_t s)
+{
+    if (d.io == RGLRU_BF16)
+        run_bwd<bf16>(d, w, u, hist_in, h0, dy, dh_last, du, dcw, dcb, dWa, dba, dWx, dbx, dLambda, dh0,
+                      ws, s);
+    else
+        run_bwd<float>(d, w, u, hist_in, h0, dy, dh_last, du, dcw, dcb, dWa, dba, dWx, dbx, dLambda, dh0,
+                       ws, s);
+}
+
+}  // namespace rglru

@@ -1,0 +1,218 @@
+// common.h -- device helpers shared by the RG-LRU kernels (gfx950 only).
+//
+// Layout conventions are those of include/rglru.h.  Activation storage is
+// either float or clang's native __bf16 (bf16 <-> f32 conversions compile to
+// a shift and to v_cvt_pk_bf16_f32, which rounds to nearest even).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/rglru.h"
+
+namespace rglru {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+
+template <typename T> __device__ __forceinline__ float ldf(const T *p) { return to_f32(*p); }
+
+// ------------------------------------------------------------- chunk carries
+// The scan over T is split into chunks of CHUNK tokens.  Each chunk publishes
+// its affine aggregate (A, X) -- the map h_in -> A h_in + X it applies to the
+// state -- and, once known, its inclusive end state.  A chunk finds its start
+// state by walking back over published words (decoupled look-back).  Every
+// word is 64 bits: the low half holds the fp32 value, the high half a tag that
+// is unique to the launch, so a word is either absent or complete and no
+// memory fence is needed.  Stale words from earlier launches carry another tag.
+//
+// The workspace starts with a header of counters; the last workgroup of a
+// launch resets the counters and advances the epoch, so a zero-filled
+// workspace stays reusable.
+struct WsHeader {
+    uint32_t counter;   // next work unit to hand out
+    uint32_t done;      // workgroups finished
+    uint32_t epoch;     // launches completed
+    uint32_t error;     // set if a look-back wait ever gave up
+    uint32_t counter2;  // second-phase counter (backward)
+    uint32_t done2;
+    uint32_t done8[8];  // per-XCD-slot finish counters of persistent launches
+    uint32_t pad[50];
+};
+static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
+
+constexpr int CHUNK = 32;               // tokens per chunk (one 32-row MFMA tile)
+constexpr uint32_t SPIN_LIMIT = 1u << 22;
+
+__device__ __forceinline__ uint32_t tag_of_epoch(uint32_t e) { return (e & 0x7FFFFFFFu) | 0x80000000u; }
+
+__device__ __forceinline__ void put_word(uint64_t *p, float v, uint32_t tag)
+{
+    const uint64_t w = ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v);
+    __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool get_word(const uint64_t *p, uint32_t tag, float &v)
+{
+    const uint64_t w = __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    v = __uint_as_float((uint32_t)w);
+    return (uint32_t)(w >> 32) == tag;
+}
+
+// Every atomic here is relaxed on purpose: no data is published through the
+// counters (each carry word holds its own tag, outputs are read only after
+// the kernel ends), and acquire/release at agent scope would write back and
+// invalidate the whole L2 on every call.
+
+// Take the next work unit and the launch tag (one thread; result via LDS).
+__device__ __forceinline__ void claim_unit(WsHeader *hdr, uint32_t *s_unit, uint32_t *s_tag,
+                                           uint32_t *counter)
+{
+    if (threadIdx.x == 0) {
+        *s_tag = tag_of_epoch(__hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        *s_unit = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+}
+
+// Called once per workgroup at its very end (after a __syncthreads).  The last
+// workgroup of the grid -- the one that sees every other one counted -- resets
+// the counters and advances the epoch; the next launch on the stream starts
+// after this kernel has ended, so it sees the reset header.
+__device__ __forceinline__ void finish_launch(WsHeader *hdr, uint32_t total_groups)
+{
+    if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == total_groups - 1) {
+            __hip_atomic_store(&hdr->counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&hdr->counter2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&hdr->done2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(&hdr->epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// Walk back from chunk `k` (the chunk just before the caller's) until a chunk
+// with a published inclusive state is found, composing published aggregates
+// on the way; chunk -1's end state is `h_before_first`.  Words are indexed
+// base + k * stride; chunks are numbered in the order the scan runs (a
+// reverse scan numbers them from the end of the sequence).  Returns the state
+// at the end of chunk k.  The words of LB_BATCH predecessors are loaded
+// together, so a walk over many published aggregates costs one memory round
+// trip per LB_BATCH chunks.  The walk only waits on chunks that were handed
+// out before the caller's chunk, so it ends once their aggregates are
+// published; a wait that exceeds SPIN_LIMIT polls flags the header and
+// returns NaN rather than hanging.
+constexpr int LB_BATCH = 4;
+
+__device__ __forceinline__ uint64_t load_word(const uint64_t *p)
+{
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float look_back(const uint64_t *aggA, const uint64_t *aggX,
+                                           const uint64_t *incl, long k, long stride,
+                                           float h_before_first, uint32_t tag, WsHeader *hdr)
+{
+    float accA = 1.0f, accX = 0.0f;
+    uint32_t spins = 0;
+    while (k >= 0) {
+        uint64_t wi[LB_BATCH], wa[LB_BATCH], wx[LB_BATCH];
+#pragma unroll
+        for (int j = 0; j < LB_BATCH; ++j) {
+            const long kk = k - j >= 0 ? k - j : 0;
+            wi[j] = load_word(incl + kk * stride);
+            wa[j] = load_word(aggA + kk * stride);
+            wx[j] = load_word(aggX + kk * stride);
+        }
+        int j = 0;
+#pragma unroll
+        for (int jj = 0; jj < LB_BATCH; ++jj) {
+            if (j != jj) continue;             // an earlier slot stopped the walk
+            if (k - jj < 0) return fmaf(accA, h_before_first, accX);
+            if ((uint32_t)(wi[jj] >> 32) == tag) return fmaf(accA, __uint_as_float((uint32_t)wi[jj]), accX);
+            if ((uint32_t)(wa[jj] >> 32) == tag && (uint32_t)(wx[jj] >> 32) == tag) {
+                accX = fmaf(accA, __uint_as_float((uint32_t)wx[jj]), accX);
+                accA = accA * __uint_as_float((uint32_t)wa[jj]);
+                ++j;
+            }
+        }
+        k -= j;
+        if (j == 0) {
+            // chunk k has not published yet: every chunk publishes its aggregate
+            // before its inclusive state, so poll that one word before reloading
+            while ((uint32_t)(load_word(aggX + k * stride) >> 32) != tag) {
+                if (++spins > SPIN_LIMIT) {
+                    __hip_atomic_store(&hdr->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    return __builtin_nanf("");
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+    }
+    return fmaf(accA, h_before_first, accX);
+}
+
+// Finish of a persistent launch: workgroups count themselves in one of 8
+// counters (blockIdx % 8), the last of each group in the top counter, and the
+// very last one resets them and advances the epoch.  Spreading the count over
+// 8 addresses keeps the end-of-launch atomics from queueing on one address.
+__device__ __forceinline__ void finish_persistent(WsHeader *hdr)
+{
+    if (threadIdx.x == 0) {
+        const uint32_t nwg = gridDim.x, grp = blockIdx.x & 7u;
+        const uint32_t in_grp = (nwg - grp + 7u) / 8u;
+        const uint32_t prev = __hip_atomic_fetch_add(&hdr->done8[grp], 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == in_grp - 1u) {
+            __hip_atomic_store(&hdr->done8[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t ngrp = nwg < 8u ? nwg : 8u;
+            const uint32_t p2 = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+            if (p2 == ngrp - 1u) {
+                __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(&hdr->epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t launch_tag(WsHeader *hdr)
+{
+    return tag_of_epoch(__hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// ---------------------------------------------------------------------- math
+// Fast forms on the hardware transcendentals (v_exp_f32 = 2^x, v_rcp_f32,
+// v_sqrt_f32, each within about 1 ulp) for bf16 I/O, where the output rounding
+// (2^-9) dominates; accurate device-library calls for fp32 I/O.
+constexpr float LOG2E = 1.4426950408889634f;
+__device__ __forceinline__ float hw_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
+__device__ __forceinline__ float hw_rcp(float v) { return __builtin_amdgcn_rcpf(v); }
+__device__ __forceinline__ float hw_sqrt(float v) { return __builtin_amdgcn_sqrtf(v); }
+
+// Accurate fp32 helpers (device-library calls).
+__device__ __forceinline__ float sigmoid_acc(float z) { return 1.0f / (1.0f + expf(-z)); }
+__device__ __forceinline__ float softplus_acc(float v)
+{
+    return v > 0.0f ? v + log1pf(expf(-v)) : log1pf(expf(v));
+}
+
+// Token held by row `r` of a 32-row MFMA tile.  The 32x32 output tile gives
+// lane l the column l%32 and the rows 8j + 4(l/32) + i (register 4j + i);
+// mapping row 8j + 4h + i to token 16h + 4j + i makes register k of lane l
+// hold token 16(l/32) + k, so every lane owns 16 consecutive tokens.
+__device__ __forceinline__ int tile_row_token(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
+
+}  // namespace rglru

@@ -1,0 +1,472 @@
+// fwd.hip -- a3..a5: decay, normalisation and the forward scan, with the conv
+// and the gates optionally fused in front (modes A, B, C of rglru_scan_fwd).
+//
+// Page "Griffin Guide: RecurrentGemma, RG-LRU & Hybrid Attention",
+// "Formulation of the RG-LRU Gating Mechanism": gates r, i; decay in log
+// space, log a_t = -c r_t softplus(-Lambda); state update
+// h_t = a_t h_{t-1} + sqrt(1 - a_t^2) (i_t x_t); output y_t = h_t.  The same
+// page's "Custom Linear Scan Kernels" section describes fusing conv, gating,
+// log-decay and the sequential state update into one kernel that keeps h on
+// chip; mode A is that fusion written for CDNA4.
+//
+// Persistent kernel.  One workgroup (8 waves) per CU, launched cooperatively
+// so that every workgroup is resident; workgroup w owns the 256-channel block
+// g = w % G and walks the chunks (32 tokens) of that block in chunk-major
+// order -- unit j = c*B + b, units rank, rank + WPG, ... -- so no per-chunk
+// atomic is needed.  For bf16 the block's gate weights stay in registers for
+// the whole launch (wave w holds W_a and W_x rows 32w..32w+31: 128 VGPRs).
+//
+// Per chunk, lane l = 32*half + n of wave w owns channel d = 256g + 32w + n
+// and the 16 consecutive tokens 32c + 16*half .. +15:
+//   front  1. inputs: the conv over a 19-token window (mode A), x (mode B),
+//             or x, r, i (mode C);
+//          2. modes A/B: x goes to an LDS tile; the gate products come back in
+//             the MFMA output layout, which hands the lane its 16 tokens of
+//             channel d;
+//          3. gates, decay, normalisation; local scan from h = 0 keeping the
+//             running state and running decay product per token;
+//          4. the halves combine across lanes l, l^32 into the chunk's affine
+//             aggregate (A, X), which is published at once;
+//   back   5. one chunk later: the chunk's start state from the decoupled
+//             look-back over earlier chunks of the same (b, g), its end state
+//             published, and y_t = local state + running product * start
+//             state stored.
+// The running state and product of the chunk waiting for its back half sit
+// in LDS, so the look-back of chunk j overlaps the front of chunk j+1.
+//
+// Forward progress: a workgroup publishes a chunk's aggregate before it waits
+// on anything, and every wait is for chunks of smaller unit index, so by
+// induction on the unit index every wait ends.
+#include "common.h"
+#include "gatemath.h"
+#include "internal.h"
+
+namespace rglru {
+
+namespace {
+
+constexpr int PSTRIDE = 36;   // floats per lane in the pending slot (b128, conflict-free)
+
+// Staged input tile (bf16, mode A, interior chunks): tokens 32c-4 .. 32c+31 of
+// the 256 channels of block g, written straight from global memory into LDS
+// by global_load_lds_dwordx4 one chunk ahead.  One wave instruction moves two
+// 512-byte rows (64 lanes x 16 bytes); blocks of two rows are padded to 1040
+// bytes so that rows 16 apart fall in different LDS banks.
+constexpr int ST_BLOCKS = 18, ST_BLK = 1040, ST_BYTES = ST_BLOCKS * ST_BLK;
+
+__device__ __forceinline__ bool stageable(int c, int T) { return c > 0 && (c + 1) * CHUNK <= T; }
+
+__device__ __forceinline__ void stage_issue(const bf16 *in, long row0, int D, int g, char *dst,
+                                            int wave, int lane)
+{
+    for (int i = wave; i < ST_BLOCKS; i += 8) {
+        const long row = row0 + 2 * i + (lane >> 5);
+        const bf16 *src = in + row * D + g * 256 + (lane & 31) * 8;
+        __builtin_amdgcn_global_load_lds((const void *)src,
+                                         (__attribute__((address_space(3))) void *)(dst + i * ST_BLK),
+                                         16, 0, 0);
+    }
+}
+
+// value of channel ch at staged row r (token 32c - 4 + r)
+__device__ __forceinline__ float stage_read(const char *buf, int r, int ch)
+{
+    return (float)*(const bf16 *)(buf + (r >> 1) * ST_BLK + (r & 1) * 512 + ch * 2);
+}
+
+struct FwdParams {
+    int B, T, D, NC, G, WPG;
+    float c;
+    const void *in, *r, *i;
+    const float *cw, *cb;
+    const void *hist_in;
+    const void *Wa, *Wx;
+    const float *ba, *bx, *Lambda, *h0;
+    void *y;
+    float *h_last;
+    void *hist_out;
+    float *hstart_out;   // nullable: state before each chunk, [B][NC][D]
+    WsHeader *hdr;
+    uint64_t *aggA, *aggX, *incl;
+};
+
+// scalars of a chunk whose back half is pending
+struct Pend {
+    int b, c;
+    float A0, X0;      // first half's product and local end state (as seen by half 1)
+    float Ach, Xch;    // chunk aggregate (half 1 lanes)
+};
+
+template <typename T, int MODE>
+__global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
+{
+    constexpr int S = XTile<T>::STRIDE;
+    constexpr bool WREG = (sizeof(T) == 2) && MODE != 2;   // weights held in registers
+    constexpr bool STAGE = (sizeof(T) == 2) && MODE == 0;     // input tile prefetched into LDS
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    T *Xs = (T *)smem;
+    float *pslot_base = (float *)(smem + (MODE == 2 ? 0 : 32 * S * sizeof(T)));
+    char *stage_base = (char *)pslot_base + 512 * PSTRIDE * sizeof(float);
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 31, half = lane >> 5;
+    const int g = blockIdx.x % p.G;
+    const int rank = blockIdx.x / p.G;
+    const int ch = wave * 32 + n;
+    const int d = g * 256 + ch;
+    const bool dv = d < p.D;
+    const uint32_t tag = launch_tag(p.hdr);
+    const T *in = (const T *)p.in;
+    float *pslot = pslot_base + (wave * 64 + lane) * PSTRIDE;
+
+    // per-channel constants
+    float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f, bias = 0.f;
+    if (MODE == 0 && dv) {
+        w0 = p.cw[4 * (long)d + 0];
+        w1 = p.cw[4 * (long)d + 1];
+        w2 = p.cw[4 * (long)d + 2];
+        w3 = p.cw[4 * (long)d + 3];
+        bias = p.cb ? p.cb[d] : 0.0f;
+    }
+    const float ncs = dv ? -p.c * softplus_acc(-p.Lambda[d]) : 0.0f;   // log a_t = ncs r_t
+    const float bav = (MODE != 2 && dv && p.ba) ? p.ba[d] : 0.0f;
+    const float bxv = (MODE != 2 && dv && p.bx) ? p.bx[d] : 0.0f;
+    // fast-path forms: 2^(-log2e (z + b)) and 2^(log2e ncs r)
+    const float kba = -LOG2E * bav, kbx = -LOG2E * bxv, kdec = LOG2E * ncs;
+
+    // gate weights of rows 32*wave .. +31 of block g, as MFMA B operands
+    bf16x8 wa[WREG ? 16 : 1], wx[WREG ? 16 : 1];
+    if constexpr (WREG) {
+        const int r = lane & 31, kg = lane >> 5;
+        const bf16 *pa = (const bf16 *)p.Wa + (size_t)g * 65536 + (size_t)(32 * wave + r) * 256 + 8 * kg;
+        const bf16 *px = (const bf16 *)p.Wx + (size_t)g * 65536 + (size_t)(32 * wave + r) * 256 + 8 * kg;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            wa[s] = *(const bf16x8 *)(pa + 16 * s);
+            wx[s] = *(const bf16x8 *)(px + 16 * s);
+        }
+    }
+
+    const long units = (long)p.B * p.NC;
+    Pend pd = {0, 0, 0.f, 0.f, 0.f, 0.f};
+    bool have_pend = false;
+    int sbuf = 0;   // stage buffer holding the current chunk's tile
+    if constexpr (STAGE) {
+        if (rank < units) {
+            const int c0 = (int)(rank / p.B), b0 = (int)(rank % p.B);
+            if (stageable(c0, p.T))
+                stage_issue((const bf16 *)in, (long)b0 * p.T + (long)c0 * CHUNK - 4, p.D, g, stage_base,
+                            wave, lane);
+        }
+    }
+
+    for (long j = rank;; j += p.WPG) {
+        const bool have = j < units;
+        if (!have && !have_pend) break;
+
+        float hl[16], P[16];
+        Pend cur = {0, 0, 0.f, 0.f, 0.f, 0.f};
+        if (have) {
+            // ------------------------------------------------ front of chunk j
+            const int c = (int)(j / p.B), b = (int)(j % p.B);
+            cur.b = b;
+            cur.c = c;
+            const long row_b = (long)b * p.T;
+            const int tb = c * CHUNK + 16 * half;
+            const bool full = (c + 1) * CHUNK <= p.T;
+            float x[16];
+            if (MODE == 0) {
+                float win[19];
+                bool staged = false;
+                if constexpr (STAGE) {
+                    staged = stageable(c, p.T);
+                    __builtin_amdgcn_s_waitcnt(0);   // this wave's tile loads have landed
+                    __syncthreads();                 // ... and every other wave's; the other
+                                                     // buffer and the x tile are free again
+                    const long jn = j + p.WPG;       // prefetch the next chunk's tile
+                    if (jn < units) {
+                        const int cn = (int)(jn / p.B), bn = (int)(jn % p.B);
+                        if (stageable(cn, p.T))
+                            stage_issue((const bf16 *)in, (long)bn * p.T + (long)cn * CHUNK - 4, p.D, g,
+                                        stage_base + (sbuf ^ 1) * ST_BYTES, wave, lane);
+                    }
+                }
+                if (staged) {
+                    const char *buf = stage_base + sbuf * ST_BYTES;
+#pragma unroll
+                    for (int m = 0; m < 19; ++m) win[m] = stage_read(buf, 16 * half + 1 + m, ch);
+                } else if (full && c > 0 && dv) {
+                    const T *src = in + (row_b + tb - 3) * p.D + d;
+#pragma unroll
+                    for (int m = 0; m < 19; ++m) win[m] = ldf(src + (long)m * p.D);
+                } else {
+#pragma unroll
+                    for (int m = 0; m < 19; ++m) {
+                        const int tau = tb - 3 + m;
+                        float v = 0.0f;
+                        if (dv && tau < p.T) {
+                            if (tau >= 0) v = ldf(in + (row_b + tau) * p.D + d);
+                            else if (p.hist_in)
+                                v = ldf((const T *)p.hist_in + ((long)b * 3 + 3 + tau) * p.D + d);
+                        }
+                        win[m] = v;
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < 16; ++k)
+                    x[k] = fmaf(w3, win[k + 3], fmaf(w2, win[k + 2], fmaf(w1, win[k + 1], fmaf(w0, win[k], bias))));
+            } else {
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    const int t = tb + k;
+                    x[k] = (dv && t < p.T) ? ldf(in + (row_b + t) * p.D + d) : 0.0f;
+                }
+            }
+
+            float za[16], zx[16];
+            if constexpr (MODE != 2) {
+                if constexpr (!STAGE) __syncthreads();   // every wave is done reading the previous tile
+#pragma unroll
+                for (int k = 0; k < 16; ++k) Xs[(16 * half + k) * S + ch] = from_f32<T>(x[k]);
+                __syncthreads();
+                if constexpr (WREG) {
+                    const int r = lane & 31, kg = lane >> 5;
+                    const bf16 *xrow = (const bf16 *)Xs + tile_row_token(r) * S + 8 * kg;
+                    f32x16 A = {}, X = {};
+#pragma unroll
+                    for (int s = 0; s < 16; ++s) {
+                        const bf16x8 av = *(const bf16x8 *)(xrow + 16 * s);
+                        A = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, wa[s], A, 0, 0, 0);
+                        X = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, wx[s], X, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) {
+                        za[k] = A[k];
+                        zx[k] = X[k];
+                    }
+                } else {
+                    gate_tile(Xs, (const T *)p.Wa + (size_t)g * 65536, (const T *)p.Wx + (size_t)g * 65536,
+                              wave, lane, za, zx);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    const int t = tb + k;
+                    const bool ok = dv && t < p.T;
+                    za[k] = ok ? ldf((const T *)p.r + (row_b + t) * p.D + d) : 0.0f;
+                    zx[k] = ok ? ldf((const T *)p.i + (row_b + t) * p.D + d) : 0.0f;
+                }
+            }
+
+            // gates, decay, normalisation, local scan from zero
+            float h = 0.0f, pr = 1.0f;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                float a, bb;
+                if constexpr (sizeof(T) == 2) {
+                    float rr, ii;
+                    if (MODE == 2) {
+                        rr = za[k];
+                        ii = zx[k];
+                    } else {
+                        rr = hw_rcp(1.0f + hw_exp2(fmaf(za[k], -LOG2E, kba)));
+                        ii = hw_rcp(1.0f + hw_exp2(fmaf(zx[k], -LOG2E, kbx)));
+                    }
+                    a = hw_exp2(rr * kdec);
+                    bb = hw_sqrt(fmaf(-a, a, 1.0f)) * ii * x[k];
+                } else {
+                    float rr, ii;
+                    if (MODE == 2) {
+                        rr = za[k];
+                        ii = zx[k];
+                    } else {
+                        rr = sigmoid_acc(za[k] + bav);
+                        ii = sigmoid_acc(zx[k] + bxv);
+                    }
+                    const float l = ncs * rr;
+                    a = expf(l);
+                    bb = sqrtf(-expm1f(2.0f * l)) * ii * x[k];
+                }
+                if (!full && !(dv && tb + k < p.T)) {   // past the end: identity step
+                    a = 1.0f;
+                    bb = 0.0f;
+                }
+                h = fmaf(a, h, bb);
+                pr *= a;
+                hl[k] = h;
+                P[k] = pr;
+            }
+
+            // chunk aggregate, published before anything waits
+            cur.A0 = __shfl_xor(P[15], 32);
+            cur.X0 = __shfl_xor(hl[15], 32);
+            cur.Ach = P[15] * cur.A0;
+            cur.Xch = fmaf(P[15], cur.X0, hl[15]);
+            if (half == 1 && dv) {
+                const long widx = ((long)b * p.NC + c) * p.D + d;
+                put_word(p.aggA + widx, cur.Ach, tag);
+                put_word(p.aggX + widx, cur.Xch, tag);
+            }
+        }
+
+        if (have_pend) {
+            // ------------------------------------------- back of the pending chunk
+            const int b = pd.b, c = pd.c;
+            const long row_b = (long)b * p.T;
+            const int tb = c * CHUNK + 16 * half;
+            float hchunk = 0.0f;   // state before the chunk (half 1 lanes)
+            if (half == 1 && dv) {
+                const long base = (long)b * p.NC * p.D + d;
+                const long widx = base + (long)c * p.D;
+                const float hbefore = p.h0 ? p.h0[(long)b * p.D + d] : 0.0f;
+                hchunk = c == 0 ? hbefore
+                                : look_back(p.aggA + base, p.aggX + base, p.incl + base, c - 1, p.D,
+                                            hbefore, tag, p.hdr);
+                put_word(p.incl + widx, fmaf(pd.Ach, hchunk, pd.Xch), tag);
+                if (p.hstart_out) p.hstart_out[widx] = hchunk;
+            }
+            const float hother = __shfl_xor(hchunk, 32);
+            const float hstart = half == 0 ? hother : fmaf(pd.A0, hchunk, pd.X0);
+            float yl[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 vh = *(const f32x4 *)(pslot + 4 * q);
+                const f32x4 vp = *(const f32x4 *)(pslot + 16 + 4 * q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) yl[4 * q + e] = fmaf(vp[e], hstart, vh[e]);
+            }
+            T *y = (T *)p.y;
+            if (y && dv) {
+                T *dst = y + (row_b + tb) * p.D + d;
+                if ((c + 1) * CHUNK <= p.T) {
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) dst[(long)k * p.D] = from_f32<T>(yl[k]);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 16; ++k)
+                        if (tb + k < p.T) dst[(long)k * p.D] = from_f32<T>(yl[k]);
+                }
+            }
+            if (c == p.NC - 1 && dv) {
+                if (half == 1 && p.h_last) p.h_last[(long)b * p.D + d] = yl[15];
+                if (MODE == 0 && half == 0 && p.hist_out) {
+                    for (int jj = 0; jj < 3; ++jj) {
+                        const int pos = p.T - 3 + jj;
+                        T v = from_f32<T>(0.0f);
+                        if (pos >= 0) v = in[(row_b + pos) * p.D + d];
+                        else if (p.hist_in) v = ((const T *)p.hist_in)[((long)b * 3 + 3 + pos) * p.D + d];
+                        ((T *)p.hist_out)[((long)b * 3 + jj) * p.D + d] = v;
+                    }
+                }
+            }
+        }
+
+        if (have) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                *(f32x4 *)(pslot + 4 * q) = f32x4{hl[4 * q], hl[4 * q + 1], hl[4 * q + 2], hl[4 * q + 3]};
+                *(f32x4 *)(pslot + 16 + 4 * q) = f32x4{P[4 * q], P[4 * q + 1], P[4 * q + 2], P[4 * q + 3]};
+            }
+            pd = cur;
+        }
+        have_pend = have;
+        sbuf ^= 1;
+    }
+    __syncthreads();
+    finish_persistent(p.hdr);
+}
+
+template <typename T, int MODE>
+void launch_mode(FwdParams p, hipStream_t s)
+{
+    const void *fn = (const void *)&fwd_kernel<T, MODE>;
+    const bool stage = sizeof(T) == 2 && MODE == 0;
+    const size_t shmem = (MODE == 2 ? 0 : 32 * XTile<T>::STRIDE * sizeof(T)) + 512 * PSTRIDE * sizeof(float) +
+                         (stage ? 2 * ST_BYTES : 0);
+    static_assert(32 * 260 * 4 + 512 * PSTRIDE * 4 <= 160 * 1024, "LDS budget (fp32)");
+    static_assert(32 * 264 * 2 + 512 * PSTRIDE * 4 + 2 * ST_BYTES <= 160 * 1024, "LDS budget (bf16)");
+    int dev = 0, ncu = 0, occ = 0;
+    // failures here surface through the launch below and hipGetLastError
+    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    (void)hipGetDevice(&dev);
+    (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, 512, shmem);
+    if (occ < 1) occ = 1;
+    if (ncu < 1) ncu = 1;
+    const long units = (long)p.B * p.NC;
+    long wpg = ((long)ncu * occ) / p.G;
+    if (wpg < 1) wpg = 1;
+    if (wpg > units) wpg = units;
+    p.WPG = (int)wpg;
+    void *args[] = {&p};
+    (void)hipLaunchCooperativeKernel(fn, dim3((unsigned)(p.G * wpg)), dim3(512), args, (unsigned)shmem, s);
+}
+
+template <typename T>
+void launch_t(const FwdParams &p, int mode, hipStream_t s)
+{
+    if (mode == 0) launch_mode<T, 0>(p, s);
+    else if (mode == 1) launch_mode<T, 1>(p, s);
+    else launch_mode<T, 2>(p, s);
+}
+
+void run_fwd(const rglru_desc &d, const rglru_weights &w, int mode, const void *in, const void *r,
+             const void *i, const void *hist_in, const float *h0, void *y, float *h_last,
+             void *hist_out, float *hstart_out, void *ws, hipStream_t s)
+{
+    FwdParams p;
+    p.B = (int)d.B;
+    p.T = (int)d.T;
+    p.D = (int)d.D;
+    p.NC = (int)((d.T + CHUNK - 1) / CHUNK);
+    p.G = (int)((d.D + 255) / 256);
+    p.WPG = 1;
+    p.c = d.c;
+    p.in = in;
+    p.r = r;
+    p.i = i;
+    p.cw = w.conv_w;
+    p.cb = w.conv_b;
+    p.hist_in = hist_in;
+    p.Wa = w.W_a;
+    p.Wx = w.W_x;
+    p.ba = w.b_a;
+    p.bx = w.b_x;
+    p.Lambda = w.Lambda;
+    p.h0 = h0;
+    p.y = y;
+    p.h_last = h_last;
+    p.hist_out = hist_out;
+    p.hstart_out = hstart_out;
+    p.hdr = (WsHeader *)ws;
+    const size_t nw = (size_t)d.B * p.NC * d.D;
+    p.aggA = (uint64_t *)((char *)ws + sizeof(WsHeader));
+    p.aggX = p.aggA + nw;
+    p.incl = p.aggX + nw;
+    if (d.io == RGLRU_BF16) launch_t<bf16>(p, mode, s);
+    else launch_t<float>(p, mode, s);
+}
+
+}  // namespace
+
+size_t fwd_workspace_bytes(int64_t B, int64_t T, int64_t D)
+{
+    const int64_t NC = (T + CHUNK - 1) / CHUNK;
+    return sizeof(WsHeader) + 3 * (size_t)B * NC * D * sizeof(uint64_t);
+}
+
+void launch_scan_fwd(const rglru_desc &d, const rglru_weights &w, int mode, const void *in,
+                     const void *r, const void *i, const void *hist_in, const float *h0, void *y,
+                     float *h_last, void *hist_out, void *ws, hipStream_t s)
+{
+    run_fwd(d, w, mode, in, r, i, hist_in, h0, y, h_last, hist_out, nullptr, ws, s);
+}
+
+void launch_fwd_states(const rglru_desc &d, const rglru_weights &w, const void *u,
+                       const void *hist_in, const float *h0, float *hstart_out, void *ws,
+                       hipStream_t s)
+{
+    run_fwd(d, w, 0, u, nullptr, nullptr, hist_in, h0, nullptr, nullptr, nullptr, hstart_out, ws, s);
+}
+
+}  // namespace rglru

@@ -1,0 +1,41 @@
+// internal.h -- launchers behind the C ABI (host side, C++ linkage).
+// Arguments have been validated by api.hip before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/rglru.h"
+
+namespace rglru {
+
+size_t fwd_workspace_bytes(int64_t B, int64_t T, int64_t D);
+size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int64_t H);
+
+void launch_conv1d(const rglru_desc &d, const float *cw, const float *cb, const void *u,
+                   const void *hist_in, void *x, void *hist_out, hipStream_t s);
+
+void launch_gates(const rglru_desc &d, const rglru_weights &w, const void *x, void *r, void *i,
+                  hipStream_t s);
+
+// mode: 0 = conv + gates + scan, 1 = gates + scan, 2 = scan only
+void launch_scan_fwd(const rglru_desc &d, const rglru_weights &w, int mode, const void *in,
+                     const void *r, const void *i, const void *hist_in, const float *h0, void *y,
+                     float *h_last, void *hist_out, void *ws, hipStream_t s);
+
+// mode A forward that stores only the state before every 32-token chunk
+// ([B][NC][D] fp32) -- the first pass of the backward
+void launch_fwd_states(const rglru_desc &d, const rglru_weights &w, const void *u,
+                       const void *hist_in, const float *h0, float *hstart_out, void *ws,
+                       hipStream_t s);
+
+void launch_step(const rglru_desc &d, const rglru_weights &w, const void *u_t, void *hist,
+                 float *h, void *y_t, hipStream_t s);
+
+void launch_scan_bwd(const rglru_desc &d, const rglru_weights &w, const void *u, const void *hist_in,
+                     const float *h0, const void *dy, const float *dh_last, void *du, float *dcw,
+                     float *dcb, float *dWa, float *dba, float *dWx, float *dbx, float *dLambda,
+                     float *dh0, void *ws, hipStream_t s);
+
+}  // namespace rglru

@@ -1,0 +1,174 @@
+/*
+ * rglru.h -- C ABI of the MI355X (gfx950) RG-LRU hot path library
+ * (librglru.so): the causal depthwise Conv1D of width 4 followed by the
+ * Real-Gated Linear Recurrent Unit of Griffin / Hawk / RecurrentGemma.
+ *
+ * The operation (page "Griffin Guide: RecurrentGemma, RG-LRU & Hybrid
+ * Attention", section "Formulation of the RG-LRU Gating Mechanism"):
+ *     r_t = sigma(W_a x_t + b_a)                       recurrence gate
+ *     i_t = sigma(W_x x_t + b_x)                       input gate
+ *     a_t = a^(c r_t),  a = sigma(Lambda),  c = 8      decay, computed as
+ *           log a_t = -c r_t softplus(-Lambda)          (log-space form)
+ *     h_t = a_t h_{t-1} + sqrt(1 - a_t^2) (i_t x_t)     state update
+ *     y_t = h_t                                        output
+ * where x is the output of a causal depthwise convolution of width 4 over
+ * the branch-1 activations u (same page, "Temporal Filtering via Separable
+ * 1D Convolutions"), and W_a, W_x are block-diagonal with square blocks of
+ * width K = D / H (same page, "Block-Diagonal Sharding for
+ * Zero-Communication Tensor Parallelism").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every tensor pointer is DEVICE memory owned by the caller.  The
+ *   library allocates nothing, keeps no global state and never synchronises
+ *   the host: a return of RGLRU_OK means the work was enqueued on `stream`.
+ * Layouts.  Row-major, channel fastest:
+ *     activations u, x, r, i, y, dy, du   [B][T][D]   (dtype desc->io)
+ *     conv history hist                   [B][3][D]   (dtype desc->io)
+ *         hist[b][j] is the pre-conv input at position t-3+j (oldest first)
+ *     state h0, h_last, h, dh_last, dh0   [B][D]      (always fp32)
+ *     conv weight conv_w                  [D][4] fp32; tap k multiplies
+ *                                          u[t-3+k], tap 3 is the current token
+ *     conv bias conv_b, b_a, b_x, Lambda  [D] fp32
+ *     gate weights W_a, W_x               [H][K][K] (dtype desc->io);
+ *         W[h][o][j] multiplies input channel hK+j into output channel hK+o
+ *     gate-weight gradients dW_a, dW_x    [H][K][K] fp32
+ * Dtypes.  desc->io is RGLRU_F32 or RGLRU_BF16 (activations, history and gate
+ *   weights).  State, biases, Lambda, conv weights and every accumulation are
+ *   fp32.
+ * Shapes.  B, T, D, H >= 1, D % H == 0.  Every call that evaluates the gates
+ *   (rglru_gates, rglru_scan_fwd without r/i, rglru_step, rglru_scan_bwd)
+ *   needs K = D / H = 256, the block width of the MFMA gate kernels.
+ *   rglru_conv1d and the scan-only mode of rglru_scan_fwd accept any D.
+ * Alignment.  Every pointer must be 16-byte aligned.
+ * Validation.  All checks run on the host before anything is enqueued; on
+ *   error nothing is enqueued and no output is touched.
+ * Aliasing.  Outputs must not overlap inputs, except hist and h of
+ *   rglru_step, which are read and rewritten in place by design.
+ * Determinism.  The same inputs on the same device give bitwise-identical
+ *   outputs (no floating-point atomics; reductions run in a fixed order).
+ * Numerics.  NaN and Inf in the inputs propagate; they are not trapped.
+ */
+#ifndef RGLRU_H
+#define RGLRU_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { RGLRU_F32 = 0, RGLRU_BF16 = 1 } rglru_dtype;
+
+typedef enum {
+    RGLRU_OK = 0,
+    RGLRU_ERR_NULL = -1,       /* a required pointer is NULL                    */
+    RGLRU_ERR_SHAPE = -2,      /* bad B, T, D, H, K != 256 where needed, T != 1 */
+    RGLRU_ERR_DTYPE = -3,      /* desc->io is not a known rglru_dtype           */
+    RGLRU_ERR_ALIGN = -4,      /* a pointer is not 16-byte aligned              */
+    RGLRU_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than required       */
+    RGLRU_ERR_LAUNCH = -6,     /* the HIP runtime reported a launch error       */
+    RGLRU_ERR_ARG = -7         /* inconsistent arguments (mode, aliasing)       */
+} rglru_status;
+
+/* Problem description.  c is the decay-exponent scale (8 on the pages). */
+typedef struct {
+    int64_t B, T, D, H;
+    int32_t io;        /* rglru_dtype */
+    float c;
+} rglru_desc;
+
+/* Parameters (device pointers).  Which ones a call reads is stated at the call. */
+typedef struct {
+    const float *conv_w;   /* [D][4]  */
+    const float *conv_b;   /* [D], NULL means zero bias */
+    const void *W_a;       /* [H][K][K], dtype io */
+    const float *b_a;      /* [D], NULL means zero */
+    const void *W_x;       /* [H][K][K], dtype io */
+    const float *b_x;      /* [D], NULL means zero */
+    const float *Lambda;   /* [D] */
+} rglru_weights;
+
+enum { RGLRU_OP_SCAN_FWD = 0, RGLRU_OP_SCAN_BWD = 1 };
+
+/* Workspace bytes that rglru_scan_fwd (op RGLRU_OP_SCAN_FWD) or rglru_scan_bwd
+ * (op RGLRU_OP_SCAN_BWD) needs for `desc`.  The workspace carries the chunk
+ * carries of the chunked scan and a small header of counters; it must be
+ * ZERO-FILLED before its first use and is left ready for the next call
+ * (every call restores the header).  One workspace must not be used by two
+ * calls that can run at the same time.  Errors: RGLRU_ERR_NULL, _SHAPE,
+ * _DTYPE, _ARG (unknown op). */
+int rglru_workspace_size(const rglru_desc *desc, int op, size_t *bytes);
+
+/* a1 -- causal depthwise Conv1D of width 4 with bias (section "Temporal
+ * Filtering via Separable 1D Convolutions"; the listing's Conv1d with
+ * padding 3 and one group per channel, first T outputs kept):
+ *     x[b][t][d] = conv_b[d] + sum_{k=0..3} conv_w[d][k] * u[b][t-3+k][d]
+ * Positions t-3+k < 0 read hist_in[b][3+(t-3+k)][d] (zeros if hist_in is
+ * NULL).  hist_out (nullable) receives the pre-conv inputs at positions
+ * T-3, T-2, T-1 bit for bit (for T < 3 partly from hist_in).  Arithmetic is
+ * fp32; x is rounded to io.  Needs conv_w, u, x.  Any D >= 1. */
+int rglru_conv1d(const rglru_desc *desc, const float *conv_w, const float *conv_b,
+                 const void *u, const void *hist_in, void *x, void *hist_out,
+                 hipStream_t stream);
+
+/* a2 -- block-diagonal gates (recurrence-gate and input-gate equations):
+ *     r[b][t][hK+o] = sigma(b_a[hK+o] + sum_j W_a[h][o][j] x[b][t][hK+j])
+ *     i[b][t][hK+o] = sigma(b_x[hK+o] + sum_j W_x[h][o][j] x[b][t][hK+j])
+ * bf16: matrix-core products of bf16 inputs with fp32 accumulation;
+ * fp32: fp32 products and sums.  Reads w->W_a, W_x, b_a, b_x.  K = 256. */
+int rglru_gates(const rglru_desc *desc, const rglru_weights *w, const void *x,
+                void *r, void *i, hipStream_t stream);
+
+/* a3..a5 -- the forward scan (state-update and output equations), i.e. the
+ * listing's RGLRU.forward(x, prev_state) -> (y, last_state), optionally with
+ * the conv fused in front.  The mode follows from the pointers:
+ *   mode A  w->conv_w != NULL, r == i == NULL : `in` is pre-conv u;
+ *           conv + gates + decay + scan in one kernel (K = 256).
+ *   mode B  w->conv_w == NULL, r == i == NULL : `in` is x; gates + scan (K = 256).
+ *   mode C  r and i given (w->conv_w must be NULL) : `in` is x; the decay and
+ *           scan only (any D); only w->Lambda is read.
+ * h0 (nullable, zeros) is the state before token 0; h_last (nullable)
+ * receives h_{T-1}; hist_in / hist_out (nullable, mode A only) carry the conv
+ * history as in rglru_conv1d.  y is rounded to io; the state stays fp32.
+ * T is split into chunks whose carries are combined through the workspace
+ * (see rglru_workspace_size).  Extra errors: RGLRU_ERR_ARG for r without i,
+ * hist with modes B/C, or conv_w with r/i. */
+int rglru_scan_fwd(const rglru_desc *desc, const rglru_weights *w, const void *in,
+                   const void *r, const void *i, const void *hist_in, const float *h0,
+                   void *y, float *h_last, void *hist_out, void *ws, size_t ws_bytes,
+                   hipStream_t stream);
+
+/* a6 -- one decode step for B independent streams (the listing's RGLRU.step,
+ * with the conv history carried in front): desc->T must be 1.
+ *     x = conv_b + conv_w[0] hist[0] + conv_w[1] hist[1] + conv_w[2] hist[2]
+ *                + conv_w[3] u_t
+ *     h <- a h + sqrt(1 - a^2) i x,   y_t = h,   hist <- (hist[1], hist[2], u_t)
+ * hist [B][3][D] (io) and h [B][D] (fp32) are updated in place.  Reads every
+ * field of w (conv_b, b_a, b_x nullable).  K = 256.  512 consecutive calls
+ * equal one rglru_scan_fwd (mode A) over the same 512 tokens. */
+int rglru_step(const rglru_desc *desc, const rglru_weights *w, const void *u_t,
+               void *hist, float *h, void *y_t, hipStream_t stream);
+
+/* a7 -- backward of mode A: gradients of L = <dy, y> + <dh_last, h_last>
+ * with respect to u, conv_w, conv_b, W_a, b_a, W_x, b_x, Lambda and h0 (the
+ * pages state no backward; this is the exact derivative of the forward
+ * above).  dh_last, h0, hist_in and dh0 are nullable.  du is io; every other
+ * gradient is fp32 and is WRITTEN, not accumulated.  The gradient of hist_in
+ * is not produced.  Reads every field of w.  K = 256. */
+int rglru_scan_bwd(const rglru_desc *desc, const rglru_weights *w, const void *u,
+                   const void *hist_in, const float *h0, const void *dy,
+                   const float *dh_last, void *du, float *dconv_w, float *dconv_b,
+                   float *dW_a, float *db_a, float *dW_x, float *db_x, float *dLambda,
+                   float *dh0, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Short English text of a status code (static storage). */
+const char *rglru_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RGLRU_H */

@@ -1,0 +1,147 @@
+"""Host-only checks of the C ABI: the library loads, exports every function that
+include/rglru.h declares, and rejects bad arguments with the documented status
+codes before anything reaches a GPU (validation runs on the host first, so
+none of these calls launches work)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_linear_recurrence_02_amd as glr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rglru.h")
+
+OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, ELAUNCH, EARG = 0, -1, -2, -3, -4, -5, -6, -7
+P = 0x7F0000000000          # a 16-byte aligned fake device address (never dereferenced)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rglru_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(glr.LIB_PATH):
+        import gated_linear_recurrence_02_amd.build as b
+        b.build()
+    return glr.lib()
+
+
+def test_library_exports_every_declared_function(L):
+    names = declared_functions()
+    assert names == sorted(glr.SYMBOLS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def desc(B=2, T=64, D=512, H=2, io=glr.BF16, c=8.0):
+    return glr._Desc(B, T, D, H, io, c)
+
+
+def weights(conv=True):
+    return glr._Weights(P if conv else None, None, P + 0x10000, None, P + 0x20000, None, P + 0x30000)
+
+
+def ws_size(d, op=glr.OP_SCAN_FWD):
+    n = ctypes.c_size_t()
+    rc = glr.lib().rglru_workspace_size(ctypes.byref(d), op, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_status_strings(L):
+    for rc in (OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, ELAUNCH, EARG):
+        assert L.rglru_status_string(rc)
+    assert L.rglru_status_string(123) == b"unknown status"
+
+
+def test_workspace_size(L):
+    rc, n = ws_size(desc())
+    assert rc == OK and n >= 256 + 3 * 2 * 2 * 512 * 8
+    assert ws_size(desc(T=65))[1] > n                      # one more chunk
+    assert ws_size(desc(io=7))[0] == EDTYPE
+    assert ws_size(desc(D=500, H=3))[0] == ESHAPE
+    assert ws_size(desc(T=0))[0] == ESHAPE
+    assert ws_size(desc(), op=9)[0] == EARG
+    assert ws_size(desc(D=768, H=2), op=glr.OP_SCAN_BWD)[0] == ESHAPE   # K = 384
+    assert L.rglru_workspace_size(None, 0, None) == ENULL
+
+
+def test_conv1d_validation(L):
+    d = desc()
+    s = None
+    assert L.rglru_conv1d(None, P, None, P, None, P, None, s) == ENULL
+    assert L.rglru_conv1d(ctypes.byref(d), None, None, P, None, P + 0x100000, None, s) == ENULL
+    assert L.rglru_conv1d(ctypes.byref(d), P + 4, None, P + 0x100000, None, P + 0x200000, None, s) == EALIGN
+    bad = desc(io=5)
+    assert L.rglru_conv1d(ctypes.byref(bad), P, None, P + 0x100000, None, P + 0x200000, None, s) == EDTYPE
+    # x overlapping u
+    assert L.rglru_conv1d(ctypes.byref(d), P, None, P + 0x100000, None, P + 0x100010, None, s) == EARG
+
+
+def test_gates_validation(L):
+    w = weights()
+    s = None
+    d = desc(D=300, H=1)                                  # K != 256
+    assert L.rglru_gates(ctypes.byref(d), ctypes.byref(w), P + 0x1000000, P + 0x2000000, P + 0x3000000, s) == ESHAPE
+    d = desc()
+    assert L.rglru_gates(ctypes.byref(d), None, P, P, P, s) == ENULL
+    assert L.rglru_gates(ctypes.byref(d), ctypes.byref(w), P + 0x1000000, P + 0x1000000, P + 0x3000000, s) == EARG
+
+
+def test_scan_fwd_validation(L):
+    d = desc()
+    rc, n = ws_size(d)
+    w = weights()
+    wb = weights(conv=False)
+    s = None
+    u, y, r, i = P + 0x1000000, P + 0x2000000, P + 0x3000000, P + 0x4000000
+    ws = P + 0x10000000
+    f = L.rglru_scan_fwd
+    assert f(ctypes.byref(d), ctypes.byref(w), u, None, None, None, None, y, None, None, None, n, s) == EWS
+    assert f(ctypes.byref(d), ctypes.byref(w), u, None, None, None, None, y, None, None, ws, n - 1, s) == EWS
+    assert f(ctypes.byref(d), ctypes.byref(w), u, r, None, None, None, y, None, None, ws, n, s) == EARG
+    assert f(ctypes.byref(d), ctypes.byref(w), u, r, i, None, None, y, None, None, ws, n, s) == EARG   # conv + r/i
+    assert f(ctypes.byref(d), ctypes.byref(wb), u, None, None, P, None, y, None, None, ws, n, s) == EARG  # hist in mode B
+    assert f(ctypes.byref(d), ctypes.byref(w), u, None, None, None, None, None, None, None, ws, n, s) == ENULL
+    assert f(ctypes.byref(d), ctypes.byref(w), u + 8, None, None, None, None, y, None, None, ws, n, s) == EALIGN
+    assert f(ctypes.byref(d), ctypes.byref(w), u, None, None, None, None, u, None, None, ws, n, s) == EARG
+    d300 = desc(D=300, H=1)
+    _, n3 = ws_size(d300)
+    assert f(ctypes.byref(d300), ctypes.byref(w), u, None, None, None, None, y, None, None, ws, n3, s) == ESHAPE
+
+
+def test_step_validation(L):
+    d = desc(T=2)
+    w = weights()
+    s = None
+    args = (P + 0x1000000, P + 0x2000000, P + 0x3000000, P + 0x4000000, s)
+    assert L.rglru_step(ctypes.byref(d), ctypes.byref(w), *args) == ESHAPE
+    d = desc(T=1)
+    assert L.rglru_step(ctypes.byref(d), ctypes.byref(weights(conv=False)), *args) == ENULL
+    # h aliasing the history
+    assert L.rglru_step(ctypes.byref(d), ctypes.byref(w), P + 0x1000000, P + 0x2000000, P + 0x2000000,
+                        P + 0x4000000, s) == EARG
+
+
+def test_scan_bwd_validation(L):
+    d = desc()
+    rc, n = ws_size(d, glr.OP_SCAN_BWD)
+    assert rc == OK
+    w = weights()
+    s = None
+    base = [P + k * 0x1000000 for k in range(1, 20)]
+    u, dy, du, dcw, dcb, dWa, dba, dWx, dbx, dL = base[:10]
+    ws = P + 0x100000000
+    f = L.rglru_scan_bwd
+    good = (u, None, None, dy, None, du, dcw, dcb, dWa, dba, dWx, dbx, dL, None)
+    assert f(ctypes.byref(d), ctypes.byref(w), *good, ws, n - 16, s) == EWS
+    bad = list(good)
+    bad[5] = None
+    assert f(ctypes.byref(d), ctypes.byref(w), *bad, ws, n, s) == ENULL
+    bad = list(good)
+    bad[5] = u                                               # du == u
+    assert f(ctypes.byref(d), ctypes.byref(w), *bad, ws, n, s) == EARG

@@ -1,0 +1,90 @@
+"""GPU parity of rglru_step (decode) against the oracle.
+
+The decode workload is B = 256 streams, D = 2560, 512 consecutive one-token
+calls with the fp32 state and the 3-token conv history carried between calls.
+The oracle's prefill over the same 512 tokens is, by definition, the same
+computation (its own step-vs-prefill consistency is pinned on the CPU), so
+every y_t of sampled (stream, block) slices is compared with it, as are the
+final state and history.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_linear_recurrence_02_amd as glr
+import oracle
+import synth
+from problems import TOL, from_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _cmp(name, got, ref, tol):
+    err = oracle.rel_err(got, ref)
+    _say(f"  {name}: err {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= tol, f"{name}: {err} > {tol}"
+
+
+def _decode_run(steps, B=None, sample_streams=(0, 1, 77, 255), sample_heads=(0, 9)):
+    cfg = synth.CONFIGS[3]
+    B = cfg.B if B is None else B
+    D, H = cfg.D, cfg.H
+    params = synth.make_params(cfg.idx, D, H, cfg.io)
+    w = glr.Weights(conv_w=to_dev(params.conv_w, DEV), W_a=to_dev(params.W_a, DEV),
+                    W_x=to_dev(params.W_x, DEV), Lambda=to_dev(params.Lambda, DEV),
+                    conv_b=to_dev(params.conv_b, DEV), b_a=to_dev(params.b_a, DEV),
+                    b_x=to_dev(params.b_x, DEV))
+    hist = torch.zeros((B, 3, D), dtype=torch.bfloat16, device=DEV)
+    h = torch.zeros((B, D), dtype=torch.float32, device=DEV)
+    us, ys = [], []
+    for s in range(steps):
+        u_s = synth.make_activation(cfg.idx, "u", (cfg.B, D), cfg.io, start=s * cfg.B * D)[:B]
+        us.append(u_s)
+        ys.append(glr.step(to_dev(u_s, DEV), w, hist, h).clone())
+    torch.cuda.synchronize()
+    u_seq = np.stack(us, axis=1)                      # [B][steps][D] stored bf16
+    y_seq = torch.stack(ys, dim=1)                    # [B][steps][D]
+    streams = [s for s in sample_streams if s < B]
+    K = D // H
+    for hh in sample_heads:
+        sl = slice(hh * K, (hh + 1) * K)
+        op = dict(conv_w=synth.widen(params.conv_w)[sl], conv_b=synth.widen(params.conv_b)[sl],
+                  W_a=synth.widen(params.W_a)[hh:hh + 1], b_a=synth.widen(params.b_a)[sl],
+                  W_x=synth.widen(params.W_x)[hh:hh + 1], b_x=synth.widen(params.b_x)[sl],
+                  Lambda=synth.widen(params.Lambda)[sl])
+        uo = synth.widen(np.ascontiguousarray(u_seq[streams][:, :, sl]))
+        ry, rh, rho = oracle.fwd(uo, **op)
+        _cmp(f"y[h={hh}]", from_dev(y_seq[streams][:, :, sl]), ry, TOL["bf16"])
+        _cmp(f"h[h={hh}]", from_dev(h[streams][:, sl]), rh, TOL["bf16"])
+        got_hist = hist[streams][:, :, sl].cpu().view(torch.int16).numpy().view(np.uint16)
+        want = np.ascontiguousarray(u_seq[streams][:, -3:, sl]) if steps >= 3 else None
+        if want is not None:
+            assert np.array_equal(got_hist, want)
+    return u_seq, y_seq, w
+
+
+def test_decode_short_all_streams():
+    _say("decode: B=256 D=2560, 8 steps")
+    _decode_run(8)
+
+
+def test_decode_full_512_steps():
+    _say("decode: B=256 D=2560, 512 steps (the decode workload)")
+    _decode_run(512)
+
+
+def test_decode_ragged_stream_count():
+    _say("decode: B=45 (not a multiple of 32), 6 steps")
+    _decode_run(6, B=45, sample_streams=(0, 31, 32, 44))
+
+
+def test_steps_equal_prefill_on_gpu():
+    u_seq, y_seq, w = _decode_run(40, B=64, sample_streams=(0,), sample_heads=(3,))
+    y, hl, ho = glr.scan_fwd(to_dev(u_seq, DEV), w)
+    torch.cuda.synchronize()
+    _cmp("steps vs prefill", from_dev(y_seq), from_dev(y), 1e-2)
