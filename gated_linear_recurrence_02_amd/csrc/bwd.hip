@@ -18,17 +18,24 @@
 //   1. forward states: the mode-A forward kernel keeps only the state before
 //      each 32-token chunk;
 //   2. transposed gate weights Wt[h][j][o'] (o' < 256: W_a, else W_x);
-//   3. the chunk kernel, one (stream, chunk, 256-channel block) per workgroup,
-//      chunks handed out from the END of the sequence: recompute conv, gates
-//      (MFMA), decay and the states inside the chunk; reverse scan whose
-//      chunk carries eps go through the same decoupled look-back as the
-//      forward (chunks numbered from the end); local gradients; dx through
-//      the gates on the matrix cores; conv backward, whose last 3 tokens need
-//      the first 3 dx of the next chunk (published as tagged words); per-chunk
-//      partial sums; dz and x written channel-major for pass 4;
+//   3. the chunk kernel: persistent and cooperatively launched like the
+//      forward, workgroup w owns block g = w % G and walks the (stream,
+//      chunk) units of that block from the END of the sequence (unit
+//      j = cr*B + b with cr the chunk index counted from the end): recompute
+//      conv, gates (MFMA), decay and the states inside the chunk; reverse
+//      scan whose chunk carries eps go through the same decoupled look-back
+//      as the forward; local gradients; dx through the gates on the matrix
+//      cores; conv backward, whose last 3 tokens need the first 3 dx of the
+//      next chunk (published as tagged words); per-chunk partial sums; dz and
+//      x written channel-major in fp32 for pass 4;
 //   4. dW = sum over rows of dz x^T on the matrix cores, split over row
 //      ranges into partials;
 //   5. deterministic reductions of the partials (fixed order, no atomics).
+// Precision (bf16 I/O): products whose operands are computed values (dz, x)
+// use a two-term split v = hi + lo with hi = bf16(v), lo = bf16(v - hi):
+// dx = W^T dz_hi + W^T dz_lo (W is exactly bf16), dW = dz_hi x_hi^T +
+// dz_hi x_lo^T + dz_lo x_hi^T; the bf16 rounding of dz or x alone would
+// cost up to 4e-2 relative on dW for short sequences.
 #include "common.h"
 #include "gatemath.h"
 #include "internal.h"
@@ -60,8 +67,8 @@ BwdLayout bwd_layout(int64_t B, int64_t T, int64_t D, int64_t H, size_t esz)
     L.bwd_words = off;  off = align256(off + 6 * NW * 8);
     L.hstart = off;     off = align256(off + NW * 4);
     L.Wt = off;         off = align256(off + (size_t)H * 256 * 512 * esz);
-    L.dZt = off;        off = align256(off + NW * 64 * esz);
-    L.Xt = off;         off = align256(off + NW * 32 * esz);
+    L.dZt = off;        off = align256(off + NW * 64 * 4);
+    L.Xt = off;         off = align256(off + NW * 32 * 4);
     L.psum = off;       off = align256(off + NW * NSUM * 4);
     L.dWpart = off;     off = align256(off + (size_t)S * H * 2 * 65536 * 4);
     L.total = off;
@@ -88,28 +95,31 @@ __global__ __launch_bounds__(256) void transpose_w_kernel(const T *Wa, const T *
     }
 }
 
-// dx[k] += sum_o Zs[16h+k][o] * Wt_part[j][o] for the lane's channel j = 32w + n
-// (Zs: 32 x 256 tile in the XTile layout; Wt_part rows have stride 512)
-__device__ __forceinline__ void dx_tile(const bf16 *Zs, const bf16 *Wt_part, int wave, int lane,
-                                        float dx[16])
+// dx[k] += sum_o Z[16h+k][o] * Wt_part[j][o] for the lane's channel j = 32w + n,
+// with Z = Zh + Zl (two LDS tiles, 32 x 256 in the XTile layout; Wt_part rows
+// have stride 512)
+__device__ __forceinline__ void dx_tile(const bf16 *Zh, const bf16 *Zl, const bf16 *Wt_part, int wave,
+                                        int lane, float dx[16])
 {
     constexpr int S = XTile<bf16>::STRIDE;
     const int r = lane & 31, kg = lane >> 5;
-    const bf16 *zrow = Zs + tile_row_token(r) * S + 8 * kg;
+    const int off = tile_row_token(r) * S + 8 * kg;
     const bf16 *wrow = Wt_part + (size_t)(32 * wave + r) * 512 + 8 * kg;
     f32x16 C = {};
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
-        const bf16x8 av = *(const bf16x8 *)(zrow + 16 * s);
         const bf16x8 bv = *(const bf16x8 *)(wrow + 16 * s);
-        C = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, C, 0, 0, 0);
+        const bf16x8 ah = *(const bf16x8 *)(Zh + off + 16 * s);
+        const bf16x8 al = *(const bf16x8 *)(Zl + off + 16 * s);
+        C = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bv, C, 0, 0, 0);
+        C = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bv, C, 0, 0, 0);
     }
 #pragma unroll
     for (int k = 0; k < 16; ++k) dx[k] += C[k];
 }
 
-__device__ __forceinline__ void dx_tile(const float *Zs, const float *Wt_part, int wave, int lane,
-                                        float dx[16])
+__device__ __forceinline__ void dx_tile(const float *Zs, const float *, const float *Wt_part, int wave,
+                                        int lane, float dx[16])
 {
     constexpr int S = XTile<float>::STRIDE;
     const int n = lane & 31, half = lane >> 5;
@@ -121,6 +131,15 @@ __device__ __forceinline__ void dx_tile(const float *Zs, const float *Wt_part, i
         for (int k = 0; k < 16; ++k) dx[k] = fmaf(zs[k * S + o], wv, dx[k]);
     }
 }
+
+// write v into the A-operand tiles: hi part (or the value itself for fp32) and lo part
+__device__ __forceinline__ void put_split(bf16 *Zh, bf16 *Zl, int idx, float v)
+{
+    const bf16 hi = (bf16)v;
+    Zh[idx] = hi;
+    Zl[idx] = (bf16)(v - (float)hi);
+}
+__device__ __forceinline__ void put_split(float *Zh, float *, int idx, float v) { Zh[idx] = v; }
 
 __device__ __forceinline__ float wait_word(const uint64_t *p, uint32_t tag, WsHeader *hdr)
 {
@@ -146,8 +165,9 @@ struct BwdParams {
     const float *hstart;
     void *du;
     float *dh0;
-    void *dZt, *Xt;
+    float *dZt, *Xt;
     float *psum;
+    int WPG;
     WsHeader *hdr;
     uint64_t *aggA, *aggX, *incl, *halo;   // halo: 3 consecutive arrays of [B][NC][D]
 };
@@ -157,29 +177,27 @@ template <typename T>
 __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p)
 {
     constexpr int S = XTile<T>::STRIDE;
-    __shared__ __attribute__((aligned(16))) T Xs[32 * S];   // x tile, then dz^a, then dz^x
-    __shared__ uint32_t s_unit, s_tag;
-    claim_unit(p.hdr, &s_unit, &s_tag, &p.hdr->counter);
-    const uint32_t unit = s_unit, tag = s_tag;
-    if (unit >= (uint32_t)p.B * p.NC * p.G) {
-        __syncthreads();
-        finish_launch(p.hdr, gridDim.x);
-        return;
-    }
-    const int g = (int)(unit % p.G);
-    const uint32_t cb_ = unit / p.G;       // chunk-major, from the end of the sequence
-    const int b = (int)(cb_ % p.B);
-    const int cr = (int)(cb_ / p.B);       // chunk index counted from the end
-    const int c = p.NC - 1 - cr;
-
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    T *Xs = (T *)smem;             // x tile, then dz (hi part)
+    T *Zl = Xs + 32 * S;           // dz lo part (bf16 only)
+    const uint32_t tag = launch_tag(p.hdr);
+    const int g = blockIdx.x % p.G;
+    const int rank = blockIdx.x / p.G;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 31, half = lane >> 5;
     const int ch = wave * 32 + n;          // channel inside the block
     const int d = g * 256 + ch;
-    const int tb = c * CHUNK + 16 * half;
     const T *u = (const T *)p.u;
+    const long units = (long)p.B * p.NC;
+
+    for (long j = rank; j < units; j += p.WPG) {
+    const int b = (int)(j % p.B);
+    const int cr = (int)(j / p.B);         // chunk index counted from the end
+    const int c = p.NC - 1 - cr;
+    const int tb = c * CHUNK + 16 * half;
     const long row_b = (long)b * p.T;
     const long cidx = ((long)b * p.NC + c) * p.D + d;   // [B][NC][D] index of this chunk
+    __syncthreads();   // the LDS tiles of the previous unit are free
 
     // conv recompute (window kept for dcw)
     const float w0 = p.cw[4 * (long)d + 0], w1 = p.cw[4 * (long)d + 1];
@@ -205,9 +223,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p)
 #pragma unroll
     for (int k = 0; k < 16; ++k) Xs[(16 * half + k) * S + ch] = from_f32<T>(x[k]);
     {   // x, channel-major per chunk, for the dW products
-        T *xt = (T *)p.Xt + ((((long)b * p.NC + c) * p.G + g) * 256 + ch) * 32 + 16 * half;
+        float *xt = p.Xt + ((((long)b * p.NC + c) * p.G + g) * 256 + ch) * 32 + 16 * half;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) xt[k] = from_f32<T>(x[k]);
+        for (int q = 0; q < 4; ++q)
+            *(f32x4 *)(xt + 4 * q) = f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
     }
     __syncthreads();
     float za[16], zx[16];
@@ -305,26 +324,26 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p)
         hprev = hk;
     }
     {   // dz, channel-major per chunk, for the dW products
-        T *zt = (T *)p.dZt + (((((long)b * p.NC + c) * p.G + g) * 2) * 256 + ch) * 32 + 16 * half;
+        float *zt = p.dZt + (((((long)b * p.NC + c) * p.G + g) * 2) * 256 + ch) * 32 + 16 * half;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            zt[k] = from_f32<T>(za[k]);
-            zt[256 * 32 + k] = from_f32<T>(zx[k]);
+        for (int q = 0; q < 4; ++q) {
+            *(f32x4 *)(zt + 4 * q) = f32x4{za[4 * q], za[4 * q + 1], za[4 * q + 2], za[4 * q + 3]};
+            *(f32x4 *)(zt + 256 * 32 + 4 * q) = f32x4{zx[4 * q], zx[4 * q + 1], zx[4 * q + 2], zx[4 * q + 3]};
         }
     }
 
-    // dx through the gates: two passes over the LDS tile (dz^a, then dz^x)
+    // dx through the gates: two passes over the LDS tiles (dz^a, then dz^x)
     const T *Wt_h = (const T *)p.Wt + (size_t)g * 131072;
     __syncthreads();   // every wave is done with the x tile
 #pragma unroll
-    for (int k = 0; k < 16; ++k) Xs[(16 * half + k) * S + ch] = from_f32<T>(za[k]);
+    for (int k = 0; k < 16; ++k) put_split(Xs, Zl, (16 * half + k) * S + ch, za[k]);
     __syncthreads();
-    dx_tile(Xs, Wt_h, wave, lane, dxv);
+    dx_tile(Xs, Zl, Wt_h, wave, lane, dxv);
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 16; ++k) Xs[(16 * half + k) * S + ch] = from_f32<T>(zx[k]);
+    for (int k = 0; k < 16; ++k) put_split(Xs, Zl, (16 * half + k) * S + ch, zx[k]);
     __syncthreads();
-    dx_tile(Xs, Wt_h + 256, wave, lane, dxv);
+    dx_tile(Xs, Zl, Wt_h + 256, wave, lane, dxv);
 #pragma unroll
     for (int k = 0; k < 16; ++k)
         if (tb + k >= p.T) dxv[k] = 0.0f;
@@ -379,15 +398,30 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p)
         dst[0] = make_float4(v[0], v[1], v[2], v[3]);
         dst[1] = make_float4(v[4], v[5], v[6], v[7]);
     }
+    }   // units
     __syncthreads();
-    finish_launch(p.hdr, gridDim.x);
+    finish_persistent(p.hdr);
 }
 
 // ------------------------------------------------------------------ pass 4
 // dW[q][o][j] over the row range of split s: sum_{units, t} dz_q[o][t] x[j][t].
-// bf16: wave w owns rows o = 32w..32w+31 and all 256 columns (8 MFMA tiles).
-__global__ __launch_bounds__(512) void dw_kernel_bf16(int units, int G, int S, const bf16 *dZt,
-                                                      const bf16 *Xt, float *dWpart)
+// bf16 I/O: wave w owns rows o = 32w..32w+31 and all 256 columns (8 MFMA
+// tiles); both operands are split into bf16 hi + lo on load and three
+// products are accumulated (hi*hi + hi*lo + lo*hi).
+__device__ __forceinline__ void split8(const float *src, bf16x8 &hi, bf16x8 &lo)
+{
+    const f32x4 v0 = *(const f32x4 *)src, v1 = *(const f32x4 *)(src + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        hi[e] = (bf16)v0[e];
+        lo[e] = (bf16)(v0[e] - (float)hi[e]);
+        hi[4 + e] = (bf16)v1[e];
+        lo[4 + e] = (bf16)(v1[e] - (float)hi[4 + e]);
+    }
+}
+
+__global__ __launch_bounds__(512) void dw_kernel_bf16(int units, int G, int S, const float *dZt,
+                                                      const float *Xt, float *dWpart)
 {
     const int g = blockIdx.x / 2, q = blockIdx.x % 2, s = blockIdx.y;
     const int u0 = (int)((long)units * s / S), u1 = (int)((long)units * (s + 1) / S);
@@ -397,15 +431,19 @@ __global__ __launch_bounds__(512) void dw_kernel_bf16(int units, int G, int S, c
 #pragma unroll
     for (int jt = 0; jt < 8; ++jt) acc[jt] = f32x16{};
     for (int un = u0; un < u1; ++un) {
-        const bf16 *zt = dZt + (((long)un * G + g) * 2 + q) * 256 * 32 + (32 * wave + r) * 32 + 8 * kg;
-        const bf16 *xt = Xt + ((long)un * G + g) * 256 * 32 + r * 32 + 8 * kg;
+        const float *zt = dZt + (((long)un * G + g) * 2 + q) * 256 * 32 + (32 * wave + r) * 32 + 8 * kg;
+        const float *xt = Xt + ((long)un * G + g) * 256 * 32 + r * 32 + 8 * kg;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 av = *(const bf16x8 *)(zt + 16 * ks);
+            bf16x8 ah, al;
+            split8(zt + 16 * ks, ah, al);
 #pragma unroll
             for (int jt = 0; jt < 8; ++jt) {
-                const bf16x8 bv = *(const bf16x8 *)(xt + jt * 32 * 32 + 16 * ks);
-                acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[jt], 0, 0, 0);
+                bf16x8 bh, bl;
+                split8(xt + jt * 32 * 32 + 16 * ks, bh, bl);
+                acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc[jt], 0, 0, 0);
+                acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[jt], 0, 0, 0);
+                acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[jt], 0, 0, 0);
             }
         }
     }
@@ -515,23 +553,39 @@ void run_bwd(const rglru_desc &d, const rglru_weights &w, const void *u, const v
     p.hstart = hstart;
     p.du = du;
     p.dh0 = dh0;
-    p.dZt = base + L.dZt;
-    p.Xt = base + L.Xt;
+    p.dZt = (float *)(base + L.dZt);
+    p.Xt = (float *)(base + L.Xt);
     p.psum = (float *)(base + L.psum);
     p.hdr = (WsHeader *)ws;
     p.aggA = (uint64_t *)(base + L.bwd_words);
     p.aggX = p.aggA + NW;
     p.incl = p.aggX + NW;
     p.halo = p.incl + NW;
-    const unsigned units = (unsigned)((size_t)d.B * NC * G);
-    hipLaunchKernelGGL((bwd_chunk_kernel<T>), dim3(units), dim3(512), 0, s, p);
+    {
+        const void *fn = (const void *)&bwd_chunk_kernel<T>;
+        const size_t shmem = 2 * 32 * XTile<T>::STRIDE * sizeof(T);
+        int dev = 0, ncu = 0, occ = 0;
+        (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+        (void)hipGetDevice(&dev);
+        (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, 512, shmem);
+        if (occ < 1) occ = 1;
+        if (ncu < 1) ncu = 1;
+        const long units = (long)d.B * NC;
+        long wpg = ((long)ncu * occ) / G;
+        if (wpg < 1) wpg = 1;
+        if (wpg > units) wpg = units;
+        p.WPG = (int)wpg;
+        void *args[] = {&p};
+        (void)hipLaunchCooperativeKernel(fn, dim3((unsigned)(G * wpg)), dim3(512), args, (unsigned)shmem, s);
+    }
 
     // pass 4
     const int chunks = (int)(d.B * NC);
     float *dWpart = (float *)(base + L.dWpart);
     if (sizeof(T) == 2)
         hipLaunchKernelGGL(dw_kernel_bf16, dim3(2 * G, L.S), dim3(512), 0, s, chunks, G, L.S,
-                           (const bf16 *)p.dZt, (const bf16 *)p.Xt, dWpart);
+                           (const float *)p.dZt, (const float *)p.Xt, dWpart);
     else
         hipLaunchKernelGGL(dw_kernel_f32, dim3(2 * G * 256, L.S), dim3(256), 0, s, chunks, G, L.S,
                            (const float *)p.dZt, (const float *)p.Xt, dWpart);
