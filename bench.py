@@ -1,18 +1,28 @@
 #!/usr/bin/env python
 """Throughput of the RG-LRU hot path on one MI355X.
 
-A step is one rglru_scan_fwd call in mode A (causal conv of width 4 + gates +
-log-space decay + chunked scan, fused) over one batch of the 2B-width prefill
-workload: B = 8 streams, T = 2048 tokens, D = 2560 channels (10 blocks of
-256), bf16 activations and gate weights, fp32 state.  Inputs are seeded
-synthetic data (the generator in synth/), resident in HBM before timing.
-Four input/output buffer sets (672 MB) rotate so that the 256 MB Infinity
-Cache cannot serve a step from the previous one.
+The headline step is one rglru_scan_fwd call in mode A (causal conv of width 4
++ block-diagonal gates + log-space decay + chunked scan, fused in one kernel)
+over one batch of the 2B-width prefill workload: B = 8 streams, T = 2048
+tokens, D = 2560 channels (10 blocks of 256), bf16 activations and gate
+weights, fp32 state.  Inputs are seeded synthetic data (the generator in
+synth/), resident in HBM before timing.  Four input/output buffer sets
+(672 MB) rotate so that the 256 MB Infinity Cache cannot serve a step from
+the previous one.
+
+The other entry points are timed the same way, each on its own workload, and
+reported under "rows": conv1d, gates and the scan stage alone on the 2B-width
+prefill, the fused forward on the 32k-token prefill, 512 decode steps of 256
+streams, and the backward of the 9B-width workload (B = 4, T = 8192,
+D = 4096).
 
 Prints ONE JSON line: tokens*channels/s for the whole job, the dominant
 kernel's achieved algorithmic HBM bandwidth against the 8 TB/s peak (kernel
 durations from HIP events recorded on the launch stream), and the CPU oracle
 timed on a bounded sample of the same workload.
+
+`--copy-calibration` instead times a plain 1 GiB device copy; its hardware
+counters calibrate FETCH_SIZE / WRITE_SIZE for the traffic figure.
 """
 from __future__ import annotations
 
@@ -27,8 +37,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
 KERNEL_SOURCES = ("fwd.hip", "common.h", "gatemath.h")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_fused_2b_prefill_pmc.json")
+ALL_ROWS = ("conv1d", "gates", "scan", "long", "decode", "bwd")
 
 
 def kernel_hash() -> str:
@@ -39,13 +51,17 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(B, T, D, H, esz):
+def fwd_bytes(B, T, D, H, esz):
     """Bytes the fused forward must move: u in, y out, gate weights, per-channel
     parameters (conv taps + bias, b_a, b_x, Lambda), h_last and the conv history."""
     act = 2 * B * T * D * esz
     weights = 2 * H * 256 * 256 * esz
     params = D * (4 + 1 + 1 + 1 + 1) * 4
     return act + weights + params + B * D * 4 + B * 3 * D * esz
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
 
 
 def cpu_baseline(prob, budget_s: float):
@@ -78,6 +94,69 @@ def cpu_baseline(prob, budget_s: float):
                        f"prefill workload ({done} tokens*ch), double precision, {dt:.1f} s")
 
 
+class Timer:
+    """Per-call durations from HIP events recorded on the launch stream."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def calls(self, fn, n, warmup):
+        torch = self.torch
+        for k in range(warmup):
+            fn(k)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        t0 = time.perf_counter()
+        for k in range(n):
+            evs[k][0].record(self.stream)
+            fn(k)
+            evs[k][1].record(self.stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / n
+        return [a.elapsed_time(b) for a, b in evs], wall
+
+    def span(self, fn, n):
+        """One event pair around n back-to-back calls; returns ms per call."""
+        torch = self.torch
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        for k in range(n):
+            fn(k)
+        b.record(self.stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+
+def row(workload, kms, tokch, nbytes, flops=None, note=None, bound="hbm"):
+    import numpy as np
+    ms = float(np.mean(kms)) if isinstance(kms, list) else float(kms)
+    r = {"workload": workload, "kernel_ms": ms, "tokens_ch_per_s": tokch / (ms * 1e-3),
+         "algorithmic_bytes": nbytes, "achieved_gbs": nbytes / (ms * 1e-3) / 1e9,
+         "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bound": bound}
+    if isinstance(kms, list):
+        r["kernel_ms_min"] = float(np.min(kms))
+    if flops is not None:
+        r["algorithmic_flops"] = flops
+        r["achieved_tflops"] = flops / (ms * 1e-3) / 1e12
+        r["mfma_frac_bf16"] = r["achieved_tflops"] / PEAK_BF16_TFLOPS
+    if note:
+        r["note"] = note
+    return r
+
+
+def copy_calibration(torch, dev, n=10):
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    tm = Timer(torch, torch.cuda.current_stream(dev))
+    kms, _ = tm.calls(lambda k: dst.copy_(src), n, 2)
+    import numpy as np
+    ms = float(np.mean(kms))
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "calls": n,
+                      "kernel_ms": ms, "gbs": 2 * nbytes / (ms * 1e-3) / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -85,12 +164,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-extra", action="store_true", help="skip the scan-only line")
+    ap.add_argument("--rows", default=",".join(ALL_ROWS),
+                    help="comma-separated extra rows to time (empty for the headline only): "
+                         + ",".join(ALL_ROWS))
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain 1 GiB device copy and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               f"(this build runs and reports a single MI355X)", file=sys.stderr)
         sys.exit(2)
+    rows = [r for r in args.rows.split(",") if r]
+    for r in rows:
+        if r not in ALL_ROWS:
+            ap.error(f"unknown row {r!r}")
 
     import numpy as np
     import torch
@@ -99,20 +186,30 @@ def main():
     import synth
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+        return
     glr.lib()
-    cfg = synth.CONFIGS[1]
-    B, T, D, H = cfg.B, cfg.T, cfg.D, cfg.H
-    params = synth.make_params(cfg.idx, D, H, cfg.io)
-    u_host = synth.make_u(cfg)
+    stream = torch.cuda.current_stream(dev)
+    tm = Timer(torch, stream)
 
     def dev_t(a):
         if a.dtype == np.uint16:
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    w = glr.Weights(conv_w=dev_t(params.conv_w), W_a=dev_t(params.W_a), W_x=dev_t(params.W_x),
-                    Lambda=dev_t(params.Lambda), conv_b=dev_t(params.conv_b),
-                    b_a=dev_t(params.b_a), b_x=dev_t(params.b_x))
+    def weights(cfg):
+        p = synth.make_params(cfg.idx, cfg.D, cfg.H, cfg.io)
+        w = glr.Weights(conv_w=dev_t(p.conv_w), W_a=dev_t(p.W_a), W_x=dev_t(p.W_x),
+                        Lambda=dev_t(p.Lambda), conv_b=dev_t(p.conv_b),
+                        b_a=dev_t(p.b_a), b_x=dev_t(p.b_x))
+        return p, w
+
+    # ------------------------------------------------ headline: fused forward
+    cfg = synth.CONFIGS[1]
+    B, T, D, H = cfg.B, cfg.T, cfg.D, cfg.H
+    params, w = weights(cfg)
+    u_host = synth.make_u(cfg)
     NSET = 4
     u0 = dev_t(u_host)
     sets = []
@@ -128,24 +225,11 @@ def main():
         s = sets[k % NSET]
         glr.scan_fwd(s["u"], w, out=s["y"], h_last_out=s["h"], hist_out_buf=s["hist"])
 
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        evs[k][0].record(stream)
-        step(k)
-        evs[k][1].record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    kms = [a.elapsed_time(b) for a, b in evs]
+    _say(f"fused forward, 2B-width prefill B={B} T={T} D={D}: {args.warmup} warmup + {args.steps} timed")
+    kms, ms_per_step = tm.calls(step, args.steps, args.warmup)
     kernel_ms = float(np.mean(kms))
     tokch = B * T * D
-    alg = algorithmic_bytes(B, T, D, H, 2)
+    alg = fwd_bytes(B, T, D, H, 2)
     achieved = alg / (kernel_ms * 1e-3) / 1e9
 
     traffic = None
@@ -173,39 +257,120 @@ def main():
                    "global_batch": B, "seq_len": T, "parallelism": "single GPU"},
         "kernel_ms": kernel_ms,
         "kernel_ms_min": float(np.min(kms)),
-        "achieved_hbm_gbs": achieved,
-        "hbm_frac_of_peak": achieved / PEAK_HBM_GBS,
+        "kernel_tokens_ch_per_s": tokch / (kernel_ms * 1e-3),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": "fwd_chunk_kernel<bf16, mode A>",
+                     "kernel": "fwd_kernel<bf16, mode A>",
                      "algorithmic_bytes_per_launch": alg},
+        "rows": {},
     }
 
-    if not args.no_extra:
-        # scan stage alone (mode C): reads x, r, i, writes y -- 8 bytes per token*channel
-        s = sets[0]
-        x, _ = glr.conv1d(s["u"], w.conv_w, w.conv_b, H=H)
-        r, i = glr.gates(x, w)
-        wc = glr.Weights(conv_w=None, W_a=None, W_x=None, Lambda=w.Lambda)
-        yc = torch.empty_like(x)
-        hc = torch.empty((B, D), dtype=torch.float32, device=dev)
-        for _ in range(3):
-            glr.scan_fwd(x, wc, r=r, i=i, out=yc, h_last_out=hc)
+    # ------------------------------------------------ other rows
+    if "conv1d" in rows or "gates" in rows or "scan" in rows:
+        for s in sets:
+            s["x"] = torch.empty_like(s["u"])
+            glr.conv1d(s["u"], w.conv_w, w.conv_b, H=H, out=s["x"], hist_out_buf=s["hist"])
+        if "conv1d" in rows:
+            _say("conv1d alone, 2B-width prefill")
+            kk, _ = tm.calls(lambda k: glr.conv1d(sets[k % NSET]["u"], w.conv_w, w.conv_b, H=H,
+                                                  out=sets[k % NSET]["x"],
+                                                  hist_out_buf=sets[k % NSET]["hist"]), 20, 3)
+            nb = 2 * tokch * 2 + B * 3 * D * 2 + D * 5 * 4
+            out["rows"]["conv1d"] = row("rglru_conv1d, 2B-width prefill (B=8 T=2048 D=2560 bf16)",
+                                        kk, tokch, nb)
+        if "gates" in rows or "scan" in rows:
+            for s in sets[:2]:
+                s["r"], s["i"] = torch.empty_like(s["u"]), torch.empty_like(s["u"])
+        if "gates" in rows:
+            _say("gates alone, 2B-width prefill")
+            kk, _ = tm.calls(lambda k: glr.gates(sets[k % 2]["x"], w, sets[k % 2]["r"],
+                                                 sets[k % 2]["i"]), 20, 3)
+            nb = 3 * tokch * 2 + 2 * H * 65536 * 2 + 2 * D * 4
+            out["rows"]["gates"] = row("rglru_gates, 2B-width prefill (B=8 T=2048 D=2560 bf16)",
+                                       kk, tokch, nb, flops=2 * 2 * 256 * tokch, bound="hbm+mfma")
+        if "scan" in rows:
+            for s in sets[:2]:
+                glr.gates(s["x"], w, s["r"], s["i"])
+            wc = glr.Weights(conv_w=None, W_a=None, W_x=None, Lambda=w.Lambda)
+            _say("scan stage alone (mode C), 2B-width prefill")
+            kk, _ = tm.calls(lambda k: glr.scan_fwd(sets[k % 2]["x"], wc, r=sets[k % 2]["r"],
+                                                    i=sets[k % 2]["i"], out=sets[k % 2]["y"],
+                                                    h_last_out=sets[k % 2]["h"]), 20, 3)
+            nb = 4 * tokch * 2 + D * 4 + B * D * 4
+            out["rows"]["scan"] = row("rglru_scan_fwd mode C (x, r, i given), 2B-width prefill",
+                                      kk, tokch, nb)
+        for s in sets:
+            for key in ("x", "r", "i"):
+                s.pop(key, None)
+    del sets
+    torch.cuda.empty_cache()
+
+    if "long" in rows:
+        c2 = synth.CONFIGS[2]
+        _, w2 = weights(c2)
+        u2 = dev_t(synth.make_u(c2))
+        l_sets = [dict(u=u2 if k == 0 else u2.clone(), y=torch.empty_like(u2),
+                       h=torch.empty((c2.B, c2.D), dtype=torch.float32, device=dev),
+                       hist=torch.empty((c2.B, 3, c2.D), dtype=torch.bfloat16, device=dev))
+                  for k in range(2)]
+        glr.workspace(glr.workspace_size(c2.B, c2.T, c2.D, c2.H, glr.BF16, glr.OP_SCAN_FWD), dev)
+        _say(f"fused forward, long prefill T={c2.T}")
+
+        def lstep(k):
+            s = l_sets[k % 2]
+            glr.scan_fwd(s["u"], w2, out=s["y"], h_last_out=s["h"], hist_out_buf=s["hist"])
+        kk, _ = tm.calls(lstep, 20, 3)
+        t2 = c2.B * c2.T * c2.D
+        out["rows"]["long"] = row(f"rglru_scan_fwd mode A, long prefill (B=1 T={c2.T} D={c2.D} bf16)",
+                                  kk, t2, fwd_bytes(c2.B, c2.T, c2.D, c2.H, 2))
+        del l_sets, u2
+        torch.cuda.empty_cache()
+
+    if "decode" in rows:
+        c3 = synth.CONFIGS[3]
+        _, w3 = weights(c3)
+        n3 = c3.B * c3.D
+        # the decode stream [steps][B][D]; call k reads the slice synth.make_decode_u(c3, k)
+        u_all = dev_t(synth.make_activation(c3.idx, "u", (c3.steps, c3.B, c3.D), c3.io))
+        y_all = torch.empty_like(u_all)
+        h = torch.zeros((c3.B, c3.D), dtype=torch.float32, device=dev)
+        hist = torch.zeros((c3.B, 3, c3.D), dtype=torch.bfloat16, device=dev)
+        _say(f"decode: {c3.steps} steps of B={c3.B} D={c3.D}")
+        for k in range(8):
+            glr.step(u_all[k], w3, hist, h, y_all[k])
+        h.zero_()
+        hist.zero_()
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
-        for a, b_ in ev:
-            a.record(stream)
-            glr.scan_fwd(x, wc, r=r, i=i, out=yc, h_last_out=hc)
-            b_.record(stream)
-        torch.cuda.synchronize()
-        cms = float(np.mean([a.elapsed_time(b_) for a, b_ in ev]))
-        cbytes = 8 * tokch + D * 4 + B * D * 4
-        out["scan_only_mode_c"] = {"kernel_ms": cms, "tokens_ch_per_s": tokch / (cms * 1e-3),
-                                   "achieved_gbs": cbytes / (cms * 1e-3) / 1e9,
-                                   "note": "x, r, i resident and reused (cache-warm), labeled separately"}
-        del x, r, i, yc
+        ms = tm.span(lambda k: glr.step(u_all[k], w3, hist, h, y_all[k]), c3.steps)
+        nb = n3 * (2 + 2 + 4 * 2 + 3 * 2 * 2) + 2 * c3.H * 65536 * 2 + c3.D * 8 * 4
+        out["rows"]["decode"] = row(f"rglru_step, {c3.steps} consecutive calls of B={c3.B} D={c3.D} bf16 "
+                                    f"(time per call)", ms, n3, nb,
+                                    note="state, history and weights (15.7 MB) stay resident in "
+                                         "L2/Infinity Cache between calls; back-to-back launches")
+        del u_all, y_all, h, hist
+        torch.cuda.empty_cache()
+
+    if "bwd" in rows:
+        c4 = synth.CONFIGS[4]
+        _, w4 = weights(c4)
+        u4 = dev_t(synth.make_u(c4))
+        dy4 = dev_t(synth.make_dy(c4))
+        glr.workspace(glr.workspace_size(c4.B, c4.T, c4.D, c4.H, glr.BF16, glr.OP_SCAN_BWD), dev)
+        _say(f"backward, 9B width B={c4.B} T={c4.T} D={c4.D}")
+        kk, _ = tm.calls(lambda k: glr.scan_bwd(u4, w4, dy4), 5, 2)
+        t4 = c4.B * c4.T * c4.D
+        nb = 3 * t4 * 2 + 2 * c4.H * 65536 * (2 + 4) + c4.D * (4 + 1 + 1 + 1 + 1) * 4 * 2
+        out["rows"]["bwd"] = row(f"rglru_scan_bwd, 9B width (B={c4.B} T={c4.T} D={c4.D} bf16), "
+                                 "all passes", kk, t4, nb, flops=3 * 2 * 2 * 256 * t4,
+                                 bound="mfma",
+                                 note="algorithmic flops: gate recompute, dX and dW products "
+                                      "(3 x 1024 per token*ch); executed MFMA work is larger "
+                                      "(split-bf16 operands)")
+        del u4, dy4
+        torch.cuda.empty_cache()
 
     if not args.no_cpu:
+        _say(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(dict(B=B, T=T, D=D, H=H, params=params, u=u_host),
                                            args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -168,30 +168,39 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 
 
 # ----------------------------------------------------------------- entry points
-def conv1d(u: torch.Tensor, conv_w: torch.Tensor, conv_b=None, hist_in=None, H: int = 1):
-    """x = causal depthwise conv of u (width 4).  Returns (x, hist_out)."""
+def conv1d(u: torch.Tensor, conv_w: torch.Tensor, conv_b=None, hist_in=None, H: int = 1,
+           out=None, hist_out_buf=None):
+    """x = causal depthwise conv of u (width 4).  Returns (x, hist_out).
+
+    out / hist_out_buf: optional preallocated outputs."""
     dev = u.device
     _need(u, "u", dev)
     B, T, D = u.shape
     _need(conv_w, "conv_w", dev, torch.float32, (D, 4))
     _need(conv_b, "conv_b", dev, torch.float32, (D,))
     _need(hist_in, "hist_in", dev, u.dtype, (B, 3, D))
-    x = torch.empty_like(u)
-    hist_out = torch.empty((B, 3, D), dtype=u.dtype, device=dev)
+    x = torch.empty_like(u) if out is None else out
+    hist_out = torch.empty((B, 3, D), dtype=u.dtype, device=dev) if hist_out_buf is None else hist_out_buf
+    _need(x, "out", dev, u.dtype, (B, T, D))
+    _need(hist_out, "hist_out_buf", dev, u.dtype, (B, 3, D))
     d = _Desc(B, T, D, H, _io(u), 8.0)
     _check(lib().rglru_conv1d(ctypes.byref(d), _ptr(conv_w), _ptr(conv_b), _ptr(u), _ptr(hist_in),
                               _ptr(x), _ptr(hist_out), _stream(dev)), "rglru_conv1d")
     return x, hist_out
 
 
-def gates(x: torch.Tensor, w: Weights):
-    """(r, i) = (sigmoid(W_a x + b_a), sigmoid(W_x x + b_x)), block-diagonal."""
+def gates(x: torch.Tensor, w: Weights, r_out=None, i_out=None):
+    """(r, i) = (sigmoid(W_a x + b_a), sigmoid(W_x x + b_x)), block-diagonal.
+
+    r_out / i_out: optional preallocated outputs."""
     dev = x.device
     _need(x, "x", dev)
     B, T, D = x.shape
     ws = _weights_struct(w, D, x.dtype, dev, conv=False, gates=True)
-    r = torch.empty_like(x)
-    i = torch.empty_like(x)
+    r = torch.empty_like(x) if r_out is None else r_out
+    i = torch.empty_like(x) if i_out is None else i_out
+    _need(r, "r_out", dev, x.dtype, (B, T, D))
+    _need(i, "i_out", dev, x.dtype, (B, T, D))
     d = _Desc(B, T, D, w.H, _io(x), w.c)
     _check(lib().rglru_gates(ctypes.byref(d), ctypes.byref(ws), _ptr(x), _ptr(r), _ptr(i),
                              _stream(dev)), "rglru_gates")

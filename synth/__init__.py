@@ -36,6 +36,8 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -43,7 +45,8 @@ GOLDEN = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 SEED_BASE = 0x52474C5500000000
-_BLOCK = 1 << 22
+_BLOCK = 1 << 20
+_THREADS = max(1, min(16, os.cpu_count() or 1))
 
 # tensor ids of the per-tensor streams
 TID = dict(u=0, conv_w=1, conv_b=2, W_a=3, W_x=4, lam_u=5, dy=6, h0=7,
@@ -69,25 +72,40 @@ def raw_u64(seed: int, start: int, count: int) -> np.ndarray:
         return _mix(np.uint64(seed) + n * GOLDEN)
 
 
+def _blocks(count: int, fill) -> None:
+    """Run fill(b0, n) over [0, count) in blocks; numpy releases the GIL, so
+    blocks run on several threads.  Every element is a pure function of its
+    index, so the result does not depend on the split."""
+    spans = [(b0, min(_BLOCK, count - b0)) for b0 in range(0, count, _BLOCK)]
+    if len(spans) <= 1:
+        for b0, n in spans:
+            fill(b0, n)
+        return
+    with ThreadPoolExecutor(min(_THREADS, len(spans))) as ex:
+        list(ex.map(lambda sp: fill(*sp), spans))
+
+
 def uniform(seed: int, start: int, count: int) -> np.ndarray:
     """Uniform float64 in [0, 1): element k of the tensor is draw start+k+1."""
     out = np.empty(count, dtype=np.float64)
-    for b0 in range(0, count, _BLOCK):
-        n = min(_BLOCK, count - b0)
+
+    def fill(b0, n):
         z = raw_u64(seed, start + b0, n)
         out[b0:b0 + n] = (z >> np.uint64(11)).astype(np.float64) * 2.0 ** -53
+    _blocks(count, fill)
     return out
 
 
 def normal(seed: int, start: int, count: int) -> np.ndarray:
     """Standard normal float64; element k of the tensor uses draws 2k+1, 2k+2."""
     out = np.empty(count, dtype=np.float64)
-    for b0 in range(0, count, _BLOCK):
-        n = min(_BLOCK, count - b0)
+
+    def fill(b0, n):
         z = raw_u64(seed, 2 * (start + b0), 2 * n)
         u1 = ((z[0::2] >> np.uint64(11)).astype(np.float64) + 1.0) * 2.0 ** -53
         u2 = (z[1::2] >> np.uint64(11)).astype(np.float64) * 2.0 ** -53
         out[b0:b0 + n] = np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * math.pi * u2)
+    _blocks(count, fill)
     return out
 
 
@@ -109,8 +127,15 @@ def store(x64: np.ndarray, io: str) -> np.ndarray:
     """Round float64 values to the storage dtype.
 
     Returns float32 for io='f32' and uint16 bf16 bit patterns for io='bf16'."""
-    f = np.asarray(x64, dtype=np.float64).astype(np.float32)
-    return f if io == "f32" else f32_to_bf16_bits(f)
+    x64 = np.asarray(x64, dtype=np.float64)
+    flat = np.ravel(x64)
+    out = np.empty(flat.size, dtype=np.float32 if io == "f32" else np.uint16)
+
+    def fill(b0, n):
+        f = flat[b0:b0 + n].astype(np.float32)
+        out[b0:b0 + n] = f if io == "f32" else f32_to_bf16_bits(f)
+    _blocks(flat.size, fill)
+    return out.reshape(x64.shape)
 
 
 def widen(stored: np.ndarray) -> np.ndarray:
