@@ -18,10 +18,10 @@
 //   1. forward states: the mode-A forward kernel keeps only the state before
 //      each 32-token chunk;
 //   2. transposed gate weights Wt[h][j][o'] (o' < 256: W_a, else W_x);
-//   3. the chunk kernel: persistent and cooperatively launched like the
-//      forward, workgroup w owns block g = w % G and walks the (stream,
-//      chunk) units of that block from the END of the sequence (unit
-//      j = cr*B + b with cr the chunk index counted from the end): recompute
+//   3. the chunk kernel: persistent like the forward, workgroup w serves
+//      block g = w % G and claims the (stream, chunk) units of that block at
+//      run time, starting from the END of the sequence (unit j = cr*B + b
+//      with cr the chunk index counted from the end): recompute
 //      conv, gates (MFMA), decay and the states inside the chunk; reverse
 //      scan whose chunk carries eps go through the same decoupled look-back
 //      as the forward; local gradients; dx through the gates on the matrix
@@ -36,6 +36,8 @@
 // dx = W^T dz_hi + W^T dz_lo (W is exactly bf16), dW = dz_hi x_hi^T +
 // dz_hi x_lo^T + dz_lo x_hi^T; the bf16 rounding of dz or x alone would
 // cost up to 4e-2 relative on dW for short sequences.
+#include <mutex>
+
 #include "common.h"
 #include "gatemath.h"
 #include "internal.h"
@@ -47,7 +49,7 @@ namespace {
 constexpr int NSUM = 8;   // per-chunk partial sums: dcw[4], dcb, db_a, db_x, dLambda
 
 struct BwdLayout {
-    size_t fwd_words, bwd_words, hstart, Wt, dZt, Xt, psum, dWpart, total;
+    size_t fwd_words, claims, bwd_words, hstart, Wt, dZt, Xt, psum, dWpart, total;
     int S;   // row-range splits of the dW products
 };
 
@@ -63,7 +65,8 @@ BwdLayout bwd_layout(int64_t B, int64_t T, int64_t D, int64_t H, size_t esz)
     if ((int64_t)S > B * NC) S = (int)(B * NC);
     L.S = S;
     size_t off = sizeof(WsHeader);
-    L.fwd_words = off;  off = align256(off + 3 * NW * 8);
+    L.fwd_words = off;  off = align256(fwd_workspace_bytes(B, T, D));   // claims + carry words
+    L.claims = off;     off = align256(off + claim_bytes(H));
     L.bwd_words = off;  off = align256(off + 6 * NW * 8);
     L.hstart = off;     off = align256(off + NW * 4);
     L.Wt = off;         off = align256(off + (size_t)H * 256 * 512 * esz);
@@ -167,8 +170,9 @@ struct BwdParams {
     float *dh0;
     float *dZt, *Xt;
     float *psum;
-    int WPG;
+    int units;          // B * NC per block
     WsHeader *hdr;
+    uint32_t *claim;    // [G] unit counters
     uint64_t *aggA, *aggX, *incl, *halo;   // halo: 3 consecutive arrays of [B][NC][D]
 };
 
@@ -180,24 +184,32 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p)
     extern __shared__ __attribute__((aligned(16))) char smem[];
     T *Xs = (T *)smem;             // x tile, then dz (hi part)
     T *Zl = Xs + 32 * S;           // dz lo part (bf16 only)
+    uint32_t *s_unit = (uint32_t *)(smem + 2 * 32 * S * sizeof(T));   // [2] + flag
     const uint32_t tag = launch_tag(p.hdr);
     const int g = blockIdx.x % p.G;
-    const int rank = blockIdx.x / p.G;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 31, half = lane >> 5;
     const int ch = wave * 32 + n;          // channel inside the block
     const int d = g * 256 + ch;
     const T *u = (const T *)p.u;
-    const long units = (long)p.B * p.NC;
+    const uint32_t units = (uint32_t)p.units;
+    uint32_t *claim = p.claim + g;
 
-    for (long j = rank; j < units; j += p.WPG) {
+    // Unit u_m of this workgroup travels through claim slot m & 1: thread 0
+    // claims u_{n+1} at the start of iteration n and stores it at the end.
+    if (tid == 0) s_unit[0] = claim_next(claim);
+    for (int it = 0;; ++it) {
+    __syncthreads();   // the claim slot and the LDS tiles of the previous unit are free
+    const uint32_t j = s_unit[it & 1];
+    if (j >= units) break;
+    uint32_t my_claim = 0;
+    if (tid == 0) my_claim = claim_next(claim);
     const int b = (int)(j % p.B);
     const int cr = (int)(j / p.B);         // chunk index counted from the end
     const int c = p.NC - 1 - cr;
     const int tb = c * CHUNK + 16 * half;
     const long row_b = (long)b * p.T;
     const long cidx = ((long)b * p.NC + c) * p.D + d;   // [B][NC][D] index of this chunk
-    __syncthreads();   // the LDS tiles of the previous unit are free
 
     // conv recompute (window kept for dcw)
     const float w0 = p.cw[4 * (long)d + 0], w1 = p.cw[4 * (long)d + 1];
@@ -398,9 +410,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p)
         dst[0] = make_float4(v[0], v[1], v[2], v[3]);
         dst[1] = make_float4(v[4], v[5], v[6], v[7]);
     }
+    if (tid == 0) s_unit[(it + 1) & 1] = my_claim;   // read after the next barrier
     }   // units
     __syncthreads();
-    finish_persistent(p.hdr);
+    finish_claimed(p.hdr, p.claim, p.G, s_unit + 2);
 }
 
 // ------------------------------------------------------------------ pass 4
@@ -508,6 +521,35 @@ __global__ __launch_bounds__(256) void psum_reduce_kernel(int units, int D, cons
     dLambda[d] = acc[7];
 }
 
+// Per device: CU count and resident workgroups per CU of the chunk kernel,
+// looked up once.
+struct LaunchShape {
+    int ncu = 0, occ = 0;
+};
+
+template <typename T>
+LaunchShape bwd_shape(size_t shmem)
+{
+    static std::mutex mu;
+    static LaunchShape cache[64];
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev < 0 || dev >= 64) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    LaunchShape &ls = cache[dev];
+    if (ls.ncu == 0) {
+        const void *fn = (const void *)&bwd_chunk_kernel<T>;
+        int ncu = 0, occ = 0;
+        // failures here surface through the launch and hipGetLastError
+        (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+        (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, 512, shmem);
+        ls.ncu = ncu < 1 ? 1 : ncu;
+        ls.occ = occ < 1 ? 1 : occ;
+    }
+    return ls;
+}
+
 template <typename T>
 void run_bwd(const rglru_desc &d, const rglru_weights &w, const void *u, const void *hist_in,
              const float *h0, const void *dy, const float *dh_last, void *du, float *dcw, float *dcb,
@@ -557,27 +599,19 @@ void run_bwd(const rglru_desc &d, const rglru_weights &w, const void *u, const v
     p.Xt = (float *)(base + L.Xt);
     p.psum = (float *)(base + L.psum);
     p.hdr = (WsHeader *)ws;
+    p.claim = (uint32_t *)(base + L.claims);
+    p.units = (int)(d.B * NC);
     p.aggA = (uint64_t *)(base + L.bwd_words);
     p.aggX = p.aggA + NW;
     p.incl = p.aggX + NW;
     p.halo = p.incl + NW;
     {
-        const void *fn = (const void *)&bwd_chunk_kernel<T>;
-        const size_t shmem = 2 * 32 * XTile<T>::STRIDE * sizeof(T);
-        int dev = 0, ncu = 0, occ = 0;
-        (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-        (void)hipGetDevice(&dev);
-        (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, 512, shmem);
-        if (occ < 1) occ = 1;
-        if (ncu < 1) ncu = 1;
-        const long units = (long)d.B * NC;
-        long wpg = ((long)ncu * occ) / G;
+        const size_t shmem = 2 * 32 * XTile<T>::STRIDE * sizeof(T) + 16;
+        const LaunchShape ls = bwd_shape<T>(shmem);
+        long wpg = ((long)ls.ncu * ls.occ) / G;   // workgroups per block
         if (wpg < 1) wpg = 1;
-        if (wpg > units) wpg = units;
-        p.WPG = (int)wpg;
-        void *args[] = {&p};
-        (void)hipLaunchCooperativeKernel(fn, dim3((unsigned)(G * wpg)), dim3(512), args, (unsigned)shmem, s);
+        if (wpg > p.units) wpg = p.units;
+        bwd_chunk_kernel<T><<<dim3((unsigned)(G * wpg)), dim3(512), shmem, s>>>(p);
     }
 
     // pass 4

@@ -38,12 +38,12 @@ template <typename T> __device__ __forceinline__ float ldf(const T *p) { return 
 // launch resets the counters and advances the epoch, so a zero-filled
 // workspace stays reusable.
 struct WsHeader {
-    uint32_t counter;   // next work unit to hand out
+    uint32_t counter;   // unused
     uint32_t done;      // workgroups finished
     uint32_t epoch;     // launches completed
     uint32_t error;     // set if a look-back wait ever gave up
-    uint32_t counter2;  // second-phase counter (backward)
-    uint32_t done2;
+    uint32_t counter2;  // unused
+    uint32_t done2;     // unused
     uint32_t done8[8];  // per-XCD-slot finish counters of persistent launches
     uint32_t pad[50];
 };
@@ -73,40 +73,11 @@ __device__ __forceinline__ bool get_word(const uint64_t *p, uint32_t tag, float 
 // the kernel ends), and acquire/release at agent scope would write back and
 // invalidate the whole L2 on every call.
 
-// Take the next work unit and the launch tag (one thread; result via LDS).
-__device__ __forceinline__ void claim_unit(WsHeader *hdr, uint32_t *s_unit, uint32_t *s_tag,
-                                           uint32_t *counter)
-{
-    if (threadIdx.x == 0) {
-        *s_tag = tag_of_epoch(__hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        *s_unit = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-}
-
-// Called once per workgroup at its very end (after a __syncthreads).  The last
-// workgroup of the grid -- the one that sees every other one counted -- resets
-// the counters and advances the epoch; the next launch on the stream starts
-// after this kernel has ended, so it sees the reset header.
-__device__ __forceinline__ void finish_launch(WsHeader *hdr, uint32_t total_groups)
-{
-    if (threadIdx.x == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        if (prev == total_groups - 1) {
-            __hip_atomic_store(&hdr->counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&hdr->counter2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&hdr->done2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_fetch_add(&hdr->epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-}
-
 // Walk back from chunk `k` (the chunk just before the caller's) until a chunk
 // with a published inclusive state is found, composing published aggregates
-// on the way; chunk -1's end state is `h_before_first`.  Words are indexed
-// base + k * stride; chunks are numbered in the order the scan runs (a
+// on the way; chunk -1's end state is `h_before_first`.  (accA, accX) is the
+// composition of the chunks after k already walked over (identity by
+// default).  Words are indexed base + k * stride; chunks are numbered in the order the scan runs (a
 // reverse scan numbers them from the end of the sequence).  Returns the state
 // at the end of chunk k.  The words of LB_BATCH predecessors are loaded
 // together, so a walk over many published aggregates costs one memory round
@@ -123,9 +94,9 @@ __device__ __forceinline__ uint64_t load_word(const uint64_t *p)
 
 __device__ __forceinline__ float look_back(const uint64_t *aggA, const uint64_t *aggX,
                                            const uint64_t *incl, long k, long stride,
-                                           float h_before_first, uint32_t tag, WsHeader *hdr)
+                                           float h_before_first, uint32_t tag, WsHeader *hdr,
+                                           float accA = 1.0f, float accX = 0.0f)
 {
-    float accA = 1.0f, accX = 0.0f;
     uint32_t spins = 0;
     while (k >= 0) {
         uint64_t wi[LB_BATCH], wa[LB_BATCH], wx[LB_BATCH];
@@ -186,6 +157,60 @@ __device__ __forceinline__ void finish_persistent(WsHeader *hdr)
             }
         }
     }
+}
+
+// Work claimed at run time.  Kernels launched without a co-residency
+// guarantee take their work units from per-group counters (relaxed
+// fetch-add, one thread per workgroup) and process them in claim order; a
+// unit only ever waits on units claimed before it, by workgroups that are
+// already running, so every wait ends whatever the number of resident
+// workgroups.  The counters live in the workspace after the header.
+__device__ __forceinline__ uint32_t claim_next(uint32_t *ctr)
+{
+    return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// End of a launch whose work was claimed from `nclaims` counters: called by
+// every thread after a __syncthreads.  Workgroups count themselves as in
+// finish_persistent; the last one zeroes the claim counters (all threads of
+// it) and advances the epoch.  `s_flag` is one word of LDS.
+__device__ __forceinline__ void finish_claimed(WsHeader *hdr, uint32_t *claims, int nclaims,
+                                               uint32_t *s_flag)
+{
+    if (threadIdx.x == 0) {
+        uint32_t last = 0;
+        const uint32_t nwg = gridDim.x, grp = blockIdx.x & 7u;
+        const uint32_t in_grp = (nwg - grp + 7u) / 8u;
+        const uint32_t prev = __hip_atomic_fetch_add(&hdr->done8[grp], 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == in_grp - 1u) {
+            __hip_atomic_store(&hdr->done8[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t ngrp = nwg < 8u ? nwg : 8u;
+            const uint32_t p2 = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+            last = p2 == ngrp - 1u;
+        }
+        *s_flag = last;
+    }
+    __syncthreads();
+    if (*s_flag) {
+        for (int i = threadIdx.x; i < nclaims; i += blockDim.x)
+            __hip_atomic_store(&claims[i], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x == 0) {
+            __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(&hdr->epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// Workspace bytes of the claim counters of `n` groups (a multiple of 256).
+inline size_t claim_bytes(int64_t n) { return (size_t)((n * 4 + 255) / 256) * 256; }
+
+// Element `e` of an array whose base is the same for the whole wave: the
+// 32-bit byte offset lets the compiler use scalar-base addressing.
+template <typename T> __device__ __forceinline__ T *at(T *base, uint32_t e)
+{
+    return (T *)((char *)base + e * (uint32_t)sizeof(T));
 }
 
 __device__ __forceinline__ uint32_t launch_tag(WsHeader *hdr)

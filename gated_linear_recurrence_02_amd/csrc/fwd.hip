@@ -9,34 +9,39 @@
 // log-decay and the sequential state update into one kernel that keeps h on
 // chip; mode A is that fusion written for CDNA4.
 //
-// Persistent kernel.  One workgroup (8 waves) per CU, launched cooperatively
-// so that every workgroup is resident; workgroup w owns the 256-channel block
-// g = w % G and walks the chunks (32 tokens) of that block in chunk-major
-// order -- unit j = c*B + b, units rank, rank + WPG, ... -- so no per-chunk
-// atomic is needed.  For bf16 the block's gate weights stay in registers for
-// the whole launch (wave w holds W_a and W_x rows 32w..32w+31: 128 VGPRs).
+// Persistent kernel, one workgroup (8 waves) per CU.  Workgroup w serves the
+// 256-channel block g = w % G; for bf16 the block's gate weights stay in
+// registers for the whole launch (wave w holds W_a and W_x rows 32w..32w+31:
+// 128 VGPRs).  Work units are chunks of 32 tokens of one stream, numbered
+// chunk-major inside the block (unit q = c*B + b) and claimed at run time from
+// the block's counter, one unit ahead, so the launch needs no co-residency
+// guarantee and no cooperative launch.
 //
-// Per chunk, lane l = 32*half + n of wave w owns channel d = 256g + 32w + n
-// and the 16 consecutive tokens 32c + 16*half .. +15:
-//   front  1. inputs: the conv over a 19-token window (mode A), x (mode B),
-//             or x, r, i (mode C);
+// Per unit, lane l = 32*half + n of wave w owns channel d = 256g + 32w + n and
+// the 16 consecutive tokens 32c + 16*half .. +15:
+//   front  1. inputs: the conv over a 19-token window (mode A; interior bf16
+//             chunks read a tile that global_load_lds brought into LDS one
+//             unit ahead), x (mode B), or x, r, i (mode C);
 //          2. modes A/B: x goes to an LDS tile; the gate products come back in
 //             the MFMA output layout, which hands the lane its 16 tokens of
 //             channel d;
 //          3. gates, decay, normalisation; local scan from h = 0 keeping the
 //             running state and running decay product per token;
-//          4. the halves combine across lanes l, l^32 into the chunk's affine
+//          4. the halves combine across lanes l, l^32 into the unit's affine
 //             aggregate (A, X), which is published at once;
-//   back   5. one chunk later: the chunk's start state from the decoupled
+//   back   5. one unit later: the unit's start state from the decoupled
 //             look-back over earlier chunks of the same (b, g), its end state
 //             published, and y_t = local state + running product * start
 //             state stored.
-// The running state and product of the chunk waiting for its back half sit
-// in LDS, so the look-back of chunk j overlaps the front of chunk j+1.
+// The running state and product of the unit waiting for its back half sit in
+// LDS, so the look-back of unit j overlaps the front of the next unit.
 //
-// Forward progress: a workgroup publishes a chunk's aggregate before it waits
-// on anything, and every wait is for chunks of smaller unit index, so by
-// induction on the unit index every wait ends.
+// Forward progress: a workgroup publishes a unit's aggregate before it waits
+// on anything, processes its units in claim order, and every wait is for a
+// unit of the same block with a smaller index, which was claimed earlier by a
+// running workgroup; by induction on the unit index every wait ends.
+#include <mutex>
+
 #include "common.h"
 #include "gatemath.h"
 #include "internal.h"
@@ -75,7 +80,7 @@ __device__ __forceinline__ float stage_read(const char *buf, int r, int ch)
 }
 
 struct FwdParams {
-    int B, T, D, NC, G, WPG;
+    int B, T, D, NC, G, units;
     float c;
     const void *in, *r, *i;
     const float *cw, *cb;
@@ -87,6 +92,7 @@ struct FwdParams {
     void *hist_out;
     float *hstart_out;   // nullable: state before each chunk, [B][NC][D]
     WsHeader *hdr;
+    uint32_t *claim;
     uint64_t *aggA, *aggX, *incl;
 };
 
@@ -111,7 +117,12 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 31, half = lane >> 5;
     const int g = blockIdx.x % p.G;
-    const int rank = blockIdx.x / p.G;
+    uint32_t *s_unit = (uint32_t *)(stage_base + (STAGE ? 2 * ST_BYTES : 0));   // 2 claim slots, flag
+    uint32_t *claim = p.claim + g;
+    if (tid == 0) {
+        s_unit[0] = claim_next(claim);
+        s_unit[1] = claim_next(claim);
+    }
     const int ch = wave * 32 + n;
     const int d = g * 256 + ch;
     const bool dv = d < p.D;
@@ -147,25 +158,38 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
         }
     }
 
-    const long units = (long)p.B * p.NC;
+    const uint32_t units = (uint32_t)p.units;
     Pend pd = {0, 0, 0.f, 0.f, 0.f, 0.f};
     bool have_pend = false;
-    int sbuf = 0;   // stage buffer holding the current chunk's tile
+    // Unit u_m of this workgroup travels through claim slot m & 1: thread 0
+    // claims u_{n+2} during iteration n and stores it at the end of the
+    // iteration; every thread reads u_{n+1} after the first barrier of
+    // iteration n.  The parity of n also selects the stage buffer.
+    __syncthreads();
+    uint32_t j = s_unit[0];
+    uint32_t t0_next = s_unit[1];   // thread 0 only: the latest unit it claimed
+    int it = 0;
     if constexpr (STAGE) {
-        if (rank < units) {
-            const int c0 = (int)(rank / p.B), b0 = (int)(rank % p.B);
+        if (j < units) {
+            const int c0 = (int)(j / p.B), b0 = (int)(j % p.B);
             if (stageable(c0, p.T))
                 stage_issue((const bf16 *)in, (long)b0 * p.T + (long)c0 * CHUNK - 4, p.D, g, stage_base,
                             wave, lane);
         }
     }
 
-    for (long j = rank;; j += p.WPG) {
+    for (;;) {
         const bool have = j < units;
         if (!have && !have_pend) break;
+        uint32_t my_claim = 0xFFFFFFFFu;
+        if (tid == 0 && t0_next < units) my_claim = claim_next(claim);
 
         float hl[16], P[16];
         Pend cur = {0, 0, 0.f, 0.f, 0.f, 0.f};
+        if constexpr (STAGE) __builtin_amdgcn_s_waitcnt(0);   // this wave's tile loads have landed
+        __syncthreads();   // ... and every wave's; the other stage buffer, the x tile and
+                           // the claim slot read last time are free again
+        const uint32_t jn = s_unit[(it + 1) & 1];   // u_{n+1}
         if (have) {
             // ------------------------------------------------ front of chunk j
             const int c = (int)(j / p.B), b = (int)(j % p.B);
@@ -180,19 +204,15 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
                 bool staged = false;
                 if constexpr (STAGE) {
                     staged = stageable(c, p.T);
-                    __builtin_amdgcn_s_waitcnt(0);   // this wave's tile loads have landed
-                    __syncthreads();                 // ... and every other wave's; the other
-                                                     // buffer and the x tile are free again
-                    const long jn = j + p.WPG;       // prefetch the next chunk's tile
-                    if (jn < units) {
+                    if (jn < units) {   // prefetch the next unit's tile
                         const int cn = (int)(jn / p.B), bn = (int)(jn % p.B);
                         if (stageable(cn, p.T))
                             stage_issue((const bf16 *)in, (long)bn * p.T + (long)cn * CHUNK - 4, p.D, g,
-                                        stage_base + (sbuf ^ 1) * ST_BYTES, wave, lane);
+                                        stage_base + ((it + 1) & 1) * ST_BYTES, wave, lane);
                     }
                 }
                 if (staged) {
-                    const char *buf = stage_base + sbuf * ST_BYTES;
+                    const char *buf = stage_base + (it & 1) * ST_BYTES;
 #pragma unroll
                     for (int m = 0; m < 19; ++m) win[m] = stage_read(buf, 16 * half + 1 + m, ch);
                 } else if (full && c > 0 && dv) {
@@ -225,7 +245,6 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
 
             float za[16], zx[16];
             if constexpr (MODE != 2) {
-                if constexpr (!STAGE) __syncthreads();   // every wave is done reading the previous tile
 #pragma unroll
                 for (int k = 0; k < 16; ++k) Xs[(16 * half + k) * S + ch] = from_f32<T>(x[k]);
                 __syncthreads();
@@ -370,36 +389,68 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
             pd = cur;
         }
         have_pend = have;
-        sbuf ^= 1;
+        if (tid == 0) {   // u_{n+2}, read after the first barrier of the next iteration
+            s_unit[it & 1] = my_claim;
+            t0_next = my_claim;
+        }
+        j = jn;
+        ++it;
     }
     __syncthreads();
-    finish_persistent(p.hdr);
+    finish_claimed(p.hdr, p.claim, p.G, s_unit + 2);
+}
+
+template <typename T, int MODE>
+size_t fwd_lds_bytes()
+{
+    const bool stage = sizeof(T) == 2 && MODE == 0;
+    return (MODE == 2 ? 0 : 32 * XTile<T>::STRIDE * sizeof(T)) + 512 * PSTRIDE * sizeof(float) +
+           (stage ? 2 * ST_BYTES : 0) + 16;
+}
+
+// Per device: CU count and resident workgroups per CU of one kernel, looked
+// up once (the attribute call and the occupancy query cost host time).
+struct LaunchShape {
+    int ncu = 0, occ = 0;
+};
+
+template <typename T, int MODE>
+LaunchShape fwd_shape()
+{
+    static std::mutex mu;
+    static LaunchShape cache[64];
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev < 0 || dev >= 64) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    LaunchShape &ls = cache[dev];
+    if (ls.ncu == 0) {
+        const void *fn = (const void *)&fwd_kernel<T, MODE>;
+        const size_t shmem = fwd_lds_bytes<T, MODE>();
+        int ncu = 0, occ = 0;
+        // failures here surface through the launch and hipGetLastError
+        (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+        (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, 512, shmem);
+        ls.ncu = ncu < 1 ? 1 : ncu;
+        ls.occ = occ < 1 ? 1 : occ;
+    }
+    return ls;
 }
 
 template <typename T, int MODE>
 void launch_mode(FwdParams p, hipStream_t s)
 {
-    const void *fn = (const void *)&fwd_kernel<T, MODE>;
-    const bool stage = sizeof(T) == 2 && MODE == 0;
-    const size_t shmem = (MODE == 2 ? 0 : 32 * XTile<T>::STRIDE * sizeof(T)) + 512 * PSTRIDE * sizeof(float) +
-                         (stage ? 2 * ST_BYTES : 0);
-    static_assert(32 * 260 * 4 + 512 * PSTRIDE * 4 <= 160 * 1024, "LDS budget (fp32)");
-    static_assert(32 * 264 * 2 + 512 * PSTRIDE * 4 + 2 * ST_BYTES <= 160 * 1024, "LDS budget (bf16)");
-    int dev = 0, ncu = 0, occ = 0;
-    // failures here surface through the launch below and hipGetLastError
-    (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-    (void)hipGetDevice(&dev);
-    (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, 512, shmem);
-    if (occ < 1) occ = 1;
-    if (ncu < 1) ncu = 1;
-    const long units = (long)p.B * p.NC;
-    long wpg = ((long)ncu * occ) / p.G;
+    static_assert(32 * 260 * 4 + 512 * PSTRIDE * 4 + 16 <= 160 * 1024, "LDS budget (fp32)");
+    static_assert(32 * 264 * 2 + 512 * PSTRIDE * 4 + 2 * ST_BYTES + 16 <= 160 * 1024, "LDS budget (bf16)");
+    const LaunchShape ls = fwd_shape<T, MODE>();
+    // workgroups per block: fill the resident slots, never more than the units
+    long wpg = ((long)ls.ncu * ls.occ) / p.G;
     if (wpg < 1) wpg = 1;
-    if (wpg > units) wpg = units;
-    p.WPG = (int)wpg;
-    void *args[] = {&p};
-    (void)hipLaunchCooperativeKernel(fn, dim3((unsigned)(p.G * wpg)), dim3(512), args, (unsigned)shmem, s);
+    if (wpg > p.units) wpg = p.units;
+    const long grid = (long)p.G * wpg;
+    const size_t shmem = fwd_lds_bytes<T, MODE>();
+    fwd_kernel<T, MODE><<<dim3((unsigned)grid), dim3(512), shmem, s>>>(p);
 }
 
 template <typename T>
@@ -420,7 +471,7 @@ void run_fwd(const rglru_desc &d, const rglru_weights &w, int mode, const void *
     p.D = (int)d.D;
     p.NC = (int)((d.T + CHUNK - 1) / CHUNK);
     p.G = (int)((d.D + 255) / 256);
-    p.WPG = 1;
+    p.units = p.B * p.NC;
     p.c = d.c;
     p.in = in;
     p.r = r;
@@ -439,8 +490,9 @@ void run_fwd(const rglru_desc &d, const rglru_weights &w, int mode, const void *
     p.hist_out = hist_out;
     p.hstart_out = hstart_out;
     p.hdr = (WsHeader *)ws;
+    p.claim = (uint32_t *)((char *)ws + sizeof(WsHeader));
     const size_t nw = (size_t)d.B * p.NC * d.D;
-    p.aggA = (uint64_t *)((char *)ws + sizeof(WsHeader));
+    p.aggA = (uint64_t *)((char *)ws + sizeof(WsHeader) + claim_bytes(p.G));
     p.aggX = p.aggA + nw;
     p.incl = p.aggX + nw;
     if (d.io == RGLRU_BF16) launch_t<bf16>(p, mode, s);
@@ -451,8 +503,8 @@ void run_fwd(const rglru_desc &d, const rglru_weights &w, int mode, const void *
 
 size_t fwd_workspace_bytes(int64_t B, int64_t T, int64_t D)
 {
-    const int64_t NC = (T + CHUNK - 1) / CHUNK;
-    return sizeof(WsHeader) + 3 * (size_t)B * NC * D * sizeof(uint64_t);
+    const int64_t NC = (T + CHUNK - 1) / CHUNK, G = (D + 255) / 256;
+    return sizeof(WsHeader) + claim_bytes(G) + 3 * (size_t)B * NC * D * sizeof(uint64_t);
 }
 
 void launch_scan_fwd(const rglru_desc &d, const rglru_weights &w, int mode, const void *in,
