@@ -42,11 +42,24 @@
  *   rglru_conv1d and the scan-only mode of rglru_scan_fwd accept any D.
  * Alignment.  Every pointer must be 16-byte aligned.
  * Validation.  All checks run on the host before anything is enqueued; on
- *   error nothing is enqueued and no output is touched.
+ *   error nothing is enqueued and no output is touched.  A launch error is
+ *   reported as RGLRU_ERR_LAUNCH after the fact (hipGetLastError).
+ * Work distribution.  The scans are persistent kernels that claim their work
+ *   units from counters in the workspace at run time; they need no
+ *   co-residency guarantee and may share the device with other work.  A
+ *   look-back wait that never sees its data (which only a corrupted or
+ *   concurrently reused workspace can cause) gives up after a bounded spin,
+ *   sets an error word in the workspace header and yields NaN.
  * Aliasing.  Outputs must not overlap inputs, except hist and h of
  *   rglru_step, which are read and rewritten in place by design.
- * Determinism.  The same inputs on the same device give bitwise-identical
- *   outputs (no floating-point atomics; reductions run in a fixed order).
+ * Determinism.  rglru_conv1d, rglru_gates and rglru_step are bitwise
+ *   repeatable, and so are the reductions of rglru_scan_bwd (fixed order, no
+ *   floating-point atomics).  The chunked scans of rglru_scan_fwd and
+ *   rglru_scan_bwd combine chunk carries through a decoupled look-back whose
+ *   path depends on timing (a chunk may compose a different number of
+ *   published aggregates), so repeated calls can differ in the last bits of
+ *   the carried state and, through it, of y and the gradients; the
+ *   difference is rounding only (the same products, grouped differently).
  * Numerics.  NaN and Inf in the inputs propagate; they are not trapped.
  */
 #ifndef RGLRU_H
