@@ -30,7 +30,8 @@
 //      x written channel-major in fp32 for pass 4;
 //   4. dW = sum over rows of dz x^T on the matrix cores, split over row
 //      ranges into partials;
-//   5. deterministic reductions of the partials (fixed order, no atomics).
+//   5. deterministic reductions of the partials (fixed order, no atomics;
+//      the per-chunk sums in two steps, over unit splits then splits).
 // Precision (bf16 I/O): products whose operands are computed values (dz, x)
 // use a two-term split v = hi + lo with hi = bf16(v), lo = bf16(v - hi):
 // dx = W^T dz_hi + W^T dz_lo (W is exactly bf16), dW = dz_hi x_hi^T +
@@ -47,9 +48,10 @@ namespace rglru {
 namespace {
 
 constexpr int NSUM = 8;   // per-chunk partial sums: dcw[4], dcb, db_a, db_x, dLambda
+constexpr int PS_SPLITS = 16;   // unit splits of the first reduction step
 
 struct BwdLayout {
-    size_t fwd_words, claims, bwd_words, hstart, Wt, dZt, Xt, psum, dWpart, total;
+    size_t fwd_words, claims, bwd_words, hstart, Wt, dZt, Xt, psum, ppart, dWpart, total;
     int S;   // row-range splits of the dW products
 };
 
@@ -73,6 +75,7 @@ BwdLayout bwd_layout(int64_t B, int64_t T, int64_t D, int64_t H, size_t esz)
     L.dZt = off;        off = align256(off + NW * 64 * 4);
     L.Xt = off;         off = align256(off + NW * 32 * 4);
     L.psum = off;       off = align256(off + NW * NSUM * 4);
+    L.ppart = off;      off = align256(off + (size_t)PS_SPLITS * D * NSUM * 4);
     L.dWpart = off;     off = align256(off + (size_t)S * H * 2 * 65536 * 4);
     L.total = off;
     return L;
@@ -498,15 +501,53 @@ __global__ __launch_bounds__(256) void dw_reduce_kernel(int G, int S, const floa
     (q == 0 ? dWa : dWx)[(long)g * 65536 + oj] = acc;
 }
 
-__global__ __launch_bounds__(256) void psum_reduce_kernel(int units, int D, const float *psum,
-                                                          float *dcw, float *dcb, float *dba,
-                                                          float *dbx, float *dLambda)
+// Per-chunk partial sums -> per-channel gradients, in two deterministic
+// steps.  Step 1: workgroup (channel group of 32, unit split s) adds the
+// units of its split; thread (l, c) takes units l, l+8, ... for channel c
+// (32 consecutive channels read 1 KB contiguously), then the 8 threads of a
+// channel are added in a fixed order through LDS.  Step 2 adds the splits in
+// order.
+__global__ __launch_bounds__(256) void psum_partial_kernel(int units, int D, const float *psum, float *part)
+{
+    __shared__ float red[8][32][NSUM + 1];
+    const int c = threadIdx.x & 31, l = threadIdx.x >> 5;
+    const int d = blockIdx.x * 32 + c;
+    const int s = blockIdx.y;
+    const int u0 = (int)((long)units * s / PS_SPLITS), u1 = (int)((long)units * (s + 1) / PS_SPLITS);
+    float acc[NSUM] = {};
+    if (d < D) {
+        for (int un = u0 + l; un < u1; un += 8) {
+            const float4 *src = (const float4 *)(psum + ((long)un * D + d) * NSUM);
+            const float4 v0 = src[0], v1 = src[1];
+            acc[0] += v0.x; acc[1] += v0.y; acc[2] += v0.z; acc[3] += v0.w;
+            acc[4] += v1.x; acc[5] += v1.y; acc[6] += v1.z; acc[7] += v1.w;
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < NSUM; ++q) red[l][c][q] = acc[q];
+    __syncthreads();
+    if (l == 0 && d < D) {
+        float out[NSUM];
+#pragma unroll
+        for (int q = 0; q < NSUM; ++q) {
+            float v = red[0][c][q];
+            for (int k = 1; k < 8; ++k) v += red[k][c][q];
+            out[q] = v;
+        }
+        float4 *dst = (float4 *)(part + ((long)s * D + d) * NSUM);
+        dst[0] = make_float4(out[0], out[1], out[2], out[3]);
+        dst[1] = make_float4(out[4], out[5], out[6], out[7]);
+    }
+}
+
+__global__ __launch_bounds__(256) void psum_reduce_kernel(int D, const float *part, float *dcw, float *dcb,
+                                                          float *dba, float *dbx, float *dLambda)
 {
     const int d = blockIdx.x * 256 + threadIdx.x;
     if (d >= D) return;
     float acc[NSUM] = {};
-    for (int un = 0; un < units; ++un) {
-        const float4 *src = (const float4 *)(psum + ((long)un * D + d) * NSUM);
+    for (int s = 0; s < PS_SPLITS; ++s) {
+        const float4 *src = (const float4 *)(part + ((long)s * D + d) * NSUM);
         const float4 v0 = src[0], v1 = src[1];
         acc[0] += v0.x; acc[1] += v0.y; acc[2] += v0.z; acc[3] += v0.w;
         acc[4] += v1.x; acc[5] += v1.y; acc[6] += v1.z; acc[7] += v1.w;
@@ -627,8 +668,11 @@ void run_bwd(const rglru_desc &d, const rglru_weights &w, const void *u, const v
     // pass 5
     hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((G * 2 * 65536 + 255) / 256)), dim3(256), 0, s,
                        G, L.S, (const float *)dWpart, dWa, dWx);
-    hipLaunchKernelGGL(psum_reduce_kernel, dim3((unsigned)((d.D + 255) / 256)), dim3(256), 0, s, chunks,
-                       (int)d.D, (const float *)p.psum, dcw, dcb, dba, dbx, dLambda);
+    float *ppart = (float *)(base + L.ppart);
+    hipLaunchKernelGGL(psum_partial_kernel, dim3((unsigned)((d.D + 31) / 32), PS_SPLITS), dim3(256), 0, s,
+                       chunks, (int)d.D, (const float *)p.psum, ppart);
+    hipLaunchKernelGGL(psum_reduce_kernel, dim3((unsigned)((d.D + 255) / 256)), dim3(256), 0, s, (int)d.D,
+                       (const float *)ppart, dcw, dcb, dba, dbx, dLambda);
 }
 
 }  // namespace
