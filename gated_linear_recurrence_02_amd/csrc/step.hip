@@ -6,12 +6,24 @@
 // width-4 causal conv of "Temporal Filtering via Separable 1D Convolutions"
 // evaluated on the carried 3-token history.
 //
-// One workgroup (8 waves) = 32 streams x one 256-channel block.  The streams
-// play the role the tokens play in the prefill kernel: lane l = 32*half + n of
-// wave w owns channel 256g + 32w + n of streams 32*blockIdx.x + 16*half .. +15.
-// The conv runs in registers from the history, the conv outputs form the
-// 32 x 256 LDS tile of the gate products, and the state, output and history
-// are rewritten in place by the lane that read them.
+// A decode step is small (B x D elements, ~18 MB touched at B = 256,
+// D = 2560, most of it resident in L2 / Infinity Cache between calls), so the
+// kernel is shaped for parallelism and latency, not reuse: one workgroup
+// (8 waves) per (16 streams, 256-channel block), 160 workgroups at B = 256,
+// D = 2560.
+//   1. the gate weights the lane needs and its own outputs' state, history
+//      and input -- 2 channels x 4 streams -- start loading first;
+//   2. every thread computes the conv of 8 channels of one stream of the
+//      block's input tile (16 streams x 256 channels) into LDS;
+//   3. bf16: wave w computes the gate products of output channels
+//      32w .. 32w+31 (two 16-channel tiles) for the 16 streams with
+//      v_mfma_f32_16x16x32_bf16 (A = x tile rows, B = W rows read from
+//      memory), which leaves lane l with streams 4(l/16)+i of channels
+//      32w + 16t + l%16; fp32: the same outputs by fp32 FMAs;
+//   4. gates, decay, normalisation and the state update for those 8
+//      elements; state, output and history are rewritten in place.
+// A workgroup reads and rewrites the history of its own (streams, block)
+// only, after the barrier that ends the reads of step 2.
 #include "common.h"
 #include "gatemath.h"
 #include "internal.h"
@@ -20,64 +32,213 @@ namespace rglru {
 
 namespace {
 
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4v;
+
+constexpr int SB = 16;   // streams per workgroup
+
+__device__ __forceinline__ void load8(const bf16 *p, float v[8])
+{
+    const bf16x8 q = *(const bf16x8 *)p;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)q[e];
+}
+
+__device__ __forceinline__ void load8(const float *p, float v[8])
+{
+    const f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v[e] = a[e];
+        v[4 + e] = b[e];
+    }
+}
+
+__device__ __forceinline__ void store8(bf16 *p, const float v[8])
+{
+    bf16x8 q;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = (bf16)v[e];
+    *(bf16x8 *)p = q;
+}
+
+__device__ __forceinline__ void store8(float *p, const float v[8])
+{
+    *(f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
+    *(f32x4 *)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
+// B operands of the lane's gate products: rows oc0 + 16t + l%16 of W_a and
+// W_x, K-steps of 32 (lane group l/16 holds 8 consecutive inputs of a step);
+// requested at kernel start so that their latency overlaps steps 1 and 2
+template <typename T> struct WOps {
+    bf16x8 a[2][8], x[2][8];
+};
+template <> struct WOps<float> {};
+
+__device__ __forceinline__ void load_wops(WOps<bf16> &w, const bf16 *Wa_h, const bf16 *Wx_h, int oc0, int lane)
+{
+    const int m = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        const bf16 *wa = Wa_h + (size_t)(oc0 + 16 * ct + m) * 256 + 8 * kq;
+        const bf16 *wx = Wx_h + (size_t)(oc0 + 16 * ct + m) * 256 + 8 * kq;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            w.a[ct][ks] = *(const bf16x8 *)(wa + 32 * ks);
+            w.x[ct][ks] = *(const bf16x8 *)(wx + 32 * ks);
+        }
+    }
+}
+__device__ __forceinline__ void load_wops(WOps<float> &, const float *, const float *, int, int) {}
+
+// gate pre-activations of the lane's 8 outputs -- streams 4(l/16)+i (i < 4)
+// of channels oc0 + 16t + l%16 (t < 2) -- bf16: two 16-channel tiles x
+// 8 K-steps x 2 gates on the matrix cores; element e = 4t + i
+__device__ __forceinline__ void step_gates(const bf16 *Xs, const WOps<bf16> &w, const bf16 *, const bf16 *,
+                                           int, int lane, float za[8], float zx[8])
+{
+    constexpr int S = XTile<bf16>::STRIDE;
+    const int m = lane & 15, kq = lane >> 4;
+    const bf16 *xrow = Xs + m * S + 8 * kq;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        f32x4v A = {}, X = {};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const bf16x8 av = *(const bf16x8 *)(xrow + 32 * ks);
+            A = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, w.a[ct][ks], A, 0, 0, 0);
+            X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, w.x[ct][ks], X, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            za[4 * ct + i] = A[i];
+            zx[4 * ct + i] = X[i];
+        }
+    }
+}
+
+// fp32: the same outputs with fp32 FMAs in input-channel order
+__device__ __forceinline__ void step_gates(const float *Xs, const WOps<float> &, const float *Wa_h,
+                                           const float *Wx_h, int oc0, int lane, float za[8], float zx[8])
+{
+    constexpr int S = XTile<float>::STRIDE;
+    const int m = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) za[e] = zx[e] = 0.0f;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+        const float *wa = Wa_h + (size_t)(oc0 + 16 * ct + m) * 256;
+        const float *wx = Wx_h + (size_t)(oc0 + 16 * ct + m) * 256;
+        for (int k = 0; k < 256; ++k) {
+            const float a = wa[k], x = wx[k];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float xv = Xs[(4 * kq + i) * S + k];
+                za[4 * ct + i] = fmaf(a, xv, za[4 * ct + i]);
+                zx[4 * ct + i] = fmaf(x, xv, zx[4 * ct + i]);
+            }
+        }
+    }
+}
+
 template <typename T>
-__global__ __launch_bounds__(512) void step_kernel(int B, int D, float c, const T *u_t,
-                                                   const float *cw, const float *cb, const T *Wa,
-                                                   const float *ba, const T *Wx, const float *bx,
-                                                   const float *Lambda, T *hist, float *hstate,
-                                                   T *y_t)
+__global__ __launch_bounds__(512) void step_kernel(int B, int D, float c, const T *u_t, const float *cw,
+                                                   const float *cb, const T *Wa, const float *ba,
+                                                   const T *Wx, const float *bx, const float *Lambda,
+                                                   T *hist, float *hstate, T *y_t)
 {
     constexpr int S = XTile<T>::STRIDE;
-    __shared__ __attribute__((aligned(16))) T Xs[32 * S];
-    const int g = blockIdx.y;
+    __shared__ __attribute__((aligned(16))) T Xs[SB * S];
+    const int sb0 = blockIdx.x * SB, g = blockIdx.y;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int n = lane & 31, half = lane >> 5;
-    const int d = g * 256 + wave * 32 + n;
-    const int s0 = blockIdx.x * 32 + 16 * half;
 
-    const float w0 = cw[4 * (long)d + 0], w1 = cw[4 * (long)d + 1];
-    const float w2 = cw[4 * (long)d + 2], w3 = cw[4 * (long)d + 3];
-    const float bias = cb ? cb[d] : 0.0f;
-
-    float x[16];
-    T hv0[16], hv1[16], hv2[16], uv[16];
+    // 1. the gate weights of the lane's outputs, then the lane's outputs'
+    //    state, history and input (stored values, converted when used):
+    //    element e = 4t + i is stream sb0 + 4(l/16) + i of channel
+    //    oc0 + 16t + l%16 of the block
+    const int oc0 = 32 * wave;
+    WOps<T> wop;
+    load_wops(wop, Wa + (size_t)g * 65536, Wx + (size_t)g * 65536, oc0, lane);
+    float hv[8];
+    T h0v[8], h1v[8], h2v[8], uv[8];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const int s = s0 + k;
-        if (s < B) {
-            hv0[k] = hist[((long)s * 3 + 0) * D + d];
-            hv1[k] = hist[((long)s * 3 + 1) * D + d];
-            hv2[k] = hist[((long)s * 3 + 2) * D + d];
-            uv[k] = u_t[(long)s * D + d];
-        } else {
-            hv0[k] = hv1[k] = hv2[k] = uv[k] = from_f32<T>(0.0f);
-        }
-        x[k] = fmaf(w3, to_f32(uv[k]),
-                    fmaf(w2, to_f32(hv2[k]), fmaf(w1, to_f32(hv1[k]), fmaf(w0, to_f32(hv0[k]), bias))));
-        Xs[(16 * half + k) * S + wave * 32 + n] = from_f32<T>(x[k]);
+    for (int e = 0; e < 8; ++e) {
+        const int s = sb0 + 4 * (lane >> 4) + (e & 3);
+        const int d = g * 256 + oc0 + 16 * (e >> 2) + (lane & 15);
+        const bool ok = s < B;
+        const long sd = ok ? (long)s * D + d : d;   // a valid address either way
+        hv[e] = hstate[sd];
+        h0v[e] = hist[((ok ? (long)s : 0) * 3 + 0) * D + d];
+        h1v[e] = hist[((ok ? (long)s : 0) * 3 + 1) * D + d];
+        h2v[e] = hist[((ok ? (long)s : 0) * 3 + 2) * D + d];
+        uv[e] = u_t[sd];
     }
-    __syncthreads();
 
-    float za[16], zx[16];
-    gate_tile(Xs, Wa + (size_t)g * 65536, Wx + (size_t)g * 65536, wave, lane, za, zx);
-
-    const float ncs = -c * softplus_acc(-Lambda[d]);
-    const float bav = ba ? ba[d] : 0.0f, bxv = bx ? bx[d] : 0.0f;
+    // 2. conv of the input tile: 8 channels of one stream per thread
+    {
+        const int cg = tid & 31, sl = tid >> 5, s = sb0 + sl;
+        const int dc = g * 256 + 8 * cg;
+        float x[8];
+        if (s < B) {
+            float a0[8], a1[8], a2[8], a3[8];
+            load8(hist + ((long)s * 3 + 0) * D + dc, a0);
+            load8(hist + ((long)s * 3 + 1) * D + dc, a1);
+            load8(hist + ((long)s * 3 + 2) * D + dc, a2);
+            load8(u_t + (long)s * D + dc, a3);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const int s = s0 + k;
-        if (s >= B) continue;
-        const float rr = sigmoid_acc(za[k] + bav);
-        const float ii = sigmoid_acc(zx[k] + bxv);
-        const float l = ncs * rr;
-        const float a = expf(l);
-        const float beta = sqrtf(-expm1f(2.0f * l));
-        const float hn = fmaf(a, hstate[(long)s * D + d], beta * ii * x[k]);
-        hstate[(long)s * D + d] = hn;
-        y_t[(long)s * D + d] = from_f32<T>(hn);
-        hist[((long)s * 3 + 0) * D + d] = hv1[k];
-        hist[((long)s * 3 + 1) * D + d] = hv2[k];
-        hist[((long)s * 3 + 2) * D + d] = uv[k];
+            for (int e = 0; e < 8; ++e) {
+                const f32x4 t = *(const f32x4 *)(cw + 4 * (long)(dc + e));
+                const float bias = cb ? cb[dc + e] : 0.0f;
+                x[e] = fmaf(t[3], a3[e], fmaf(t[2], a2[e], fmaf(t[1], a1[e], fmaf(t[0], a0[e], bias))));
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+        }
+        store8(Xs + sl * S + 8 * cg, x);
+    }
+    __syncthreads();   // the tile is complete and every read of the history is done
+
+    // 3. gate pre-activations of the lane's outputs
+    float za[8], zx[8];
+    step_gates(Xs, wop, Wa + (size_t)g * 65536, Wx + (size_t)g * 65536, oc0, lane, za, zx);
+
+    // 4. gates, decay, normalisation, state update
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int d = g * 256 + oc0 + 16 * t + (lane & 15);
+        const f32x4 cwd = *(const f32x4 *)(cw + 4 * (long)d);
+        const float bd = cb ? cb[d] : 0.0f;
+        const float ncs = -c * softplus_acc(-Lambda[d]);
+        const float bav = ba ? ba[d] : 0.0f, bxv = bx ? bx[d] : 0.0f;
+        const float kba = -LOG2E * bav, kbx = -LOG2E * bxv, kdec = LOG2E * ncs;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * t + i;
+            const int s = sb0 + 4 * (lane >> 4) + i;
+            if (s >= B) continue;
+            const float x = fmaf(cwd[3], to_f32(uv[e]),
+                                 fmaf(cwd[2], to_f32(h2v[e]), fmaf(cwd[1], to_f32(h1v[e]), fmaf(cwd[0], to_f32(h0v[e]), bd))));
+            float a, bb;
+            if constexpr (sizeof(T) == 2) {
+                const float rr = hw_rcp(1.0f + hw_exp2(fmaf(za[e], -LOG2E, kba)));
+                const float ii = hw_rcp(1.0f + hw_exp2(fmaf(zx[e], -LOG2E, kbx)));
+                a = hw_exp2(rr * kdec);
+                bb = hw_sqrt(fmaf(-a, a, 1.0f)) * ii * x;
+            } else {
+                const float rr = sigmoid_acc(za[e] + bav);
+                const float ii = sigmoid_acc(zx[e] + bxv);
+                const float l = ncs * rr;
+                a = expf(l);
+                bb = sqrtf(-expm1f(2.0f * l)) * ii * x;
+            }
+            const float hn = fmaf(a, hv[e], bb);
+            hstate[(long)s * D + d] = hn;
+            y_t[(long)s * D + d] = from_f32<T>(hn);
+            hist[((long)s * 3 + 0) * D + d] = h1v[e];
+            hist[((long)s * 3 + 1) * D + d] = h2v[e];
+            hist[((long)s * 3 + 2) * D + d] = uv[e];
+        }
     }
 }
 
@@ -85,7 +246,7 @@ template <typename T>
 void launch_step_t(const rglru_desc &d, const rglru_weights &w, const void *u_t, void *hist,
                    float *h, void *y_t, hipStream_t s)
 {
-    const dim3 grid((unsigned)((d.B + 31) / 32), (unsigned)d.H);
+    const dim3 grid((unsigned)((d.B + SB - 1) / SB), (unsigned)d.H);
     hipLaunchKernelGGL((step_kernel<T>), grid, dim3(512), 0, s, (int)d.B, (int)d.D, d.c,
                        (const T *)u_t, w.conv_w, w.conv_b, (const T *)w.W_a, w.b_a,
                        (const T *)w.W_x, w.b_x, w.Lambda, (T *)hist, h, (T *)y_t);

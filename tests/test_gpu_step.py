@@ -88,3 +88,31 @@ def test_steps_equal_prefill_on_gpu():
     y, hl, ho = glr.scan_fwd(to_dev(u_seq, DEV), w)
     torch.cuda.synchronize()
     _cmp("steps vs prefill", from_dev(y_seq), from_dev(y), 1e-2)
+
+
+def test_decode_fp32_tiny_width():
+    # fp32 I/O on the tiny workload's parameters (D = 256, one block),
+    # 20 streams with a nonzero starting history and state, 10 steps
+    cfg = synth.CONFIGS[0]
+    B, D, steps = 20, cfg.D, 10
+    params = synth.make_params(cfg.idx, D, cfg.H, "f32")
+    w = glr.Weights(conv_w=to_dev(params.conv_w, DEV), W_a=to_dev(params.W_a, DEV),
+                    W_x=to_dev(params.W_x, DEV), Lambda=to_dev(params.Lambda, DEV),
+                    conv_b=to_dev(params.conv_b, DEV), b_a=to_dev(params.b_a, DEV),
+                    b_x=to_dev(params.b_x, DEV))
+    hist0 = synth.make_activation(cfg.idx, "hist", (B, 3, D), "f32")
+    h00 = synth.store(synth.normal(synth.seed_for(cfg.idx, "h0"), 0, B * D), "f32").reshape(B, D)
+    u_seq = synth.make_activation(cfg.idx, "u", (B, steps, D), "f32")
+    hist = to_dev(hist0, DEV)
+    h = to_dev(h00, DEV)
+    _say(f"decode fp32: B={B} D={D}, {steps} steps with history and state")
+    ys = [glr.step(to_dev(np.ascontiguousarray(u_seq[:, s]), DEV), w, hist, h).clone() for s in range(steps)]
+    torch.cuda.synchronize()
+    op = dict(conv_w=synth.widen(params.conv_w), conv_b=synth.widen(params.conv_b),
+              W_a=synth.widen(params.W_a), b_a=synth.widen(params.b_a),
+              W_x=synth.widen(params.W_x), b_x=synth.widen(params.b_x),
+              Lambda=synth.widen(params.Lambda))
+    ry, rh, rho = oracle.fwd(synth.widen(u_seq), **op, h0=h00.astype(np.float64), hist_in=synth.widen(hist0))
+    _cmp("y", from_dev(torch.stack(ys, dim=1)), ry, TOL["f32"])
+    _cmp("h", from_dev(h), rh, TOL["f32"])
+    assert np.array_equal(hist.cpu().numpy(), u_seq[:, -3:, :])
