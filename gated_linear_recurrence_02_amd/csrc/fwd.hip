@@ -41,6 +41,7 @@
 // unit of the same block with a smaller index, which was claimed earlier by a
 // running workgroup; by induction on the unit index every wait ends.
 #include <mutex>
+#include <type_traits>
 
 #include "common.h"
 #include "gatemath.h"
@@ -277,44 +278,50 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
                 }
             }
 
-            // gates, decay, normalisation, local scan from zero
-            float h = 0.0f, pr = 1.0f;
+            // gates, decay, normalisation, local scan from zero; interior
+            // chunks take a copy of the loop without the end-of-sequence test
+            auto scan16 = [&](auto edge_tag) {
+                constexpr bool EDGE = decltype(edge_tag)::value;
+                float h = 0.0f, pr = 1.0f;
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                float a, bb;
-                if constexpr (sizeof(T) == 2) {
-                    float rr, ii;
-                    if (MODE == 2) {
-                        rr = za[k];
-                        ii = zx[k];
+                for (int k = 0; k < 16; ++k) {
+                    float a, bb;
+                    if constexpr (sizeof(T) == 2) {
+                        float rr, ii;
+                        if (MODE == 2) {
+                            rr = za[k];
+                            ii = zx[k];
+                        } else {
+                            rr = hw_rcp(1.0f + hw_exp2(fmaf(za[k], -LOG2E, kba)));
+                            ii = hw_rcp(1.0f + hw_exp2(fmaf(zx[k], -LOG2E, kbx)));
+                        }
+                        a = hw_exp2(rr * kdec);
+                        bb = hw_sqrt(fmaf(-a, a, 1.0f)) * ii * x[k];
                     } else {
-                        rr = hw_rcp(1.0f + hw_exp2(fmaf(za[k], -LOG2E, kba)));
-                        ii = hw_rcp(1.0f + hw_exp2(fmaf(zx[k], -LOG2E, kbx)));
+                        float rr, ii;
+                        if (MODE == 2) {
+                            rr = za[k];
+                            ii = zx[k];
+                        } else {
+                            rr = sigmoid_acc(za[k] + bav);
+                            ii = sigmoid_acc(zx[k] + bxv);
+                        }
+                        const float l = ncs * rr;
+                        a = expf(l);
+                        bb = sqrtf(-expm1f(2.0f * l)) * ii * x[k];
                     }
-                    a = hw_exp2(rr * kdec);
-                    bb = hw_sqrt(fmaf(-a, a, 1.0f)) * ii * x[k];
-                } else {
-                    float rr, ii;
-                    if (MODE == 2) {
-                        rr = za[k];
-                        ii = zx[k];
-                    } else {
-                        rr = sigmoid_acc(za[k] + bav);
-                        ii = sigmoid_acc(zx[k] + bxv);
+                    if (EDGE && !(dv && tb + k < p.T)) {   // past the end: identity step
+                        a = 1.0f;
+                        bb = 0.0f;
                     }
-                    const float l = ncs * rr;
-                    a = expf(l);
-                    bb = sqrtf(-expm1f(2.0f * l)) * ii * x[k];
+                    h = fmaf(a, h, bb);
+                    pr *= a;
+                    hl[k] = h;
+                    P[k] = pr;
                 }
-                if (!full && !(dv && tb + k < p.T)) {   // past the end: identity step
-                    a = 1.0f;
-                    bb = 0.0f;
-                }
-                h = fmaf(a, h, bb);
-                pr *= a;
-                hl[k] = h;
-                P[k] = pr;
-            }
+            };
+            if (full && dv) scan16(std::false_type{});
+            else scan16(std::true_type{});
 
             // chunk aggregate, published before anything waits
             cur.A0 = __shfl_xor(P[15], 32);
