@@ -21,7 +21,8 @@
 // the 16 consecutive tokens 32c + 16*half .. +15:
 //   front  1. inputs: the conv over a 19-token window (mode A; interior bf16
 //             chunks read a tile that global_load_lds brought into LDS one
-//             unit ahead), x (mode B), or x, r, i (mode C);
+//             unit ahead), x (mode B), or x, r, i (mode C, requested into
+//             registers one unit ahead);
 //          2. modes A/B: x goes to an LDS tile; the gate products come back in
 //             the MFMA output layout, which hands the lane its 16 tokens of
 //             channel d;
@@ -97,6 +98,30 @@ struct FwdParams {
     uint64_t *aggA, *aggX, *incl;
 };
 
+// Mode C: the x, r and i values of a lane's 16 tokens of unit q, as stored
+// (requested one unit ahead and kept in registers until used); tokens past the
+// end and channels past D read element 0 and are masked where used
+template <typename T>
+struct ScanIn {
+    T x[16], r[16], i[16];
+};
+
+template <typename T>
+__device__ __forceinline__ void scan_in_load(ScanIn<T> &v, const FwdParams &p, uint32_t q, int d, int half)
+{
+    const T *x = (const T *)p.in, *r = (const T *)p.r, *i = (const T *)p.i;
+    const int c = (int)(q / p.B), b = (int)(q % p.B);
+    const bool ok_unit = q < (uint32_t)p.units && d < p.D;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int t = c * CHUNK + 16 * half + k;
+        const long e = (ok_unit && t < p.T) ? ((long)b * p.T + t) * p.D + d : 0;
+        v.x[k] = x[e];
+        v.r[k] = r[e];
+        v.i[k] = i[e];
+    }
+}
+
 // scalars of a chunk whose back half is pending
 struct Pend {
     int b, c;
@@ -170,6 +195,8 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
     uint32_t j = s_unit[0];
     uint32_t t0_next = s_unit[1];   // thread 0 only: the latest unit it claimed
     int it = 0;
+    ScanIn<T> sin;   // mode C: inputs of unit j
+    if constexpr (MODE == 2) scan_in_load(sin, p, j, d, half);
     if constexpr (STAGE) {
         if (j < units) {
             const int c0 = (int)(j / p.B), b0 = (int)(j % p.B);
@@ -191,6 +218,8 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
         __syncthreads();   // ... and every wave's; the other stage buffer, the x tile and
                            // the claim slot read last time are free again
         const uint32_t jn = s_unit[(it + 1) & 1];   // u_{n+1}
+        ScanIn<T> sin_next;   // mode C: inputs of the next unit, requested now
+        if constexpr (MODE == 2) scan_in_load(sin_next, p, jn, d, half);
         if (have) {
             // ------------------------------------------------ front of chunk j
             const int c = (int)(j / p.B), b = (int)(j % p.B);
@@ -236,6 +265,9 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
 #pragma unroll
                 for (int k = 0; k < 16; ++k)
                     x[k] = fmaf(w3, win[k + 3], fmaf(w2, win[k + 2], fmaf(w1, win[k + 1], fmaf(w0, win[k], bias))));
+            } else if (MODE == 2) {
+#pragma unroll
+                for (int k = 0; k < 16; ++k) x[k] = (dv && tb + k < p.T) ? to_f32(sin.x[k]) : 0.0f;
             } else {
 #pragma unroll
                 for (int k = 0; k < 16; ++k) {
@@ -271,10 +303,9 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
             } else {
 #pragma unroll
                 for (int k = 0; k < 16; ++k) {
-                    const int t = tb + k;
-                    const bool ok = dv && t < p.T;
-                    za[k] = ok ? ldf((const T *)p.r + (row_b + t) * p.D + d) : 0.0f;
-                    zx[k] = ok ? ldf((const T *)p.i + (row_b + t) * p.D + d) : 0.0f;
+                    const bool ok = dv && tb + k < p.T;
+                    za[k] = ok ? to_f32(sin.r[k]) : 0.0f;
+                    zx[k] = ok ? to_f32(sin.i[k]) : 0.0f;
                 }
             }
 
@@ -396,6 +427,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
             pd = cur;
         }
         have_pend = have;
+        if constexpr (MODE == 2) sin = sin_next;
         if (tid == 0) {   // u_{n+2}, read after the first barrier of the next iteration
             s_unit[it & 1] = my_claim;
             t0_next = my_claim;
