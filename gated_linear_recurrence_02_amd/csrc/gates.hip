@@ -5,10 +5,17 @@
 // Gating Mechanism", with W_a, W_x block-diagonal per "Block-Diagonal Sharding
 // for Zero-Communication Tensor Parallelism" (blocks of K = 256 channels).
 //
-// One workgroup (8 waves) = one 32-row tile of the flattened [B*T] rows times
-// one 256-channel block.  The tile is staged in LDS (16-byte loads of whole
-// rows), the products run on the matrix cores (bf16) or on fp32 FMAs (fp32);
-// lane l of wave w writes channel 32w + l%32 of rows 16(l/32) .. +15.
+// bf16: a persistent kernel like the fused forward -- one workgroup (8 waves)
+// per CU serves one 256-channel block g = w % G with the block's W_a and W_x
+// held in registers (wave w: rows 32w..32w+31, 128 VGPRs) and walks the
+// 32-row tiles of the flattened [B*T] rows assigned to it (tile q,
+// q + WPG, ...; no tile waits on another).  The next tile is requested into
+// registers (two 16-byte loads per thread) while the current one is on the
+// matrix cores; tiles alternate between two LDS buffers, so one barrier per
+// tile suffices.  Lane l of wave w gets channel 32w + l%32 of rows
+// 16(l/32) .. +15 back from the MFMA output layout.
+// fp32: one workgroup per (tile, block); the tile is staged in LDS and the
+// products run on fp32 FMAs.
 #include "common.h"
 #include "gatemath.h"
 #include "internal.h"
@@ -54,14 +61,94 @@ __global__ __launch_bounds__(512) void gates_kernel(long rows, int D, const T *x
     }
 }
 
+// bf16, persistent and weight-stationary
+__global__ __launch_bounds__(512) void gates_kernel_w(long rows, int D, int G, int wpg, const bf16 *x,
+                                                      const bf16 *Wa, const float *ba, const bf16 *Wx,
+                                                      const float *bx, bf16 *r, bf16 *i)
+{
+    constexpr int S = XTile<bf16>::STRIDE;
+    __shared__ __attribute__((aligned(16))) bf16 Xs[2][32 * S];
+    const int g = blockIdx.x % G, rank = blockIdx.x / G;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 31, half = lane >> 5;
+    const int d = g * 256 + 32 * wave + n;
+    const long ntiles = (rows + 31) / 32;
+
+    bf16x8 wa[16], wx[16];
+    {
+        const int rr = lane & 31, kg = lane >> 5;
+        const bf16 *pa = Wa + (size_t)g * 65536 + (size_t)(32 * wave + rr) * 256 + 8 * kg;
+        const bf16 *px = Wx + (size_t)g * 65536 + (size_t)(32 * wave + rr) * 256 + 8 * kg;
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2) {
+            wa[s2] = *(const bf16x8 *)(pa + 16 * s2);
+            wx[s2] = *(const bf16x8 *)(px + 16 * s2);
+        }
+    }
+    const float kba = -LOG2E * (ba ? ba[d] : 0.0f), kbx = -LOG2E * (bx ? bx[d] : 0.0f);
+
+    // thread t moves 16 bytes of rows t/32 and t/32 + 16 (channels 8(t%32) .. +7)
+    const int lr = tid >> 5, lc = 8 * (tid & 31);
+    auto fetch = [&](long q, uint4 v[2]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const long row = q * 32 + lr + 16 * h;
+            v[h] = row < rows ? *(const uint4 *)(x + row * D + g * 256 + lc) : uint4{0u, 0u, 0u, 0u};
+        }
+    };
+    uint4 cur[2];
+    long q = rank;
+    if (q < ntiles) fetch(q, cur);
+    for (int it = 0; q < ntiles; q += wpg, ++it) {
+        bf16 *X = Xs[it & 1];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) *(uint4 *)(X + (lr + 16 * h) * S + lc) = cur[h];
+        __syncthreads();   // the tile is in LDS; the other buffer's readers are done
+        if (q + wpg < ntiles) fetch(q + wpg, cur);
+
+        const int rr = lane & 31, kg = lane >> 5;
+        const bf16 *xrow = X + tile_row_token(rr) * S + 8 * kg;
+        f32x16 A = {}, Xc = {};
+#pragma unroll
+        for (int s2 = 0; s2 < 16; ++s2) {
+            const bf16x8 av = *(const bf16x8 *)(xrow + 16 * s2);
+            A = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, wa[s2], A, 0, 0, 0);
+            Xc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, wx[s2], Xc, 0, 0, 0);
+        }
+        const long row0 = q * 32 + 16 * half;
+        bf16 *rp = r + row0 * D + d, *ip = i + row0 * D + d;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            if (row0 + k < rows) {
+                rp[(long)k * D] = (bf16)hw_rcp(1.0f + hw_exp2(fmaf(A[k], -LOG2E, kba)));
+                ip[(long)k * D] = (bf16)hw_rcp(1.0f + hw_exp2(fmaf(Xc[k], -LOG2E, kbx)));
+            }
+        }
+    }
+}
+
 template <typename T>
 void launch_gates_t(const rglru_desc &d, const rglru_weights &w, const void *x, void *r, void *i,
                     hipStream_t s)
 {
     const long rows = d.B * d.T;
-    const dim3 grid((unsigned)((rows + 31) / 32), (unsigned)d.H);
-    hipLaunchKernelGGL((gates_kernel<T>), grid, dim3(512), 0, s, rows, (int)d.D, (const T *)x,
-                       (const T *)w.W_a, w.b_a, (const T *)w.W_x, w.b_x, (T *)r, (T *)i);
+    if constexpr (sizeof(T) == 2) {
+        int dev = 0, ncu = 0;
+        (void)hipGetDevice(&dev);
+        (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (ncu < 1) ncu = 1;
+        const long ntiles = (rows + 31) / 32;
+        long wpg = ncu / d.H;   // one workgroup per CU
+        if (wpg < 1) wpg = 1;
+        if (wpg > ntiles) wpg = ntiles;
+        hipLaunchKernelGGL(gates_kernel_w, dim3((unsigned)(d.H * wpg)), dim3(512), 0, s, rows, (int)d.D,
+                           (int)d.H, (int)wpg, (const bf16 *)x, (const bf16 *)w.W_a, w.b_a,
+                           (const bf16 *)w.W_x, w.b_x, (bf16 *)r, (bf16 *)i);
+    } else {
+        const dim3 grid((unsigned)((rows + 31) / 32), (unsigned)d.H);
+        hipLaunchKernelGGL((gates_kernel<T>), grid, dim3(512), 0, s, rows, (int)d.D, (const T *)x,
+                           (const T *)w.W_a, w.b_a, (const T *)w.W_x, w.b_x, (T *)r, (T *)i);
+    }
 }
 
 }  // namespace

@@ -84,6 +84,23 @@ def test_config0_fp32_conv_gates_scan_stages():
     _cmp("h_last", from_dev(hl), rh, TOL["f32"])
 
 
+def test_gates_bf16_blocks_and_ragged_rows():
+    # the bf16 gate kernel on the 2B-width parameters; B*T = 2*77 rows is not a
+    # multiple of the 32-row tile, and the conv output is the gate input
+    prob = make_problem(1, B=2, T=77)
+    _say("gates: B=2 T=77 D=2560 bf16")
+    w = prob.weights(DEV)
+    x, _ = glr.conv1d(to_dev(prob.u, DEV), w.conv_w, w.conv_b, H=prob.H)
+    r, i = glr.gates(x, w)
+    torch.cuda.synchronize()
+    xs = from_dev(x)
+    for h in (0, 9):
+        op = prob.oracle_params(h)
+        rr, ri = oracle.gates(prob.slice_block(xs, None, h), op["W_a"], op["b_a"], op["W_x"], op["b_x"])
+        _cmp(f"r[h={h}]", prob.slice_block(from_dev(r), None, h), rr, TOL["bf16"])
+        _cmp(f"i[h={h}]", prob.slice_block(from_dev(i), None, h), ri, TOL["bf16"])
+
+
 # ------------------------------------------------------ ragged / edge shapes
 @pytest.mark.parametrize("T", [1, 2, 3, 17, 31, 32, 33, 95, 130])
 def test_mode_a_ragged_lengths_with_state(T):
