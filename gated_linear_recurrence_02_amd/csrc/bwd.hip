@@ -218,16 +218,26 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p)
     const float w0 = p.cw[4 * (long)d + 0], w1 = p.cw[4 * (long)d + 1];
     const float w2 = p.cw[4 * (long)d + 2], w3 = p.cw[4 * (long)d + 3];
     const float bias = p.cb ? p.cb[d] : 0.0f;
+    // the 19 loads go out together: addresses are selected, not branched on
+    // (positions past the end or before a missing history read element 0 and
+    // are zeroed afterwards)
     float win[19];
+    {
+        T raw[19];
 #pragma unroll
-    for (int m = 0; m < 19; ++m) {
-        const int tau = tb - 3 + m;
-        float v = 0.0f;
-        if (tau < p.T) {
-            if (tau >= 0) v = ldf(u + (row_b + tau) * p.D + d);
-            else if (p.hist_in) v = ldf((const T *)p.hist_in + ((long)b * 3 + 3 + tau) * p.D + d);
+        for (int m = 0; m < 19; ++m) {
+            const int tau = tb - 3 + m;
+            const T *src = u;
+            if (tau >= 0 && tau < p.T) src = u + (row_b + tau) * p.D + d;
+            else if (tau < 0 && p.hist_in) src = (const T *)p.hist_in + ((long)b * 3 + 3 + tau) * p.D + d;
+            raw[m] = *src;
         }
-        win[m] = v;
+#pragma unroll
+        for (int m = 0; m < 19; ++m) {
+            const int tau = tb - 3 + m;
+            const bool ok = tau < p.T && (tau >= 0 || p.hist_in);
+            win[m] = ok ? to_f32(raw[m]) : 0.0f;
+        }
     }
     float x[16];
 #pragma unroll
@@ -277,11 +287,19 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p)
 
     // reverse scan inside the lane (eps entering the lane's last token = 0)
     const T *dyp = (const T *)p.dy;
+    float gdy[16];
+    {
+        T raw[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) raw[k] = dyp[tb + k < p.T ? (row_b + tb + k) * p.D + d : 0];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) gdy[k] = tb + k < p.T ? to_f32(raw[k]) : 0.0f;
+    }
     float dl[16], R[16];
     float e = 0.0f, Rrun = 1.0f;
 #pragma unroll
     for (int k = 15; k >= 0; --k) {
-        const float gk = (tb + k < p.T) ? ldf(dyp + (row_b + tb + k) * p.D + d) : 0.0f;
+        const float gk = gdy[k];
         dl[k] = gk + e;
         R[k] = Rrun;
         e = a[k] * dl[k];
@@ -422,44 +440,79 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p)
 // ------------------------------------------------------------------ pass 4
 // dW[q][o][j] over the row range of split s: sum_{units, t} dz_q[o][t] x[j][t].
 // bf16 I/O: wave w owns rows o = 32w..32w+31 and all 256 columns (8 MFMA
-// tiles); both operands are split into bf16 hi + lo on load and three
-// products are accumulated (hi*hi + hi*lo + lo*hi).
-__device__ __forceinline__ void split8(const float *src, bf16x8 &hi, bf16x8 &lo)
-{
-    const f32x4 v0 = *(const f32x4 *)src, v1 = *(const f32x4 *)(src + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        hi[e] = (bf16)v0[e];
-        lo[e] = (bf16)(v0[e] - (float)hi[e]);
-        hi[4 + e] = (bf16)v1[e];
-        lo[4 + e] = (bf16)(v1[e] - (float)hi[4 + e]);
-    }
-}
+// tiles); both operands are split into bf16 hi + lo and three products are
+// accumulated (hi*hi + hi*lo + lo*hi).  Each unit's x tile is split once and
+// staged in LDS for all 8 waves; the next unit's x and dz are requested while
+// the current one is on the matrix cores.
+constexpr int DW_XS = 40;   // LDS row stride (bf16) of a staged x tile: 32 tokens + 8 pad
 
 __global__ __launch_bounds__(512) void dw_kernel_bf16(int units, int G, int S, const float *dZt,
                                                       const float *Xt, float *dWpart)
 {
+    // x of the current unit, split into bf16 hi and lo, [256 j][32 t] each
+    __shared__ __attribute__((aligned(16))) bf16 Xh[256 * DW_XS], Xl[256 * DW_XS];
     const int g = blockIdx.x / 2, q = blockIdx.x % 2, s = blockIdx.y;
     const int u0 = (int)((long)units * s / S), u1 = (int)((long)units * (s + 1) / S);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 31, kg = lane >> 5;
+    // staging: thread t splits x[j = t/2][16 (t&1) .. +15]
+    const int sj = tid >> 1, st = 16 * (tid & 1);
     f32x16 acc[8];
 #pragma unroll
     for (int jt = 0; jt < 8; ++jt) acc[jt] = f32x16{};
-    for (int un = u0; un < u1; ++un) {
+    f32x4 xv[4], zv[2][2];
+    auto fetch = [&](int un) {
+        const float *xt = Xt + ((long)un * G + g) * 256 * 32 + sj * 32 + st;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xv[e] = *(const f32x4 *)(xt + 4 * e);
         const float *zt = dZt + (((long)un * G + g) * 2 + q) * 256 * 32 + (32 * wave + r) * 32 + 8 * kg;
-        const float *xt = Xt + ((long)un * G + g) * 256 * 32 + r * 32 + 8 * kg;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 ah, al;
-            split8(zt + 16 * ks, ah, al);
+            zv[ks][0] = *(const f32x4 *)(zt + 16 * ks);
+            zv[ks][1] = *(const f32x4 *)(zt + 16 * ks + 4);
+        }
+    };
+    if (u0 < u1) fetch(u0);
+    for (int un = u0; un < u1; ++un) {
+        // stage this unit's x (split) and take its dz operands
+        bf16x8 hx[2], lx[2];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float v = xv[e][c];
+                const bf16 h = (bf16)v;
+                hx[e >> 1][4 * (e & 1) + c] = h;
+                lx[e >> 1][4 * (e & 1) + c] = (bf16)(v - (float)h);
+            }
+        bf16x8 ah[2], al[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = zv[ks][e >> 2][e & 3];
+                const bf16 h = (bf16)v;
+                ah[ks][e] = h;
+                al[ks][e] = (bf16)(v - (float)h);
+            }
+        __syncthreads();   // every wave is done with the previous unit's tile
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            *(bf16x8 *)(Xh + sj * DW_XS + st + 8 * h2) = hx[h2];
+            *(bf16x8 *)(Xl + sj * DW_XS + st + 8 * h2) = lx[h2];
+        }
+        __syncthreads();
+        if (un + 1 < u1) fetch(un + 1);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
             for (int jt = 0; jt < 8; ++jt) {
-                bf16x8 bh, bl;
-                split8(xt + jt * 32 * 32 + 16 * ks, bh, bl);
-                acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc[jt], 0, 0, 0);
-                acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[jt], 0, 0, 0);
-                acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[jt], 0, 0, 0);
+                const int off = (32 * jt + r) * DW_XS + 8 * kg + 16 * ks;
+                const bf16x8 bh = *(const bf16x8 *)(Xh + off);
+                const bf16x8 bl = *(const bf16x8 *)(Xl + off);
+                acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[ks], bh, acc[jt], 0, 0, 0);
+                acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[ks], bl, acc[jt], 0, 0, 0);
+                acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[ks], bh, acc[jt], 0, 0, 0);
             }
         }
     }
