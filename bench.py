@@ -226,7 +226,17 @@ def main():
         glr.scan_fwd(s["u"], w, out=s["y"], h_last_out=s["h"], hist_out_buf=s["hist"])
 
     _say(f"fused forward, 2B-width prefill B={B} T={T} D={D}: {args.warmup} warmup + {args.steps} timed")
-    kms, ms_per_step = tm.calls(step, args.steps, args.warmup)
+    # the step rate: K steps back to back, synchronised on both sides
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    # the kernel's own duration: the same steps again, each between two events
+    kms, _ = tm.calls(step, args.steps, 0)
     kernel_ms = float(np.mean(kms))
     tokch = B * T * D
     alg = fwd_bytes(B, T, D, H, 2)
