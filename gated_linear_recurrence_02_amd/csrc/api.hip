@@ -86,7 +86,7 @@ int rglru_workspace_size(const rglru_desc *desc, int op, size_t *bytes)
     if (op == RGLRU_OP_SCAN_FWD) *bytes = fwd_workspace_bytes(desc->B, desc->T, desc->D);
     else if (op == RGLRU_OP_SCAN_BWD) {
         if (desc->D / desc->H != 256) return RGLRU_ERR_SHAPE;
-        *bytes = bwd_workspace_bytes(desc->B, desc->T, desc->D, desc->H);
+        *bytes = bwd_workspace_bytes(desc->B, desc->T, desc->D, desc->H, esize(*desc));
     } else return RGLRU_ERR_ARG;
     return RGLRU_OK;
 }
@@ -201,7 +201,7 @@ int rglru_scan_bwd(const rglru_desc *desc, const rglru_weights *w, const void *u
     for (const void *p : all)
         if (p && !aligned16(p)) return RGLRU_ERR_ALIGN;
     const rglru_desc &d = *desc;
-    const size_t need = bwd_workspace_bytes(d.B, d.T, d.D, d.H);
+    const size_t need = bwd_workspace_bytes(d.B, d.T, d.D, d.H, esize(d));
     if (ws_bytes < need) return RGLRU_ERR_WORKSPACE;
     const size_t act = d.B * d.T * d.D * esize(d), hist = d.B * 3 * d.D * esize(d);
     const size_t sb = d.B * d.D * 4, vec = d.D * 4, wb = d.H * 65536 * esize(d), wf = d.H * 65536 * 4;

@@ -15,28 +15,49 @@
 //     du_t    = sum_k cw[k] dx_{t+3-k},   dcw[k] = sum dx_t u_{t-3+k},   dcb = sum dx
 //
 // Passes (all on the caller's stream):
-//   1. forward states: the mode-A forward kernel keeps only the state before
-//      each 32-token chunk;
-//   2. transposed gate weights Wt[h][j][o'] (o' < 256: W_a, else W_x);
-//   3. the chunk kernel: persistent like the forward, workgroup w serves
-//      block g = w % G and claims the (stream, chunk) units of that block at
-//      run time, starting from the END of the sequence (unit j = cr*B + b
-//      with cr the chunk index counted from the end): recompute
-//      conv, gates (MFMA), decay and the states inside the chunk; reverse
-//      scan whose chunk carries eps go through the same decoupled look-back
-//      as the forward; local gradients; dx through the gates on the matrix
-//      cores; conv backward, whose last 3 tokens need the first 3 dx of the
-//      next chunk (published as tagged words); per-chunk partial sums; dz and
-//      x written channel-major in fp32 for pass 4;
-//   4. dW = sum over rows of dz x^T on the matrix cores, split over row
+//   1. forward states: a mode-A forward that keeps the state before each
+//      32-token chunk and the gate values r, i of every token (r in fp16 for
+//      bf16 I/O, i in fp32), and writes no y;
+//   2. the transposed gate weights, for bf16 in the exact order in which the
+//      dx products take them as matrix-core operands;
+//   3. the reverse carries: the affine aggregate of the reverse scan over
+//      each chunk (from r and dy), then a scan over the chunks of each
+//      stream, giving eps entering every chunk from its end, and dh0;
+//   4. the unit kernel.  With both carries known at every chunk, the
+//      (stream, chunk) units are independent: workgroup w serves block
+//      g = w % G and a contiguous range of its units taken stream by stream
+//      from the end of the sequence, so that each unit after the first of a
+//      range is the chunk before the previous one and finds that chunk's
+//      first 3 dx (which its conv backward needs) in registers.  Per unit,
+//      lane l = 32*half + n of wave w owns channel 32w + n and tokens
+//      32c + 16*half .. +15:
+//        - the conv window, r, i, dy and the chunk's two carries are loaded
+//          together;
+//        - two passes over the lane's tokens rebuild the forward states
+//          (aggregate, combine the halves, then the states themselves); one
+//          pass aggregates the reverse scan to combine the halves' eps;
+//        - the local gradients token by token, last token first;
+//        - dz goes to LDS, dx = delta beta i + W^T dz on the matrix cores with
+//          the weight operands streamed in batches of 8 K steps, prefetched
+//          one batch ahead;
+//        - conv backward, per-chunk partial sums; dz written channel-major
+//          in fp32 for the dW products.  At the first unit of a
+//          range the du of the chunk's last 3 tokens waits for dx that another
+//          workgroup makes: both sides leave their 3 dx in a small buffer and
+//          pass 5 finishes those tokens, so no workgroup ever waits on
+//          another;
+//   5. du of the range boundaries;
+//   6. dW = sum over rows of dz x^T on the matrix cores, split over row
 //      ranges into partials;
-//   5. deterministic reductions of the partials (fixed order, no atomics;
+//   7. deterministic reductions of the partials (fixed order, no atomics;
 //      the per-chunk sums in two steps, over unit splits then splits).
 // Precision (bf16 I/O): products whose operands are computed values (dz, x)
 // use a two-term split v = hi + lo with hi = bf16(v), lo = bf16(v - hi):
 // dx = W^T dz_hi + W^T dz_lo (W is exactly bf16), dW = dz_hi x_hi^T +
 // dz_hi x_lo^T + dz_lo x_hi^T; the bf16 rounding of dz or x alone would
-// cost up to 4e-2 relative on dW for short sequences.
+// cost up to 4e-2 relative on dW for short sequences.  The decay and its
+// normalisation are recomputed from r through e^l - 1 (l = log a), since
+// 1 - a^2 computed from a cancels for small |l|.
 #include <mutex>
 
 #include "common.h"
@@ -49,13 +70,17 @@ namespace {
 
 constexpr int NSUM = 8;   // per-chunk partial sums: dcw[4], dcb, db_a, db_x, dLambda
 constexpr int PS_SPLITS = 16;   // unit splits of the first reduction step
+constexpr int SCAN_SEGS = 4;    // chunk segments per stream in the carry scan
 
 struct BwdLayout {
-    size_t fwd_words, claims, bwd_words, hstart, Wt, dZt, Xt, psum, ppart, dWpart, total;
+    size_t fwd_words, hstart, ri, Wt, aggA, aggX, ein, bnd, dZt, psum, ppart, dWpart, total;
     int S;   // row-range splits of the dW products
 };
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// boundary buffers are sized for max(H, MAX_UNIT_WGS) unit workgroups
+constexpr int MAX_UNIT_WGS = 4096;
 
 BwdLayout bwd_layout(int64_t B, int64_t T, int64_t D, int64_t H, size_t esz)
 {
@@ -66,14 +91,17 @@ BwdLayout bwd_layout(int64_t B, int64_t T, int64_t D, int64_t H, size_t esz)
     if (S < 1) S = 1;
     if ((int64_t)S > B * NC) S = (int)(B * NC);
     L.S = S;
+    const size_t riu = esz == 2 ? GateStore<bf16>::UNIT_BYTES : GateStore<float>::UNIT_BYTES;
     size_t off = sizeof(WsHeader);
     L.fwd_words = off;  off = align256(fwd_workspace_bytes(B, T, D));   // claims + carry words
-    L.claims = off;     off = align256(off + claim_bytes(H));
-    L.bwd_words = off;  off = align256(off + 6 * NW * 8);
     L.hstart = off;     off = align256(off + NW * 4);
+    L.ri = off;         off = align256(off + (size_t)B * NC * H * riu);
     L.Wt = off;         off = align256(off + (size_t)H * 256 * 512 * esz);
+    L.aggA = off;       off = align256(off + NW * 4);
+    L.aggX = off;       off = align256(off + NW * 4);
+    L.ein = off;        off = align256(off + NW * 4);
+    L.bnd = off;        off = align256(off + (size_t)(H > MAX_UNIT_WGS ? H : MAX_UNIT_WGS) * 2 * 3 * 256 * 4);
     L.dZt = off;        off = align256(off + NW * 64 * 4);
-    L.Xt = off;         off = align256(off + NW * 32 * 4);
     L.psum = off;       off = align256(off + NW * NSUM * 4);
     L.ppart = off;      off = align256(off + (size_t)PS_SPLITS * D * NSUM * 4);
     L.dWpart = off;     off = align256(off + (size_t)S * H * 2 * 65536 * 4);
@@ -81,14 +109,52 @@ BwdLayout bwd_layout(int64_t B, int64_t T, int64_t D, int64_t H, size_t esz)
     return L;
 }
 
-// ------------------------------------------------------------------ pass 2
-template <typename T>
-__global__ __launch_bounds__(256) void transpose_w_kernel(const T *Wa, const T *Wx, T *Wt)
+// e^x - 1 for x <= 0 without the cancellation of exp(x) - 1 near 0: the
+// Taylor series through x^9/9! (Horner) for x > -1/2, where the first
+// omitted term is below 3e-10 of the result, else the hardware 2^x minus 1
+// (there |e^x - 1| > 0.39, so the subtraction costs under 2 ulp).
+__device__ __forceinline__ float expm1_neg(float x)
 {
-    // tile of 32 (o) x 32 (j); grid (256/32 j-tiles, 512/32 o'-tiles, H)
-    __shared__ T tile[32][33];
+    float t = fmaf(x, 1.0f / 362880.0f, 1.0f / 40320.0f);
+    t = fmaf(x, t, 1.0f / 5040.0f);
+    t = fmaf(x, t, 1.0f / 720.0f);
+    t = fmaf(x, t, 1.0f / 120.0f);
+    t = fmaf(x, t, 1.0f / 24.0f);
+    t = fmaf(x, t, 1.0f / 6.0f);
+    t = fmaf(x, t, 0.5f);
+    t = fmaf(x, t, 1.0f);
+    const float series = x * t;
+    const float big = hw_exp2(x * LOG2E) - 1.0f;
+    return x > -0.5f ? series : big;
+}
+
+// ------------------------------------------------------------------ pass 2
+// bf16: W^T as the B operands of the dx products.  Wave w of the unit kernel
+// makes dx for channels j = 32w .. 32w+31; K step s (0..31) covers rows
+// o' = 16s .. 16s+15 of the stacked [W_a; W_x] (o' < 256: W_a row o', else
+// W_x row o' - 256).  Lane l takes B[k][n] = W[o' = 16s + 8(l/32) + e][j = 32w
+// + l%32], e = 0..7, as the 16-byte vector WtOp[g][w][s][l], so a wave's load
+// of one K step is 1 KB of contiguous memory.  One thread per vector.
+__global__ __launch_bounds__(256) void wt_operands_kernel(const bf16 *Wa, const bf16 *Wx, bf16x8 *WtOp)
+{
+    const long v = (long)blockIdx.x * 256 + threadIdx.x;   // over G * 8 * 32 * 64 vectors
+    const int l = (int)(v & 63), s = (int)((v >> 6) & 31), w = (int)((v >> 11) & 7);
+    const int g = (int)(v >> 14);
+    const int j = 32 * w + (l & 31), o0 = 16 * s + 8 * (l >> 5);
+    const bf16 *src = (o0 < 256 ? Wa : Wx) + (size_t)g * 65536 + (size_t)(o0 & 255) * 256 + j;
+    bf16x8 out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = src[e * 256];
+    WtOp[v] = out;
+}
+
+// fp32: Wt[h][j][o'] row-major, tiles of 32 (o) x 32 (j); grid (256/32 j-tiles,
+// 512/32 o'-tiles, H)
+__global__ __launch_bounds__(256) void transpose_w_kernel(const float *Wa, const float *Wx, float *Wt)
+{
+    __shared__ float tile[32][33];
     const int h = blockIdx.z, j0 = blockIdx.x * 32, o0 = blockIdx.y * 32;
-    const T *src = (o0 < 256 ? Wa : Wx) + (size_t)h * 65536;
+    const float *src = (o0 < 256 ? Wa : Wx) + (size_t)h * 65536;
     const int ob = o0 & 255;
     for (int e = threadIdx.x; e < 1024; e += 256) {
         const int oo = e >> 5, jj = e & 31;
@@ -101,31 +167,88 @@ __global__ __launch_bounds__(256) void transpose_w_kernel(const T *Wa, const T *
     }
 }
 
-// dx[k] += sum_o Z[16h+k][o] * Wt_part[j][o] for the lane's channel j = 32w + n,
-// with Z = Zh + Zl (two LDS tiles, 32 x 256 in the XTile layout; Wt_part rows
-// have stride 512)
-__device__ __forceinline__ void dx_tile(const bf16 *Zh, const bf16 *Zl, const bf16 *Wt_part, int wave,
-                                        int lane, float dx[16])
+// ------------------------------------------------------------------ pass 3
+// Aggregate of the reverse scan over one chunk: eps_out = A eps_in + X with
+// eps_in entering at the chunk's last token.  One workgroup per (unit, block),
+// one thread per channel; tokens past the end are identity steps.
+template <typename T>
+__global__ __launch_bounds__(256) void rev_agg_kernel(int B, int T_, int D, int NC, int G, float c_,
+                                                      const float *Lambda, const void *ri, const void *dy,
+                                                      float *aggA, float *aggX)
 {
-    constexpr int S = XTile<bf16>::STRIDE;
-    const int r = lane & 31, kg = lane >> 5;
-    const int off = tile_row_token(r) * S + 8 * kg;
-    const bf16 *wrow = Wt_part + (size_t)(32 * wave + r) * 512 + 8 * kg;
-    f32x16 C = {};
+    using RT = typename GateStore<T>::rtype;
+    const int g = blockIdx.x % G;
+    const long unit = blockIdx.x / G;
+    const int b = (int)(unit / NC), c = (int)(unit % NC);
+    const int ch = threadIdx.x, d = g * 256 + ch;
+    const float ncs = -c_ * softplus_acc(-Lambda[d]);
+    RT rv[32];
+    {
+        const RT *rip = (const RT *)gate_store_unit<T>((void *)ri, b, c, NC, G, g) + ch * 32;
+        constexpr int V = 16 / sizeof(RT);
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-        const bf16x8 bv = *(const bf16x8 *)(wrow + 16 * s);
-        const bf16x8 ah = *(const bf16x8 *)(Zh + off + 16 * s);
-        const bf16x8 al = *(const bf16x8 *)(Zl + off + 16 * s);
-        C = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bv, C, 0, 0, 0);
-        C = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bv, C, 0, 0, 0);
+        for (int q = 0; q < 32 / V; ++q) *(uint4 *)(rv + q * V) = *(const uint4 *)(rip + q * V);
     }
+    const T *dyp = (const T *)dy + ((long)b * T_ + (long)c * CHUNK) * D + d;
+    const int nt = T_ - c * CHUNK < CHUNK ? T_ - c * CHUNK : CHUNK;
+    float g_[32];
+    if (nt == CHUNK) {   // full chunks: the 32 loads go out together
 #pragma unroll
-    for (int k = 0; k < 16; ++k) dx[k] += C[k];
+        for (int k = 0; k < 32; ++k) g_[k] = to_f32(dyp[(long)k * D]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 32; ++k) g_[k] = k < nt ? to_f32(dyp[(long)k * D]) : 0.0f;
+    }
+    float e = 0.0f, Rr = 1.0f;
+#pragma unroll
+    for (int k = 31; k >= 0; --k) {
+        const float ak = k < nt ? 1.0f + expm1_neg(ncs * (float)rv[k]) : 1.0f;
+        e = ak * (g_[k] + e);
+        Rr *= ak;
+    }
+    const long idx = ((long)b * NC + c) * D + d;
+    aggA[idx] = Rr;
+    aggX[idx] = e;
 }
 
-__device__ __forceinline__ void dx_tile(const float *Zs, const float *, const float *Wt_part, int wave,
-                                        int lane, float dx[16])
+// eps entering every chunk from its end, and dh0.  Each stream's chunks are
+// cut into SCAN_SEGS consecutive segments; thread (s, dd) of a workgroup of
+// (SCAN_SEGS x 64 channels) composes segment s, the segments' aggregates are
+// combined through LDS, and each thread then walks its segment again.
+// Grid (D / 64, B).
+__global__ __launch_bounds__(256) void rev_scan_kernel(int NC, int D, const float *aggA, const float *aggX,
+                                                       const float *dh_last, float *ein, float *dh0)
+{
+    __shared__ float sA[SCAN_SEGS][64], sX[SCAN_SEGS][64];
+    const int dd = threadIdx.x & 63, s = threadIdx.x >> 6;
+    const int d = blockIdx.x * 64 + dd, b = blockIdx.y;
+    const int c0 = (int)((long)NC * s / SCAN_SEGS), c1 = (int)((long)NC * (s + 1) / SCAN_SEGS);
+    const float *pa = aggA + (long)b * NC * D + d, *px = aggX + (long)b * NC * D + d;
+    float Ag = 1.0f, Xg = 0.0f;   // composition of chunks c1-1 .. c, last chunk first
+#pragma unroll 8
+    for (int c = c1 - 1; c >= c0; --c) {
+        const float a = pa[(long)c * D], x = px[(long)c * D];
+        Xg = fmaf(a, Xg, x);
+        Ag *= a;
+    }
+    sA[s][dd] = Ag;
+    sX[s][dd] = Xg;
+    __syncthreads();
+    float e = dh_last ? dh_last[(long)b * D + d] : 0.0f;
+    for (int t = SCAN_SEGS - 1; t > s; --t) e = fmaf(sA[t][dd], e, sX[t][dd]);
+    float *pe = ein + (long)b * NC * D + d;
+#pragma unroll 8
+    for (int c = c1 - 1; c >= c0; --c) {
+        pe[(long)c * D] = e;
+        e = fmaf(pa[(long)c * D], e, px[(long)c * D]);
+    }
+    if (s == 0 && dh0) dh0[(long)b * D + d] = e;
+}
+
+// fp32: dx[k] += sum_o Z[16 half + k][o] * Wt_part[j][o] for the lane's channel
+// j = 32w + n (Z: one LDS tile in the XTile layout; Wt_part rows have stride 512)
+__device__ __forceinline__ void dx_tile_f32(const float *Zs, const float *Wt_part, int wave, int lane,
+                                            float dx[16])
 {
     constexpr int S = XTile<float>::STRIDE;
     const int n = lane & 31, half = lane >> 5;
@@ -138,279 +261,349 @@ __device__ __forceinline__ void dx_tile(const float *Zs, const float *, const fl
     }
 }
 
-// write v into the A-operand tiles: hi part (or the value itself for fp32) and lo part
-__device__ __forceinline__ void put_split(bf16 *Zh, bf16 *Zl, int idx, float v)
-{
-    const bf16 hi = (bf16)v;
-    Zh[idx] = hi;
-    Zl[idx] = (bf16)(v - (float)hi);
-}
-__device__ __forceinline__ void put_split(float *Zh, float *, int idx, float v) { Zh[idx] = v; }
-
-__device__ __forceinline__ float wait_word(const uint64_t *p, uint32_t tag, WsHeader *hdr)
-{
-    float v;
-    uint32_t spins = 0;
-    while (!get_word(p, tag, v)) {
-        if (++spins > SPIN_LIMIT) {
-            __hip_atomic_store(&hdr->error, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            return __builtin_nanf("");
-        }
-        __builtin_amdgcn_s_sleep(4);
-    }
-    return v;
-}
-
 struct BwdParams {
-    int B, T, D, NC, G;
+    int B, T, D, NC, G, wpg;
     float c;
     const void *u, *hist_in, *dy;
-    const float *h0, *dh_last;
-    const float *cw, *cb, *ba, *bx, *Lambda;
-    const void *Wa, *Wx, *Wt;
-    const float *hstart;
+    const float *cw, *cb, *Lambda;
+    const void *Wt;       // bf16: operand order (pass 2); fp32: [H][256][512]
+    const void *ri;       // gate values of every token (GateStore layout)
+    const float *hstart;  // state before each chunk, [B][NC][D]
+    const float *ein;     // eps entering each chunk from its end, [B][NC][D]
     void *du;
-    float *dh0;
-    float *dZt, *Xt;
+    float *bnd;           // [unit workgroup][2][3][256]: range-boundary dx
+    float *dZt;
     float *psum;
-    int units;          // B * NC per block
-    WsHeader *hdr;
-    uint32_t *claim;    // [G] unit counters
-    uint64_t *aggA, *aggX, *incl, *halo;   // halo: 3 consecutive arrays of [B][NC][D]
 };
 
-// ------------------------------------------------------------------ pass 3
+// Inputs of one unit as loaded (raw storage types), and their loader.  Every
+// address is a workgroup-uniform base plus a 32-bit per-lane offset (D is at
+// most 2^24, so 35 rows of D channels stay below 2^32 bytes).  Tokens past the
+// end read the last token, and positions before the sequence read row 0; both
+// are masked where used.
 template <typename T>
-__global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p)
+struct UnitIn {
+    T win[19];                                   // u at tokens tb - 3 .. tb + 15
+    typename GateStore<T>::rtype rv[16];         // r, i at tokens tb .. tb + 15
+    float iv[16];
+    T dy[16];
+    T hist[3];                                   // history rows (chunk 0, when given)
+    float hs, es;                                // the chunk's two carries
+};
+
+template <typename T>
+__device__ __forceinline__ void unit_load(UnitIn<T> &v, const BwdParams &p, long q, int g, int ch, int half)
 {
+    using RT = typename GateStore<T>::rtype;
+    const int b = (int)(q / p.NC), c = p.NC - 1 - (int)(q % p.NC);
+    const long row_b = (long)b * p.T;
+    const int t0 = c * CHUNK, tb = t0 + 16 * half;
+    const uint32_t D = (uint32_t)p.D;
+    const int rb = c > 0 ? t0 - 3 : 0;   // first row the window reads
+    const T *ub = (const T *)p.u + (row_b + rb) * p.D + g * 256;
+    const T *dyb = (const T *)p.dy + (row_b + t0) * p.D + g * 256;
+    if (c > 0 && t0 + CHUNK <= p.T) {   // interior chunk: straight rows
+        uint32_t lo = (uint32_t)(16 * half) * D + (uint32_t)ch;
+        asm volatile("" : "+v"(lo));   // keep the 35 offsets inside the unit loop
+#pragma unroll
+        for (int m = 0; m < 19; ++m) v.win[m] = *at(ub, lo + (uint32_t)m * D);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v.dy[k] = *at(dyb, lo + (uint32_t)k * D);
+    } else {
+#pragma unroll
+        for (int m = 0; m < 19; ++m) {
+            const int tau = tb - 3 + m;
+            const int tc = tau < 0 ? 0 : (tau > p.T - 1 ? p.T - 1 : tau);
+            v.win[m] = *at(ub, (uint32_t)(tc - rb) * D + (uint32_t)ch);
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int tc = tb + k > p.T - 1 ? p.T - 1 : tb + k;
+            v.dy[k] = *at(dyb, (uint32_t)(tc - t0) * D + (uint32_t)ch);
+        }
+    }
+    if (c == 0 && p.hist_in) {
+        const T *hb = (const T *)p.hist_in + (long)b * 3 * p.D + g * 256;
+#pragma unroll
+        for (int m = 0; m < 3; ++m) v.hist[m] = *at(hb, (uint32_t)m * D + (uint32_t)ch);
+    }
+    const char *u0 = gate_store_unit<T>((void *)p.ri, b, c, p.NC, p.G, g);
+    const RT *rib = (const RT *)u0;
+    const float *iib = (const float *)(u0 + GateStore<T>::R_BYTES);
+    constexpr int V = 16 / sizeof(RT);
+    const uint32_t ro = (uint32_t)(ch * 32 + 16 * half);
+#pragma unroll
+    for (int qq = 0; qq < 16 / V; ++qq) *(uint4 *)(v.rv + qq * V) = *at((const uint4 *)rib, (ro + qq * V) / V);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) *(uint4 *)(v.iv + qq * 4) = *at((const uint4 *)iib, (ro + qq * 4) / 4);
+    const long cb = ((long)b * p.NC + c) * p.D + g * 256;
+    v.hs = *at(p.hstart + cb, (uint32_t)ch);
+    v.es = *at(p.ein + cb, (uint32_t)ch);
+}
+
+// LDS of the unit kernel: two pairs of dz^a and dz^x tiles for the dx
+// products (consecutive units alternate), 32 token rows each in the XTile
+// layout.
+// bf16: dz enters the dx products as hi + lo (the two-term split), so each
+// set holds four tiles (dz^a hi, lo, dz^x hi, lo)
+constexpr bool DX_SPLIT = true;
+template <typename T> constexpr int unit_tiles() { return sizeof(T) == 2 && DX_SPLIT ? 4 : 2; }
+template <typename T> constexpr size_t unit_lds_bytes()
+{
+    return (size_t)2 * unit_tiles<T>() * 32 * XTile<T>::STRIDE * sizeof(T);
+}
+
+// ------------------------------------------------------------------ pass 4
+template <typename T>
+__global__ __launch_bounds__(512) void bwd_unit_kernel(BwdParams p)
+{
+    using RT = typename GateStore<T>::rtype;
+    constexpr bool MF = sizeof(T) == 2;   // dx on the matrix cores
     constexpr int S = XTile<T>::STRIDE;
+    constexpr int TILE = 32 * S;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    T *Xs = (T *)smem;             // x tile, then dz (hi part)
-    T *Zl = Xs + 32 * S;           // dz lo part (bf16 only)
-    uint32_t *s_unit = (uint32_t *)(smem + 2 * 32 * S * sizeof(T));   // [2] + flag
-    const uint32_t tag = launch_tag(p.hdr);
-    const int g = blockIdx.x % p.G;
+    T *Z = (T *)smem;
+    const int g = blockIdx.x % p.G, kw = blockIdx.x / p.G;   // block, range index
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 31, half = lane >> 5;
     const int ch = wave * 32 + n;          // channel inside the block
-    const int d = g * 256 + ch;
+    const int d = g * 256 + ch;            // D = 256 G: always a real channel
     const T *u = (const T *)p.u;
-    const uint32_t units = (uint32_t)p.units;
-    uint32_t *claim = p.claim + g;
 
-    // Unit u_m of this workgroup travels through claim slot m & 1: thread 0
-    // claims u_{n+1} at the start of iteration n and stores it at the end.
-    if (tid == 0) s_unit[0] = claim_next(claim);
-    for (int it = 0;; ++it) {
-    __syncthreads();   // the claim slot and the LDS tiles of the previous unit are free
-    const uint32_t j = s_unit[it & 1];
-    if (j >= units) break;
-    uint32_t my_claim = 0;
-    if (tid == 0) my_claim = claim_next(claim);
-    const int b = (int)(j % p.B);
-    const int cr = (int)(j / p.B);         // chunk index counted from the end
-    const int c = p.NC - 1 - cr;
+    const float w0 = p.cw[4 * (long)d + 0], w1 = p.cw[4 * (long)d + 1];
+    const float w2 = p.cw[4 * (long)d + 2], w3 = p.cw[4 * (long)d + 3];
+    const float bias = p.cb ? p.cb[d] : 0.0f;
+    const float lam = p.Lambda[d];
+    const float ncs = -p.c * softplus_acc(-lam);   // log a_t = ncs r_t
+    const float sgm = sigmoid_acc(-lam);
+    // this wave's weight operands: a wave-uniform base and a 32-bit offset per load
+    const bf16x8 *wop = (const bf16x8 *)p.Wt + (size_t)(g * 8 + __builtin_amdgcn_readfirstlane(wave)) * 32 * 64;
+
+    // units q = b NC + (NC - 1 - c): streams in order, chunks from the end
+    const long U = (long)p.B * p.NC;
+    const long q0 = U * kw / p.wpg, q1 = U * (kw + 1) / p.wpg;
+    float cx0 = 0.0f, cx1 = 0.0f, cx2 = 0.0f;   // half 1: first 3 dx of the chunk after this one
+    for (long q = q0; q < q1; ++q) {
+    const int b = (int)(q / p.NC);
+    const int c = p.NC - 1 - (int)(q % p.NC);
     const int tb = c * CHUNK + 16 * half;
     const long row_b = (long)b * p.T;
     const long cidx = ((long)b * p.NC + c) * p.D + d;   // [B][NC][D] index of this chunk
 
-    // conv recompute (window kept for dcw)
-    const float w0 = p.cw[4 * (long)d + 0], w1 = p.cw[4 * (long)d + 1];
-    const float w2 = p.cw[4 * (long)d + 2], w3 = p.cw[4 * (long)d + 3];
-    const float bias = p.cb ? p.cb[d] : 0.0f;
-    // the 19 loads go out together: addresses are selected, not branched on
-    // (positions past the end or before a missing history read element 0 and
-    // are zeroed afterwards)
+    UnitIn<T> cur;
+    unit_load(cur, p, q, g, ch, half);
+    const bool c0hist = c == 0 && p.hist_in;
     float win[19];
-    {
-        T raw[19];
 #pragma unroll
-        for (int m = 0; m < 19; ++m) {
-            const int tau = tb - 3 + m;
-            const T *src = u;
-            if (tau >= 0 && tau < p.T) src = u + (row_b + tau) * p.D + d;
-            else if (tau < 0 && p.hist_in) src = (const T *)p.hist_in + ((long)b * 3 + 3 + tau) * p.D + d;
-            raw[m] = *src;
-        }
-#pragma unroll
-        for (int m = 0; m < 19; ++m) {
-            const int tau = tb - 3 + m;
-            const bool ok = tau < p.T && (tau >= 0 || p.hist_in);
-            win[m] = ok ? to_f32(raw[m]) : 0.0f;
-        }
+    for (int m = 0; m < 19; ++m) {
+        const int tau = tb - 3 + m;
+        float v = tau < p.T ? to_f32(cur.win[m]) : 0.0f;
+        if (m < 3 && tau < 0) v = c0hist ? to_f32(cur.hist[m]) : 0.0f;
+        win[m] = v;
     }
-    float x[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k)
-        x[k] = fmaf(w3, win[k + 3], fmaf(w2, win[k + 2], fmaf(w1, win[k + 1], fmaf(w0, win[k], bias))));
-
-    // gates
-#pragma unroll
-    for (int k = 0; k < 16; ++k) Xs[(16 * half + k) * S + ch] = from_f32<T>(x[k]);
-    {   // x, channel-major per chunk, for the dW products
-        float *xt = p.Xt + ((((long)b * p.NC + c) * p.G + g) * 256 + ch) * 32 + 16 * half;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            *(f32x4 *)(xt + 4 * q) = f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
-    }
-    __syncthreads();
-    float za[16], zx[16];
-    gate_tile(Xs, (const T *)p.Wa + (size_t)g * 65536, (const T *)p.Wx + (size_t)g * 65536, wave, lane,
-              za, zx);
-
-    // decay, normalisation and the forward states inside the chunk
-    const float lam = p.Lambda[d];
-    const float ncs = -p.c * softplus_acc(-lam);
-    const float sgm = sigmoid_acc(-lam);
-    const float bav = p.ba ? p.ba[d] : 0.0f, bxv = p.bx ? p.bx[d] : 0.0f;
-    float a[16], hl[16], P[16];
-    float h = 0.0f, pr = 1.0f;
+    RT rv[16];
+    float iv[16];
+    T dyr[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-        za[k] = sigmoid_acc(za[k] + bav);   // r
-        zx[k] = sigmoid_acc(zx[k] + bxv);   // i
-        float ak = expf(ncs * za[k]);
-        float bb = sqrtf(-expm1f(2.0f * ncs * za[k])) * zx[k] * x[k];
-        if (tb + k >= p.T) {
-            ak = 1.0f;
-            bb = 0.0f;
-        }
-        a[k] = ak;
-        h = fmaf(ak, h, bb);
-        pr *= ak;
-        hl[k] = h;
-        P[k] = pr;
+        rv[k] = cur.rv[k];
+        iv[k] = cur.iv[k];
+        dyr[k] = cur.dy[k];
     }
-    const float A0 = __shfl_xor(P[15], 32), X0 = __shfl_xor(hl[15], 32);
-    const float hs_chunk = p.hstart[cidx];
-    const float hs_lane = half == 0 ? hs_chunk : fmaf(A0, hs_chunk, X0);
+    const float hs_chunk = cur.hs, es_chunk = cur.es;
+    auto xk = [&](int k) {
+        return fmaf(w3, win[k + 3], fmaf(w2, win[k + 2], fmaf(w1, win[k + 1], fmaf(w0, win[k], bias))));
+    };
 
-    // reverse scan inside the lane (eps entering the lane's last token = 0)
-    const T *dyp = (const T *)p.dy;
-    float gdy[16];
+    // ---- forward aggregate of the lane's tokens.  With l = ncs r and
+    // m = e^l - 1 (kept per token): a = 1 + m, and 1 - a^2 = -m (2 + m)
+    // without cancellation; beta = sqrt(1 - a^2).  Tokens past the end get
+    // m = 0 (a = 1, beta = 0: the identity step).
+    float em[16];
+    auto dec = [&](int k, float &ak, float &om) {
+        ak = 1.0f + em[k];
+        om = -em[k] * (2.0f + em[k]);
+    };
+    float hs_lane;   // state before the lane's first token
     {
-        T raw[16];
+        float h = 0.0f, pr = 1.0f;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) raw[k] = dyp[tb + k < p.T ? (row_b + tb + k) * p.D + d : 0];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) gdy[k] = tb + k < p.T ? to_f32(raw[k]) : 0.0f;
-    }
-    float dl[16], R[16];
-    float e = 0.0f, Rrun = 1.0f;
-#pragma unroll
-    for (int k = 15; k >= 0; --k) {
-        const float gk = gdy[k];
-        dl[k] = gk + e;
-        R[k] = Rrun;
-        e = a[k] * dl[k];
-        Rrun *= a[k];
-    }
-    // chunk carry: half 1 is first in reverse order
-    const float A1 = __shfl_xor(Rrun, 32), X1 = __shfl_xor(e, 32);
-    float ein_chunk = 0.0f;
-    if (half == 0) {
-        const float Ach = Rrun * A1;
-        const float Xch = fmaf(Rrun, X1, e);
-        const long base = (long)b * p.NC * p.D + d;
-        const long widx = base + (long)cr * p.D;
-        const float ebefore = p.dh_last ? p.dh_last[(long)b * p.D + d] : 0.0f;
-        put_word(p.aggA + widx, Ach, tag);
-        put_word(p.aggX + widx, Xch, tag);
-        if (cr == 0) {
-            ein_chunk = ebefore;
-        } else {
-            ein_chunk = look_back(p.aggA + base, p.aggX + base, p.incl + base, cr - 1, p.D, ebefore,
-                                  tag, p.hdr);
+        for (int k = 0; k < 16; ++k) {
+            const float mk = expm1_neg(ncs * (float)rv[k]);
+            em[k] = tb + k < p.T ? mk : 0.0f;
+            float ak, om;
+            dec(k, ak, om);
+            h = fmaf(ak, h, hw_sqrt(om) * (float)iv[k] * xk(k));
+            pr *= ak;
         }
-        const float eout = fmaf(Ach, ein_chunk, Xch);
-        put_word(p.incl + widx, eout, tag);
-        if (c == 0 && p.dh0) p.dh0[(long)b * p.D + d] = eout;
+        const float A0 = __shfl_xor(pr, 32), X0 = __shfl_xor(h, 32);
+        // half 0 starts at the chunk's start state, half 1 after half 0's tokens
+        hs_lane = half == 0 ? hs_chunk : fmaf(A0, hs_chunk, X0);
     }
-    const float eother = __shfl_xor(ein_chunk, 32);
-    const float ein_lane = half == 1 ? eother : fmaf(A1, ein_chunk, X1);
 
-    // local gradients
+    // ---- eps entering the lane's last token: half 1 gets the chunk's, half 0
+    // that after half 1's tokens (aggregate of half 1's reverse scan)
+    float gd[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) gd[k] = tb + k < p.T ? to_f32(dyr[k]) : 0.0f;
+    float eps;
+    {
+        float e = 0.0f, Rr = 1.0f;
+#pragma unroll
+        for (int k = 15; k >= 0; --k) {
+            const float ak = 1.0f + em[k];
+            e = ak * (gd[k] + e);
+            Rr *= ak;
+        }
+        const float A1 = __shfl_xor(Rr, 32), X1 = __shfl_xor(e, 32);
+        eps = half == 1 ? es_chunk : fmaf(A1, es_chunk, X1);
+    }
+
+    // ---- the states before each token, from the lane's start state
+    float hp[16];
+    {
+        float h = hs_lane;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            float ak, om;
+            dec(k, ak, om);
+            hp[k] = h;
+            h = fmaf(ak, h, hw_sqrt(om) * (float)iv[k] * xk(k));
+        }
+    }
+
+    // ---- local gradients, last token first (a^2 / beta = a^2 rsq(1 - a^2)).
+    // dz goes to this unit's LDS tiles (the two tile pairs alternate between
+    // units, and the barrier ending the previous unit's tiles also ended all
+    // reads of this pair) and, 4 tokens at a time, to the dW staging.
+    constexpr int NT = unit_tiles<T>();
+    constexpr int ZX = NT / 2 * TILE;   // offset of the dz^x tile(s)
+    T *Zu = Z + (q & 1) * NT * TILE;
+    float *zt = p.dZt + (((((long)b * p.NC + c) * p.G + g) * 2) * 256 + ch) * 32 + 16 * half;
     float dxv[16];
     float s_ba = 0.0f, s_bx = 0.0f, s_rl = 0.0f;
-    float hprev = hs_lane;
+    f32x4 za4, zx4;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const float delta = fmaf(R[k], ein_lane, dl[k]);
-        const float hk = fmaf(P[k], hs_lane, hl[k]);
-        const float r = za[k], ii = zx[k];
-        float dza = 0.0f, dzx = 0.0f, dxd = 0.0f;
-        if (tb + k < p.T) {
-            const float l = ncs * r;
-            const float beta = sqrtf(-expm1f(2.0f * l));
-            const float dlk = delta * (a[k] * hprev - (a[k] * a[k] / beta) * ii * x[k]);
-            const float di = delta * beta * x[k];
-            dxd = delta * beta * ii;
-            dza = ncs * dlk * r * (1.0f - r);
-            dzx = di * ii * (1.0f - ii);
-            s_rl = fmaf(r, dlk, s_rl);
+    for (int k = 15; k >= 0; --k) {
+        float ak, om;
+        dec(k, ak, om);
+        const float delta = gd[k] + eps;
+        eps = ak * delta;
+        const float r = (float)rv[k], ii = (float)iv[k], x = xk(k);
+        const float bk = hw_sqrt(om), qk = ak * ak * __builtin_amdgcn_rsqf(om);
+        const float dl = delta * (ak * hp[k] - qk * ii * x);
+        const float di = delta * bk * x;
+        const bool ok = tb + k < p.T;
+        const float za = ok ? ncs * dl * r * (1.0f - r) : 0.0f;
+        const float zx = ok ? di * ii * (1.0f - ii) : 0.0f;
+        dxv[k] = ok ? delta * bk * ii : 0.0f;
+        s_rl += ok ? r * dl : 0.0f;
+        s_ba += za;
+        s_bx += zx;
+        const int idx = (16 * half + k) * S + ch;
+        if constexpr (NT == 4) {
+            const bf16 ha = (bf16)za, hx = (bf16)zx;
+            Zu[idx] = ha;
+            Zu[TILE + idx] = (bf16)(za - (float)ha);
+            Zu[ZX + idx] = hx;
+            Zu[ZX + TILE + idx] = (bf16)(zx - (float)hx);
+        } else {
+            Zu[idx] = from_f32<T>(za);
+            Zu[ZX + idx] = from_f32<T>(zx);
         }
-        s_ba += dza;
-        s_bx += dzx;
-        dxv[k] = dxd;
-        za[k] = dza;   // reuse: dz^a
-        zx[k] = dzx;   // reuse: dz^x
-        hprev = hk;
+        za4[k & 3] = za;
+        zx4[k & 3] = zx;
+        if ((k & 3) == 0) {
+            *(f32x4 *)(zt + k) = za4;
+            *(f32x4 *)(zt + 256 * 32 + k) = zx4;
+        }
     }
-    {   // dz, channel-major per chunk, for the dW products
-        float *zt = p.dZt + (((((long)b * p.NC + c) * p.G + g) * 2) * 256 + ch) * 32 + 16 * half;
+    __syncthreads();   // the dz tiles are complete 
+
+    // ---- dx through the gates
+    if constexpr (MF) {
+        // A = dz rows (tokens, permuted by tile_row_token) x o', B = W^T; the
+        // accumulator starts at the direct term and ends as dx in the lane's
+        // own layout (register k = token 16 half + k)
+        const int r = lane & 31, kg = lane >> 5;
+        const int roff = tile_row_token(r) * S + 8 * kg;
+        f32x16 C;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            *(f32x4 *)(zt + 4 * q) = f32x4{za[4 * q], za[4 * q + 1], za[4 * q + 2], za[4 * q + 3]};
-            *(f32x4 *)(zt + 256 * 32 + 4 * q) = f32x4{zx[4 * q], zx[4 * q + 1], zx[4 * q + 2], zx[4 * q + 3]};
+        for (int k = 0; k < 16; ++k) C[k] = dxv[k];
+        // K steps in batches of 8 (batch t: steps 8t .. 8t+7, dz^a for t < 2);
+        // batch t + 1 is requested before batch t goes to the matrix cores
+        bf16x8 b0[8], b1[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) b0[s] = *at(wop, (uint32_t)(s * 64 + lane));
+#pragma unroll 1
+        for (int bp = 0; bp < 2; ++bp) {   // batches 2bp (in b0) and 2bp + 1 (in b1)
+            const T *zt = Zu + bp * ZX + roff;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) b1[s] = *at(wop, (uint32_t)((16 * bp + 8 + s) * 64 + lane));
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const bf16x8 av = *(const bf16x8 *)(zt + 16 * s);
+                C = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b0[s], C, 0, 0, 0);
+                if constexpr (NT == 4) {
+                    const bf16x8 al = *(const bf16x8 *)(zt + TILE + 16 * s);
+                    C = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b0[s], C, 0, 0, 0);
+                }
+            }
+            if (bp == 0) {
+#pragma unroll
+                for (int s = 0; s < 8; ++s) b0[s] = *at(wop, (uint32_t)((16 + s) * 64 + lane));
+            }
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const bf16x8 av = *(const bf16x8 *)(zt + 16 * (8 + s));
+                C = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b1[s], C, 0, 0, 0);
+                if constexpr (NT == 4) {
+                    const bf16x8 al = *(const bf16x8 *)(zt + TILE + 16 * (8 + s));
+                    C = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b1[s], C, 0, 0, 0);
+                }
+            }
         }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) dxv[k] = C[k];
+    } else {
+        const float *Wt_h = (const float *)p.Wt + (size_t)g * 131072;
+        dx_tile_f32((const float *)Zu, Wt_h, wave, lane, dxv);
+        dx_tile_f32((const float *)Zu + ZX, Wt_h + 256, wave, lane, dxv);
     }
 
-    // dx through the gates: two passes over the LDS tiles (dz^a, then dz^x)
-    const T *Wt_h = (const T *)p.Wt + (size_t)g * 131072;
-    __syncthreads();   // every wave is done with the x tile
-#pragma unroll
-    for (int k = 0; k < 16; ++k) put_split(Xs, Zl, (16 * half + k) * S + ch, za[k]);
-    __syncthreads();
-    dx_tile(Xs, Zl, Wt_h, wave, lane, dxv);
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 16; ++k) put_split(Xs, Zl, (16 * half + k) * S + ch, zx[k]);
-    __syncthreads();
-    dx_tile(Xs, Zl, Wt_h + 256, wave, lane, dxv);
-#pragma unroll
-    for (int k = 0; k < 16; ++k)
-        if (tb + k >= p.T) dxv[k] = 0.0f;
-
-    // conv backward: publish this chunk's first 3 dx before waiting for the next chunk's
-    const long NW = (long)p.B * p.NC * p.D;
-    if (half == 0) {
-        put_word(p.halo + cidx, dxv[0], tag);
-        put_word(p.halo + NW + cidx, dxv[1], tag);
-        put_word(p.halo + 2 * NW + cidx, dxv[2], tag);
-    }
+    // ---- conv backward.  The 3 tokens after the lane's 16: half 0 takes
+    // half 1's first dx; half 1 those of the next chunk, carried from the
+    // previous unit of the range; at the range's first unit they come from
+    // another workgroup, so those 3 du are left to the boundary pass.
+    const bool first = q == q0, last_chunk = c == p.NC - 1;
     const float o0 = __shfl_xor(dxv[0], 32), o1 = __shfl_xor(dxv[1], 32), o2 = __shfl_xor(dxv[2], 32);
-    float n0 = 0.0f, n1 = 0.0f, n2 = 0.0f;   // dx of the 3 tokens after the lane's 16
-    if (half == 0) {
-        n0 = o0;
-        n1 = o1;
-        n2 = o2;
-    } else if (c + 1 < p.NC) {
-        const long nidx = cidx + p.D;        // chunk c+1
-        n0 = wait_word(p.halo + nidx, tag, p.hdr);
-        n1 = wait_word(p.halo + NW + nidx, tag, p.hdr);
-        n2 = wait_word(p.halo + 2 * NW + nidx, tag, p.hdr);
-    }
     float ext[19];
 #pragma unroll
     for (int k = 0; k < 16; ++k) ext[k] = dxv[k];
-    ext[16] = n0;
-    ext[17] = n1;
-    ext[18] = n2;
+    ext[16] = half == 0 ? o0 : (last_chunk ? 0.0f : cx0);
+    ext[17] = half == 0 ? o1 : (last_chunk ? 0.0f : cx1);
+    ext[18] = half == 0 ? o2 : (last_chunk ? 0.0f : cx2);
+    const bool open_end = half == 1 && first && !last_chunk;   // last 3 du wait for pass 5
+    float *bnd = p.bnd + (long)blockIdx.x * 2 * 3 * 256;
+    if (open_end) {
+        bnd[0 * 256 + ch] = dxv[13];
+        bnd[1 * 256 + ch] = dxv[14];
+        bnd[2 * 256 + ch] = dxv[15];
+    }
+    if (q == q1 - 1 && half == 0 && kw + 1 < p.wpg) {   // first 3 dx, for the next range's boundary
+        float *nb = p.bnd + ((long)blockIdx.x + p.G) * 2 * 3 * 256 + 3 * 256;
+        nb[0 * 256 + ch] = dxv[0];
+        nb[1 * 256 + ch] = dxv[1];
+        nb[2 * 256 + ch] = dxv[2];
+    }
+    cx0 = o0;   // half 1: this chunk's first dx, for the unit after
+    cx1 = o1;
+    cx2 = o2;
     T *du = (T *)p.du;
     float s_cb = 0.0f, s_w0 = 0.0f, s_w1 = 0.0f, s_w2 = 0.0f, s_w3 = 0.0f;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-        if (tb + k < p.T) {
+        if (tb + k < p.T && !(open_end && k >= 13)) {
             const float duk = fmaf(w0, ext[k + 3], fmaf(w1, ext[k + 2], fmaf(w2, ext[k + 1], w3 * ext[k])));
             du[(row_b + tb + k) * p.D + d] = from_f32<T>(duk);
         }
@@ -424,30 +617,114 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdParams p)
     // per-chunk partial sums (half 0 + half 1), written by half 0
     float v[NSUM] = {s_w0, s_w1, s_w2, s_w3, s_cb, s_ba, s_bx, s_rl};
 #pragma unroll
-    for (int q = 0; q < NSUM; ++q) v[q] += __shfl_xor(v[q], 32);
+    for (int qq = 0; qq < NSUM; ++qq) v[qq] += __shfl_xor(v[qq], 32);
     if (half == 0) {
         v[7] *= p.c * sgm;
         float4 *dst = (float4 *)(p.psum + cidx * NSUM);
         dst[0] = make_float4(v[0], v[1], v[2], v[3]);
         dst[1] = make_float4(v[4], v[5], v[6], v[7]);
     }
-    if (tid == 0) s_unit[(it + 1) & 1] = my_claim;   // read after the next barrier
     }   // units
-    __syncthreads();
-    finish_claimed(p.hdr, p.claim, p.G, s_unit + 2);
 }
 
-// ------------------------------------------------------------------ pass 4
+// ------------------------------------------------------------------ pass 5
+// du of the last 3 tokens of each range's first chunk, from that chunk's last
+// 3 dx and the next chunk's first 3 dx, both left by the unit kernel.  One
+// workgroup per unit workgroup, one thread per channel of its block.
+template <typename T>
+__global__ __launch_bounds__(256) void range_bound_kernel(int B, int T_, int D, int NC, int G, int wpg,
+                                                          const float *cw, const float *bnd, void *du_)
+{
+    const int w = blockIdx.x, g = w % G, kw = w / G;
+    if (kw == 0) return;
+    const long U = (long)B * NC, q0 = U * kw / wpg;
+    const int b = (int)(q0 / NC), c = NC - 1 - (int)(q0 % NC);
+    if (c == NC - 1) return;   // the stream's last chunk: nothing after it
+    const int ch = threadIdx.x, d = g * 256 + ch;
+    const float *own = bnd + (long)w * 2 * 3 * 256, *nxt = own + 3 * 256;
+    const float e[6] = {own[ch], own[256 + ch], own[512 + ch], nxt[ch], nxt[256 + ch], nxt[512 + ch]};
+    const float w0 = cw[4 * (long)d + 0], w1 = cw[4 * (long)d + 1];
+    const float w2 = cw[4 * (long)d + 2], w3 = cw[4 * (long)d + 3];
+    T *du = (T *)du_;
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+        const long t = (long)c * CHUNK + 29 + m;   // chunk c is full: t < T
+        const float v = fmaf(w0, e[m + 3], fmaf(w1, e[m + 2], fmaf(w2, e[m + 1], w3 * e[m])));
+        du[((long)b * T_ + t) * D + d] = from_f32<T>(v);
+    }
+}
+
+// ------------------------------------------------------------------ pass 6
 // dW[q][o][j] over the row range of split s: sum_{units, t} dz_q[o][t] x[j][t].
+// x is recomputed from u (the conv in the unit kernel's order of operations,
+// so the values are the same), which costs less memory traffic than staging
+// it.  Positions past the end give finite values whose dz is 0.
+struct ConvIn {
+    const void *u, *hist_in;
+    const float *cw, *cb;
+    int T, D, NC;
+};
+
+// the 19 inputs of tokens t0 .. t0+15 of unit un (b = un / NC, c = un % NC),
+// channel d, as stored
+template <typename T>
+__device__ __forceinline__ void conv_window_load(const ConvIn &ci, int un, int t_off, int d, T raw[19])
+{
+    const int b = un / ci.NC, c = un % ci.NC;
+    const int t0 = c * CHUNK + t_off;
+    const T *u = (const T *)ci.u + (long)b * ci.T * ci.D + d;
+    if (c > 0 && (c + 1) * CHUNK <= ci.T) {
+        const T *src = u + (long)(t0 - 3) * ci.D;
+#pragma unroll
+        for (int m = 0; m < 19; ++m) raw[m] = src[(long)m * ci.D];
+    } else {
+#pragma unroll
+        for (int m = 0; m < 19; ++m) {
+            const int tau = t0 - 3 + m;
+            const int tc = tau < 0 ? 0 : (tau > ci.T - 1 ? ci.T - 1 : tau);
+            raw[m] = u[(long)tc * ci.D];
+            if (tau < 0 && ci.hist_in) raw[m] = ((const T *)ci.hist_in)[((long)b * 3 + 3 + tau) * ci.D + d];
+        }
+    }
+}
+
+// conv taps and bias of one channel
+struct ConvTaps {
+    float w0, w1, w2, w3, bias;
+};
+__device__ __forceinline__ ConvTaps conv_taps(const ConvIn &ci, int d)
+{
+    return ConvTaps{ci.cw[4 * (long)d + 0], ci.cw[4 * (long)d + 1], ci.cw[4 * (long)d + 2],
+                    ci.cw[4 * (long)d + 3], ci.cb ? ci.cb[d] : 0.0f};
+}
+
+template <typename T>
+__device__ __forceinline__ void conv_window_x(const ConvIn &ci, const ConvTaps &w, int un, int t_off,
+                                              const T raw[19], float x[16])
+{
+    const int c = un % ci.NC;
+    const int t0 = c * CHUNK + t_off;
+    const float w0 = w.w0, w1 = w.w1, w2 = w.w2, w3 = w.w3, bias = w.bias;
+    float win[19];
+#pragma unroll
+    for (int m = 0; m < 19; ++m) {
+        const int tau = t0 - 3 + m;
+        win[m] = tau < ci.T && (tau >= 0 || ci.hist_in) ? to_f32(raw[m]) : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+        x[k] = fmaf(w3, win[k + 3], fmaf(w2, win[k + 2], fmaf(w1, win[k + 1], fmaf(w0, win[k], bias))));
+}
+
 // bf16 I/O: wave w owns rows o = 32w..32w+31 and all 256 columns (8 MFMA
 // tiles); both operands are split into bf16 hi + lo and three products are
-// accumulated (hi*hi + hi*lo + lo*hi).  Each unit's x tile is split once and
-// staged in LDS for all 8 waves; the next unit's x and dz are requested while
-// the current one is on the matrix cores.
+// accumulated (hi*hi + hi*lo + lo*hi).  Each unit's x tile is computed and
+// split once and staged in LDS for all 8 waves; the next unit's u window and
+// dz are requested while the current one is on the matrix cores.
 constexpr int DW_XS = 40;   // LDS row stride (bf16) of a staged x tile: 32 tokens + 8 pad
 
-__global__ __launch_bounds__(512) void dw_kernel_bf16(int units, int G, int S, const float *dZt,
-                                                      const float *Xt, float *dWpart)
+__global__ __launch_bounds__(512) void dw_kernel_bf16(int units, int G, int S, const float *dZt, ConvIn ci,
+                                                      float *dWpart)
 {
     // x of the current unit, split into bf16 hi and lo, [256 j][32 t] each
     __shared__ __attribute__((aligned(16))) bf16 Xh[256 * DW_XS], Xl[256 * DW_XS];
@@ -455,16 +732,17 @@ __global__ __launch_bounds__(512) void dw_kernel_bf16(int units, int G, int S, c
     const int u0 = (int)((long)units * s / S), u1 = (int)((long)units * (s + 1) / S);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 31, kg = lane >> 5;
-    // staging: thread t splits x[j = t/2][16 (t&1) .. +15]
+    // staging: thread t makes x[j = t/2][16 (t&1) .. +15]
     const int sj = tid >> 1, st = 16 * (tid & 1);
+    const int dj = g * 256 + sj;
+    const ConvTaps taps = conv_taps(ci, dj);
     f32x16 acc[8];
 #pragma unroll
     for (int jt = 0; jt < 8; ++jt) acc[jt] = f32x16{};
-    f32x4 xv[4], zv[2][2];
+    bf16 xr[19];
+    f32x4 zv[2][2];
     auto fetch = [&](int un) {
-        const float *xt = Xt + ((long)un * G + g) * 256 * 32 + sj * 32 + st;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) xv[e] = *(const f32x4 *)(xt + 4 * e);
+        conv_window_load<bf16>(ci, un, st, dj, xr);
         const float *zt = dZt + (((long)un * G + g) * 2 + q) * 256 * 32 + (32 * wave + r) * 32 + 8 * kg;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -476,15 +754,16 @@ __global__ __launch_bounds__(512) void dw_kernel_bf16(int units, int G, int S, c
     for (int un = u0; un < u1; ++un) {
         // stage this unit's x (split) and take its dz operands
         bf16x8 hx[2], lx[2];
+        {
+            float xv[16];
+            conv_window_x<bf16>(ci, taps, un, st, xr, xv);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const float v = xv[e][c];
-                const bf16 h = (bf16)v;
-                hx[e >> 1][4 * (e & 1) + c] = h;
-                lx[e >> 1][4 * (e & 1) + c] = (bf16)(v - (float)h);
+            for (int e = 0; e < 16; ++e) {
+                const bf16 h = (bf16)xv[e];
+                hx[e >> 3][e & 7] = h;
+                lx[e >> 3][e & 7] = (bf16)(xv[e] - (float)h);
             }
+        }
         bf16x8 ah[2], al[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
@@ -526,23 +805,29 @@ __global__ __launch_bounds__(512) void dw_kernel_bf16(int units, int G, int S, c
         }
 }
 
-// fp32: one thread per (o, j), rows in order
-__global__ __launch_bounds__(256) void dw_kernel_f32(int units, int G, int S, const float *dZt,
-                                                     const float *Xt, float *dWpart)
+// fp32: one thread per (o, j), rows in order; x of the thread's channel is
+// recomputed per unit
+__global__ __launch_bounds__(256) void dw_kernel_f32(int units, int G, int S, const float *dZt, ConvIn ci,
+                                                     float *dWpart)
 {
     const int gq = blockIdx.x / 256, o = blockIdx.x % 256, s = blockIdx.y;
     const int g = gq / 2, q = gq % 2, j = threadIdx.x;
     const int u0 = (int)((long)units * s / S), u1 = (int)((long)units * (s + 1) / S);
+    const ConvTaps taps = conv_taps(ci, g * 256 + j);
     float acc = 0.0f;
     for (int un = u0; un < u1; ++un) {
         const float *zt = dZt + (((long)un * G + g) * 2 + q) * 256 * 32 + o * 32;
-        const float *xt = Xt + ((long)un * G + g) * 256 * 32 + j * 32;
-        for (int t = 0; t < 32; ++t) acc = fmaf(zt[t], xt[t], acc);
+        for (int h = 0; h < 2; ++h) {
+            float raw[19], xv[16];
+            conv_window_load<float>(ci, un, 16 * h, g * 256 + j, raw);
+            conv_window_x<float>(ci, taps, un, 16 * h, raw, xv);
+            for (int t = 0; t < 16; ++t) acc = fmaf(zt[16 * h + t], xv[t], acc);
+        }
     }
     dWpart[(((long)s * G + g) * 2 + q) * 65536 + o * 256 + j] = acc;
 }
 
-// ------------------------------------------------------------------ pass 5
+// ------------------------------------------------------------------ pass 7
 __global__ __launch_bounds__(256) void dw_reduce_kernel(int G, int S, const float *dWpart, float *dWa,
                                                         float *dWx)
 {
@@ -615,33 +900,26 @@ __global__ __launch_bounds__(256) void psum_reduce_kernel(int D, const float *pa
     dLambda[d] = acc[7];
 }
 
-// Per device: CU count and resident workgroups per CU of the chunk kernel,
-// looked up once.
-struct LaunchShape {
-    int ncu = 0, occ = 0;
-};
-
+// CU count of the device, looked up once per device; the unit kernel's LDS
+// attribute is set at the same time.
 template <typename T>
-LaunchShape bwd_shape(size_t shmem)
+int unit_ncu()
 {
     static std::mutex mu;
-    static LaunchShape cache[64];
+    static int cache[64];
     int dev = 0;
     (void)hipGetDevice(&dev);
     if (dev < 0 || dev >= 64) dev = 0;
     std::lock_guard<std::mutex> lock(mu);
-    LaunchShape &ls = cache[dev];
-    if (ls.ncu == 0) {
-        const void *fn = (const void *)&bwd_chunk_kernel<T>;
-        int ncu = 0, occ = 0;
+    if (cache[dev] == 0) {
+        int ncu = 0;
         // failures here surface through the launch and hipGetLastError
-        (void)hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+        (void)hipFuncSetAttribute((const void *)&bwd_unit_kernel<T>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)unit_lds_bytes<T>());
         (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, 512, shmem);
-        ls.ncu = ncu < 1 ? 1 : ncu;
-        ls.occ = occ < 1 ? 1 : occ;
+        cache[dev] = ncu < 1 ? 1 : ncu;
     }
-    return ls;
+    return cache[dev];
 }
 
 template <typename T>
@@ -654,18 +932,32 @@ void run_bwd(const rglru_desc &d, const rglru_weights &w, const void *u, const v
     char *base = (char *)ws;
     const int NC = (int)((d.T + CHUNK - 1) / CHUNK);
     const int G = (int)d.H;
-    const size_t NW = (size_t)d.B * NC * d.D;
+    const long U = (long)d.B * NC;   // units per block
 
-    // pass 1: states before each chunk (the forward kernel shares the header)
+    // pass 1: states before each chunk and the gate values (the forward kernel
+    // shares the header)
     float *hstart = (float *)(base + L.hstart);
-    launch_fwd_states(d, w, u, hist_in, h0, hstart, ws, s);
+    void *ri = base + L.ri;
+    launch_fwd_states(d, w, u, hist_in, h0, hstart, ri, ws, s);
 
     // pass 2
-    T *Wt = (T *)(base + L.Wt);
-    hipLaunchKernelGGL((transpose_w_kernel<T>), dim3(8, 16, G), dim3(256), 0, s, (const T *)w.W_a,
-                       (const T *)w.W_x, Wt);
+    void *Wt = base + L.Wt;
+    if (sizeof(T) == 2)
+        hipLaunchKernelGGL(wt_operands_kernel, dim3((unsigned)(64 * G)), dim3(256), 0, s, (const bf16 *)w.W_a,
+                           (const bf16 *)w.W_x, (bf16x8 *)Wt);
+    else
+        hipLaunchKernelGGL(transpose_w_kernel, dim3(8, 16, G), dim3(256), 0, s, (const float *)w.W_a,
+                           (const float *)w.W_x, (float *)Wt);
 
     // pass 3
+    float *aggA = (float *)(base + L.aggA), *aggX = (float *)(base + L.aggX);
+    float *ein = (float *)(base + L.ein);
+    hipLaunchKernelGGL((rev_agg_kernel<T>), dim3((unsigned)(U * G)), dim3(256), 0, s, (int)d.B, (int)d.T,
+                       (int)d.D, NC, G, d.c, w.Lambda, (const void *)ri, dy, aggA, aggX);
+    hipLaunchKernelGGL(rev_scan_kernel, dim3((unsigned)(d.D / 64), (unsigned)d.B), dim3(256), 0, s, NC,
+                       (int)d.D, (const float *)aggA, (const float *)aggX, dh_last, ein, dh0);
+
+    // pass 4
     BwdParams p;
     p.B = (int)d.B;
     p.T = (int)d.T;
@@ -676,49 +968,49 @@ void run_bwd(const rglru_desc &d, const rglru_weights &w, const void *u, const v
     p.u = u;
     p.hist_in = hist_in;
     p.dy = dy;
-    p.h0 = h0;
-    p.dh_last = dh_last;
     p.cw = w.conv_w;
     p.cb = w.conv_b;
-    p.ba = w.b_a;
-    p.bx = w.b_x;
     p.Lambda = w.Lambda;
-    p.Wa = w.W_a;
-    p.Wx = w.W_x;
     p.Wt = Wt;
+    p.ri = ri;
     p.hstart = hstart;
+    p.ein = ein;
     p.du = du;
-    p.dh0 = dh0;
+    p.bnd = (float *)(base + L.bnd);
     p.dZt = (float *)(base + L.dZt);
-    p.Xt = (float *)(base + L.Xt);
     p.psum = (float *)(base + L.psum);
-    p.hdr = (WsHeader *)ws;
-    p.claim = (uint32_t *)(base + L.claims);
-    p.units = (int)(d.B * NC);
-    p.aggA = (uint64_t *)(base + L.bwd_words);
-    p.aggX = p.aggA + NW;
-    p.incl = p.aggX + NW;
-    p.halo = p.incl + NW;
     {
-        const size_t shmem = 2 * 32 * XTile<T>::STRIDE * sizeof(T) + 16;
-        const LaunchShape ls = bwd_shape<T>(shmem);
-        long wpg = ((long)ls.ncu * ls.occ) / G;   // workgroups per block
+        long wpg = unit_ncu<T>() / G;   // workgroups per block: one per CU
         if (wpg < 1) wpg = 1;
-        if (wpg > p.units) wpg = p.units;
-        bwd_chunk_kernel<T><<<dim3((unsigned)(G * wpg)), dim3(512), shmem, s>>>(p);
+        if (wpg > U) wpg = U;
+        if (wpg * G > MAX_UNIT_WGS) wpg = MAX_UNIT_WGS / G;
+        if (wpg < 1) wpg = 1;
+        p.wpg = (int)wpg;
+        bwd_unit_kernel<T><<<dim3((unsigned)(G * wpg)), dim3(512), unit_lds_bytes<T>(), s>>>(p);
+        // pass 5
+        hipLaunchKernelGGL((range_bound_kernel<T>), dim3((unsigned)(G * wpg)), dim3(256), 0, s, (int)d.B,
+                           (int)d.T, (int)d.D, NC, G, (int)wpg, w.conv_w, (const float *)p.bnd, du);
     }
 
-    // pass 4
-    const int chunks = (int)(d.B * NC);
+    // pass 6
+    const int chunks = (int)U;
     float *dWpart = (float *)(base + L.dWpart);
+    ConvIn ci;
+    ci.u = u;
+    ci.hist_in = hist_in;
+    ci.cw = w.conv_w;
+    ci.cb = w.conv_b;
+    ci.T = (int)d.T;
+    ci.D = (int)d.D;
+    ci.NC = NC;
     if (sizeof(T) == 2)
         hipLaunchKernelGGL(dw_kernel_bf16, dim3(2 * G, L.S), dim3(512), 0, s, chunks, G, L.S,
-                           (const float *)p.dZt, (const float *)p.Xt, dWpart);
+                           (const float *)p.dZt, ci, dWpart);
     else
         hipLaunchKernelGGL(dw_kernel_f32, dim3(2 * G * 256, L.S), dim3(256), 0, s, chunks, G, L.S,
-                           (const float *)p.dZt, (const float *)p.Xt, dWpart);
+                           (const float *)p.dZt, ci, dWpart);
 
-    // pass 5
+    // pass 7
     hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((G * 2 * 65536 + 255) / 256)), dim3(256), 0, s,
                        G, L.S, (const float *)dWpart, dWa, dWx);
     float *ppart = (float *)(base + L.ppart);
@@ -730,9 +1022,9 @@ void run_bwd(const rglru_desc &d, const rglru_weights &w, const void *u, const v
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int64_t H)
+size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int64_t H, size_t esz)
 {
-    return bwd_layout(B, T, D, H, 4).total;   // sized for fp32 I/O, enough for bf16 too
+    return bwd_layout(B, T, D, H, esz).total;
 }
 
 void launch_scan_bwd(const rglru_desc &d, const rglru_weights &w, const void *u, const void *hist_in,

@@ -234,6 +234,30 @@ __device__ __forceinline__ float softplus_acc(float v)
     return v > 0.0f ? v + log1pf(expf(-v)) : log1pf(expf(v));
 }
 
+// Gate values r and i that the backward's state pass keeps for every token.
+// r is stored in fp16 for bf16 I/O (it lies in (0, 1), where fp16 resolves
+// 2^-11 relative), i always in fp32: the gradient of u is sensitive enough
+// to i that fp16 i doubles its error.  Per 32-token unit (stream b, chunk c)
+// and 256-channel block g: [(b NC + c) G + g] { r[channel][token],
+// i[channel][token] }, so the 16 tokens of one channel that a lane owns are
+// contiguous.
+template <typename T> struct GateStore {
+    using rtype = float;
+    static constexpr size_t R_BYTES = 256 * 32 * sizeof(rtype);    // r block of a unit
+    static constexpr size_t UNIT_BYTES = R_BYTES + 256 * 32 * 4;   // r and i blocks
+};
+template <> struct GateStore<bf16> {
+    using rtype = _Float16;
+    static constexpr size_t R_BYTES = 256 * 32 * sizeof(rtype);
+    static constexpr size_t UNIT_BYTES = R_BYTES + 256 * 32 * 4;
+};
+// start of unit (b, c), block g
+template <typename T>
+__device__ __forceinline__ char *gate_store_unit(void *base, int b, int c, int NC, int G, int g)
+{
+    return (char *)base + ((size_t)((long)b * NC + c) * G + g) * GateStore<T>::UNIT_BYTES;
+}
+
 // Token held by row `r` of a 32-row MFMA tile.  The 32x32 output tile gives
 // lane l the column l%32 and the rows 8j + 4(l/32) + i (register 4j + i);
 // mapping row 8j + 4h + i to token 16h + 4j + i makes register k of lane l

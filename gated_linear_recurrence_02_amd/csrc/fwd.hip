@@ -93,6 +93,7 @@ struct FwdParams {
     float *h_last;
     void *hist_out;
     float *hstart_out;   // nullable: state before each chunk, [B][NC][D]
+    void *ri_out;        // mode 3: r and i of every token in the backward's unit layout
     WsHeader *hdr;
     uint32_t *claim;
     uint64_t *aggA, *aggX, *incl;
@@ -133,8 +134,10 @@ template <typename T, int MODE>
 __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
 {
     constexpr int S = XTile<T>::STRIDE;
+    constexpr bool CONV = MODE == 0 || MODE == 3;           // conv fused in front
+    constexpr bool RI = MODE == 3;                          // gate values stored
     constexpr bool WREG = (sizeof(T) == 2) && MODE != 2;   // weights held in registers
-    constexpr bool STAGE = (sizeof(T) == 2) && MODE == 0;     // input tile prefetched into LDS
+    constexpr bool STAGE = (sizeof(T) == 2) && CONV;        // input tile prefetched into LDS
     extern __shared__ __attribute__((aligned(16))) char smem[];
     T *Xs = (T *)smem;
     float *pslot_base = (float *)(smem + (MODE == 2 ? 0 : 32 * S * sizeof(T)));
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
 
     // per-channel constants
     float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f, bias = 0.f;
-    if (MODE == 0 && dv) {
+    if (CONV && dv) {
         w0 = p.cw[4 * (long)d + 0];
         w1 = p.cw[4 * (long)d + 1];
         w2 = p.cw[4 * (long)d + 2];
@@ -229,7 +232,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
             const int tb = c * CHUNK + 16 * half;
             const bool full = (c + 1) * CHUNK <= p.T;
             float x[16];
-            if (MODE == 0) {
+            if (CONV) {
                 float win[19];
                 bool staged = false;
                 if constexpr (STAGE) {
@@ -311,6 +314,25 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
 
             // gates, decay, normalisation, local scan from zero; interior
             // chunks take a copy of the loop without the end-of-sequence test
+            using RT = typename GateStore<T>::rtype;
+            RT rs[4];   // mode 3: r and i of 4 tokens, stored as they complete
+            f32x4 is4;
+            RT *r_dst = nullptr;
+            float *i_dst = nullptr;
+            if constexpr (RI) {   // d < D always holds here (D = 256 G)
+                char *u0 = gate_store_unit<T>(p.ri_out, b, c, p.NC, p.G, g);
+                r_dst = (RT *)u0 + ch * 32 + 16 * half;
+                i_dst = (float *)(u0 + GateStore<T>::R_BYTES) + ch * 32 + 16 * half;
+            }
+            auto put_ri = [&](int k, float rr, float ii) {
+                rs[k & 3] = (RT)rr;
+                is4[k & 3] = ii;
+                if ((k & 3) == 3) {
+                    typedef __attribute__((__vector_size__(4 * sizeof(RT)))) RT rt4;
+                    *(rt4 *)(r_dst + k - 3) = rt4{rs[0], rs[1], rs[2], rs[3]};
+                    *(f32x4 *)(i_dst + k - 3) = is4;
+                }
+            };
             auto scan16 = [&](auto edge_tag) {
                 constexpr bool EDGE = decltype(edge_tag)::value;
                 float h = 0.0f, pr = 1.0f;
@@ -326,6 +348,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
                             rr = hw_rcp(1.0f + hw_exp2(fmaf(za[k], -LOG2E, kba)));
                             ii = hw_rcp(1.0f + hw_exp2(fmaf(zx[k], -LOG2E, kbx)));
                         }
+                        if constexpr (RI) put_ri(k, rr, ii);
                         a = hw_exp2(rr * kdec);
                         bb = hw_sqrt(fmaf(-a, a, 1.0f)) * ii * x[k];
                     } else {
@@ -337,6 +360,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
                             rr = sigmoid_acc(za[k] + bav);
                             ii = sigmoid_acc(zx[k] + bxv);
                         }
+                        if constexpr (RI) put_ri(k, rr, ii);
                         const float l = ncs * rr;
                         a = expf(l);
                         bb = sqrtf(-expm1f(2.0f * l)) * ii * x[k];
@@ -406,7 +430,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
             }
             if (c == p.NC - 1 && dv) {
                 if (half == 1 && p.h_last) p.h_last[(long)b * p.D + d] = yl[15];
-                if (MODE == 0 && half == 0 && p.hist_out) {
+                if (CONV && half == 0 && p.hist_out) {
                     for (int jj = 0; jj < 3; ++jj) {
                         const int pos = p.T - 3 + jj;
                         T v = from_f32<T>(0.0f);
@@ -442,7 +466,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
 template <typename T, int MODE>
 size_t fwd_lds_bytes()
 {
-    const bool stage = sizeof(T) == 2 && MODE == 0;
+    const bool stage = sizeof(T) == 2 && (MODE == 0 || MODE == 3);
     return (MODE == 2 ? 0 : 32 * XTile<T>::STRIDE * sizeof(T)) + 512 * PSTRIDE * sizeof(float) +
            (stage ? 2 * ST_BYTES : 0) + 16;
 }
@@ -497,12 +521,13 @@ void launch_t(const FwdParams &p, int mode, hipStream_t s)
 {
     if (mode == 0) launch_mode<T, 0>(p, s);
     else if (mode == 1) launch_mode<T, 1>(p, s);
-    else launch_mode<T, 2>(p, s);
+    else if (mode == 2) launch_mode<T, 2>(p, s);
+    else launch_mode<T, 3>(p, s);
 }
 
 void run_fwd(const rglru_desc &d, const rglru_weights &w, int mode, const void *in, const void *r,
              const void *i, const void *hist_in, const float *h0, void *y, float *h_last,
-             void *hist_out, float *hstart_out, void *ws, hipStream_t s)
+             void *hist_out, float *hstart_out, void *ri_out, void *ws, hipStream_t s)
 {
     FwdParams p;
     p.B = (int)d.B;
@@ -528,6 +553,7 @@ void run_fwd(const rglru_desc &d, const rglru_weights &w, int mode, const void *
     p.h_last = h_last;
     p.hist_out = hist_out;
     p.hstart_out = hstart_out;
+    p.ri_out = ri_out;
     p.hdr = (WsHeader *)ws;
     p.claim = (uint32_t *)((char *)ws + sizeof(WsHeader));
     const size_t nw = (size_t)d.B * p.NC * d.D;
@@ -550,14 +576,15 @@ void launch_scan_fwd(const rglru_desc &d, const rglru_weights &w, int mode, cons
                      const void *r, const void *i, const void *hist_in, const float *h0, void *y,
                      float *h_last, void *hist_out, void *ws, hipStream_t s)
 {
-    run_fwd(d, w, mode, in, r, i, hist_in, h0, y, h_last, hist_out, nullptr, ws, s);
+    run_fwd(d, w, mode, in, r, i, hist_in, h0, y, h_last, hist_out, nullptr, nullptr, ws, s);
 }
 
 void launch_fwd_states(const rglru_desc &d, const rglru_weights &w, const void *u,
-                       const void *hist_in, const float *h0, float *hstart_out, void *ws,
-                       hipStream_t s)
+                       const void *hist_in, const float *h0, float *hstart_out, void *ri_out,
+                       void *ws, hipStream_t s)
 {
-    run_fwd(d, w, 0, u, nullptr, nullptr, hist_in, h0, nullptr, nullptr, nullptr, hstart_out, ws, s);
+    run_fwd(d, w, 3, u, nullptr, nullptr, hist_in, h0, nullptr, nullptr, nullptr, hstart_out, ri_out, ws,
+            s);
 }
 
 }  // namespace rglru

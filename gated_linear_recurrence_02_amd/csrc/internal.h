@@ -11,7 +11,8 @@
 namespace rglru {
 
 size_t fwd_workspace_bytes(int64_t B, int64_t T, int64_t D);
-size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int64_t H);
+// esz: bytes per activation element (2 for bf16 I/O, 4 for fp32)
+size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int64_t H, size_t esz);
 
 void launch_conv1d(const rglru_desc &d, const float *cw, const float *cb, const void *u,
                    const void *hist_in, void *x, void *hist_out, hipStream_t s);
@@ -24,11 +25,12 @@ void launch_scan_fwd(const rglru_desc &d, const rglru_weights &w, int mode, cons
                      const void *r, const void *i, const void *hist_in, const float *h0, void *y,
                      float *h_last, void *hist_out, void *ws, hipStream_t s);
 
-// mode A forward that stores only the state before every 32-token chunk
-// ([B][NC][D] fp32) -- the first pass of the backward
+// mode A forward that stores no outputs but the state before every 32-token
+// chunk ([B][NC][D] fp32) and the gate values r, i of every token (layout of
+// GateStore in common.h) -- the first pass of the backward
 void launch_fwd_states(const rglru_desc &d, const rglru_weights &w, const void *u,
-                       const void *hist_in, const float *h0, float *hstart_out, void *ws,
-                       hipStream_t s);
+                       const void *hist_in, const float *h0, float *hstart_out, void *ri_out,
+                       void *ws, hipStream_t s);
 
 void launch_step(const rglru_desc &d, const rglru_weights &w, const void *u_t, void *hist,
                  float *h, void *y_t, hipStream_t s);
