@@ -184,10 +184,10 @@ __global__ __launch_bounds__(256) void rev_agg_kernel(int B, int T_, int D, int 
     const float ncs = -c_ * softplus_acc(-Lambda[d]);
     RT rv[32];
     {
-        const RT *rip = (const RT *)gate_store_unit<T>((void *)ri, b, c, NC, G, g) + ch * 32;
+        const RT *rip = (const RT *)gate_store_unit<T>((void *)ri, b, c, NC, G, g);
         constexpr int V = 16 / sizeof(RT);
 #pragma unroll
-        for (int q = 0; q < 32 / V; ++q) *(uint4 *)(rv + q * V) = *(const uint4 *)(rip + q * V);
+        for (int q = 0; q < 32 / V; ++q) *(uint4 *)(rv + q * V) = *(const uint4 *)(rip + gate_off<RT>(ch, q * V));
     }
     const T *dyp = (const T *)dy + ((long)b * T_ + (long)c * CHUNK) * D + d;
     const int nt = T_ - c * CHUNK < CHUNK ? T_ - c * CHUNK : CHUNK;
@@ -331,17 +331,18 @@ __device__ __forceinline__ void unit_load(UnitIn<T> &v, const BwdParams &p, long
     const RT *rib = (const RT *)u0;
     const float *iib = (const float *)(u0 + GateStore<T>::R_BYTES);
     constexpr int V = 16 / sizeof(RT);
-    const uint32_t ro = (uint32_t)(ch * 32 + 16 * half);
+    uint32_t pr = gate_off<RT>(ch, 16 * half) / V, pi = gate_off<float>(ch, 16 * half) / 4;   // 16-byte pieces
+    asm volatile("" : "+v"(pr), "+v"(pi));
 #pragma unroll
-    for (int qq = 0; qq < 16 / V; ++qq) *(uint4 *)(v.rv + qq * V) = *at((const uint4 *)rib, (ro + qq * V) / V);
+    for (int qq = 0; qq < 16 / V; ++qq) *(uint4 *)(v.rv + qq * V) = *at((const uint4 *)rib, pr + qq * 256);
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) *(uint4 *)(v.iv + qq * 4) = *at((const uint4 *)iib, (ro + qq * 4) / 4);
+    for (int qq = 0; qq < 4; ++qq) *(uint4 *)(v.iv + qq * 4) = *at((const uint4 *)iib, pi + qq * 256);
     const long cb = ((long)b * p.NC + c) * p.D + g * 256;
     v.hs = *at(p.hstart + cb, (uint32_t)ch);
     v.es = *at(p.ein + cb, (uint32_t)ch);
 }
 
-// LDS of the unit kernel: two pairs of dz^a and dz^x tiles for the dx
+// LDS of the unit kernel: two sets of dz^a and dz^x tiles for the dx
 // products (consecutive units alternate), 32 token rows each in the XTile
 // layout.
 // bf16: dz enters the dx products as hi + lo (the two-term split), so each
@@ -352,6 +353,8 @@ template <typename T> constexpr size_t unit_lds_bytes()
 {
     return (size_t)2 * unit_tiles<T>() * 32 * XTile<T>::STRIDE * sizeof(T);
 }
+static_assert(unit_lds_bytes<bf16>() <= 160 * 1024, "unit kernel LDS (bf16)");
+static_assert(unit_lds_bytes<float>() <= 160 * 1024, "unit kernel LDS (fp32)");
 
 // ------------------------------------------------------------------ pass 4
 template <typename T>
@@ -390,27 +393,31 @@ __global__ __launch_bounds__(512) void bwd_unit_kernel(BwdParams p)
     const long row_b = (long)b * p.T;
     const long cidx = ((long)b * p.NC + c) * p.D + d;   // [B][NC][D] index of this chunk
 
-    UnitIn<T> cur;
-    unit_load(cur, p, q, g, ch, half);
+    // ---- this unit's inputs
     const bool c0hist = c == 0 && p.hist_in;
-    float win[19];
-#pragma unroll
-    for (int m = 0; m < 19; ++m) {
-        const int tau = tb - 3 + m;
-        float v = tau < p.T ? to_f32(cur.win[m]) : 0.0f;
-        if (m < 3 && tau < 0) v = c0hist ? to_f32(cur.hist[m]) : 0.0f;
-        win[m] = v;
-    }
+    float win[19], gd[16];
     RT rv[16];
     float iv[16];
-    T dyr[16];
+    float hs_chunk, es_chunk;
+    {
+        UnitIn<T> cur;
+        unit_load(cur, p, q, g, ch, half);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        rv[k] = cur.rv[k];
-        iv[k] = cur.iv[k];
-        dyr[k] = cur.dy[k];
+        for (int m = 0; m < 19; ++m) {
+            const int tau = tb - 3 + m;
+            float v = tau < p.T ? to_f32(cur.win[m]) : 0.0f;
+            if (m < 3 && tau < 0) v = c0hist ? to_f32(cur.hist[m]) : 0.0f;
+            win[m] = v;
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            rv[k] = cur.rv[k];
+            iv[k] = cur.iv[k];
+            gd[k] = tb + k < p.T ? to_f32(cur.dy[k]) : 0.0f;
+        }
+        hs_chunk = cur.hs;
+        es_chunk = cur.es;
     }
-    const float hs_chunk = cur.hs, es_chunk = cur.es;
     auto xk = [&](int k) {
         return fmaf(w3, win[k + 3], fmaf(w2, win[k + 2], fmaf(w1, win[k + 1], fmaf(w0, win[k], bias))));
     };
@@ -443,9 +450,6 @@ __global__ __launch_bounds__(512) void bwd_unit_kernel(BwdParams p)
 
     // ---- eps entering the lane's last token: half 1 gets the chunk's, half 0
     // that after half 1's tokens (aggregate of half 1's reverse scan)
-    float gd[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) gd[k] = tb + k < p.T ? to_f32(dyr[k]) : 0.0f;
     float eps;
     {
         float e = 0.0f, Rr = 1.0f;
@@ -518,7 +522,7 @@ __global__ __launch_bounds__(512) void bwd_unit_kernel(BwdParams p)
             *(f32x4 *)(zt + 256 * 32 + k) = zx4;
         }
     }
-    __syncthreads();   // the dz tiles are complete 
+    __syncthreads();   // the dz tiles are complete
 
     // ---- dx through the gates
     if constexpr (MF) {
@@ -718,16 +722,60 @@ __device__ __forceinline__ void conv_window_x(const ConvIn &ci, const ConvTaps &
 
 // bf16 I/O: wave w owns rows o = 32w..32w+31 and all 256 columns (8 MFMA
 // tiles); both operands are split into bf16 hi + lo and three products are
-// accumulated (hi*hi + hi*lo + lo*hi).  Each unit's x tile is computed and
-// split once and staged in LDS for all 8 waves; the next unit's u window and
-// dz are requested while the current one is on the matrix cores.
+// accumulated (hi*hi + hi*lo + lo*hi).  Each unit's dz rows and u window go
+// from global memory straight into LDS (global_load_lds, 16 bytes per lane)
+// two units ahead, in a ring of two stage buffers; per unit the x tile is
+// computed and split once and kept in LDS for all 8 waves.
+//   stage, dz part: 32 chunks of 1 KB; chunk (w, ks, p) holds, for lane l,
+//     dz[o = 32w + l%32][t = 16ks + 8(l/32) + 4p .. +3], so each wave reads
+//     its A operands as consecutive 16-byte pieces;
+//   stage, u part: 24 chunks of 1 KB, rows t0 - 3 + 2i and + 1 of the block's
+//     256 channels in chunk i (35 rows used; rows outside [0, T) read a
+//     clamped row and are masked where used).
+// Every wave issues the same number of copies per unit (4 dz + 3 u), so a
+// wait for "all but the last unit's copies" is one vmcnt value.
 constexpr int DW_XS = 40;   // LDS row stride (bf16) of a staged x tile: 32 tokens + 8 pad
+constexpr int DW_DZ_BYTES = 32 * 1024, DW_U_BYTES = 24 * 1024;
+constexpr int DW_STAGE = DW_DZ_BYTES + DW_U_BYTES;
+constexpr int DW_COPIES = 7;   // global_load_lds instructions per wave and unit
+constexpr size_t DW_LDS = 2 * (size_t)DW_STAGE + 2 * 256 * DW_XS * sizeof(bf16);
+
+// copy k (0..6) of this wave's share of unit un's stage: k < 4 a dz chunk,
+// else a u chunk
+__device__ __forceinline__ void dw_stage_copy(const float *dZt, const ConvIn &ci, int un, int G, int g, int q,
+                                              char *stage, int wave, int lane, int k)
+{
+    typedef __attribute__((address_space(3))) void lds_void;
+    if (k < 4) {   // chunk (w = wave, ks = k / 2, p = k % 2)
+        const float *dz = dZt + (((long)un * G + g) * 2 + q) * 256 * 32;
+        const int ks = k >> 1, pp = k & 1;
+        const int o = 32 * wave + (lane & 31), t = 16 * ks + 8 * (lane >> 5) + 4 * pp;
+        __builtin_amdgcn_global_load_lds((const void *)(dz + o * 32 + t),
+                                         (lds_void *)(stage + (wave * 4 + k) * 1024), 16, 0, 0);
+    } else {
+        const int b = un / ci.NC, c = un % ci.NC;
+        const bf16 *u = (const bf16 *)ci.u + (long)b * ci.T * ci.D + (long)g * 256;
+        const int i = wave * 3 + (k - 4);
+        int tau = c * CHUNK - 3 + 2 * i + (lane >> 5);
+        tau = tau < 0 ? 0 : (tau > ci.T - 1 ? ci.T - 1 : tau);
+        __builtin_amdgcn_global_load_lds((const void *)(u + (long)tau * ci.D + (lane & 31) * 8),
+                                         (lds_void *)(stage + DW_DZ_BYTES + i * 1024), 16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void dw_stage_issue(const float *dZt, const ConvIn &ci, int un, int G, int g, int q,
+                                               char *stage, int wave, int lane)
+{
+#pragma unroll
+    for (int k = 0; k < DW_COPIES; ++k) dw_stage_copy(dZt, ci, un, G, g, q, stage, wave, lane, k);
+}
 
 __global__ __launch_bounds__(512) void dw_kernel_bf16(int units, int G, int S, const float *dZt, ConvIn ci,
                                                       float *dWpart)
 {
-    // x of the current unit, split into bf16 hi and lo, [256 j][32 t] each
-    __shared__ __attribute__((aligned(16))) bf16 Xh[256 * DW_XS], Xl[256 * DW_XS];
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    char *stage0 = smem;                                        // [2][DW_STAGE]
+    bf16 *Xh = (bf16 *)(smem + 2 * DW_STAGE), *Xl = Xh + 256 * DW_XS;   // x split, [256 j][32 t]
     const int g = blockIdx.x / 2, q = blockIdx.x % 2, s = blockIdx.y;
     const int u0 = (int)((long)units * s / S), u1 = (int)((long)units * (s + 1) / S);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -739,49 +787,70 @@ __global__ __launch_bounds__(512) void dw_kernel_bf16(int units, int G, int S, c
     f32x16 acc[8];
 #pragma unroll
     for (int jt = 0; jt < 8; ++jt) acc[jt] = f32x16{};
-    bf16 xr[19];
-    f32x4 zv[2][2];
-    auto fetch = [&](int un) {
-        conv_window_load<bf16>(ci, un, st, dj, xr);
-        const float *zt = dZt + (((long)un * G + g) * 2 + q) * 256 * 32 + (32 * wave + r) * 32 + 8 * kg;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            zv[ks][0] = *(const f32x4 *)(zt + 16 * ks);
-            zv[ks][1] = *(const f32x4 *)(zt + 16 * ks + 4);
-        }
-    };
-    if (u0 < u1) fetch(u0);
+    // the taps are in registers before any copy is in flight, so no wait
+    // inside the loop has to cover them
+    __builtin_amdgcn_s_waitcnt(0);
+    if (u0 < u1) dw_stage_issue(dZt, ci, u0, G, g, q, stage0, wave, lane);
+    if (u0 + 1 < u1) dw_stage_issue(dZt, ci, u0 + 1, G, g, q, stage0 + DW_STAGE, wave, lane);
     for (int un = u0; un < u1; ++un) {
-        // stage this unit's x (split) and take its dz operands
-        bf16x8 hx[2], lx[2];
+        char *stg = stage0 + (un - u0) % 2 * DW_STAGE;
+        // this unit's copies have landed (the next unit's may still be in flight)
+        if (un + 1 < u1) __builtin_amdgcn_s_waitcnt((DW_COPIES & 0xF) | (0x7 << 4) | (0xF << 8));
+        else __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+        // every wave's copies have landed; the previous unit's x tile is free.
+        // (A plain barrier: __syncthreads would also wait for the next
+        // unit's copies.)
+        __builtin_amdgcn_s_barrier();
+        // x of this unit (the unit kernel's arithmetic), split, to the x tile
         {
-            float xv[16];
-            conv_window_x<bf16>(ci, taps, un, st, xr, xv);
+            const int c = un % ci.NC, b = un / ci.NC;
+            const int t0 = c * CHUNK + st;
+            const char *ust = stg + DW_DZ_BYTES;
+            float win[19];
+#pragma unroll
+            for (int m = 0; m < 19; ++m) {
+                const int row = st + m, tau = t0 - 3 + m;
+                float v = (float)*(const bf16 *)(ust + row * 512 + sj * 2);
+                if (tau >= ci.T) v = 0.0f;
+                if (m < 3 && tau < 0)
+                    v = ci.hist_in ? (float)((const bf16 *)ci.hist_in)[((long)b * 3 + 3 + tau) * ci.D + dj] : 0.0f;
+                win[m] = v;
+            }
+            bf16x8 hx[2], lx[2];
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const bf16 h = (bf16)xv[e];
+                const float xv = fmaf(taps.w3, win[e + 3],
+                                      fmaf(taps.w2, win[e + 2], fmaf(taps.w1, win[e + 1], fmaf(taps.w0, win[e], taps.bias))));
+                const bf16 h = (bf16)xv;
                 hx[e >> 3][e & 7] = h;
-                lx[e >> 3][e & 7] = (bf16)(xv[e] - (float)h);
+                lx[e >> 3][e & 7] = (bf16)(xv - (float)h);
+            }
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                *(bf16x8 *)(Xh + sj * DW_XS + st + 8 * h2) = hx[h2];
+                *(bf16x8 *)(Xl + sj * DW_XS + st + 8 * h2) = lx[h2];
             }
         }
+        // this wave's dz operands, split
         bf16x8 ah[2], al[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float v = zv[ks][e >> 2][e & 3];
-                const bf16 h = (bf16)v;
-                ah[ks][e] = h;
-                al[ks][e] = (bf16)(v - (float)h);
-            }
-        __syncthreads();   // every wave is done with the previous unit's tile
+            for (int pp = 0; pp < 2; ++pp) {
+                const f32x4 v4 = *(const f32x4 *)(stg + (wave * 4 + 2 * ks + pp) * 1024 + lane * 16);
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-            *(bf16x8 *)(Xh + sj * DW_XS + st + 8 * h2) = hx[h2];
-            *(bf16x8 *)(Xl + sj * DW_XS + st + 8 * h2) = lx[h2];
-        }
-        __syncthreads();
-        if (un + 1 < u1) fetch(un + 1);
+                for (int e = 0; e < 4; ++e) {
+                    const bf16 h = (bf16)v4[e];
+                    ah[ks][4 * pp + e] = h;
+                    al[ks][4 * pp + e] = (bf16)(v4[e] - (float)h);
+                }
+            }
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_s_barrier();   // the x tile is complete; the stage buffer has been read
+        // the products, with the copies for unit un + 2 (into the buffer just
+        // read) spread between them: a copy's issue can stall for a while,
+        // and the matrix cores keep working meanwhile
+        const bool more = un + 2 < u1;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -792,6 +861,12 @@ __global__ __launch_bounds__(512) void dw_kernel_bf16(int units, int G, int S, c
                 acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[ks], bh, acc[jt], 0, 0, 0);
                 acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[ks], bl, acc[jt], 0, 0, 0);
                 acc[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[ks], bh, acc[jt], 0, 0, 0);
+                const int step = 8 * ks + jt;
+                if ((step & 1) && step < 2 * DW_COPIES && more) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    dw_stage_copy(dZt, ci, un + 2, G, g, q, stg, wave, lane, step >> 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
     }
@@ -922,6 +997,23 @@ int unit_ncu()
     return cache[dev];
 }
 
+// the bf16 dW kernel's dynamic LDS limit, set once per device
+void dw_lds_attr()
+{
+    static std::mutex mu;
+    static bool done[64];
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev < 0 || dev >= 64) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!done[dev]) {
+        // failures here surface through the launch and hipGetLastError
+        (void)hipFuncSetAttribute((const void *)&dw_kernel_bf16, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)DW_LDS);
+        done[dev] = true;
+    }
+}
+
 template <typename T>
 void run_bwd(const rglru_desc &d, const rglru_weights &w, const void *u, const void *hist_in,
              const float *h0, const void *dy, const float *dh_last, void *du, float *dcw, float *dcb,
@@ -1003,9 +1095,11 @@ void run_bwd(const rglru_desc &d, const rglru_weights &w, const void *u, const v
     ci.T = (int)d.T;
     ci.D = (int)d.D;
     ci.NC = NC;
-    if (sizeof(T) == 2)
-        hipLaunchKernelGGL(dw_kernel_bf16, dim3(2 * G, L.S), dim3(512), 0, s, chunks, G, L.S,
+    if (sizeof(T) == 2) {
+        dw_lds_attr();
+        hipLaunchKernelGGL(dw_kernel_bf16, dim3(2 * G, L.S), dim3(512), DW_LDS, s, chunks, G, L.S,
                            (const float *)p.dZt, ci, dWpart);
+    }
     else
         hipLaunchKernelGGL(dw_kernel_f32, dim3(2 * G * 256, L.S), dim3(256), 0, s, chunks, G, L.S,
                            (const float *)p.dZt, ci, dWpart);

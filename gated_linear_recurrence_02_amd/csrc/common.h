@@ -238,9 +238,11 @@ __device__ __forceinline__ float softplus_acc(float v)
 // r is stored in fp16 for bf16 I/O (it lies in (0, 1), where fp16 resolves
 // 2^-11 relative), i always in fp32: the gradient of u is sensitive enough
 // to i that fp16 i doubles its error.  Per 32-token unit (stream b, chunk c)
-// and 256-channel block g: [(b NC + c) G + g] { r[channel][token],
-// i[channel][token] }, so the 16 tokens of one channel that a lane owns are
-// contiguous.
+// and 256-channel block g: [(b NC + c) G + g] { r block, i block }.  Inside a
+// block (element type E, V = 16 / sizeof(E) values per 16-byte piece),
+// token t of channel ch sits in piece (t / 16, (t % 16) / V) of channel ch:
+// pieces are ordered (half, piece, channel), so the lanes of a wave, which
+// hold consecutive channels, touch consecutive 16-byte pieces.
 template <typename T> struct GateStore {
     using rtype = float;
     static constexpr size_t R_BYTES = 256 * 32 * sizeof(rtype);    // r block of a unit
@@ -256,6 +258,12 @@ template <typename T>
 __device__ __forceinline__ char *gate_store_unit(void *base, int b, int c, int NC, int G, int g)
 {
     return (char *)base + ((size_t)((long)b * NC + c) * G + g) * GateStore<T>::UNIT_BYTES;
+}
+// element offset of token t (0..31) of channel ch inside a block of type E
+template <typename E> __device__ __forceinline__ uint32_t gate_off(int ch, int t)
+{
+    constexpr int V = 16 / sizeof(E);
+    return (uint32_t)((((t >> 4) * (16 / V) + ((t & 15) / V)) * 256 + ch) * V + (t % V));
 }
 
 // Token held by row `r` of a 32-row MFMA tile.  The 32x32 output tile gives

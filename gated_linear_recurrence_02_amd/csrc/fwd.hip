@@ -321,16 +321,16 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
             float *i_dst = nullptr;
             if constexpr (RI) {   // d < D always holds here (D = 256 G)
                 char *u0 = gate_store_unit<T>(p.ri_out, b, c, p.NC, p.G, g);
-                r_dst = (RT *)u0 + ch * 32 + 16 * half;
-                i_dst = (float *)(u0 + GateStore<T>::R_BYTES) + ch * 32 + 16 * half;
+                r_dst = (RT *)u0;
+                i_dst = (float *)(u0 + GateStore<T>::R_BYTES);
             }
             auto put_ri = [&](int k, float rr, float ii) {
                 rs[k & 3] = (RT)rr;
                 is4[k & 3] = ii;
                 if ((k & 3) == 3) {
                     typedef __attribute__((__vector_size__(4 * sizeof(RT)))) RT rt4;
-                    *(rt4 *)(r_dst + k - 3) = rt4{rs[0], rs[1], rs[2], rs[3]};
-                    *(f32x4 *)(i_dst + k - 3) = is4;
+                    *(rt4 *)(r_dst + gate_off<RT>(ch, 16 * half + k - 3)) = rt4{rs[0], rs[1], rs[2], rs[3]};
+                    *(f32x4 *)(i_dst + gate_off<float>(ch, 16 * half + k - 3)) = is4;
                 }
             };
             auto scan16 = [&](auto edge_tag) {
