@@ -373,9 +373,9 @@ def main():
         out["rows"]["bwd"] = row(f"rglru_scan_bwd, 9B width (B={c4.B} T={c4.T} D={c4.D} bf16), "
                                  "all passes", kk, t4, nb, flops=3 * 2 * 2 * 256 * t4,
                                  bound="mfma",
-                                 note="algorithmic flops: gate recompute, dX and dW products "
-                                      "(3 x 1024 per token*ch); executed MFMA work is larger "
-                                      "(split-bf16 operands)")
+                                 note="algorithmic flops: the gate products of the state pass, "
+                                      "dX and dW (3 x 1024 per token*ch); executed MFMA work is "
+                                      "larger (split-bf16 operands)")
         del u4, dy4
         torch.cuda.empty_cache()
 

@@ -11,6 +11,7 @@ using namespace rglru;
 namespace {
 
 constexpr int64_t MAX_DIM = (int64_t)1 << 30;
+constexpr int64_t BWD_MAX_D = (int64_t)1 << 24;   // 32-bit row offsets in the backward
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -85,7 +86,7 @@ int rglru_workspace_size(const rglru_desc *desc, int op, size_t *bytes)
     if (st) return st;
     if (op == RGLRU_OP_SCAN_FWD) *bytes = fwd_workspace_bytes(desc->B, desc->T, desc->D);
     else if (op == RGLRU_OP_SCAN_BWD) {
-        if (desc->D / desc->H != 256) return RGLRU_ERR_SHAPE;
+        if (desc->D / desc->H != 256 || desc->D > BWD_MAX_D) return RGLRU_ERR_SHAPE;
         *bytes = bwd_workspace_bytes(desc->B, desc->T, desc->D, desc->H, esize(*desc));
     } else return RGLRU_ERR_ARG;
     return RGLRU_OK;
@@ -191,6 +192,7 @@ int rglru_scan_bwd(const rglru_desc *desc, const rglru_weights *w, const void *u
 {
     int st = check_desc(desc, true);
     if (st) return st;
+    if (desc->D > BWD_MAX_D) return RGLRU_ERR_SHAPE;
     if (!w || !w->conv_w || !w->W_a || !w->W_x || !w->Lambda || !u || !dy || !du || !dconv_w ||
         !dconv_b || !dW_a || !db_a || !dW_x || !db_x || !dLambda)
         return RGLRU_ERR_NULL;

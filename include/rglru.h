@@ -44,22 +44,24 @@
  * Validation.  All checks run on the host before anything is enqueued; on
  *   error nothing is enqueued and no output is touched.  A launch error is
  *   reported as RGLRU_ERR_LAUNCH after the fact (hipGetLastError).
- * Work distribution.  The scans are persistent kernels that claim their work
- *   units from counters in the workspace at run time; they need no
- *   co-residency guarantee and may share the device with other work.  A
+ * Work distribution.  The forward scans are persistent kernels that claim
+ *   their work units from counters in the workspace at run time; they need
+ *   no co-residency guarantee and may share the device with other work.  A
  *   look-back wait that never sees its data (which only a corrupted or
  *   concurrently reused workspace can cause) gives up after a bounded spin,
- *   sets an error word in the workspace header and yields NaN.
+ *   sets an error word in the workspace header and yields NaN.  The
+ *   backward's own kernels never wait on one another's workgroups.
  * Aliasing.  Outputs must not overlap inputs, except hist and h of
  *   rglru_step, which are read and rewritten in place by design.
  * Determinism.  rglru_conv1d, rglru_gates and rglru_step are bitwise
- *   repeatable, and so are the reductions of rglru_scan_bwd (fixed order, no
- *   floating-point atomics).  The chunked scans of rglru_scan_fwd and
- *   rglru_scan_bwd combine chunk carries through a decoupled look-back whose
- *   path depends on timing (a chunk may compose a different number of
- *   published aggregates), so repeated calls can differ in the last bits of
- *   the carried state and, through it, of y and the gradients; the
- *   difference is rounding only (the same products, grouped differently).
+ *   repeatable, and so are the reverse scan and the reductions of
+ *   rglru_scan_bwd (fixed order, no floating-point atomics).  The chunked
+ *   forward scan of rglru_scan_fwd, which the backward also runs first,
+ *   combines chunk carries through a decoupled look-back whose path depends
+ *   on timing (a chunk may compose a different number of published
+ *   aggregates), so repeated calls can differ in the last bits of the
+ *   carried state and, through it, of y and the gradients; the difference is
+ *   rounding only (the same products, grouped differently).
  * Numerics.  NaN and Inf in the inputs propagate; they are not trapped.
  */
 #ifndef RGLRU_H
@@ -170,7 +172,9 @@ int rglru_step(const rglru_desc *desc, const rglru_weights *w, const void *u_t,
  * pages state no backward; this is the exact derivative of the forward
  * above).  dh_last, h0, hist_in and dh0 are nullable.  du is io; every other
  * gradient is fp32 and is WRITTEN, not accumulated.  The gradient of hist_in
- * is not produced.  Reads every field of w.  K = 256. */
+ * is not produced.  Reads every field of w.  K = 256; D <= 2^24 (its
+ * kernels address a chunk's rows with 32-bit offsets).  The workspace size
+ * depends on desc->io. */
 int rglru_scan_bwd(const rglru_desc *desc, const rglru_weights *w, const void *u,
                    const void *hist_in, const float *h0, const void *dy,
                    const float *dh_last, void *du, float *dconv_w, float *dconv_b,

@@ -67,6 +67,11 @@ def test_workspace_size(L):
     assert ws_size(desc(T=0))[0] == ESHAPE
     assert ws_size(desc(), op=9)[0] == EARG
     assert ws_size(desc(D=768, H=2), op=glr.OP_SCAN_BWD)[0] == ESHAPE   # K = 384
+    # the backward addresses rows with 32-bit offsets: D <= 2^24
+    assert ws_size(desc(B=1, T=1, D=(1 << 24) + 256, H=(1 << 16) + 1), op=glr.OP_SCAN_BWD)[0] == ESHAPE
+    assert ws_size(desc(B=1, T=1, D=1 << 24, H=1 << 16), op=glr.OP_SCAN_BWD)[0] == OK
+    # the backward's workspace depends on the I/O type (fp16 r and fp32 i for bf16)
+    assert ws_size(desc(io=glr.BF16), op=glr.OP_SCAN_BWD)[1] < ws_size(desc(io=glr.F32), op=glr.OP_SCAN_BWD)[1]
     assert L.rglru_workspace_size(None, 0, None) == ENULL
 
 
