@@ -10,7 +10,9 @@
 // of one stream over SEG consecutive tokens and slides the 4-tap window in
 // registers, so every u row is read once per thread plus a 3-row halo.  Rows
 // are read and written as 16-byte vectors; lanes of a wave cover consecutive
-// channel groups, so a wave touches whole 1 KB row segments.
+// channel groups, so a wave touches whole 1 KB row segments.  Whole segments
+// request all their rows at once (SEG loads in flight per thread), which is
+// what keeps enough bytes in flight to approach HBM bandwidth.
 #include "common.h"
 #include "internal.h"
 
@@ -79,9 +81,7 @@ __global__ __launch_bounds__(256) void conv1d_kernel(int B, int T_, int D, int n
 #pragma unroll
     for (int m = 0; m < 3; ++m) load_row<T, VEC>(u, hist_in, T_, D, b, t0 - 3 + m, d0, nv, win[m]);
 
-    for (int t = t0; t < t1; ++t) {
-        float cur[V];
-        load_row<T, VEC>(u, hist_in, T_, D, b, t, d0, nv, cur);
+    auto step = [&](int t, const float (&cur)[V]) {
         T out[V];
 #pragma unroll
         for (int v = 0; v < V; ++v) {
@@ -101,6 +101,26 @@ __global__ __launch_bounds__(256) void conv1d_kernel(int B, int T_, int D, int n
 #pragma unroll
             for (int v = 0; v < V; ++v)
                 if (v < nv) dst[v] = out[v];
+        }
+    };
+    if (VEC && t1 - t0 == SEG) {
+        uint4 raw[SEG];
+        const T *src = u + ((long)b * T_ + t0) * D + d0;
+#pragma unroll
+        for (int k = 0; k < SEG; ++k) raw[k] = *(const uint4 *)(src + (long)k * D);
+#pragma unroll
+        for (int k = 0; k < SEG; ++k) {
+            const T *tmp = (const T *)&raw[k];
+            float cur[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) cur[v] = to_f32(tmp[v]);
+            step(t0 + k, cur);
+        }
+    } else {
+        for (int t = t0; t < t1; ++t) {
+            float cur[V];
+            load_row<T, VEC>(u, hist_in, T_, D, b, t, d0, nv, cur);
+            step(t, cur);
         }
     }
 
