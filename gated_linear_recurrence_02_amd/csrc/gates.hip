@@ -11,9 +11,10 @@
 // 32-row tiles of the flattened [B*T] rows assigned to it (tile q,
 // q + WPG, ...; no tile waits on another).  The next tile is requested into
 // registers (two 16-byte loads per thread) while the current one is on the
-// matrix cores; tiles alternate between two LDS buffers, so one barrier per
-// tile suffices.  Lane l of wave w gets channel 32w + l%32 of rows
-// 16(l/32) .. +15 back from the MFMA output layout.
+// matrix cores; tiles alternate between two LDS buffers.  Lane l of wave w
+// gets channel 32w + l%32 of rows 16(l/32) .. +15 back from the MFMA output
+// layout; r and i go through an LDS output tile ([token][channel]) and leave
+// in 16-byte pieces rather than as 2-byte stores.
 // fp32: one workgroup per (tile, block); the tile is staged in LDS and the
 // products run on fp32 FMAs.
 #include "common.h"
@@ -67,7 +68,11 @@ __global__ __launch_bounds__(512) void gates_kernel_w(long rows, int D, int G, i
                                                       const float *bx, bf16 *r, bf16 *i)
 {
     constexpr int S = XTile<bf16>::STRIDE;
+    constexpr int OS = 264;   // output tile row stride (bf16): 256 channels + 8 pad
     __shared__ __attribute__((aligned(16))) bf16 Xs[2][32 * S];
+    __shared__ __attribute__((aligned(16))) bf16 Os[2][32 * OS];   // r and i of the tile, [token][channel]
+    // (the output tile is rewritten only after the next tile's barrier, which
+    // every thread reaches after its reads of it)
     const int g = blockIdx.x % G, rank = blockIdx.x / G;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 31, half = lane >> 5;
@@ -115,13 +120,23 @@ __global__ __launch_bounds__(512) void gates_kernel_w(long rows, int D, int G, i
             A = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, wa[s2], A, 0, 0, 0);
             Xc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, wx[s2], Xc, 0, 0, 0);
         }
-        const long row0 = q * 32 + 16 * half;
-        bf16 *rp = r + row0 * D + d, *ip = i + row0 * D + d;
+        // r and i to the output tile, then out in 16-byte pieces
+        {
+            uint32_t oo = (uint32_t)(16 * half * OS + 32 * wave + n);
+            asm volatile("" : "+v"(oo));
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            if (row0 + k < rows) {
-                rp[(long)k * D] = (bf16)hw_rcp(1.0f + hw_exp2(fmaf(A[k], -LOG2E, kba)));
-                ip[(long)k * D] = (bf16)hw_rcp(1.0f + hw_exp2(fmaf(Xc[k], -LOG2E, kbx)));
+            for (int k = 0; k < 16; ++k) {
+                Os[0][oo + k * OS] = (bf16)hw_rcp(1.0f + hw_exp2(fmaf(A[k], -LOG2E, kba)));
+                Os[1][oo + k * OS] = (bf16)hw_rcp(1.0f + hw_exp2(fmaf(Xc[k], -LOG2E, kbx)));
+            }
+        }
+        __syncthreads();   // the output tile is complete
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const long row = q * 32 + lr + 16 * h;
+            if (row < rows) {
+                *(uint4 *)(r + row * D + g * 256 + lc) = *(const uint4 *)(&Os[0][(lr + 16 * h) * OS + lc]);
+                *(uint4 *)(i + row * D + g * 256 + lc) = *(const uint4 *)(&Os[1][(lr + 16 * h) * OS + lc]);
             }
         }
     }

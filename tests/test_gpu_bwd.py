@@ -111,3 +111,54 @@ def test_bwd_config4_full_size():
     for h in (0, 11):
         ref = _oracle_block(prob, dy, h)
         _compare_block(prob, g, ref, h, TOL["bf16"])
+
+
+def test_bwd_ranges_cross_stream_boundaries():
+    # 4 streams x 15 chunks = 60 units per block over 25 workgroups: ranges of 2
+    # or 3 units, some of which start a new stream inside the range, and range
+    # starts in the middle of a stream (the boundary pass finishes those du)
+    prob = make_problem(1, B=4, T=480, with_state=True)
+    dy = synth.make_activation(1, "dy", (4, 480, 2560), "bf16")
+    dh = synth.store(synth.normal(11, 0, 4 * 2560), "f32").reshape(4, 2560)
+    _say("bwd bf16: B=4 T=480 D=2560, ranges across stream boundaries")
+    g = _run(prob, dy, prob.h0, prob.hist, dh)
+    for h in (0, 9):
+        ref = _oracle_block(prob, dy, h, prob.h0, prob.hist, dh)
+        _compare_block(prob, g, ref, h, TOL["bf16"])
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 31])
+def test_bwd_tiny_lengths(T):
+    # one partial chunk, shorter than the conv window for T < 3 (history rows
+    # feed every token), fp32 and bf16
+    for cfg, tol in ((0, 1e-4), (1, TOL["bf16"])):
+        prob = make_problem(cfg, B=2, T=T, with_state=True)
+        D = prob.D
+        dy = synth.make_activation(cfg, "dy", (2, T, D), prob.io)
+        dh = synth.store(synth.normal(13, 0, 2 * D), "f32").reshape(2, D)
+        _say(f"bwd {prob.io}: B=2 T={T} D={D} with h0, history, dh_last")
+        g = _run(prob, dy, prob.h0, prob.hist, dh)
+        ref = _oracle_block(prob, dy, 0, prob.h0, prob.hist, dh)
+        _compare_block(prob, g, ref, 0, tol)
+
+
+def test_bwd_repeat_with_workspace_reuse():
+    # the same call twice with a forward of another shape in between (one shared
+    # workspace): the reverse scan and reductions are fixed-order, the state
+    # pass's look-back may regroup products, so the repeat agrees to rounding:
+    # fp32 gradients to 1e-5, du (stored in bf16) to one bf16 step at its
+    # largest magnitude (2^-7 relative), since a last-bit change in fp32 can
+    # move an element across a bf16 rounding boundary
+    prob = make_problem(1, B=3, T=100, with_state=True)
+    dy = synth.make_activation(1, "dy", (3, 100, 2560), "bf16")
+    _say("bwd bf16: B=3 T=100 D=2560, repeated with a forward in between")
+    g1 = {k: v.clone() for k, v in _run(prob, dy, prob.h0, prob.hist).items()}
+    other = make_problem(1, B=2, T=77)
+    glr.scan_fwd(to_dev(other.u, DEV), other.weights(DEV))
+    torch.cuda.synchronize()
+    g2 = _run(prob, dy, prob.h0, prob.hist)
+    for n in NAMES:
+        a, b = from_dev(g1[n]), from_dev(g2[n])
+        e = oracle.rel_err(b, a)
+        _say(f"  {n}: repeat difference {e:.3e}")
+        assert e <= (2.0 ** -7 if n == "du" else 1e-5), n
