@@ -155,6 +155,45 @@ def bwd(u, conv_w, conv_b, W_a, b_a, W_x, b_x, Lambda, dy, h0=None, hist_in=None
     return g
 
 
+def linear(x, W):
+    """A linear layer without bias: y[..., n] = sum_k x[..., k] W[n][k] (W [N][K])."""
+    x, W = _f64(x), _f64(W)
+    K = x.shape[-1]
+    N = W.shape[0]
+    M = x.size // K
+    y = np.empty(x.shape[:-1] + (N,))
+    lib().oracle_linear(ctypes.c_long(M), K, N, _p(x), _p(W), _p(y))
+    return y
+
+
+def gelu(v):
+    """GeLU(v) = 0.5 v (1 + erf(v / sqrt 2)) (the exact form, reading R6)."""
+    v = _f64(v)
+    out = np.empty_like(v)
+    lib().oracle_gelu(ctypes.c_long(v.size), _p(v), _p(out))
+    return out
+
+
+def merge(y, g):
+    """z = y * GeLU(g), elementwise."""
+    y, g = _f64(y), _f64(g)
+    z = np.empty_like(y)
+    lib().oracle_merge(ctypes.c_long(y.size), _p(y), _p(g), _p(z))
+    return z
+
+
+def block_fwd(x, proj_in_1, proj_in_2, proj_out, conv_w, conv_b, W_a, b_a, W_x, b_x, Lambda,
+              h0=None, hist_in=None, c=8.0):
+    """Recurrent block (reading R6): out = proj_out(y * GeLU(proj_in_2 x)) with y the
+    RG-LRU of conv(proj_in_1 x).  x [B][T][d_model]; proj_in_* [D][d_model];
+    proj_out [d_model][D].  Returns (out, h_last, hist_out) -- the state and the
+    conv history are those of branch 1."""
+    b1 = linear(x, proj_in_1)
+    b2 = linear(x, proj_in_2)
+    y, h_last, hist_out = fwd(b1, conv_w, conv_b, W_a, b_a, W_x, b_x, Lambda, h0=h0, hist_in=hist_in, c=c)
+    return linear(merge(y, b2), proj_out), h_last, hist_out
+
+
 def rel_err(got, ref) -> float:
     """max_i |g_i - o_i| / max(|o_i|, RMS(o)): elementwise relative error with
     an RMS floor, so that outputs crossing zero are judged against the

@@ -44,6 +44,13 @@
  *  R5  the backward is the exact derivative of the forward above (the pages
  *      state no backward); dh_last is an optional extra upstream gradient on
  *      the final state.
+ *  R6  the recurrent block ([G] "Non-Linear Multiplicative Gating with GeLU"
+ *      and the listing's RecurrentBlock): out = proj_out(y * GeLU(proj_in_2
+ *      x)), y the RG-LRU of conv(proj_in_1 x); linear layers without bias,
+ *      weights stored [out][in]; GeLU is the exact one, 0.5 v (1 + erf(v /
+ *      sqrt 2)), which is what the listing's F.gelu computes (the pages also
+ *      show a tanh form for the MLP, not for this merge); the residual add is
+ *      the decoder layer's, outside the block.
  */
 #include <math.h>
 #include <stddef.h>
@@ -357,4 +364,33 @@ void oracle_bwd(int B, int T, int D, int H, double c, const double *u,
 
     free(x); free(r); free(i); free(a); free(beta); free(hprev);
     free(dl); free(dza); free(dzx); free(dx);
+}
+
+/* ---------------------------------------------------------- recurrent block
+ * [G] "Non-Linear Multiplicative Gating with GeLU" (R6). */
+
+/* y[m][n] = sum_k x[m][k] W[n][k]  (a linear layer without bias, W [N][K]) */
+void oracle_linear(long M, int K, int N, const double *x, const double *W, double *y)
+{
+    #pragma omp parallel for schedule(static)
+    for (long m = 0; m < M; ++m)
+        for (int n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int k = 0; k < K; ++k) acc += x[(size_t)m * K + k] * W[(size_t)n * K + k];
+            y[(size_t)m * N + n] = acc;
+        }
+}
+
+/* GeLU(v) = v Phi(v) = 0.5 v (1 + erf(v / sqrt 2)) */
+void oracle_gelu(long n, const double *v, double *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (long e = 0; e < n; ++e) out[e] = 0.5 * v[e] * (1.0 + erf(v[e] / sqrt(2.0)));
+}
+
+/* z = y * GeLU(g), elementwise */
+void oracle_merge(long n, const double *y, const double *g, double *z)
+{
+    #pragma omp parallel for schedule(static)
+    for (long e = 0; e < n; ++e) z[e] = y[e] * (0.5 * g[e] * (1.0 + erf(g[e] / sqrt(2.0))));
 }

@@ -26,7 +26,10 @@ Gating Mechanism" and the module's Lambda initialiser): the decay base
 a = sigmoid(Lambda) is drawn so that a^c is uniform on [0.9, 0.999], i.e.
 u ~ U[0.9, 0.999], a = u^(1/c), Lambda = log(a / (1 - a)); c = 8.  Gate
 weights are N(0, 1/K) (variance; std 1/sqrt(K)), conv weights N(0, 1/4)
-(std 0.5), biases 0, activations N(0, 1).
+(std 0.5), biases 0, activations N(0, 1).  The recurrent block's
+projections (no bias, stored [out][in]) are N(0, 1/fan_in), which keeps
+unit-variance activations at unit variance; the pages give no initialiser
+for them.
 
 Rounding: values are generated in float64, rounded to float32 (IEEE
 round-to-nearest-even) and, for bf16 storage, from float32 to bf16 with
@@ -50,7 +53,8 @@ _THREADS = max(1, min(16, os.cpu_count() or 1))
 
 # tensor ids of the per-tensor streams
 TID = dict(u=0, conv_w=1, conv_b=2, W_a=3, W_x=4, lam_u=5, dy=6, h0=7,
-           b_a=8, b_x=9, hist=10, dh_last=11)
+           b_a=8, b_x=9, hist=10, dh_last=11,
+           block_x=12, proj_in_1=13, proj_in_2=14, proj_out=15)
 
 C_CONST = 8.0
 
@@ -224,3 +228,19 @@ def make_decode_u(cfg: Config, step: int) -> np.ndarray:
 
 def make_dy(cfg: Config) -> np.ndarray:
     return make_activation(cfg.idx, "dy", (cfg.B, cfg.T, cfg.D), cfg.io)
+
+
+@dataclasses.dataclass
+class BlockParams:
+    """Projections of the recurrent block, stored [out][in] in the io form."""
+    proj_in_1: np.ndarray   # [D][d_model]
+    proj_in_2: np.ndarray   # [D][d_model]
+    proj_out: np.ndarray    # [d_model][D]
+
+
+def make_block_params(cfg: int, d_model: int, D: int, io: str) -> BlockParams:
+    s_in, s_out = 1.0 / math.sqrt(d_model), 1.0 / math.sqrt(D)
+    p1 = store(s_in * normal(seed_for(cfg, "proj_in_1"), 0, D * d_model), io).reshape(D, d_model)
+    p2 = store(s_in * normal(seed_for(cfg, "proj_in_2"), 0, D * d_model), io).reshape(D, d_model)
+    po = store(s_out * normal(seed_for(cfg, "proj_out"), 0, d_model * D), io).reshape(d_model, D)
+    return BlockParams(p1, p2, po)
