@@ -204,3 +204,32 @@ def rel_err(got, ref) -> float:
     den = np.maximum(np.abs(ref), rms)
     den = np.where(den == 0.0, 1.0, den)
     return float(np.max(np.abs(got - ref) / den)) if ref.size else 0.0
+
+
+# ------------------------------------------------------------ local attention
+def attn_fwd(q, k, v, window: int, scale: float):
+    """Sliding-window MQA (reading R7): q [B][T][Hq][dh], k, v [B][T][dh].
+    Token t attends to positions t-window+1 .. t.  Returns o [B][T][Hq][dh]."""
+    q, k, v = map(_f64, (q, k, v))
+    B, T, Hq, dh = q.shape
+    assert k.shape == (B, T, dh) and v.shape == (B, T, dh)
+    o = np.empty_like(q)
+    lib().oracle_attn_fwd(B, T, Hq, dh, int(window), ctypes.c_double(scale), _p(q), _p(k), _p(v), _p(o))
+    return o
+
+
+def attn_step(q_t, k_t, v_t, kcache, vcache, pos, scale: float):
+    """One decode step with ring caches kcache, vcache [B][W][dh] (updated in
+    place: the new key/value go to slot pos mod W).  q_t [B][Hq][dh], k_t, v_t
+    [B][dh], pos [B] (int, the new token's position).  Returns o_t."""
+    q_t, k_t, v_t = map(_f64, (q_t, k_t, v_t))
+    assert kcache.dtype == np.float64 and kcache.flags["C_CONTIGUOUS"]
+    assert vcache.dtype == np.float64 and vcache.flags["C_CONTIGUOUS"]
+    B, Hq, dh = q_t.shape
+    W = kcache.shape[1]
+    pos = np.ascontiguousarray(pos, dtype=np.int64)
+    o = np.empty_like(q_t)
+    lib().oracle_attn_step(B, Hq, dh, W, ctypes.c_double(scale), _p(q_t), _p(k_t), _p(v_t),
+                           _p(kcache), _p(vcache), pos.ctypes.data_as(ctypes.POINTER(ctypes.c_long)),
+                           _p(o))
+    return o

@@ -28,6 +28,12 @@
  *         RecurrentBlock: Conv1d with padding k-1, groups = width, keep the
  *         first T outputs).
  *  [W]  "Griffin" (wiki note), section "Gated Linear Recurrence".
+ *  [N]  "Griffin" (wiki note), section "Local Attention Path": the window
+ *       N(t) = {i : t - w < i <= t} and y_t = sum over N(t) of
+ *       softmax_i(q_t . k_i) v_i; [G] "Local Sliding-Window Multi-Query
+ *       Attention (MQA)" (one key head and one value head shared by all query
+ *       heads) and "Bounding the Key-Value Cache Footprint" (the cache holds
+ *       at most W positions, the oldest evicted ring-buffer fashion).
  *
  * Readings where the pages are silent or disagree (each is stated where used):
  *  R1  gates are block-diagonal with K = D/H; W[h][o][j] multiplies input
@@ -51,6 +57,11 @@
  *      sqrt 2)), which is what the listing's F.gelu computes (the pages also
  *      show a tanh form for the MLP, not for this merge); the residual add is
  *      the decoder layer's, outside the block.
+ *  R7  local attention: the scores carry a caller-given scale (the page's
+ *      formula shows none; the workloads pass 1/sqrt(d_head)); the inputs q,
+ *      k are taken after any rotary embedding (positional encoding is the
+ *      attention block's, outside this operation); the ring slot of position
+ *      p is p mod W.
  */
 #include <math.h>
 #include <stddef.h>
@@ -393,4 +404,99 @@ void oracle_merge(long n, const double *y, const double *g, double *z)
 {
     #pragma omp parallel for schedule(static)
     for (long e = 0; e < n; ++e) z[e] = y[e] * (0.5 * g[e] * (1.0 + erf(g[e] / sqrt(2.0))));
+}
+
+/* ------------------------------------------------------------ local attention
+ * [N] "Local Attention Path" and [G] "Local Sliding-Window Multi-Query
+ * Attention (MQA)" (R7).  q [B][T][Hq][dh], k and v [B][T][dh] (one shared key
+ * head and value head), o [B][T][Hq][dh]. */
+
+/* softmax over the scores of one query row, then the weighted sum of values:
+ * s_j = scale * (q . key_j) for the n keys given by row pointers, o = sum_j
+ * p_j val_j with p = softmax(s) (the maximum is subtracted first, which leaves
+ * softmax unchanged) */
+static void attend_rows(int n, int dh, double scale, const double *q, const double *const *keys,
+                        const double *const *vals, double *s, double *o)
+{
+    double m = -INFINITY;
+    for (int j = 0; j < n; ++j) {
+        double acc = 0.0;
+        for (int e = 0; e < dh; ++e) acc += q[e] * keys[j][e];
+        s[j] = scale * acc;
+        if (s[j] > m) m = s[j];
+    }
+    double sum = 0.0;
+    for (int j = 0; j < n; ++j) {
+        s[j] = exp(s[j] - m);
+        sum += s[j];
+    }
+    for (int e = 0; e < dh; ++e) o[e] = 0.0;
+    for (int j = 0; j < n; ++j) {
+        const double p = s[j] / sum;
+        for (int e = 0; e < dh; ++e) o[e] += p * vals[j][e];
+    }
+}
+
+/* prefill: token t of stream b attends to positions t-W+1 .. t (those >= 0) */
+void oracle_attn_fwd(int B, int T, int Hq, int dh, int W, double scale, const double *q,
+                     const double *k, const double *v, double *o)
+{
+    #pragma omp parallel
+    {
+        const double **keys = malloc(sizeof(double *) * (size_t)W);
+        const double **vals = malloc(sizeof(double *) * (size_t)W);
+        double *s = malloc(sizeof(double) * (size_t)W);
+        #pragma omp for schedule(dynamic) collapse(2)
+        for (int b = 0; b < B; ++b)
+            for (int t = 0; t < T; ++t) {
+                const int lo = t - W + 1 < 0 ? 0 : t - W + 1;
+                const int n = t - lo + 1;
+                for (int j = 0; j < n; ++j) {
+                    keys[j] = k + ((size_t)b * T + lo + j) * dh;
+                    vals[j] = v + ((size_t)b * T + lo + j) * dh;
+                }
+                for (int h = 0; h < Hq; ++h) {
+                    const size_t row = (((size_t)b * T + t) * Hq + h) * dh;
+                    attend_rows(n, dh, scale, q + row, keys, vals, s, o + row);
+                }
+            }
+        free(keys);
+        free(vals);
+        free(s);
+    }
+}
+
+/* decode: the ring caches kc, vc [B][W][dh] hold the positions before pos[b]
+ * (position p in slot p mod W); the new key and value (k_t, v_t [B][dh]) go to
+ * slot pos[b] mod W, evicting position pos[b] - W, and q_t [B][Hq][dh]
+ * attends to the positions max(0, pos[b]-W+1) .. pos[b]. */
+void oracle_attn_step(int B, int Hq, int dh, int W, double scale, const double *q_t,
+                      const double *k_t, const double *v_t, double *kc, double *vc,
+                      const long *pos, double *o_t)
+{
+    const double **keys = malloc(sizeof(double *) * (size_t)W);
+    const double **vals = malloc(sizeof(double *) * (size_t)W);
+    double *s = malloc(sizeof(double) * (size_t)W);
+    for (int b = 0; b < B; ++b) {
+        const long p = pos[b];
+        const size_t slot = (size_t)(p % W);
+        for (int e = 0; e < dh; ++e) {
+            kc[((size_t)b * W + slot) * dh + e] = k_t[(size_t)b * dh + e];
+            vc[((size_t)b * W + slot) * dh + e] = v_t[(size_t)b * dh + e];
+        }
+        const long lo = p - W + 1 < 0 ? 0 : p - W + 1;
+        const int n = (int)(p - lo + 1);
+        for (int j = 0; j < n; ++j) {
+            const size_t sl = (size_t)((lo + j) % W);
+            keys[j] = kc + ((size_t)b * W + sl) * dh;
+            vals[j] = vc + ((size_t)b * W + sl) * dh;
+        }
+        for (int h = 0; h < Hq; ++h) {
+            const size_t row = ((size_t)b * Hq + h) * dh;
+            attend_rows(n, dh, scale, q_t + row, keys, vals, s, o_t + row);
+        }
+    }
+    free(keys);
+    free(vals);
+    free(s);
 }
