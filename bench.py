@@ -12,9 +12,10 @@ the previous one.
 
 The other entry points are timed the same way, each on its own workload, and
 reported under "rows": conv1d, gates and the scan stage alone on the 2B-width
-prefill, the fused forward on the 32k-token prefill, 512 decode steps of 256
-streams, and the backward of the 9B-width workload (B = 4, T = 8192,
-D = 4096).
+prefill, the recurrent block around the path on the same shape (three
+projections plus the fused forward with the GeLU merge, d_model = D = 2560),
+the fused forward on the 32k-token prefill, 512 decode steps of 256 streams,
+and the backward of the 9B-width workload (B = 4, T = 8192, D = 4096).
 
 Prints ONE JSON line: tokens*channels/s for the whole job, the dominant
 kernel's achieved algorithmic HBM bandwidth against the 8 TB/s peak (kernel
@@ -40,7 +41,7 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 KERNEL_SOURCES = ("fwd.hip", "common.h", "gatemath.h")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_fused_2b_prefill_pmc.json")
-ALL_ROWS = ("conv1d", "gates", "scan", "long", "decode", "bwd")
+ALL_ROWS = ("conv1d", "gates", "scan", "block", "long", "decode", "bwd")
 
 
 def kernel_hash() -> str:
@@ -315,6 +316,50 @@ def main():
     del sets
     torch.cuda.empty_cache()
 
+    if "block" in rows:
+        # the recurrent block around the path: two input projections, the fused
+        # forward with the GeLU merge (mode 4), the output projection
+        dm = D
+        bp = synth.make_block_params(cfg.idx, dm, D, cfg.io)
+        bw = glr.BlockWeights(dev_t(bp.proj_in_1), dev_t(bp.proj_in_2), dev_t(bp.proj_out))
+        x0 = dev_t(synth.make_activation(cfg.idx, "block_x", (B, T, dm), cfg.io))
+        b_sets = [dict(x=x0 if k == 0 else x0.clone(), o=torch.empty_like(x0)) for k in range(2)]
+        hb = torch.empty((B, D), dtype=torch.float32, device=dev)
+        sb = torch.empty((B, 3, D), dtype=torch.bfloat16, device=dev)
+        glr.workspace(glr.block_workspace_size(B, T, D, H, dm, glr.BF16), dev, "block",
+                      (B, T, D, H, dm, glr.BF16))
+        _say(f"recurrent block, 2B width B={B} T={T} D=d_model={D}")
+
+        def bstep(k):
+            s = b_sets[k % 2]
+            glr.block_fwd(s["x"], w, bw, out=s["o"], h_last_out=hb, hist_out_buf=sb)
+        kk, _ = tm.calls(bstep, 20, 3)
+        M = B * T
+        gemm_flops = 3 * 2 * M * dm * D
+        # algorithmic bytes: x in, out, the three projections, the RG-LRU's own
+        # parameters, state and history (b1, b2 and the merged product are the
+        # block's intermediates)
+        nb = 2 * M * dm * 2 + 3 * D * dm * 2 + 2 * H * 65536 * 2 + D * 8 * 4 + B * D * 4 + B * 3 * D * 2
+        r = row(f"rglru_block_fwd, 2B width (B={B} T={T} D=d_model={D} bf16): 3 projections "
+                "(rocBLAS) + fused forward with the GeLU merge", kk, tokch, nb,
+                flops=gemm_flops + 2 * 2 * 256 * tokch, bound="mfma",
+                note="algorithmic flops: the three projections (3 x 2 M d_model D) and the gate "
+                     "products; tokens_ch counts B*T*D")
+        # the same three products through torch (hipBLASLt/rocBLAS as torch picks), for context
+        import torch.nn.functional as F
+        zt = torch.empty((B, T, D), dtype=torch.bfloat16, device=dev)
+
+        def tstep(k):
+            s = b_sets[k % 2]
+            F.linear(s["x"], bw.proj_in_1)
+            F.linear(s["x"], bw.proj_in_2)
+            F.linear(zt, bw.proj_out)
+        tk, _ = tm.calls(tstep, 10, 2)
+        r["torch_linear_x3_ms"] = float(np.mean(tk))
+        out["rows"]["block"] = r
+        del b_sets, x0, zt, bw
+        torch.cuda.empty_cache()
+
     if "long" in rows:
         c2 = synth.CONFIGS[2]
         _, w2 = weights(c2)
@@ -365,7 +410,8 @@ def main():
         _, w4 = weights(c4)
         u4 = dev_t(synth.make_u(c4))
         dy4 = dev_t(synth.make_dy(c4))
-        glr.workspace(glr.workspace_size(c4.B, c4.T, c4.D, c4.H, glr.BF16, glr.OP_SCAN_BWD), dev)
+        glr.workspace(glr.workspace_size(c4.B, c4.T, c4.D, c4.H, glr.BF16, glr.OP_SCAN_BWD), dev, "bwd",
+                      (c4.B, c4.T, c4.D, c4.H, glr.BF16))
         _say(f"backward, 9B width B={c4.B} T={c4.T} D={c4.D}")
         kk, _ = tm.calls(lambda k: glr.scan_bwd(u4, w4, dy4), 5, 2)
         t4 = c4.B * c4.T * c4.D

@@ -44,9 +44,15 @@ class _Weights(ctypes.Structure):
                 ("Lambda", ctypes.c_void_p)]
 
 
+class _Block(ctypes.Structure):
+    _fields_ = [("proj_in_1", ctypes.c_void_p), ("proj_in_2", ctypes.c_void_p),
+                ("proj_out", ctypes.c_void_p)]
+
+
 _lib = None
 SYMBOLS = ("rglru_workspace_size", "rglru_conv1d", "rglru_gates", "rglru_scan_fwd",
-           "rglru_step", "rglru_scan_bwd", "rglru_status_string")
+           "rglru_step", "rglru_scan_bwd", "rglru_block_workspace_size", "rglru_block_fwd",
+           "rglru_status_string")
 
 
 def lib():
@@ -66,6 +72,9 @@ def lib():
         L.rglru_scan_fwd.argtypes = [D, W, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.rglru_step.argtypes = [D, W, vp, vp, vp, vp, vp]
         L.rglru_scan_bwd.argtypes = [D, W, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.rglru_block_workspace_size.argtypes = [D, ctypes.c_int64, ctypes.POINTER(sz)]
+        L.rglru_block_fwd.argtypes = [D, ctypes.c_int64, W, ctypes.POINTER(_Block), vp, vp, vp, vp, vp, vp,
+                                      vp, sz, vp]
         for s in SYMBOLS:
             if s != "rglru_status_string":
                 getattr(L, s).restype = ctypes.c_int
@@ -143,7 +152,7 @@ def _weights_struct(w: Weights, D: int, dtype, device, conv: bool, gates: bool):
 
 
 # ------------------------------------------------------------------ workspace
-_ws_cache = {}
+_ws_cache = {}   # (device, kind) -> [buffer, layout key]
 
 
 def workspace_size(B, T, D, H, io=BF16, op=OP_SCAN_FWD, c=8.0) -> int:
@@ -153,18 +162,35 @@ def workspace_size(B, T, D, H, io=BF16, op=OP_SCAN_FWD, c=8.0) -> int:
     return int(n.value)
 
 
-def workspace(nbytes: int, device) -> torch.Tensor:
-    """A zero-filled workspace of at least nbytes, cached per device.
+def block_workspace_size(B, T, D, H, d_model, io=BF16, c=8.0) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().rglru_block_workspace_size(ctypes.byref(_Desc(B, T, D, H, io, c)), d_model,
+                                            ctypes.byref(n)), "rglru_block_workspace_size")
+    return int(n.value)
+
+
+def workspace(nbytes: int, device, kind: str = "fwd", key=None) -> torch.Tensor:
+    """A zero-filled workspace of at least nbytes, one cached buffer per device
+    and kind ("fwd", "bwd", "block").
 
     The library restores the workspace header at the end of every call, so the
     cached buffer can be reused by calls that run one after another (one
-    stream).  Calls that may overlap need workspaces of their own."""
+    stream).  A forward-scan workspace holds only counters and tagged carry
+    words, so it serves calls of any shape.  The backward's and the block's
+    also keep plain data, which must not sit where a later call of another
+    layout expects carry words: when `key` (the layout: shape and dtype)
+    differs from the previous call's, the buffer is zero-filled again, on the
+    current stream, before it is handed out.  Calls that may overlap need
+    workspaces of their own."""
     device = torch.device(device)
-    buf = _ws_cache.get(device)
-    if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
-        _ws_cache[device] = buf
-    return buf
+    ent = _ws_cache.get((device, kind))
+    if ent is None or ent[0].numel() < nbytes:
+        ent = [torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device), key]
+        _ws_cache[(device, kind)] = ent
+    elif key != ent[1]:
+        ent[0].zero_()
+        ent[1] = key
+    return ent[0]
 
 
 # ----------------------------------------------------------------- entry points
@@ -281,10 +307,57 @@ def scan_bwd(u: torch.Tensor, w: Weights, dy: torch.Tensor, *, h0=None, hist_in=
              dh0=torch.empty((B, D), **f) if want_dh0 else None)
     d = _Desc(B, T, D, H, _io(u), w.c)
     nbytes = workspace_size(B, T, D, H, _io(u), OP_SCAN_BWD, w.c)
-    wsb = workspace(nbytes, dev)
+    wsb = workspace(nbytes, dev, "bwd", (B, T, D, H, _io(u)))
     _check(lib().rglru_scan_bwd(ctypes.byref(d), ctypes.byref(ws_), _ptr(u), _ptr(hist_in), _ptr(h0),
                                 _ptr(dy), _ptr(dh_last), _ptr(g["du"]), _ptr(g["dconv_w"]),
                                 _ptr(g["dconv_b"]), _ptr(g["dW_a"]), _ptr(g["db_a"]), _ptr(g["dW_x"]),
                                 _ptr(g["db_x"]), _ptr(g["dLambda"]), _ptr(g["dh0"]), _ptr(wsb),
                                 wsb.numel(), _stream(dev)), "rglru_scan_bwd")
     return g
+
+
+@dataclasses.dataclass
+class BlockWeights:
+    """Device tensors of the recurrent block's projections (activation dtype):
+    proj_in_1, proj_in_2 [D][d_model], proj_out [d_model][D]."""
+    proj_in_1: torch.Tensor
+    proj_in_2: torch.Tensor
+    proj_out: torch.Tensor
+
+    @property
+    def d_model(self) -> int:
+        return int(self.proj_in_1.shape[1])
+
+
+def block_fwd(x: torch.Tensor, w: Weights, bw: BlockWeights, *, h0=None, hist_in=None,
+              want_hist: bool = True, out=None, h_last_out=None, hist_out_buf=None):
+    """Recurrent block forward: out = proj_out(RG-LRU(conv(proj_in_1 x)) * GeLU(proj_in_2 x)).
+
+    x [B][T][d_model].  Returns (out, h_last, hist_out or None); the state and
+    the conv history are those of branch 1 (width D)."""
+    dev = x.device
+    _need(x, "x", dev)
+    B, T, d_model = x.shape
+    D = int(bw.proj_in_1.shape[0])
+    _need(bw.proj_in_1, "proj_in_1", dev, x.dtype, (D, d_model))
+    _need(bw.proj_in_2, "proj_in_2", dev, x.dtype, (D, d_model))
+    _need(bw.proj_out, "proj_out", dev, x.dtype, (d_model, D))
+    _need(h0, "h0", dev, torch.float32, (B, D))
+    _need(hist_in, "hist_in", dev, x.dtype, (B, 3, D))
+    ws_ = _weights_struct(w, D, x.dtype, dev, conv=True, gates=True)
+    o = torch.empty_like(x) if out is None else out
+    h_last = torch.empty((B, D), dtype=torch.float32, device=dev) if h_last_out is None else h_last_out
+    hist_out = None
+    if want_hist:
+        hist_out = hist_out_buf if hist_out_buf is not None else torch.empty((B, 3, D), dtype=x.dtype, device=dev)
+    _need(o, "out", dev, x.dtype, (B, T, d_model))
+    _need(h_last, "h_last_out", dev, torch.float32, (B, D))
+    _need(hist_out, "hist_out_buf", dev, x.dtype, (B, 3, D))
+    d = _Desc(B, T, D, w.H, _io(x), w.c)
+    nbytes = block_workspace_size(B, T, D, w.H, d_model, _io(x), w.c)
+    wsb = workspace(nbytes, dev, "block", (B, T, D, w.H, d_model, _io(x)))
+    blk = _Block(_ptr(bw.proj_in_1), _ptr(bw.proj_in_2), _ptr(bw.proj_out))
+    _check(lib().rglru_block_fwd(ctypes.byref(d), d_model, ctypes.byref(ws_), ctypes.byref(blk), _ptr(x),
+                                 _ptr(hist_in), _ptr(h0), _ptr(o), _ptr(h_last), _ptr(hist_out), _ptr(wsb),
+                                 wsb.numel(), _stream(dev)), "rglru_block_fwd")
+    return o, h_last, hist_out

@@ -31,6 +31,18 @@ int check_desc(const rglru_desc *d, bool need_k256)
     return RGLRU_OK;
 }
 
+// the recurrent block: the scan's checks plus the GEMM sizes (rocBLAS takes
+// 64-bit sizes; each dimension is kept below 2^31 all the same)
+int check_block(const rglru_desc *d, int64_t d_model)
+{
+    int st = check_desc(d, true);
+    if (st) return st;
+    if (d_model < 1 || d_model > MAX_DIM) return RGLRU_ERR_SHAPE;
+    if (d->B * d->T >= 2147483647 || d->D >= 2147483647) return RGLRU_ERR_SHAPE;
+    if ((double)d->B * (double)d->T * (double)d_model > 9.0e15) return RGLRU_ERR_SHAPE;
+    return RGLRU_OK;
+}
+
 struct Range {
     const void *p;
     size_t bytes;
@@ -75,6 +87,7 @@ const char *rglru_status_string(int status)
     case RGLRU_ERR_WORKSPACE: return "workspace missing or too small";
     case RGLRU_ERR_LAUNCH: return "HIP launch error";
     case RGLRU_ERR_ARG: return "inconsistent arguments";
+    case RGLRU_ERR_BLAS: return "a rocBLAS call failed";
     default: return "unknown status";
     }
 }
@@ -215,6 +228,44 @@ int rglru_scan_bwd(const rglru_desc *desc, const rglru_weights *w, const void *u
     if (any_alias(outs, 10, ins, 12)) return RGLRU_ERR_ARG;
     launch_scan_bwd(d, *w, u, hist_in, h0, dy, dh_last, du, dconv_w, dconv_b, dW_a, db_a, dW_x, db_x,
                     dLambda, dh0, ws, stream);
+    return launch_status();
+}
+
+int rglru_block_workspace_size(const rglru_desc *desc, int64_t d_model, size_t *bytes)
+{
+    if (!bytes) return RGLRU_ERR_NULL;
+    int st = check_block(desc, d_model);
+    if (st) return st;
+    *bytes = block_layout(desc->B, desc->T, desc->D, esize(*desc)).bytes;
+    return RGLRU_OK;
+}
+
+int rglru_block_fwd(const rglru_desc *desc, int64_t d_model, const rglru_weights *w, const rglru_block *blk,
+                    const void *x, const void *hist_in, const float *h0, void *out, float *h_last,
+                    void *hist_out, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int st = check_block(desc, d_model);
+    if (st) return st;
+    if (!w || !blk || !w->conv_w || !w->W_a || !w->W_x || !w->Lambda || !blk->proj_in_1 ||
+        !blk->proj_in_2 || !blk->proj_out || !x || !out)
+        return RGLRU_ERR_NULL;
+    if (!ws) return RGLRU_ERR_WORKSPACE;
+    const void *all[] = {x, hist_in, h0, out, h_last, hist_out, ws, w->conv_w, w->conv_b, w->W_a,
+                         w->b_a, w->W_x, w->b_x, w->Lambda, blk->proj_in_1, blk->proj_in_2, blk->proj_out};
+    for (const void *p : all)
+        if (p && !aligned16(p)) return RGLRU_ERR_ALIGN;
+    const rglru_desc &d = *desc;
+    const size_t need = block_layout(d.B, d.T, d.D, esize(d)).bytes;
+    if (ws_bytes < need) return RGLRU_ERR_WORKSPACE;
+    const size_t e = esize(d), io_x = d.B * d.T * d_model * e, hist = d.B * 3 * d.D * e;
+    const size_t sb = d.B * d.D * 4, vec = d.D * 4, wb = d.H * 65536 * e, pw = d.D * d_model * e;
+    const Range outs[] = {{out, io_x}, {h_last, sb}, {hist_out, hist}, {ws, need}};
+    const Range ins[] = {{x, io_x}, {hist_in, hist}, {h0, sb}, {w->conv_w, vec * 4}, {w->conv_b, vec},
+                         {w->W_a, wb}, {w->b_a, vec}, {w->W_x, wb}, {w->b_x, vec}, {w->Lambda, vec},
+                         {blk->proj_in_1, pw}, {blk->proj_in_2, pw}, {blk->proj_out, pw}};
+    if (any_alias(outs, 4, ins, 13)) return RGLRU_ERR_ARG;
+    st = launch_block_fwd(d, d_model, *w, *blk, x, hist_in, h0, out, h_last, hist_out, ws, stream);
+    if (st) return st;
     return launch_status();
 }
 

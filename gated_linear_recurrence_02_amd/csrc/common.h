@@ -266,6 +266,24 @@ template <typename E> __device__ __forceinline__ uint32_t gate_off(int ch, int t
     return (uint32_t)((((t >> 4) * (16 / V) + ((t & 15) / V)) * 256 + ch) * V + (t % V));
 }
 
+// GeLU(v) = v Phi(v) = 0.5 v (1 + erf(v / sqrt 2)), the exact form, with erfc
+// from Abramowitz & Stegun, Handbook of Mathematical Functions (1964), eq.
+// 7.1.26 (|error| <= 1.5e-7): for x >= 0, erfc(x) = p(s) s e^(-x^2),
+// s = 1 / (1 + 0.3275911 x), p of degree 4.  With h = erfc(|v| / sqrt 2) / 2,
+// v Phi(v) = max(v, 0) - |v| h on both sides of zero (Phi(-w) = erfc(w / sqrt 2) / 2),
+// so the left tail has no cancellation; h's polynomial carries the 1/2.
+__device__ __forceinline__ float gelu_exact(float v)
+{
+    const float a = fabsf(v);
+    const float s = hw_rcp(fmaf(0.2316418883f, a, 1.0f));   // 0.3275911 / sqrt 2
+    float p = fmaf(0.5307027145f, s, -0.7265760135f);
+    p = fmaf(p, s, 0.7107068705f);
+    p = fmaf(p, s, -0.142248368f);
+    p = fmaf(p, s, 0.127414796f);
+    const float h = p * s * hw_exp2((v * v) * -0.72134752044448170f);   // e^(-v^2 / 2)
+    return fmaf(-a, h, fmaxf(v, 0.0f));
+}
+
 // Token held by row `r` of a 32-row MFMA tile.  The 32x32 output tile gives
 // lane l the column l%32 and the rows 8j + 4(l/32) + i (register 4j + i);
 // mapping row 8j + 4h + i to token 16h + 4j + i makes register k of lane l

@@ -60,15 +60,24 @@ constexpr int PSTRIDE = 36;   // floats per lane in the pending slot (b128, conf
 // 512-byte rows (64 lanes x 16 bytes); blocks of two rows are padded to 1040
 // bytes so that rows 16 apart fall in different LDS banks.
 constexpr int ST_BLOCKS = 18, ST_BLK = 1040, ST_BYTES = ST_BLOCKS * ST_BLK;
+// Mode 4: the branch-2 tile of a full chunk (tokens 32c .. 32c+31), same row
+// layout, brought in while the chunk's front runs and read by its back half
+constexpr int GT_BLOCKS = 16, GT_BYTES = GT_BLOCKS * ST_BLK;
 
 __device__ __forceinline__ bool stageable(int c, int T) { return c > 0 && (c + 1) * CHUNK <= T; }
 
+// OPQ: the lane's part of the address is rebuilt at every call instead of
+// being kept live (as a 64-bit pointer) across the caller's loop -- fewer
+// spilled registers in mode 4, a little slower where registers suffice
+template <int NBLK = ST_BLOCKS, bool OPQ = false>
 __device__ __forceinline__ void stage_issue(const bf16 *in, long row0, int D, int g, char *dst,
                                             int wave, int lane)
 {
-    for (int i = wave; i < ST_BLOCKS; i += 8) {
-        const long row = row0 + 2 * i + (lane >> 5);
-        const bf16 *src = in + row * D + g * 256 + (lane & 31) * 8;
+    int loff = (lane >> 5) * D + (lane & 31) * 8;
+    if constexpr (OPQ) asm volatile("" : "+v"(loff));
+    for (int i = wave; i < NBLK; i += 8) {
+        const bf16 *src = OPQ ? in + (row0 + 2 * i) * D + g * 256 + loff
+                              : in + (row0 + 2 * i + (lane >> 5)) * D + g * 256 + (lane & 31) * 8;
         __builtin_amdgcn_global_load_lds((const void *)src,
                                          (__attribute__((address_space(3))) void *)(dst + i * ST_BLK),
                                          16, 0, 0);
@@ -94,6 +103,7 @@ struct FwdParams {
     void *hist_out;
     float *hstart_out;   // nullable: state before each chunk, [B][NC][D]
     void *ri_out;        // mode 3: r and i of every token in the backward's unit layout
+    const void *gate_in; // mode 4: branch-2 pre-activation g; y becomes y * GeLU(g)
     WsHeader *hdr;
     uint32_t *claim;
     uint64_t *aggA, *aggX, *incl;
@@ -134,10 +144,12 @@ template <typename T, int MODE>
 __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
 {
     constexpr int S = XTile<T>::STRIDE;
-    constexpr bool CONV = MODE == 0 || MODE == 3;           // conv fused in front
+    constexpr bool CONV = MODE == 0 || MODE == 3 || MODE == 4;   // conv fused in front
     constexpr bool RI = MODE == 3;                          // gate values stored
+    constexpr bool MERGE = MODE == 4;                       // y * GeLU(g) stored instead of y
     constexpr bool WREG = (sizeof(T) == 2) && MODE != 2;   // weights held in registers
     constexpr bool STAGE = (sizeof(T) == 2) && CONV;        // input tile prefetched into LDS
+    constexpr bool GTILE = STAGE && MERGE;                   // branch-2 tile staged too
     extern __shared__ __attribute__((aligned(16))) char smem[];
     T *Xs = (T *)smem;
     float *pslot_base = (float *)(smem + (MODE == 2 ? 0 : 32 * S * sizeof(T)));
@@ -146,7 +158,8 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 31, half = lane >> 5;
     const int g = blockIdx.x % p.G;
-    uint32_t *s_unit = (uint32_t *)(stage_base + (STAGE ? 2 * ST_BYTES : 0));   // 2 claim slots, flag
+    char *gt_base = stage_base + (STAGE ? 2 * ST_BYTES : 0);   // mode 4: two branch-2 tiles
+    uint32_t *s_unit = (uint32_t *)(gt_base + (GTILE ? 2 * GT_BYTES : 0));   // 2 claim slots, flag
     uint32_t *claim = p.claim + g;
     if (tid == 0) {
         s_unit[0] = claim_next(claim);
@@ -204,8 +217,8 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
         if (j < units) {
             const int c0 = (int)(j / p.B), b0 = (int)(j % p.B);
             if (stageable(c0, p.T))
-                stage_issue((const bf16 *)in, (long)b0 * p.T + (long)c0 * CHUNK - 4, p.D, g, stage_base,
-                            wave, lane);
+                stage_issue<ST_BLOCKS, MERGE>((const bf16 *)in, (long)b0 * p.T + (long)c0 * CHUNK - 4, p.D,
+                                              g, stage_base, wave, lane);
         }
     }
 
@@ -240,9 +253,14 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
                     if (jn < units) {   // prefetch the next unit's tile
                         const int cn = (int)(jn / p.B), bn = (int)(jn % p.B);
                         if (stageable(cn, p.T))
-                            stage_issue((const bf16 *)in, (long)bn * p.T + (long)cn * CHUNK - 4, p.D, g,
-                                        stage_base + ((it + 1) & 1) * ST_BYTES, wave, lane);
+                            stage_issue<ST_BLOCKS, MERGE>((const bf16 *)in, (long)bn * p.T + (long)cn * CHUNK - 4,
+                                                          p.D, g, stage_base + ((it + 1) & 1) * ST_BYTES, wave,
+                                                          lane);
                     }
+                    // this unit's branch-2 tile, read by its back half in the next iteration
+                    if (GTILE && full)
+                        stage_issue<GT_BLOCKS, true>((const bf16 *)p.gate_in, row_b + (long)c * CHUNK, p.D, g,
+                                                     gt_base + (it & 1) * GT_BYTES, wave, lane);
                 }
                 if (staged) {
                     const char *buf = stage_base + (it & 1) * ST_BYTES;
@@ -416,16 +434,39 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) yl[4 * q + e] = fmaf(vp[e], hstart, vh[e]);
             }
+            float zl[16];   // what is stored: y, or y * GeLU(g) in mode 4
+            if constexpr (MERGE) {
+                float gv[16];
+                if (GTILE && (c + 1) * CHUNK <= p.T) {   // staged during the chunk's front
+                    // the lane's offset is rebuilt here rather than kept live
+                    // across the loop, where registers are short
+                    int off = ((it + 1) & 1) * GT_BYTES + half * 8 * ST_BLK + ch * 2;
+                    asm volatile("" : "+v"(off));
+                    const char *buf = gt_base + off;
+#pragma unroll
+                    for (int k = 0; k < 16; ++k)
+                        gv[k] = (float)*(const bf16 *)(buf + (k >> 1) * ST_BLK + (k & 1) * 512);
+                } else {
+                    const T *gp = (const T *)p.gate_in + (row_b + tb) * p.D + d;
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) gv[k] = (dv && tb + k < p.T) ? ldf(gp + (long)k * p.D) : 0.0f;
+                }
+#pragma unroll
+                for (int k = 0; k < 16; ++k) zl[k] = yl[k] * gelu_exact(gv[k]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 16; ++k) zl[k] = yl[k];
+            }
             T *y = (T *)p.y;
             if (y && dv) {
                 T *dst = y + (row_b + tb) * p.D + d;
                 if ((c + 1) * CHUNK <= p.T) {
 #pragma unroll
-                    for (int k = 0; k < 16; ++k) dst[(long)k * p.D] = from_f32<T>(yl[k]);
+                    for (int k = 0; k < 16; ++k) dst[(long)k * p.D] = from_f32<T>(zl[k]);
                 } else {
 #pragma unroll
                     for (int k = 0; k < 16; ++k)
-                        if (tb + k < p.T) dst[(long)k * p.D] = from_f32<T>(yl[k]);
+                        if (tb + k < p.T) dst[(long)k * p.D] = from_f32<T>(zl[k]);
                 }
             }
             if (c == p.NC - 1 && dv) {
@@ -466,9 +507,10 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
 template <typename T, int MODE>
 size_t fwd_lds_bytes()
 {
-    const bool stage = sizeof(T) == 2 && (MODE == 0 || MODE == 3);
+    const bool stage = sizeof(T) == 2 && (MODE == 0 || MODE == 3 || MODE == 4);
+    const bool gtile = sizeof(T) == 2 && MODE == 4;
     return (MODE == 2 ? 0 : 32 * XTile<T>::STRIDE * sizeof(T)) + 512 * PSTRIDE * sizeof(float) +
-           (stage ? 2 * ST_BYTES : 0) + 16;
+           (stage ? 2 * ST_BYTES : 0) + (gtile ? 2 * GT_BYTES : 0) + 16;
 }
 
 // Per device: CU count and resident workgroups per CU of one kernel, looked
@@ -505,7 +547,8 @@ template <typename T, int MODE>
 void launch_mode(FwdParams p, hipStream_t s)
 {
     static_assert(32 * 260 * 4 + 512 * PSTRIDE * 4 + 16 <= 160 * 1024, "LDS budget (fp32)");
-    static_assert(32 * 264 * 2 + 512 * PSTRIDE * 4 + 2 * ST_BYTES + 16 <= 160 * 1024, "LDS budget (bf16)");
+    static_assert(32 * 264 * 2 + 512 * PSTRIDE * 4 + 2 * ST_BYTES + 2 * GT_BYTES + 16 <= 160 * 1024,
+                  "LDS budget (bf16)");
     const LaunchShape ls = fwd_shape<T, MODE>();
     // workgroups per block: fill the resident slots, never more than the units
     long wpg = ((long)ls.ncu * ls.occ) / p.G;
@@ -522,12 +565,14 @@ void launch_t(const FwdParams &p, int mode, hipStream_t s)
     if (mode == 0) launch_mode<T, 0>(p, s);
     else if (mode == 1) launch_mode<T, 1>(p, s);
     else if (mode == 2) launch_mode<T, 2>(p, s);
-    else launch_mode<T, 3>(p, s);
+    else if (mode == 3) launch_mode<T, 3>(p, s);
+    else launch_mode<T, 4>(p, s);
 }
 
 void run_fwd(const rglru_desc &d, const rglru_weights &w, int mode, const void *in, const void *r,
              const void *i, const void *hist_in, const float *h0, void *y, float *h_last,
-             void *hist_out, float *hstart_out, void *ri_out, void *ws, hipStream_t s)
+             void *hist_out, float *hstart_out, void *ri_out, const void *gate_in, void *ws,
+             hipStream_t s)
 {
     FwdParams p;
     p.B = (int)d.B;
@@ -554,6 +599,7 @@ void run_fwd(const rglru_desc &d, const rglru_weights &w, int mode, const void *
     p.hist_out = hist_out;
     p.hstart_out = hstart_out;
     p.ri_out = ri_out;
+    p.gate_in = gate_in;
     p.hdr = (WsHeader *)ws;
     p.claim = (uint32_t *)((char *)ws + sizeof(WsHeader));
     const size_t nw = (size_t)d.B * p.NC * d.D;
@@ -576,15 +622,22 @@ void launch_scan_fwd(const rglru_desc &d, const rglru_weights &w, int mode, cons
                      const void *r, const void *i, const void *hist_in, const float *h0, void *y,
                      float *h_last, void *hist_out, void *ws, hipStream_t s)
 {
-    run_fwd(d, w, mode, in, r, i, hist_in, h0, y, h_last, hist_out, nullptr, nullptr, ws, s);
+    run_fwd(d, w, mode, in, r, i, hist_in, h0, y, h_last, hist_out, nullptr, nullptr, nullptr, ws, s);
 }
 
 void launch_fwd_states(const rglru_desc &d, const rglru_weights &w, const void *u,
                        const void *hist_in, const float *h0, float *hstart_out, void *ri_out,
                        void *ws, hipStream_t s)
 {
-    run_fwd(d, w, 3, u, nullptr, nullptr, hist_in, h0, nullptr, nullptr, nullptr, hstart_out, ri_out, ws,
-            s);
+    run_fwd(d, w, 3, u, nullptr, nullptr, hist_in, h0, nullptr, nullptr, nullptr, hstart_out, ri_out, nullptr,
+            ws, s);
+}
+
+void launch_scan_fwd_merge(const rglru_desc &d, const rglru_weights &w, const void *u, const void *g,
+                           const void *hist_in, const float *h0, void *z, float *h_last, void *hist_out,
+                           void *ws, hipStream_t s)
+{
+    run_fwd(d, w, 4, u, nullptr, nullptr, hist_in, h0, z, h_last, hist_out, nullptr, nullptr, g, ws, s);
 }
 
 }  // namespace rglru

@@ -32,6 +32,24 @@ void launch_fwd_states(const rglru_desc &d, const rglru_weights &w, const void *
                        const void *hist_in, const float *h0, float *hstart_out, void *ri_out,
                        void *ws, hipStream_t s);
 
+// mode A with the recurrent block's merge: z = y * GeLU(g) is stored instead
+// of y (g: branch-2 pre-activation, [B][T][D] io)
+void launch_scan_fwd_merge(const rglru_desc &d, const rglru_weights &w, const void *u, const void *g,
+                           const void *hist_in, const float *h0, void *z, float *h_last, void *hist_out,
+                           void *ws, hipStream_t s);
+
+// Recurrent block: byte offsets inside its workspace (scan carries at 0,
+// then the two projections b1 and b2) and the whole size
+struct BlockLayout {
+    size_t scan, b1, b2, bytes;
+};
+BlockLayout block_layout(int64_t B, int64_t T, int64_t D, size_t esz);
+
+// returns an rglru_status (the GEMMs report their own failures)
+int launch_block_fwd(const rglru_desc &d, int64_t d_model, const rglru_weights &w, const rglru_block &blk,
+                     const void *x, const void *hist_in, const float *h0, void *out, float *h_last,
+                     void *hist_out, void *ws, hipStream_t s);
+
 void launch_step(const rglru_desc &d, const rglru_weights &w, const void *u_t, void *hist,
                  float *h, void *y_t, hipStream_t s);
 

@@ -20,8 +20,11 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Pointers.  Every tensor pointer is DEVICE memory owned by the caller.  The
- *   library allocates nothing, keeps no global state and never synchronises
- *   the host: a return of RGLRU_OK means the work was enqueued on `stream`.
+ *   library never synchronises the host: a return of RGLRU_OK means the work
+ *   was enqueued on `stream`.  It allocates nothing and keeps no global state,
+ *   with one exception: rglru_block_fwd creates one rocBLAS handle per device
+ *   on its first call there (rocBLAS allocates its own device memory) and
+ *   keeps it until the process ends.
  * Layouts.  Row-major, channel fastest:
  *     activations u, x, r, i, y, dy, du   [B][T][D]   (dtype desc->io)
  *     conv history hist                   [B][3][D]   (dtype desc->io)
@@ -85,7 +88,8 @@ typedef enum {
     RGLRU_ERR_ALIGN = -4,      /* a pointer is not 16-byte aligned              */
     RGLRU_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than required       */
     RGLRU_ERR_LAUNCH = -6,     /* the HIP runtime reported a launch error       */
-    RGLRU_ERR_ARG = -7         /* inconsistent arguments (mode, aliasing)       */
+    RGLRU_ERR_ARG = -7,        /* inconsistent arguments (mode, aliasing)       */
+    RGLRU_ERR_BLAS = -8        /* a rocBLAS call of rglru_block_fwd failed      */
 } rglru_status;
 
 /* Problem description.  c is the decay-exponent scale (8 on the pages). */
@@ -112,8 +116,12 @@ enum { RGLRU_OP_SCAN_FWD = 0, RGLRU_OP_SCAN_BWD = 1 };
  * (op RGLRU_OP_SCAN_BWD) needs for `desc`.  The workspace carries the chunk
  * carries of the chunked scan and a small header of counters; it must be
  * ZERO-FILLED before its first use and is left ready for the next call
- * (every call restores the header).  One workspace must not be used by two
- * calls that can run at the same time.  Errors: RGLRU_ERR_NULL, _SHAPE,
+ * (every call restores the header).  Its layout depends on the op and on
+ * desc: the carry words of one layout can fall where another layout keeps
+ * plain data, which a later look-back could take for a published carry.  So
+ * reuse a workspace without zero-filling it again only for calls with the same
+ * op and the same desc (B, T, D, H, io).  One workspace must not be used by
+ * two calls that can run at the same time.  Errors: RGLRU_ERR_NULL, _SHAPE,
  * _DTYPE, _ARG (unknown op). */
 int rglru_workspace_size(const rglru_desc *desc, int op, size_t *bytes);
 
@@ -180,6 +188,43 @@ int rglru_scan_bwd(const rglru_desc *desc, const rglru_weights *w, const void *u
                    const float *dh_last, void *du, float *dconv_w, float *dconv_b,
                    float *dW_a, float *db_a, float *dW_x, float *db_x, float *dLambda,
                    float *dh0, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Recurrent-block projections (device pointers, dtype desc->io, row-major,
+ * stored [out][in] like a bias-free linear layer's weight). */
+typedef struct {
+    const void *proj_in_1;   /* [D][d_model]: branch 1 (conv + RG-LRU)  */
+    const void *proj_in_2;   /* [D][d_model]: branch 2 (GeLU gate)      */
+    const void *proj_out;    /* [d_model][D]: back to the model width   */
+} rglru_block;
+
+/* Workspace bytes of rglru_block_fwd for desc and d_model: the forward scan's
+ * carries (same rules as rglru_workspace_size: ZERO-FILLED before first use,
+ * reused only for calls with the same desc and d_model) followed by the two
+ * branch activations.  Errors: RGLRU_ERR_NULL, _SHAPE (as rglru_block_fwd),
+ * _DTYPE. */
+int rglru_block_workspace_size(const rglru_desc *desc, int64_t d_model, size_t *bytes);
+
+/* Recurrent block forward (page "Griffin Guide: RecurrentGemma, RG-LRU &
+ * Hybrid Attention", section "The Recurrent Block Architecture", parts
+ * "Temporal Filtering via Separable 1D Convolutions" and "Non-Linear
+ * Multiplicative Gating with GeLU"; the listing's RecurrentBlock.forward):
+ *     b1 = x proj_in_1^T,  b2 = x proj_in_2^T            [B][T][D]
+ *     y  = RG-LRU(conv(b1))                              as rglru_scan_fwd mode A
+ *     out = (y * GeLU(b2)) proj_out^T                    [B][T][d_model]
+ * with GeLU(v) = v Phi(v), Phi the standard normal CDF (the exact form).  The
+ * block has no biases and no residual add (that is the decoder layer's).
+ * x and out are [B][T][d_model] in desc->io; h0, h_last, hist_in, hist_out
+ * (nullable) are the state and conv history of branch 1, as in
+ * rglru_scan_fwd.  The three projections are rocBLAS GEMMs with fp32
+ * accumulation; b1 and b2 are rounded to io, and so is the merged product
+ * that feeds proj_out.  Reads every field of w (conv_b, b_a, b_x nullable).
+ * K = 256; 1 <= d_model <= 2^30 and B*T, D, d_model each below 2^31 for the
+ * GEMMs.  Extra error: RGLRU_ERR_BLAS when a rocBLAS call fails (work enqueued
+ * before it stays enqueued). */
+int rglru_block_fwd(const rglru_desc *desc, int64_t d_model, const rglru_weights *w,
+                    const rglru_block *blk, const void *x, const void *hist_in, const float *h0,
+                    void *out, float *h_last, void *hist_out, void *ws, size_t ws_bytes,
+                    hipStream_t stream);
 
 /* Short English text of a status code (static storage). */
 const char *rglru_status_string(int status);

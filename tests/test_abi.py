@@ -13,7 +13,7 @@ import gated_linear_recurrence_02_amd as glr
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rglru.h")
 
-OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, ELAUNCH, EARG = 0, -1, -2, -3, -4, -5, -6, -7
+OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, ELAUNCH, EARG, EBLAS = 0, -1, -2, -3, -4, -5, -6, -7, -8
 P = 0x7F0000000000          # a 16-byte aligned fake device address (never dereferenced)
 
 
@@ -53,7 +53,7 @@ def ws_size(d, op=glr.OP_SCAN_FWD):
 
 
 def test_status_strings(L):
-    for rc in (OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, ELAUNCH, EARG):
+    for rc in (OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, ELAUNCH, EARG, EBLAS):
         assert L.rglru_status_string(rc)
     assert L.rglru_status_string(123) == b"unknown status"
 
@@ -150,3 +150,48 @@ def test_scan_bwd_validation(L):
     bad = list(good)
     bad[5] = u                                               # du == u
     assert f(ctypes.byref(d), ctypes.byref(w), *bad, ws, n, s) == EARG
+
+
+def block_ws_size(d, d_model):
+    n = ctypes.c_size_t()
+    rc = glr.lib().rglru_block_workspace_size(ctypes.byref(d), d_model, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_block_workspace_size(L):
+    d = desc()
+    rc, n = block_ws_size(d, 384)
+    _, nf = ws_size(d)
+    act = d.B * d.T * d.D * 2
+    assert rc == OK and n >= nf + 2 * act                 # scan carries + b1 + b2
+    assert block_ws_size(desc(io=glr.F32), 384)[1] >= nf + 2 * 2 * act
+    assert block_ws_size(d, 0)[0] == ESHAPE
+    assert block_ws_size(desc(D=768, H=2), 384)[0] == ESHAPE   # K = 384
+    assert block_ws_size(desc(io=4), 384)[0] == EDTYPE
+    assert L.rglru_block_workspace_size(ctypes.byref(d), 384, None) == ENULL
+
+
+def test_block_fwd_validation(L):
+    d = desc()
+    dm = 384
+    rc, n = block_ws_size(d, dm)
+    assert rc == OK
+    w = weights()
+    s = None
+    x, out = P + 0x1000000, P + 0x2000000
+    ws = P + 0x10000000
+    blk = glr._Block(P + 0x3000000, P + 0x4000000, P + 0x5000000)
+    f = L.rglru_block_fwd
+    args = lambda **k: [k.get(a, v) for a, v in (("x", x), ("hin", None), ("h0", None), ("out", out),
+                                                   ("hl", None), ("hout", None), ("ws", ws), ("n", n))]
+    assert f(ctypes.byref(d), dm, ctypes.byref(w), ctypes.byref(blk), *args(n=n - 1), s) == EWS
+    assert f(ctypes.byref(d), dm, ctypes.byref(w), ctypes.byref(blk), *args(ws=None), s) == EWS
+    assert f(ctypes.byref(d), dm, ctypes.byref(w), None, *args(), s) == ENULL
+    assert f(ctypes.byref(d), dm, ctypes.byref(weights(conv=False)), ctypes.byref(blk), *args(), s) == ENULL
+    assert f(ctypes.byref(d), 0, ctypes.byref(w), ctypes.byref(blk), *args(), s) == ESHAPE
+    assert f(ctypes.byref(d), dm, ctypes.byref(w), ctypes.byref(blk), *args(x=x + 4), s) == EALIGN
+    assert f(ctypes.byref(d), dm, ctypes.byref(w), ctypes.byref(blk), *args(out=x + 16), s) == EARG
+    # the workspace overlapping a projection weight
+    assert f(ctypes.byref(d), dm, ctypes.byref(w), ctypes.byref(blk), *args(ws=P + 0x3000000), s) == EARG
+    bad = glr._Block(P + 0x3000000, None, P + 0x5000000)
+    assert f(ctypes.byref(d), dm, ctypes.byref(w), ctypes.byref(bad), *args(), s) == ENULL

@@ -218,5 +218,5 @@ def test_workspace_reused_across_shapes():
         y, hl, _ = _run_fwd(prob)
         ry, rh, _ = _oracle_slice(prob, 0, 2)
         _cmp(f"T={T} y", prob.slice_block(from_dev(y), 0, 2), ry, TOL["bf16"])
-    hdr = glr._ws_cache[DEV][:16].cpu().numpy().view(np.uint32)
+    hdr = glr._ws_cache[(torch.device(DEV), "fwd")][0][:16].cpu().numpy().view(np.uint32)
     assert hdr[0] == 0 and hdr[1] == 0 and hdr[3] == 0     # counters reset, no look-back timeout
