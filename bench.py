@@ -15,7 +15,9 @@ reported under "rows": conv1d, gates and the scan stage alone on the 2B-width
 prefill, the recurrent block around the path on the same shape (three
 projections plus the fused forward with the GeLU merge, d_model = D = 2560),
 the fused forward on the 32k-token prefill, 512 decode steps of 256 streams,
-and the backward of the 9B-width workload (B = 4, T = 8192, D = 4096).
+the backward of the 9B-width workload (B = 4, T = 8192, D = 4096), and the
+local sliding-window MQA (10 query heads of 256, window 2048) as prefill on
+the 2B-width and 32k-token shapes and as a decode step of 256 streams.
 
 Prints ONE JSON line: tokens*channels/s for the whole job, the dominant
 kernel's achieved algorithmic HBM bandwidth against the 8 TB/s peak (kernel
@@ -41,7 +43,7 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 KERNEL_SOURCES = ("fwd.hip", "common.h", "gatemath.h")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_fused_2b_prefill_pmc.json")
-ALL_ROWS = ("conv1d", "gates", "scan", "block", "long", "decode", "bwd")
+ALL_ROWS = ("conv1d", "gates", "scan", "block", "long", "decode", "bwd", "attn", "attn_long", "attn_decode")
 
 
 def kernel_hash() -> str:
@@ -423,6 +425,55 @@ def main():
                                       "dX and dW (3 x 1024 per token*ch); executed MFMA work is "
                                       "larger (split-bf16 operands)")
         del u4, dy4
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------ local sliding-window MQA
+    # 10 query heads of 256 (Hq * dh = D = 2560), one key/value head, window 2048
+    AH, ADH, AW = 10, 256, 2048
+
+    def attn_flops(Bq, Tq):
+        # 4 dh flops per (query row, key in its window): q.k and p v
+        keys = sum(min(t + 1, AW) for t in range(Tq))
+        return 4 * ADH * AH * Bq * keys
+
+    for name, (Bq, Tq) in (("attn", (B, T)), ("attn_long", (1, 32768))):
+        if name not in rows:
+            continue
+        qa = dev_t(synth.make_activation(30, "attn_q", (Bq, Tq, AH, ADH), "bf16"))
+        ka = dev_t(synth.make_activation(30, "attn_k", (Bq, Tq, ADH), "bf16"))
+        va = dev_t(synth.make_activation(30, "attn_v", (Bq, Tq, ADH), "bf16"))
+        oa = torch.empty_like(qa)
+        _say(f"local attention prefill B={Bq} T={Tq} Hq={AH} dh={ADH} W={AW}")
+        kk, _ = tm.calls(lambda k: glr.attn_fwd(qa, ka, va, AW, 1.0 / 16, out=oa), 10, 2)
+        fl = attn_flops(Bq, Tq)
+        nb = 2 * qa.numel() * 2 + 2 * ka.numel() * 2
+        out["rows"][name] = row(f"rglru_attn_fwd, sliding-window MQA prefill (B={Bq} T={Tq} Hq={AH} dh={ADH} "
+                                f"W={AW} bf16)", kk, Bq * Tq * AH * ADH, nb, flops=fl, bound="mfma",
+                                note="algorithmic flops 4*dh per (query row, key in window); tokens_ch "
+                                     "counts B*T*Hq*dh outputs")
+        del qa, ka, va, oa
+        torch.cuda.empty_cache()
+
+    if "attn_decode" in rows:
+        Bd = 256
+        kc = dev_t(synth.make_activation(31, "attn_hk", (Bd, AW, ADH), "bf16"))
+        vc = dev_t(synth.make_activation(31, "attn_hv", (Bd, AW, ADH), "bf16"))
+        qd = dev_t(synth.make_activation(31, "attn_q", (64, Bd, AH, ADH), "bf16"))
+        kd = dev_t(synth.make_activation(31, "attn_k", (64, Bd, ADH), "bf16"))
+        vd = dev_t(synth.make_activation(31, "attn_v", (64, Bd, ADH), "bf16"))
+        od = torch.empty((Bd, AH, ADH), dtype=torch.bfloat16, device=dev)
+        pos = torch.full((Bd,), 4096, dtype=torch.int32, device=dev)   # every window full
+        glr.workspace(glr.attn_workspace_size(Bd, AH, ADH, AW), dev, "attn")
+        _say(f"local attention decode B={Bd} W={AW} Hq={AH} dh={ADH}")
+        kk, _ = tm.calls(lambda k: glr.attn_step(qd[k % 64], kd[k % 64], vd[k % 64], kc, vc, pos, 1.0 / 16,
+                                                 out=od), 30, 3)
+        nb = Bd * AW * ADH * 2 * 2 + 2 * Bd * AH * ADH * 2 + 4 * Bd * ADH * 2
+        out["rows"]["attn_decode"] = row(f"rglru_attn_step, sliding-window MQA decode (B={Bd}, ring of {AW}, "
+                                         f"Hq={AH} dh={ADH} bf16, full windows), per call", kk, Bd * AH * ADH,
+                                         nb, note="bytes: the whole ring of keys and values read once, q_t, "
+                                                  "o_t, the new key/value written; two launches (splits, "
+                                                  "combine)")
+        del kc, vc, qd, kd, vd, od
         torch.cuda.empty_cache()
 
     if not args.no_cpu:

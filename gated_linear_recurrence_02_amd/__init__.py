@@ -44,6 +44,12 @@ class _Weights(ctypes.Structure):
                 ("Lambda", ctypes.c_void_p)]
 
 
+class _AttnDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("Hq", ctypes.c_int64),
+                ("dh", ctypes.c_int64), ("W", ctypes.c_int64), ("io", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
 class _Block(ctypes.Structure):
     _fields_ = [("proj_in_1", ctypes.c_void_p), ("proj_in_2", ctypes.c_void_p),
                 ("proj_out", ctypes.c_void_p)]
@@ -52,7 +58,7 @@ class _Block(ctypes.Structure):
 _lib = None
 SYMBOLS = ("rglru_workspace_size", "rglru_conv1d", "rglru_gates", "rglru_scan_fwd",
            "rglru_step", "rglru_scan_bwd", "rglru_block_workspace_size", "rglru_block_fwd",
-           "rglru_status_string")
+           "rglru_attn_fwd", "rglru_attn_workspace_size", "rglru_attn_step", "rglru_status_string")
 
 
 def lib():
@@ -72,6 +78,10 @@ def lib():
         L.rglru_scan_fwd.argtypes = [D, W, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.rglru_step.argtypes = [D, W, vp, vp, vp, vp, vp]
         L.rglru_scan_bwd.argtypes = [D, W, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        A = ctypes.POINTER(_AttnDesc)
+        L.rglru_attn_fwd.argtypes = [A, vp, vp, vp, vp, vp, vp, vp]
+        L.rglru_attn_workspace_size.argtypes = [A, ctypes.POINTER(sz)]
+        L.rglru_attn_step.argtypes = [A, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.rglru_block_workspace_size.argtypes = [D, ctypes.c_int64, ctypes.POINTER(sz)]
         L.rglru_block_fwd.argtypes = [D, ctypes.c_int64, W, ctypes.POINTER(_Block), vp, vp, vp, vp, vp, vp,
                                       vp, sz, vp]
@@ -361,3 +371,60 @@ def block_fwd(x: torch.Tensor, w: Weights, bw: BlockWeights, *, h0=None, hist_in
                                  _ptr(hist_in), _ptr(h0), _ptr(o), _ptr(h_last), _ptr(hist_out), _ptr(wsb),
                                  wsb.numel(), _stream(dev)), "rglru_block_fwd")
     return o, h_last, hist_out
+
+
+# ------------------------------------------------------------ local attention
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, window: int, scale: Optional[float] = None,
+             *, kcache=None, vcache=None, out=None):
+    """Sliding-window MQA prefill: q [B][T][Hq][dh], k, v [B][T][dh]; token t
+    attends to t-window+1 .. t.  scale defaults to 1/sqrt(dh).  kcache /
+    vcache [B][W][dh] (optional, both or neither) receive the last W positions
+    in ring order.  Returns o [B][T][Hq][dh]."""
+    dev = q.device
+    _need(q, "q", dev)
+    B, T, Hq, dh = q.shape
+    _need(k, "k", dev, q.dtype, (B, T, dh))
+    _need(v, "v", dev, q.dtype, (B, T, dh))
+    if (kcache is None) != (vcache is None):
+        raise ValueError("kcache and vcache go together")
+    _need(kcache, "kcache", dev, q.dtype, (B, window, dh))
+    _need(vcache, "vcache", dev, q.dtype, (B, window, dh))
+    o = torch.empty_like(q) if out is None else out
+    _need(o, "out", dev, q.dtype, (B, T, Hq, dh))
+    sc = dh ** -0.5 if scale is None else float(scale)
+    d = _AttnDesc(B, T, Hq, dh, window, _io(q), sc)
+    _check(lib().rglru_attn_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(kcache),
+                                _ptr(vcache), _stream(dev)), "rglru_attn_fwd")
+    return o
+
+
+def attn_workspace_size(B, Hq, dh, W, io=BF16, scale=1.0) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().rglru_attn_workspace_size(ctypes.byref(_AttnDesc(B, 1, Hq, dh, W, io, scale)),
+                                           ctypes.byref(n)), "rglru_attn_workspace_size")
+    return int(n.value)
+
+
+def attn_step(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, kcache: torch.Tensor,
+              vcache: torch.Tensor, pos: torch.Tensor, scale: Optional[float] = None, out=None):
+    """One decode step: q_t [B][Hq][dh], k_t, v_t [B][dh], ring caches
+    [B][W][dh] (updated in place), pos [B] int32 (device; the new token's
+    position, not advanced here).  Returns o_t [B][Hq][dh]."""
+    dev = q_t.device
+    _need(q_t, "q_t", dev)
+    B, Hq, dh = q_t.shape
+    W = int(kcache.shape[1])
+    _need(k_t, "k_t", dev, q_t.dtype, (B, dh))
+    _need(v_t, "v_t", dev, q_t.dtype, (B, dh))
+    _need(kcache, "kcache", dev, q_t.dtype, (B, W, dh))
+    _need(vcache, "vcache", dev, q_t.dtype, (B, W, dh))
+    _need(pos, "pos", dev, torch.int32, (B,))
+    o = torch.empty_like(q_t) if out is None else out
+    _need(o, "out", dev, q_t.dtype, (B, Hq, dh))
+    sc = dh ** -0.5 if scale is None else float(scale)
+    d = _AttnDesc(B, 1, Hq, dh, W, _io(q_t), sc)
+    n = attn_workspace_size(B, Hq, dh, W, _io(q_t), sc)
+    wsb = workspace(n, dev, "attn")
+    _check(lib().rglru_attn_step(ctypes.byref(d), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(kcache), _ptr(vcache),
+                                 _ptr(pos), _ptr(o), _ptr(wsb), wsb.numel(), _stream(dev)), "rglru_attn_step")
+    return o

@@ -43,6 +43,24 @@ int check_block(const rglru_desc *d, int64_t d_model)
     return RGLRU_OK;
 }
 
+// local attention: shapes of the descriptor (prefill also needs T)
+int check_attn(const rglru_attn_desc *d, bool prefill)
+{
+    if (!d) return RGLRU_ERR_NULL;
+    if (d->io != RGLRU_F32 && d->io != RGLRU_BF16) return RGLRU_ERR_DTYPE;
+    if (d->B < 1 || d->Hq < 1 || d->W < 1 || d->dh < 8 || d->dh > 256 || d->dh % 8 != 0)
+        return RGLRU_ERR_SHAPE;
+    if (d->B > MAX_DIM || d->Hq > 4096 || d->W > MAX_DIM) return RGLRU_ERR_SHAPE;
+    if (prefill && (d->T < 1 || d->T > MAX_DIM)) return RGLRU_ERR_SHAPE;
+    const double T = prefill ? (double)d->T : 1.0;
+    if ((double)d->B * T * d->Hq * d->dh > 9.0e15 || (double)d->B * d->W * d->dh > 9.0e15) return RGLRU_ERR_SHAPE;
+    // grids: one workgroup per 128 rows (prefill) or per 4 rows (vector path)
+    if ((double)d->B * T * d->Hq / 4.0 >= 2147483647.0) return RGLRU_ERR_SHAPE;
+    if (prefill && d->T * d->Hq >= 2147483647) return RGLRU_ERR_SHAPE;
+    if (!isfinite(d->scale)) return RGLRU_ERR_ARG;
+    return RGLRU_OK;
+}
+
 struct Range {
     const void *p;
     size_t bytes;
@@ -266,6 +284,60 @@ int rglru_block_fwd(const rglru_desc *desc, int64_t d_model, const rglru_weights
     if (any_alias(outs, 4, ins, 13)) return RGLRU_ERR_ARG;
     st = launch_block_fwd(d, d_model, *w, *blk, x, hist_in, h0, out, h_last, hist_out, ws, stream);
     if (st) return st;
+    return launch_status();
+}
+
+int rglru_attn_workspace_size(const rglru_attn_desc *desc, size_t *bytes)
+{
+    if (!bytes) return RGLRU_ERR_NULL;
+    int st = check_attn(desc, false);
+    if (st) return st;
+    *bytes = attn_workspace_bytes(*desc);
+    return RGLRU_OK;
+}
+
+int rglru_attn_fwd(const rglru_attn_desc *desc, const void *q, const void *k, const void *v, void *o,
+                   void *kcache, void *vcache, hipStream_t stream)
+{
+    int st = check_attn(desc, true);
+    if (st) return st;
+    if (!q || !k || !v || !o) return RGLRU_ERR_NULL;
+    if ((kcache == nullptr) != (vcache == nullptr)) return RGLRU_ERR_ARG;
+    const void *all[] = {q, k, v, o, kcache, vcache};
+    for (const void *p : all)
+        if (p && !aligned16(p)) return RGLRU_ERR_ALIGN;
+    const rglru_attn_desc &d = *desc;
+    const size_t e = d.io == RGLRU_BF16 ? 2 : 4;
+    const size_t qb = d.B * d.T * d.Hq * d.dh * e, kb = d.B * d.T * d.dh * e, cb = d.B * d.W * d.dh * e;
+    const Range outs[] = {{o, qb}, {kcache, cb}, {vcache, cb}};
+    const Range ins[] = {{q, qb}, {k, kb}, {v, kb}};
+    if (any_alias(outs, 3, ins, 3)) return RGLRU_ERR_ARG;
+    launch_attn_fwd(d, q, k, v, o, kcache, vcache, stream);
+    return launch_status();
+}
+
+int rglru_attn_step(const rglru_attn_desc *desc, const void *q_t, const void *k_t, const void *v_t,
+                    void *kcache, void *vcache, const int32_t *pos, void *o_t, void *ws, size_t ws_bytes,
+                    hipStream_t stream)
+{
+    int st = check_attn(desc, false);
+    if (st) return st;
+    if (!q_t || !k_t || !v_t || !kcache || !vcache || !pos || !o_t) return RGLRU_ERR_NULL;
+    if (!ws) return RGLRU_ERR_WORKSPACE;
+    const void *all[] = {q_t, k_t, v_t, kcache, vcache, o_t, ws};
+    for (const void *p : all)
+        if (!aligned16(p)) return RGLRU_ERR_ALIGN;
+    if (((uintptr_t)pos & 3u) != 0) return RGLRU_ERR_ALIGN;
+    const rglru_attn_desc &d = *desc;
+    const size_t need = attn_workspace_bytes(d);
+    if (ws_bytes < need) return RGLRU_ERR_WORKSPACE;
+    const size_t e = d.io == RGLRU_BF16 ? 2 : 4;
+    const size_t qb = d.B * d.Hq * d.dh * e, kb = d.B * d.dh * e, cb = d.B * d.W * d.dh * e;
+    // the caches are read and rewritten in place by design
+    const Range outs[] = {{o_t, qb}, {kcache, cb}, {vcache, cb}, {ws, need}};
+    const Range ins[] = {{q_t, qb}, {k_t, kb}, {v_t, kb}, {pos, (size_t)d.B * 4}};
+    if (any_alias(outs, 4, ins, 4)) return RGLRU_ERR_ARG;
+    launch_attn_step(d, q_t, k_t, v_t, kcache, vcache, pos, o_t, ws, stream);
     return launch_status();
 }
 

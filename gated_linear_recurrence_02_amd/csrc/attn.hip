@@ -1,0 +1,594 @@
+// attn.hip -- local sliding-window multi-query attention, the other temporal
+// mixer of Griffin (wiki note "Griffin", section "Local Attention Path": token t
+// attends to the window t-W+1 .. t with softmax weights; page "Griffin Guide:
+// RecurrentGemma, RG-LRU & Hybrid Attention", "Local Sliding-Window Multi-Query
+// Attention (MQA)": all query heads share one key head and one value head, and
+// "Bounding the Key-Value Cache Footprint": the decode cache keeps the last W
+// positions, evicted ring-buffer fashion -- position p lives in slot p mod W).
+//
+// Layouts (row-major): q, o [B][T][Hq][dh]; k, v [B][T][dh]; caches
+// [B][W][dh]; decode q_t, o_t [B][Hq][dh], k_t, v_t [B][dh], pos [B] int32.
+// Scores are scale * q.k; softmax and sums in fp32.
+//
+// Kernels
+//   attn_prefill_mfma  bf16, dh = 256.  A workgroup (4 waves) takes 128
+//       consecutive rows of the flattened (token, head) index of one stream
+//       -- for MQA, rows of neighbouring tokens share their keys -- and walks
+//       the union of their windows in tiles of 32 keys, double-buffered in
+//       LDS.  Per tile and wave: S^T = K Q^T (16 v_mfma_f32_32x32x16_bf16; K
+//       rows are read in the order that gives each lane 16 consecutive keys of
+//       one query), an online softmax per query (a lane and its partner 32
+//       lanes away hold the tile's 32 scores), and O^T += V^T P^T (16 MFMAs;
+//       the lane's own probabilities are the B operand, and V^T, staged
+//       transposed through registers, is the A operand).
+//   attn_step_mfma     bf16, dh = 256, Hq <= 16.  Decode, split over the ring:
+//       a workgroup scores 256 slots for all heads with
+//       v_mfma_f32_16x16x32_bf16 (K rows straight from HBM, heads padded to
+//       16), keeps exp-weights in LDS and accumulates P V on the vector ALUs;
+//       attn_combine merges the splits and writes the new key and value into
+//       their slot.
+//   attn_*_generic     any io, dh <= 256: one wave per query row, the
+//       reference-shaped loop (fp32 I/O and shapes the fast kernels exclude).
+#include <math.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace rglru {
+
+namespace {
+
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+template <typename T> __device__ __forceinline__ float ld1(const T *p) { return (float)*p; }
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// ------------------------------------------------------------------ generic
+// One wave per (stream, token, head): lanes split dh; per key a wave-wide dot
+// product, then the online softmax update.  Accurate exp for fp32 I/O.
+template <typename T>
+__global__ __launch_bounds__(256) void attn_prefill_generic(int B, int T_, int Hq, int dh, int W, float scale,
+                                                           const T *q, const T *k, const T *v, T *o)
+{
+    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= (long)B * T_ * Hq) return;
+    const int b = (int)(row / ((long)T_ * Hq));
+    const int t = (int)((row / Hq) % T_);
+    float qv[4], acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        qv[i] = e < dh ? ld1(q + row * dh + e) : 0.0f;
+    }
+    float m = -INFINITY, l = 0.0f;
+    const int lo = t - W + 1 < 0 ? 0 : t - W + 1;
+    for (int j = lo; j <= t; ++j) {
+        const T *kr = k + ((long)b * T_ + j) * dh, *vr = v + ((long)b * T_ + j) * dh;
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane + 64 * i;
+            if (e < dh) part = fmaf(qv[i], ld1(kr + e), part);
+        }
+        const float s = wave_sum(part) * scale;
+        const float mn = fmaxf(m, s);
+        const float alpha = expf(m - mn), p = expf(s - mn);
+        l = fmaf(l, alpha, p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane + 64 * i;
+            acc[i] = fmaf(acc[i], alpha, e < dh ? p * ld1(vr + e) : 0.0f);
+        }
+        m = mn;
+    }
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        if (e < dh) o[row * dh + e] = from_f32<T>(acc[i] * inv);
+    }
+}
+
+// Decode, one wave per (stream, head): positions max(0, pos-W+1) .. pos, the
+// newest from k_t / v_t, the rest from their ring slots.  The wave of head 0
+// writes k_t, v_t into slot pos mod W afterwards; that slot holds position
+// pos - W, which no wave reads.
+template <typename T>
+__global__ __launch_bounds__(256) void attn_step_generic(int B, int Hq, int dh, int W, float scale, const T *q_t,
+                                                        const T *k_t, const T *v_t, T *kc, T *vc,
+                                                        const int32_t *pos, T *o_t)
+{
+    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= (long)B * Hq) return;
+    const int b = (int)(row / Hq), h = (int)(row % Hq);
+    const long p = pos[b];
+    float qv[4], acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        qv[i] = e < dh ? ld1(q_t + row * dh + e) : 0.0f;
+    }
+    float m = -INFINITY, l = 0.0f;
+    const long lo = p - W + 1 < 0 ? 0 : p - W + 1;
+    for (long j = lo; j <= p; ++j) {
+        const T *kr = j == p ? k_t + (long)b * dh : kc + ((long)b * W + j % W) * dh;
+        const T *vr = j == p ? v_t + (long)b * dh : vc + ((long)b * W + j % W) * dh;
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane + 64 * i;
+            if (e < dh) part = fmaf(qv[i], ld1(kr + e), part);
+        }
+        const float s = wave_sum(part) * scale;
+        const float mn = fmaxf(m, s);
+        const float alpha = expf(m - mn), pr = expf(s - mn);
+        l = fmaf(l, alpha, pr);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane + 64 * i;
+            acc[i] = fmaf(acc[i], alpha, e < dh ? pr * ld1(vr + e) : 0.0f);
+        }
+        m = mn;
+    }
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        if (e < dh) o_t[row * dh + e] = from_f32<T>(acc[i] * inv);
+    }
+    if (h == 0) {
+        const long slot = ((long)b * W + p % W) * dh;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane + 64 * i;
+            if (e < dh) {
+                kc[slot + e] = k_t[(long)b * dh + e];
+                vc[slot + e] = v_t[(long)b * dh + e];
+            }
+        }
+    }
+}
+
+// Prefill's ring fill: positions max(0, T-W) .. T-1 into slots p mod W.
+// One thread per 16-byte piece (dh * esz is a multiple of 16).
+__global__ __launch_bounds__(256) void attn_fill_cache(int B, int T_, int W, int pieces_per_row, const uint4 *k,
+                                                      const uint4 *v, uint4 *kc, uint4 *vc)
+{
+    const int n = T_ < W ? T_ : W;
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long)B * n * pieces_per_row) return;
+    const int c = (int)(idx % pieces_per_row);
+    const long r = idx / pieces_per_row;
+    const int b = (int)(r / n);
+    const int p = T_ - n + (int)(r % n);
+    const long src = ((long)b * T_ + p) * pieces_per_row + c;
+    const long dst = ((long)b * W + p % W) * pieces_per_row + c;
+    kc[dst] = k[src];
+    vc[dst] = v[src];
+}
+
+// ------------------------------------------------------------ MFMA prefill
+constexpr int PF_ROWS = 128;            // flattened (token, head) rows per workgroup
+constexpr int PF_KEYS = 32;             // keys per tile
+constexpr int PF_KSTRIDE = 264;         // bf16 per K row in LDS (528 B, conflict-free b128 reads)
+constexpr int PF_VSTRIDE = 40;          // bf16 per V^T row (80 B)
+constexpr int PF_KBYTES = PF_KEYS * PF_KSTRIDE * 2;   // 16,896
+constexpr int PF_VBYTES = 256 * PF_VSTRIDE * 2;       // 20,480
+constexpr int PF_STAGE = PF_KBYTES + PF_VBYTES;
+constexpr int PF_LDS = 2 * PF_STAGE;                  // 74,752
+
+// The staged pieces of one key tile: threads 0..127 carry 8 pieces of one K
+// row each; threads 128..255 an 8 x 8 block of V (8 keys x 8 dh), which they
+// transpose before writing so that V^T rows hold consecutive keys.
+struct PfStage {
+    u32x4 r[8];
+};
+
+__device__ __forceinline__ void pf_load(PfStage &st, const bf16 *k, const bf16 *v, long kv0, int key0, int T_,
+                                        int tid)
+{
+    if (tid < 128) {
+        const int row = tid >> 2, seg = (tid & 3) * 64;   // 64 dh per thread
+        const int key = key0 + row;
+        const u32x4 *src = (const u32x4 *)(k + (kv0 + (key < T_ ? key : 0)) * 256 + seg);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) st.r[i] = key < T_ ? src[i] : u32x4{0, 0, 0, 0};
+    } else {
+        const int t2 = tid - 128, kg = t2 >> 5, dg = t2 & 31;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int key = key0 + 8 * kg + i;
+            const u32x4 *src = (const u32x4 *)(v + (kv0 + (key < T_ ? key : 0)) * 256 + 8 * dg);
+            st.r[i] = key < T_ ? *src : u32x4{0, 0, 0, 0};
+        }
+    }
+}
+
+__device__ __forceinline__ void pf_store(const PfStage &st, char *stage, int tid)
+{
+    if (tid < 128) {
+        const int row = tid >> 2, seg = (tid & 3) * 64;
+        u32x4 *dst = (u32x4 *)(stage + (row * PF_KSTRIDE + seg) * 2);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dst[i] = st.r[i];
+    } else {
+        const int t2 = tid - 128, kg = t2 >> 5, dg = t2 & 31;
+        // st.r[i] holds keys 8kg+i, dh 8dg..8dg+7 (dword c = dh pair 2c, 2c+1);
+        // output row 8dg + j holds keys 8kg..8kg+7 for dh 8dg + j
+        char *vt = stage + PF_KBYTES;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
+            const int c = j >> 1;
+            u32x4 o;
+            o[0] = __builtin_amdgcn_perm(st.r[1][c], st.r[0][c], sel);
+            o[1] = __builtin_amdgcn_perm(st.r[3][c], st.r[2][c], sel);
+            o[2] = __builtin_amdgcn_perm(st.r[5][c], st.r[4][c], sel);
+            o[3] = __builtin_amdgcn_perm(st.r[7][c], st.r[6][c], sel);
+            *(u32x4 *)(vt + ((8 * dg + j) * PF_VSTRIDE + 8 * kg) * 2) = o;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void attn_prefill_mfma(int T_, int Hq, int W, float scale_log2e,
+                                                         const bf16 *q, const bf16 *k, const bf16 *v, bf16 *o)
+{
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int n = lane & 31, half = lane >> 5;
+    const long rows_per_b = (long)T_ * Hq;
+    const long tiles_per_b = (rows_per_b + PF_ROWS - 1) / PF_ROWS;
+    const int b = (int)(blockIdx.x / tiles_per_b);
+    const long f0 = (blockIdx.x % tiles_per_b) * PF_ROWS;   // first flattened row of the workgroup
+    const long kv0 = (long)b * T_;                          // first key row of stream b
+
+    // this lane's query row (column n of the wave's 32 rows)
+    const long f = f0 + 32 * wave + n;
+    const bool row_ok = f < rows_per_b;
+    const int t = row_ok ? (int)(f / Hq) : -1;
+    bf16x8 qb[16];
+    {
+        const bf16 *qr = q + ((long)b * rows_per_b + (row_ok ? f : 0)) * 256 + 8 * half;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) qb[s] = row_ok ? *(const bf16x8 *)(qr + 16 * s) : bf16x8{};
+    }
+
+    // keys of the union of the workgroup's windows
+    const long f_last = (f0 + PF_ROWS - 1 < rows_per_b ? f0 + PF_ROWS - 1 : rows_per_b - 1);
+    const int t_first = (int)(f0 / Hq), t_last = (int)(f_last / Hq);
+    const int k_lo = t_first - W + 1 < 0 ? 0 : t_first - W + 1;
+    const int tile0 = k_lo / PF_KEYS, tile1 = t_last / PF_KEYS;
+
+    f32x16 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = f32x16{};
+    float m = -INFINITY, l = 0.0f;
+
+    PfStage st;
+    pf_load(st, k, v, kv0, tile0 * PF_KEYS, T_, tid);
+    pf_store(st, smem + (tile0 & 1) * PF_STAGE, tid);
+    __syncthreads();
+
+    // lane's K row inside a tile: row r of the A operand is key tile_row_token(r),
+    // so that register k of the score tile is key 16*half + k
+    const int krow = tile_row_token(n);
+    for (int tile = tile0; tile <= tile1; ++tile) {
+        const bool more = tile < tile1;
+        if (more) pf_load(st, k, v, kv0, (tile + 1) * PF_KEYS, T_, tid);
+        const char *stage = smem + (tile & 1) * PF_STAGE;
+
+        // S^T = K Q^T over dh = 256
+        // (two accumulator chains, so that back-to-back MFMAs do not wait on
+        // each other's results)
+        f32x16 s = {}, s2 = {};
+        {
+            const bf16 *kr = (const bf16 *)stage + krow * PF_KSTRIDE + 8 * half;
+#pragma unroll
+            for (int ks = 0; ks < 16; ks += 2) {
+                const bf16x8 a0 = *(const bf16x8 *)(kr + 16 * ks);
+                const bf16x8 a1 = *(const bf16x8 *)(kr + 16 * ks + 16);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[ks], s, 0, 0, 0);
+                s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[ks + 1], s2, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] += s2[r];
+        }
+        // mask, scale into log2 units, tile maximum per query
+        const int key_base = tile * PF_KEYS + 16 * half;
+        float mt = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = key_base + r;
+            const bool ok = key <= t && key > t - W;
+            s[r] = ok ? s[r] * scale_log2e : -INFINITY;
+            mt = fmaxf(mt, s[r]);
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mn = fmaxf(m, mt);
+        const float mu = mn == -INFINITY ? 0.0f : mn;
+        const float alpha = hw_exp2(m - mu);   // 0 while m is -inf
+        float ls = 0.0f;
+        bf16x8 pb[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float pr = hw_exp2(s[r] - mu);
+            ls += pr;
+            pb[r >> 3][r & 7] = (bf16)pr;
+        }
+        ls += __shfl_xor(ls, 32);
+        l = fmaf(l, alpha, ls);
+        m = mn;
+        if (__any(alpha != 1.0f)) {   // rescale only when some query's maximum moved
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
+        }
+        // O^T += V^T P^T: k-step ks covers keys 16*half + 8*ks .. +8 of this lane
+        {
+            const bf16 *vt = (const bf16 *)(stage + PF_KBYTES) + n * PF_VSTRIDE + 16 * half;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x8 a = *(const bf16x8 *)(vt + 32 * dt * PF_VSTRIDE + 8 * ks);
+                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], acc[dt], 0, 0, 0);
+                }
+        }
+        if (more) pf_store(st, smem + ((tile + 1) & 1) * PF_STAGE, tid);
+        __syncthreads();
+    }
+
+    if (row_ok) {
+        const float inv = 1.0f / l;
+        bf16 *orow = o + ((long)b * rows_per_b + f) * 256;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+                bf16x4 w4;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w4[i] = (bf16)(acc[dt][4 * j + i] * inv);
+                *(bf16x4 *)(orow + 32 * dt + 8 * j + 4 * half) = w4;
+            }
+    }
+}
+
+// -------------------------------------------------------------- MFMA decode
+constexpr int DS_SLOTS = 256;   // ring slots per workgroup
+
+// Partial results per (stream, split, head): dh sums of exp-weighted values,
+// the split's maximum score (log2 units) and its exp-weight sum.
+struct StepWs {
+    float *o;   // [B][NS][16][256]
+    float *m;   // [B][NS][16]
+    float *l;   // [B][NS][16]
+};
+
+__global__ __launch_bounds__(256) void attn_step_mfma(int Hq, int W, int NS, float scale_log2e, const bf16 *q_t,
+                                                     const bf16 *k_t, const bf16 *v_t, const bf16 *kc,
+                                                     const bf16 *vc, const int32_t *pos, StepWs ws)
+{
+    __shared__ float Ps[DS_SLOTS][17];   // exp-weights [slot][head]
+    __shared__ float wmax[4][16];
+    __shared__ float wsum[4][16];
+    __shared__ __attribute__((aligned(16))) float red[128][2][16];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int b = blockIdx.x / NS, sp = blockIdx.x % NS;
+    const long p = pos[b];
+    const int cur = (int)(p % W);
+    const int n16 = lane & 15, kg = lane >> 4;
+
+    // q^T as B operand: lane holds head n16, dh 32*ks + 8*kg .. +8
+    bf16x8 qb[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+        qb[ks] = n16 < Hq ? *(const bf16x8 *)(q_t + ((long)b * Hq + (n16 < Hq ? n16 : 0)) * 256 + 32 * ks + 8 * kg)
+                          : bf16x8{};
+
+    // scores of this wave's 64 slots, 16 at a time
+    float sc[4][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const int slot_a = sp * DS_SLOTS + 64 * wave + 16 * st + n16;   // A-operand row of this lane
+        const bool a_ok = slot_a < W;
+        const bf16 *kr = slot_a == cur ? k_t + (long)b * 256 : kc + ((long)b * W + (a_ok ? slot_a : 0)) * 256;
+        f32x4_t acc = {};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const bf16x8 a = a_ok ? *(const bf16x8 *)(kr + 32 * ks + 8 * kg) : bf16x8{};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], acc, 0, 0, 0);
+        }
+        // lane holds head n16 for slots 4*kg + i of the 16
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int slot = sp * DS_SLOTS + 64 * wave + 16 * st + 4 * kg + i;
+            const long ppos = p - ((p - slot) % W + W) % W;   // position held by the slot
+            const bool ok = slot < W && ppos >= 0 && n16 < Hq;
+            sc[st][i] = ok ? acc[i] * scale_log2e : -INFINITY;
+            mx = fmaxf(mx, sc[st][i]);
+        }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (kg == 0) wmax[wave][n16] = mx;
+    __syncthreads();
+    float M = fmaxf(fmaxf(wmax[0][n16], wmax[1][n16]), fmaxf(wmax[2][n16], wmax[3][n16]));
+    const float mu = M == -INFINITY ? 0.0f : M;
+    float ls = 0.0f;
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float pr = hw_exp2(sc[st][i] - mu);
+            ls += pr;
+            Ps[64 * wave + 16 * st + 4 * kg + i][n16] = pr;
+        }
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+    if (kg == 0) wsum[wave][n16] = ls;
+    __syncthreads();
+
+    // P V on the vector ALUs: thread = (slot parity, dh pair)
+    const int par = tid >> 7, d2 = tid & 127;
+    float acc[16][2];
+#pragma unroll
+    for (int h = 0; h < 16; ++h) acc[h][0] = acc[h][1] = 0.0f;
+    for (int j = par; j < DS_SLOTS; j += 2) {
+        const int slot = sp * DS_SLOTS + j;
+        if (slot >= W) break;
+        if (p - ((p - slot) % W + W) % W < 0) continue;   // never written (pos < W): may hold anything
+        const bf16 *vr = slot == cur ? v_t + (long)b * 256 : vc + ((long)b * W + slot) * 256;
+        typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+        const bf16x2 vv = *(const bf16x2 *)(vr + 2 * d2);
+        const float v0 = (float)vv[0], v1 = (float)vv[1];
+#pragma unroll
+        for (int h = 0; h < 16; ++h) {
+            if (h < Hq) {
+                const float pr = Ps[j][h];
+                acc[h][0] = fmaf(pr, v0, acc[h][0]);
+                acc[h][1] = fmaf(pr, v1, acc[h][1]);
+            }
+        }
+    }
+    // the odd-slot half hands its sums to the even half
+    if (par == 1) {
+#pragma unroll
+        for (int h = 0; h < 16; ++h) {
+            red[d2][0][h] = acc[h][0];
+            red[d2][1][h] = acc[h][1];
+        }
+    }
+    __syncthreads();
+    if (par == 0) {
+        const long base = ((long)b * NS + sp) * 16;
+#pragma unroll
+        for (int h = 0; h < 16; ++h) {
+            if (h < Hq) {
+                ws.o[(base + h) * 256 + 2 * d2] = acc[h][0] + red[d2][0][h];
+                ws.o[(base + h) * 256 + 2 * d2 + 1] = acc[h][1] + red[d2][1][h];
+            }
+        }
+        if (d2 < 16) {
+            ws.m[base + d2] = M;
+            ws.l[base + d2] = wsum[0][d2] + wsum[1][d2] + wsum[2][d2] + wsum[3][d2];
+        }
+    }
+}
+
+// One workgroup per stream: merge the splits of every head, then write the
+// new key and value into slot pos mod W (every read of this step is done).
+__global__ __launch_bounds__(256) void attn_combine(int Hq, int W, int NS, StepWs ws, const bf16 *k_t,
+                                                   const bf16 *v_t, bf16 *kc, bf16 *vc, const int32_t *pos,
+                                                   bf16 *o_t)
+{
+    const int b = blockIdx.x, d = threadIdx.x;   // 256 threads = dh
+    for (int h = 0; h < Hq; ++h) {
+        float M = -INFINITY;
+        for (int s = 0; s < NS; ++s) M = fmaxf(M, ws.m[((long)b * NS + s) * 16 + h]);
+        float num = 0.0f, den = 0.0f;
+        for (int s = 0; s < NS; ++s) {
+            const long base = ((long)b * NS + s) * 16 + h;
+            const float wgt = hw_exp2(ws.m[base] - M);   // 0 for an empty split
+            den = fmaf(wgt, ws.l[base], den);
+            num = fmaf(wgt, ws.o[base * 256 + d], num);
+        }
+        o_t[((long)b * Hq + h) * 256 + d] = (bf16)(num / den);
+    }
+    const long slot = ((long)b * W + pos[b] % W) * 256 + d;
+    kc[slot] = k_t[(long)b * 256 + d];
+    vc[slot] = v_t[(long)b * 256 + d];
+}
+
+}  // namespace
+
+bool attn_fast_prefill(const rglru_attn_desc &d) { return d.io == RGLRU_BF16 && d.dh == 256; }
+bool attn_fast_step(const rglru_attn_desc &d) { return d.io == RGLRU_BF16 && d.dh == 256 && d.Hq <= 16; }
+
+size_t attn_workspace_bytes(const rglru_attn_desc &d)
+{
+    if (!attn_fast_step(d)) return 256;
+    const int64_t NS = (d.W + DS_SLOTS - 1) / DS_SLOTS;
+    return (size_t)d.B * NS * 16 * (256 + 2) * 4 + 512;
+}
+
+void launch_attn_fwd(const rglru_attn_desc &d, const void *q, const void *k, const void *v, void *o, void *kc,
+                     void *vc, hipStream_t s)
+{
+    const float scale = d.scale;
+    if (attn_fast_prefill(d)) {
+        static bool attr = false;
+        if (!attr) {
+            (void)hipFuncSetAttribute((const void *)&attn_prefill_mfma,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, PF_LDS);
+            attr = true;
+        }
+        const long tiles = (d.T * d.Hq + PF_ROWS - 1) / PF_ROWS;
+        attn_prefill_mfma<<<dim3((unsigned)(d.B * tiles)), dim3(256), PF_LDS, s>>>(
+            (int)d.T, (int)d.Hq, (int)d.W, scale * 1.4426950408889634f, (const bf16 *)q, (const bf16 *)k,
+            (const bf16 *)v, (bf16 *)o);
+    } else {
+        const long rows = d.B * d.T * d.Hq;
+        const unsigned grid = (unsigned)((rows + 3) / 4);
+        if (d.io == RGLRU_BF16)
+            attn_prefill_generic<bf16><<<grid, 256, 0, s>>>((int)d.B, (int)d.T, (int)d.Hq, (int)d.dh, (int)d.W,
+                                                            scale, (const bf16 *)q, (const bf16 *)k,
+                                                            (const bf16 *)v, (bf16 *)o);
+        else
+            attn_prefill_generic<float><<<grid, 256, 0, s>>>((int)d.B, (int)d.T, (int)d.Hq, (int)d.dh,
+                                                             (int)d.W, scale, (const float *)q, (const float *)k,
+                                                             (const float *)v, (float *)o);
+    }
+    if (kc) {
+        const int esz = d.io == RGLRU_BF16 ? 2 : 4;
+        const int ppr = (int)(d.dh * esz / 16);
+        const long n = d.T < d.W ? d.T : d.W;
+        const long total = d.B * n * ppr;
+        attn_fill_cache<<<dim3((unsigned)((total + 255) / 256)), 256, 0, s>>>(
+            (int)d.B, (int)d.T, (int)d.W, ppr, (const uint4 *)k, (const uint4 *)v, (uint4 *)kc, (uint4 *)vc);
+    }
+}
+
+void launch_attn_step(const rglru_attn_desc &d, const void *q_t, const void *k_t, const void *v_t, void *kc,
+                      void *vc, const int32_t *pos, void *o_t, void *ws, hipStream_t s)
+{
+    const float scale = d.scale;
+    if (attn_fast_step(d)) {
+        const int NS = (int)((d.W + DS_SLOTS - 1) / DS_SLOTS);
+        StepWs w;
+        w.o = (float *)ws;
+        w.m = w.o + (size_t)d.B * NS * 16 * 256;
+        w.l = w.m + (size_t)d.B * NS * 16;
+        attn_step_mfma<<<dim3((unsigned)(d.B * NS)), 256, 0, s>>>(
+            (int)d.Hq, (int)d.W, NS, scale * 1.4426950408889634f, (const bf16 *)q_t, (const bf16 *)k_t,
+            (const bf16 *)v_t, (const bf16 *)kc, (const bf16 *)vc, pos, w);
+        attn_combine<<<dim3((unsigned)d.B), 256, 0, s>>>((int)d.Hq, (int)d.W, NS, w, (const bf16 *)k_t,
+                                                         (const bf16 *)v_t, (bf16 *)kc, (bf16 *)vc, pos,
+                                                         (bf16 *)o_t);
+    } else {
+        const long rows = d.B * d.Hq;
+        const unsigned grid = (unsigned)((rows + 3) / 4);
+        if (d.io == RGLRU_BF16)
+            attn_step_generic<bf16><<<grid, 256, 0, s>>>((int)d.B, (int)d.Hq, (int)d.dh, (int)d.W, scale,
+                                                         (const bf16 *)q_t, (const bf16 *)k_t, (const bf16 *)v_t,
+                                                         (bf16 *)kc, (bf16 *)vc, pos, (bf16 *)o_t);
+        else
+            attn_step_generic<float><<<grid, 256, 0, s>>>((int)d.B, (int)d.Hq, (int)d.dh, (int)d.W, scale,
+                                                          (const float *)q_t, (const float *)k_t,
+                                                          (const float *)v_t, (float *)kc, (float *)vc, pos,
+                                                          (float *)o_t);
+    }
+}
+
+}  // namespace rglru

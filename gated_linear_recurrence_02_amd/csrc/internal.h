@@ -50,6 +50,15 @@ int launch_block_fwd(const rglru_desc &d, int64_t d_model, const rglru_weights &
                      const void *x, const void *hist_in, const float *h0, void *out, float *h_last,
                      void *hist_out, void *ws, hipStream_t s);
 
+// local sliding-window MQA (attn.hip)
+bool attn_fast_prefill(const rglru_attn_desc &d);
+bool attn_fast_step(const rglru_attn_desc &d);
+size_t attn_workspace_bytes(const rglru_attn_desc &d);
+void launch_attn_fwd(const rglru_attn_desc &d, const void *q, const void *k, const void *v, void *o, void *kc,
+                     void *vc, hipStream_t s);
+void launch_attn_step(const rglru_attn_desc &d, const void *q_t, const void *k_t, const void *v_t, void *kc,
+                      void *vc, const int32_t *pos, void *o_t, void *ws, hipStream_t s);
+
 void launch_step(const rglru_desc &d, const rglru_weights &w, const void *u_t, void *hist,
                  float *h, void *y_t, hipStream_t s);
 

@@ -226,6 +226,51 @@ int rglru_block_fwd(const rglru_desc *desc, int64_t d_model, const rglru_weights
                     void *out, float *h_last, void *hist_out, void *ws, size_t ws_bytes,
                     hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Local sliding-window multi-query attention, Griffin's other temporal mixer
+ * (wiki note "Griffin", section "Local Attention Path": token t attends to the
+ * positions t-W+1 .. t, y_t = sum_i softmax_i(scale q_t . k_i) v_i; page
+ * "Griffin Guide: RecurrentGemma, RG-LRU & Hybrid Attention", "Local
+ * Sliding-Window Multi-Query Attention (MQA)": every query head shares one key
+ * head and one value head; "Bounding the Key-Value Cache Footprint": the
+ * decode cache holds the last W positions and evicts ring-buffer fashion).
+ * The page's formula shows no score scale; `scale` is the caller's (1/sqrt(dh)
+ * is the usual one).  q and k are taken after any rotary embedding, which
+ * belongs to the attention block around this operation.
+ *
+ * Layouts (row-major, dtype io): q, o [B][T][Hq][dh]; k, v [B][T][dh];
+ * caches kcache, vcache [B][W][dh], position p of stream b in slot p mod W;
+ * decode: q_t, o_t [B][Hq][dh], k_t, v_t [B][dh], pos [B] int32 on the device
+ * (the position of the new token, >= 0).  Scores, softmax and sums are fp32;
+ * bf16 I/O with dh = 256 runs on the matrix cores (probabilities rounded to
+ * bf16 for the P V product), every other shape on a vector-ALU path with
+ * accurate exp.  Shapes: B, T, Hq >= 1; 1 <= W <= 2^30; 8 <= dh <= 256,
+ * dh % 8 == 0. */
+typedef struct {
+    int64_t B, T, Hq, dh, W;
+    int32_t io;        /* rglru_dtype */
+    float scale;
+} rglru_attn_desc;
+
+/* Prefill: o for every token.  kcache / vcache (both or neither) receive the
+ * keys and values of positions max(0, T-W) .. T-1 in their ring slots, ready
+ * for rglru_attn_step at pos = T; other slots are left as they are. */
+int rglru_attn_fwd(const rglru_attn_desc *desc, const void *q, const void *k, const void *v, void *o,
+                   void *kcache, void *vcache, hipStream_t stream);
+
+/* Workspace bytes of rglru_attn_step (desc->T is ignored): per-split partial
+ * sums of the decode.  Contents need no initialisation. */
+int rglru_attn_workspace_size(const rglru_attn_desc *desc, size_t *bytes);
+
+/* One decode step for B streams: writes k_t, v_t into slot pos[b] mod W (the
+ * slot of position pos[b] - W, evicted) and computes o_t over positions
+ * max(0, pos[b]-W+1) .. pos[b] (desc->T is ignored).  Slots of positions
+ * below 0 are never read, so a fresh cache needs no initialisation.  The
+ * caller advances pos. */
+int rglru_attn_step(const rglru_attn_desc *desc, const void *q_t, const void *k_t, const void *v_t,
+                    void *kcache, void *vcache, const int32_t *pos, void *o_t, void *ws, size_t ws_bytes,
+                    hipStream_t stream);
+
 /* Short English text of a status code (static storage). */
 const char *rglru_status_string(int status);
 

@@ -54,7 +54,8 @@ _THREADS = max(1, min(16, os.cpu_count() or 1))
 # tensor ids of the per-tensor streams
 TID = dict(u=0, conv_w=1, conv_b=2, W_a=3, W_x=4, lam_u=5, dy=6, h0=7,
            b_a=8, b_x=9, hist=10, dh_last=11,
-           block_x=12, proj_in_1=13, proj_in_2=14, proj_out=15)
+           block_x=12, proj_in_1=13, proj_in_2=14, proj_out=15,
+           attn_q=16, attn_k=17, attn_v=18, attn_hk=19, attn_hv=20)
 
 C_CONST = 8.0
 

@@ -195,3 +195,32 @@ def test_block_fwd_validation(L):
     assert f(ctypes.byref(d), dm, ctypes.byref(w), ctypes.byref(blk), *args(ws=P + 0x3000000), s) == EARG
     bad = glr._Block(P + 0x3000000, None, P + 0x5000000)
     assert f(ctypes.byref(d), dm, ctypes.byref(w), ctypes.byref(bad), *args(), s) == ENULL
+
+
+def adesc(B=2, T=64, Hq=10, dh=256, W=128, io=glr.BF16, scale=0.0625):
+    return glr._AttnDesc(B, T, Hq, dh, W, io, scale)
+
+
+def test_attn_validation(L):
+    s = None
+    q, k, v, o = P + 0x1000000, P + 0x2000000, P + 0x3000000, P + 0x4000000
+    kc, vc = P + 0x5000000, P + 0x6000000
+    f = L.rglru_attn_fwd
+    assert f(None, q, k, v, o, None, None, s) == ENULL
+    assert f(ctypes.byref(adesc(dh=260)), q, k, v, o, None, None, s) == ESHAPE
+    assert f(ctypes.byref(adesc(dh=12)), q, k, v, o, None, None, s) == ESHAPE
+    assert f(ctypes.byref(adesc(W=0)), q, k, v, o, None, None, s) == ESHAPE
+    assert f(ctypes.byref(adesc(T=0)), q, k, v, o, None, None, s) == ESHAPE
+    assert f(ctypes.byref(adesc(io=3)), q, k, v, o, None, None, s) == EDTYPE
+    assert f(ctypes.byref(adesc()), q, k, v, o, kc, None, s) == EARG            # caches go together
+    assert f(ctypes.byref(adesc()), q, k, v, q + 16, None, None, s) == EARG     # o overlaps q
+    assert f(ctypes.byref(adesc()), q + 8, k, v, o, None, None, s) == EALIGN
+    assert f(ctypes.byref(adesc(scale=float("inf"))), q, k, v, o, None, None, s) == EARG
+    n = ctypes.c_size_t()
+    assert L.rglru_attn_workspace_size(ctypes.byref(adesc(T=0)), ctypes.byref(n)) == OK   # T ignored
+    g = L.rglru_attn_step
+    ws, pos = P + 0x10000000, P + 0x7000000
+    assert g(ctypes.byref(adesc()), q, k, v, kc, vc, pos, o, ws, n.value - 1, s) == EWS
+    assert g(ctypes.byref(adesc()), q, k, v, kc, vc, None, o, ws, n.value, s) == ENULL
+    assert g(ctypes.byref(adesc()), q, k, v, kc, vc, pos + 2, o, ws, n.value, s) == EALIGN
+    assert g(ctypes.byref(adesc()), q, k, v, kc, kc, pos, o, ws, n.value, s) == EARG   # caches overlap

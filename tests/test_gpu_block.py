@@ -4,9 +4,13 @@ The block: out = proj_out(RG-LRU(conv(proj_in_1 x)) * GeLU(proj_in_2 x)) (page
 "Griffin Guide: RecurrentGemma, RG-LRU & Hybrid Attention", "The Recurrent
 Block Architecture", and the listing's RecurrentBlock).  Same metric and
 tolerances as the scan: max |g - o| / max(|o|, RMS(o)) per output, 1e-5 for
-fp32 I/O, 2e-2 for bf16 I/O.  The oracle keeps every intermediate in double;
-the library rounds b1, b2 and the merged product to the I/O type, which the
-bf16 tolerance covers.  The full-size case runs the 2B-width prefill shape
+fp32 I/O, 2e-2 for bf16 I/O.  The oracle keeps every intermediate in double.
+The block's interface stores b1, b2 and the merged product in the I/O type;
+for bf16 the reference composes the oracle's functions with that same
+storage rounding at those three points (the rounding of synth/, which is the
+input recipe's), so that the 2e-2 bar measures the path rather than three
+extra bf16 roundings; the error against the all-double composition is
+printed beside it.  The full-size case runs the 2B-width prefill shape
 (B=8, T=2048, D = d_model = 2560) and checks one whole stream: the block is
 causal and streams are independent, so a stream is a problem of its own.
 """
@@ -54,6 +58,20 @@ def _oracle_block(prob, bp, x, b0, b1, T=None, with_state=False):
                             c=8.0)
 
 
+def _oracle_block_stored(prob, bp, x, b0, b1, with_state=False):
+    """The block with b1, b2 and the merged product stored in the I/O type."""
+    def st(a):
+        return synth.widen(synth.store(a, prob.io))
+    xs = synth.widen(x[b0:b1])
+    h0 = prob.h0[b0:b1].astype(np.float64) if with_state else None
+    hist = synth.widen(prob.hist[b0:b1]) if with_state else None
+    br1 = st(oracle.linear(xs, synth.widen(bp.proj_in_1)))
+    br2 = st(oracle.linear(xs, synth.widen(bp.proj_in_2)))
+    y, h_last, hist_out = oracle.fwd(br1, **prob.oracle_params(), h0=h0, hist_in=hist, c=8.0)
+    out = oracle.linear(st(oracle.merge(y, br2)), synth.widen(bp.proj_out))
+    return out, h_last, hist_out
+
+
 def _run(prob, bp, x, with_state):
     w = prob.weights(DEV)
     h0 = to_dev(prob.h0, DEV) if with_state else None
@@ -81,7 +99,8 @@ def test_block_bf16_2b_width_short():
     prob, bp, x = _block_setup(1, 2, 70, 2560, with_state=True)
     _say(f"block bf16: B=2 T=70 D={prob.D} H={prob.H} d_model=2560, with state")
     out, hl, ho = _run(prob, bp, x, True)
-    ro, rh, rhist = _oracle_block(prob, bp, x, 0, 2, with_state=True)
+    ro, rh, rhist = _oracle_block_stored(prob, bp, x, 0, 2, with_state=True)
+    _say(f"  (out against the all-double block: {oracle.rel_err(out, _oracle_block(prob, bp, x, 0, 2, with_state=True)[0]):.3e})")
     _cmp("out", out, ro, TOL["bf16"])
     _cmp("h_last", hl, rh, TOL["bf16"])
     # hist_out holds branch-1 activations, which the library rounds to bf16
@@ -108,7 +127,8 @@ def test_block_full_size_one_stream():
     prob, bp, x = _block_setup(1, B, T, dm, with_state=False)
     _say(f"block bf16 full size: B={B} T={T} D={prob.D} d_model={dm}; oracle on stream 5")
     out, hl, _ = _run(prob, bp, x, False)
-    ro, rh, _ = _oracle_block(prob, bp, x, 5, 6)
+    ro, rh, _ = _oracle_block_stored(prob, bp, x, 5, 6)
+    _say(f"  (out[5] against the all-double block: {oracle.rel_err(out[5:6], _oracle_block(prob, bp, x, 5, 6)[0]):.3e})")
     _cmp("out[5]", out[5:6], ro, TOL["bf16"])
     _cmp("h_last[5]", hl[5:6], rh, TOL["bf16"])
 
