@@ -11,22 +11,23 @@
 // Scores are scale * q.k; softmax and sums in fp32.
 //
 // Kernels
-//   attn_prefill_mfma  bf16, dh = 256.  A workgroup (4 waves) takes 128
-//       consecutive rows of the flattened (token, head) index of one stream
-//       -- for MQA, rows of neighbouring tokens share their keys -- and walks
-//       the union of their windows in tiles of 32 keys, double-buffered in
-//       LDS.  Per tile and wave: S^T = K Q^T (16 v_mfma_f32_32x32x16_bf16; K
-//       rows are read in the order that gives each lane 16 consecutive keys of
-//       one query), an online softmax per query (a lane and its partner 32
-//       lanes away hold the tile's 32 scores), and O^T += V^T P^T (16 MFMAs;
-//       the lane's own probabilities are the B operand, and V^T, staged
-//       transposed through registers, is the A operand).
+//   attn_prefill_mfma  bf16, dh = 256.  A workgroup (8 waves of 16 rows)
+//       takes 128 consecutive rows of the flattened (token, head) index of
+//       one stream -- for MQA, rows of neighbouring tokens share their keys --
+//       and walks the union of their windows in tiles of 64 keys,
+//       double-buffered in LDS, the next tile's loads issued a tile ahead.
+//       Per tile and wave: S^T = K Q^T (32 v_mfma_f32_16x16x32_bf16; K rows
+//       read in the order that gives each lane 8 consecutive keys of one
+//       query), an online softmax per query (the 4 lanes of a query hold the
+//       tile's 64 scores), and O^T += V^T P^T (32 MFMAs; the lane's own
+//       probabilities are the B operand, V^T -- staged transposed through
+//       registers -- the A operand).
 //   attn_step_mfma     bf16, dh = 256, Hq <= 16.  Decode, split over the ring:
 //       a workgroup scores 256 slots for all heads with
 //       v_mfma_f32_16x16x32_bf16 (K rows straight from HBM, heads padded to
-//       16), keeps exp-weights in LDS and accumulates P V on the vector ALUs;
-//       attn_combine merges the splits and writes the new key and value into
-//       their slot.
+//       16), keeps the exp-weights in LDS as bf16 and forms O^T = V^T P^T with
+//       the same MFMA, V staged transposed in 64-slot chunks; attn_combine
+//       merges the splits and writes the new key and value into their slot.
 //   attn_*_generic     any io, dh <= 256: one wave per query row, the
 //       reference-shaped loop (fp32 I/O and shapes the fast kernels exclude).
 #include <math.h>
@@ -177,89 +178,100 @@ __global__ __launch_bounds__(256) void attn_fill_cache(int B, int T_, int W, int
 }
 
 // ------------------------------------------------------------ MFMA prefill
-constexpr int PF_ROWS = 128;            // flattened (token, head) rows per workgroup
-constexpr int PF_KEYS = 32;             // keys per tile
+constexpr int PF_ROWS = 128;            // flattened (token, head) rows per workgroup (8 waves x 16)
+constexpr int PF_KEYS = 64;             // keys per tile
 constexpr int PF_KSTRIDE = 264;         // bf16 per K row in LDS (528 B, conflict-free b128 reads)
-constexpr int PF_VSTRIDE = 40;          // bf16 per V^T row (80 B)
-constexpr int PF_KBYTES = PF_KEYS * PF_KSTRIDE * 2;   // 16,896
-constexpr int PF_VBYTES = 256 * PF_VSTRIDE * 2;       // 20,480
+constexpr int PF_VSTRIDE = 72;          // bf16 per V^T row (144 B, conflict-free b128 reads)
+constexpr int PF_KBYTES = PF_KEYS * PF_KSTRIDE * 2;   // 33,792
+constexpr int PF_VBYTES = 256 * PF_VSTRIDE * 2;       // 36,864
 constexpr int PF_STAGE = PF_KBYTES + PF_VBYTES;
-constexpr int PF_LDS = 2 * PF_STAGE;                  // 74,752
+constexpr int PF_LDS = 2 * PF_STAGE;                  // 141,312
 
-// The staged pieces of one key tile: threads 0..127 carry 8 pieces of one K
-// row each; threads 128..255 an 8 x 8 block of V (8 keys x 8 dh), which they
-// transpose before writing so that V^T rows hold consecutive keys.
+// The staged pieces of one key tile.  Threads 0..255 carry 8 pieces (128 B)
+// of one K row; threads 256..511 a block of 8 keys x 8 dh of V, transposed in
+// registers before the LDS write so that V^T rows hold consecutive keys.
+// Lane-to-block maps keep each 16-lane group's LDS writes in distinct banks.
 struct PfStage {
-    u32x4 r[8];
+    u32x4 kp[8];
+    u32x4 vp[8];
 };
 
 __device__ __forceinline__ void pf_load(PfStage &st, const bf16 *k, const bf16 *v, long kv0, int key0, int T_,
                                         int tid)
 {
-    if (tid < 128) {
-        const int row = tid >> 2, seg = (tid & 3) * 64;   // 64 dh per thread
+    if (tid < 256) {
+        const int row = tid >> 2, seg = tid & 3;   // 64 dh per thread
         const int key = key0 + row;
-        const u32x4 *src = (const u32x4 *)(k + (kv0 + (key < T_ ? key : 0)) * 256 + seg);
+        const u32x4 *src = (const u32x4 *)(k + (kv0 + (key < T_ ? key : 0)) * 256 + 64 * seg);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) st.r[i] = key < T_ ? src[i] : u32x4{0, 0, 0, 0};
+        for (int i = 0; i < 8; ++i) st.kp[i] = key < T_ ? src[i] : u32x4{0, 0, 0, 0};
     } else {
-        const int t2 = tid - 128, kg = t2 >> 5, dg = t2 & 31;
+        const int t2 = tid - 256, kg = t2 & 7, dg = t2 >> 3;   // keys 8kg.., dh 8dg..
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int key = key0 + 8 * kg + i;
             const u32x4 *src = (const u32x4 *)(v + (kv0 + (key < T_ ? key : 0)) * 256 + 8 * dg);
-            st.r[i] = key < T_ ? *src : u32x4{0, 0, 0, 0};
+            st.vp[i] = key < T_ ? *src : u32x4{0, 0, 0, 0};
         }
     }
 }
 
 __device__ __forceinline__ void pf_store(const PfStage &st, char *stage, int tid)
 {
-    if (tid < 128) {
-        const int row = tid >> 2, seg = (tid & 3) * 64;
-        u32x4 *dst = (u32x4 *)(stage + (row * PF_KSTRIDE + seg) * 2);
+    if (tid < 256) {
+        const int row = tid >> 2, seg = tid & 3;
+        // key 32j + 8a + 4u + i goes to LDS row 32j + 16u + 4a + i, so that the
+        // 16 keys one score tile reads together sit in 16 consecutive rows
+        const int lrow = (row & 0x23) | ((row & 0x4) << 2) | ((row & 0x18) >> 1);
+        u32x4 *dst = (u32x4 *)(stage + (lrow * PF_KSTRIDE + 64 * seg) * 2);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dst[i] = st.r[i];
+        for (int i = 0; i < 8; ++i) dst[i] = st.kp[i];
     } else {
-        const int t2 = tid - 128, kg = t2 >> 5, dg = t2 & 31;
-        // st.r[i] holds keys 8kg+i, dh 8dg..8dg+7 (dword c = dh pair 2c, 2c+1);
-        // output row 8dg + j holds keys 8kg..8kg+7 for dh 8dg + j
+        const int t2 = tid - 256, kg = t2 & 7, dg = t2 >> 3;
+        // vp[i] holds key 8kg+i, dh 8dg..8dg+7 (dword c = dh pair 2c, 2c+1);
+        // V^T row 8dg + j receives keys 8kg..8kg+7 of dh 8dg + j
         char *vt = stage + PF_KBYTES;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
             const int c = j >> 1;
             u32x4 o;
-            o[0] = __builtin_amdgcn_perm(st.r[1][c], st.r[0][c], sel);
-            o[1] = __builtin_amdgcn_perm(st.r[3][c], st.r[2][c], sel);
-            o[2] = __builtin_amdgcn_perm(st.r[5][c], st.r[4][c], sel);
-            o[3] = __builtin_amdgcn_perm(st.r[7][c], st.r[6][c], sel);
+            o[0] = __builtin_amdgcn_perm(st.vp[1][c], st.vp[0][c], sel);
+            o[1] = __builtin_amdgcn_perm(st.vp[3][c], st.vp[2][c], sel);
+            o[2] = __builtin_amdgcn_perm(st.vp[5][c], st.vp[4][c], sel);
+            o[3] = __builtin_amdgcn_perm(st.vp[7][c], st.vp[6][c], sel);
             *(u32x4 *)(vt + ((8 * dg + j) * PF_VSTRIDE + 8 * kg) * 2) = o;
         }
     }
 }
 
-__global__ __launch_bounds__(256) void attn_prefill_mfma(int T_, int Hq, int W, float scale_log2e,
+// 16 query rows per wave on v_mfma_f32_16x16x32_bf16.  In the score tiles
+// (keys x queries, four of 16 keys per 64-key tile) A row r of tile st is key
+// 32(st/2) + 8(r/4) + 4(st%2) + r%4, so that lane (n, g) -- query n = lane%16,
+// g = lane/16 -- ends up with keys 32j + 8g .. +7 for j = 0, 1: exactly the
+// k-slots it supplies as the B operand of step j of O^T += V^T P^T, whose A
+// operand then reads 8 consecutive keys of a V^T row.
+__global__ __launch_bounds__(512) void attn_prefill_mfma(int T_, int Hq, int W, float scale_log2e,
                                                          const bf16 *q, const bf16 *k, const bf16 *v, bf16 *o)
 {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int n = lane & 31, half = lane >> 5;
+    const int n = lane & 15, g = lane >> 4;
     const long rows_per_b = (long)T_ * Hq;
     const long tiles_per_b = (rows_per_b + PF_ROWS - 1) / PF_ROWS;
     const int b = (int)(blockIdx.x / tiles_per_b);
     const long f0 = (blockIdx.x % tiles_per_b) * PF_ROWS;   // first flattened row of the workgroup
     const long kv0 = (long)b * T_;                          // first key row of stream b
 
-    // this lane's query row (column n of the wave's 32 rows)
-    const long f = f0 + 32 * wave + n;
+    // this lane's query row
+    const long f = f0 + 16 * wave + n;
     const bool row_ok = f < rows_per_b;
     const int t = row_ok ? (int)(f / Hq) : -1;
-    bf16x8 qb[16];
+    bf16x8 qb[8];
     {
-        const bf16 *qr = q + ((long)b * rows_per_b + (row_ok ? f : 0)) * 256 + 8 * half;
+        const bf16 *qr = q + ((long)b * rows_per_b + (row_ok ? f : 0)) * 256 + 8 * g;
 #pragma unroll
-        for (int s = 0; s < 16; ++s) qb[s] = row_ok ? *(const bf16x8 *)(qr + 16 * s) : bf16x8{};
+        for (int ks = 0; ks < 8; ++ks) qb[ks] = row_ok ? *(const bf16x8 *)(qr + 32 * ks) : bf16x8{};
     }
 
     // keys of the union of the workgroup's windows
@@ -268,99 +280,103 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma(int T_, int Hq, int W, 
     const int k_lo = t_first - W + 1 < 0 ? 0 : t_first - W + 1;
     const int tile0 = k_lo / PF_KEYS, tile1 = t_last / PF_KEYS;
 
-    f32x16 acc[8];
+    f32x4_t acc[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = f32x16{};
+    for (int i = 0; i < 16; ++i) acc[i] = f32x4_t{};
     float m = -INFINITY, l = 0.0f;
 
+    // tile i is computed from LDS while tile i+1 is on its way from memory
+    // (the second wave of each SIMD covers the wait)
     PfStage st;
     pf_load(st, k, v, kv0, tile0 * PF_KEYS, T_, tid);
     pf_store(st, smem + (tile0 & 1) * PF_STAGE, tid);
     __syncthreads();
 
-    // lane's K row inside a tile: row r of the A operand is key tile_row_token(r),
-    // so that register k of the score tile is key 16*half + k
-    const int krow = tile_row_token(n);
+    // A row of this lane in score tile st: key 32(st/2) + 8(n/4) + 4(st%2) + n%4,
+    // held in LDS row 32(st/2) + 16(st%2) + n
     for (int tile = tile0; tile <= tile1; ++tile) {
-        const bool more = tile < tile1;
-        if (more) pf_load(st, k, v, kv0, (tile + 1) * PF_KEYS, T_, tid);
+        if (tile < tile1) pf_load(st, k, v, kv0, (tile + 1) * PF_KEYS, T_, tid);
         const char *stage = smem + (tile & 1) * PF_STAGE;
 
-        // S^T = K Q^T over dh = 256
-        // (two accumulator chains, so that back-to-back MFMAs do not wait on
-        // each other's results)
-        f32x16 s = {}, s2 = {};
+        // S^T = K Q^T over dh = 256, four tiles of 16 keys
+        f32x4_t sa[4] = {};
         {
-            const bf16 *kr = (const bf16 *)stage + krow * PF_KSTRIDE + 8 * half;
+            const bf16 *kr = (const bf16 *)stage + n * PF_KSTRIDE + 8 * g;
 #pragma unroll
-            for (int ks = 0; ks < 16; ks += 2) {
-                const bf16x8 a0 = *(const bf16x8 *)(kr + 16 * ks);
-                const bf16x8 a1 = *(const bf16x8 *)(kr + 16 * ks + 16);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qb[ks], s, 0, 0, 0);
-                s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qb[ks + 1], s2, 0, 0, 0);
-            }
+            for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[r] += s2[r];
+                for (int st4 = 0; st4 < 4; ++st4) {
+                    const int off = (32 * (st4 >> 1) + 16 * (st4 & 1)) * PF_KSTRIDE;
+                    const bf16x8 a = *(const bf16x8 *)(kr + off + 32 * ks);
+                    sa[st4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], sa[st4], 0, 0, 0);
+                }
         }
-        // mask, scale into log2 units, tile maximum per query
-        const int key_base = tile * PF_KEYS + 16 * half;
+        // this lane's keys: 32j + 8g + e, e = 4(st%2) + i, j = st/2
+        float sv[16];
+#pragma unroll
+        for (int st4 = 0; st4 < 4; ++st4)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv[8 * (st4 >> 1) + 4 * (st4 & 1) + i] = sa[st4][i];
         float mt = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = key_base + r;
+        for (int e = 0; e < 16; ++e) {
+            const int key = tile * PF_KEYS + 32 * (e >> 3) + 8 * g + (e & 7);
             const bool ok = key <= t && key > t - W;
-            s[r] = ok ? s[r] * scale_log2e : -INFINITY;
-            mt = fmaxf(mt, s[r]);
+            sv[e] = ok ? sv[e] * scale_log2e : -INFINITY;
+            mt = fmaxf(mt, sv[e]);
         }
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
         mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float mn = fmaxf(m, mt);
+        // the reference maximum moves only when the tile's maximum passes it
+        // by more than 8 (log2 units): the weights then stay below 2^8 and
+        // the accumulators are rescaled rarely
+        const float mn = mt > m + 8.0f ? mt : m;
         const float mu = mn == -INFINITY ? 0.0f : mn;
         const float alpha = hw_exp2(m - mu);   // 0 while m is -inf
         float ls = 0.0f;
         bf16x8 pb[2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float pr = hw_exp2(s[r] - mu);
+        for (int e = 0; e < 16; ++e) {
+            const float pr = hw_exp2(sv[e] - mu);
             ls += pr;
-            pb[r >> 3][r & 7] = (bf16)pr;
+            pb[e >> 3][e & 7] = (bf16)pr;
         }
+        ls += __shfl_xor(ls, 16);
         ls += __shfl_xor(ls, 32);
         l = fmaf(l, alpha, ls);
         m = mn;
         if (__any(alpha != 1.0f)) {   // rescale only when some query's maximum moved
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < 16; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][r] *= alpha;
+                for (int r = 0; r < 4; ++r) acc[i][r] *= alpha;
         }
-        // O^T += V^T P^T: k-step ks covers keys 16*half + 8*ks .. +8 of this lane
+        // O^T += V^T P^T: 16 dh tiles, two 32-key steps each
         {
-            const bf16 *vt = (const bf16 *)(stage + PF_KBYTES) + n * PF_VSTRIDE + 16 * half;
+            const bf16 *vt = (const bf16 *)(stage + PF_KBYTES) + n * PF_VSTRIDE + 8 * g;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const bf16x8 a = *(const bf16x8 *)(vt + 32 * dt * PF_VSTRIDE + 8 * ks);
-                    acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks], acc[dt], 0, 0, 0);
+                for (int dt = 0; dt < 16; ++dt) {
+                    const bf16x8 a = *(const bf16x8 *)(vt + 16 * dt * PF_VSTRIDE + 32 * j);
+                    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[j], acc[dt], 0, 0, 0);
                 }
         }
-        if (more) pf_store(st, smem + ((tile + 1) & 1) * PF_STAGE, tid);
+        if (tile < tile1) pf_store(st, smem + ((tile + 1) & 1) * PF_STAGE, tid);
         __syncthreads();
     }
 
     if (row_ok) {
         const float inv = 1.0f / l;
         bf16 *orow = o + ((long)b * rows_per_b + f) * 256;
+        typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
+        for (int dt = 0; dt < 16; ++dt) {
+            bf16x4 w4;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
-                bf16x4 w4;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) w4[i] = (bf16)(acc[dt][4 * j + i] * inv);
-                *(bf16x4 *)(orow + 32 * dt + 8 * j + 4 * half) = w4;
-            }
+            for (int i = 0; i < 4; ++i) w4[i] = (bf16)(acc[dt][i] * inv);
+            *(bf16x4 *)(orow + 16 * dt + 4 * g) = w4;   // lane holds dh 16 dt + 4 g + i
+        }
     }
 }
 
@@ -379,10 +395,12 @@ __global__ __launch_bounds__(256) void attn_step_mfma(int Hq, int W, int NS, flo
                                                      const bf16 *k_t, const bf16 *v_t, const bf16 *kc,
                                                      const bf16 *vc, const int32_t *pos, StepWs ws)
 {
-    __shared__ float Ps[DS_SLOTS][17];   // exp-weights [slot][head]
+    constexpr int PT = DS_SLOTS + 8;   // bf16 per row of P^T (16-byte pieces, rows apart in banks)
+    constexpr int VS = 72;             // bf16 per V^T row of a 64-slot chunk (144 B)
+    __shared__ __attribute__((aligned(16))) bf16 Pt[16][PT];    // exp-weights [head][slot]
+    __shared__ __attribute__((aligned(16))) bf16 Vt[256][VS];   // one chunk of V, transposed
     __shared__ float wmax[4][16];
     __shared__ float wsum[4][16];
-    __shared__ __attribute__((aligned(16))) float red[128][2][16];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int b = blockIdx.x / NS, sp = blockIdx.x % NS;
     const long p = pos[b];
@@ -424,91 +442,100 @@ __global__ __launch_bounds__(256) void attn_step_mfma(int Hq, int W, int NS, flo
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     if (kg == 0) wmax[wave][n16] = mx;
     __syncthreads();
-    float M = fmaxf(fmaxf(wmax[0][n16], wmax[1][n16]), fmaxf(wmax[2][n16], wmax[3][n16]));
+    const float M = fmaxf(fmaxf(wmax[0][n16], wmax[1][n16]), fmaxf(wmax[2][n16], wmax[3][n16]));
     const float mu = M == -INFINITY ? 0.0f : M;
     float ls = 0.0f;
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
+    for (int st = 0; st < 4; ++st) {
+        typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+        bf16x4 w4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float pr = hw_exp2(sc[st][i] - mu);
             ls += pr;
-            Ps[64 * wave + 16 * st + 4 * kg + i][n16] = pr;
+            w4[i] = (bf16)pr;
         }
+        *(bf16x4 *)&Pt[n16][64 * wave + 16 * st + 4 * kg] = w4;
+    }
     ls += __shfl_xor(ls, 16);
     ls += __shfl_xor(ls, 32);
     if (kg == 0) wsum[wave][n16] = ls;
-    __syncthreads();
 
-    // P V on the vector ALUs: thread = (slot parity, dh pair)
-    const int par = tid >> 7, d2 = tid & 127;
-    float acc[16][2];
+    // O^T = V^T P^T on the matrix cores, 64 slots at a time: V is staged
+    // transposed (thread = 8 slots x 8 dh, transposed in registers); slots
+    // never written (position < 0) and slots past W enter as zeros, so that
+    // whatever they hold cannot reach the sums.  Wave w owns dh 64w .. 64w+63.
+    f32x4_t o4[4] = {};
+    const int sg = tid >> 5, dg = tid & 31;
+    for (int ch = 0; ch < DS_SLOTS / 64; ++ch) {
+        u32x4 r[8];
 #pragma unroll
-    for (int h = 0; h < 16; ++h) acc[h][0] = acc[h][1] = 0.0f;
-    for (int j = par; j < DS_SLOTS; j += 2) {
-        const int slot = sp * DS_SLOTS + j;
-        if (slot >= W) break;
-        if (p - ((p - slot) % W + W) % W < 0) continue;   // never written (pos < W): may hold anything
-        const bf16 *vr = slot == cur ? v_t + (long)b * 256 : vc + ((long)b * W + slot) * 256;
-        typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-        const bf16x2 vv = *(const bf16x2 *)(vr + 2 * d2);
-        const float v0 = (float)vv[0], v1 = (float)vv[1];
+        for (int i = 0; i < 8; ++i) {
+            const int slot = sp * DS_SLOTS + 64 * ch + 8 * sg + i;
+            const long ppos = p - ((p - slot) % W + W) % W;
+            const bool ok = slot < W && ppos >= 0;
+            const bf16 *vr = slot == cur ? v_t + (long)b * 256 : vc + ((long)b * W + (ok ? slot : 0)) * 256;
+            r[i] = ok ? *(const u32x4 *)(vr + 8 * dg) : u32x4{0, 0, 0, 0};
+        }
+        __syncthreads();   // the previous chunk's V^T has been read (first pass: P^T is complete)
 #pragma unroll
-        for (int h = 0; h < 16; ++h) {
-            if (h < Hq) {
-                const float pr = Ps[j][h];
-                acc[h][0] = fmaf(pr, v0, acc[h][0]);
-                acc[h][1] = fmaf(pr, v1, acc[h][1]);
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+            const int c = j >> 1;
+            u32x4 o;
+            o[0] = __builtin_amdgcn_perm(r[1][c], r[0][c], sel);
+            o[1] = __builtin_amdgcn_perm(r[3][c], r[2][c], sel);
+            o[2] = __builtin_amdgcn_perm(r[5][c], r[4][c], sel);
+            o[3] = __builtin_amdgcn_perm(r[7][c], r[6][c], sel);
+            *(u32x4 *)&Vt[8 * dg + j][8 * sg] = o;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 pb = *(const bf16x8 *)&Pt[n16][64 * ch + 32 * ks + 8 * kg];
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const bf16x8 a = *(const bf16x8 *)&Vt[64 * wave + 16 * dt + n16][32 * ks + 8 * kg];
+                o4[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o4[dt], 0, 0, 0);
             }
         }
     }
-    // the odd-slot half hands its sums to the even half
-    if (par == 1) {
+    // lane holds head n16 and dh 64*wave + 16*dt + 4*kg + i
+    const long base = ((long)b * NS + sp) * 16;
+    if (n16 < Hq) {
 #pragma unroll
-        for (int h = 0; h < 16; ++h) {
-            red[d2][0][h] = acc[h][0];
-            red[d2][1][h] = acc[h][1];
-        }
+        for (int dt = 0; dt < 4; ++dt)
+            *(f32x4_t *)(ws.o + (base + n16) * 256 + 64 * wave + 16 * dt + 4 * kg) = o4[dt];
     }
-    __syncthreads();
-    if (par == 0) {
-        const long base = ((long)b * NS + sp) * 16;
-#pragma unroll
-        for (int h = 0; h < 16; ++h) {
-            if (h < Hq) {
-                ws.o[(base + h) * 256 + 2 * d2] = acc[h][0] + red[d2][0][h];
-                ws.o[(base + h) * 256 + 2 * d2 + 1] = acc[h][1] + red[d2][1][h];
-            }
-        }
-        if (d2 < 16) {
-            ws.m[base + d2] = M;
-            ws.l[base + d2] = wsum[0][d2] + wsum[1][d2] + wsum[2][d2] + wsum[3][d2];
-        }
+    if (tid < 16) {
+        ws.m[base + tid] = fmaxf(fmaxf(wmax[0][tid], wmax[1][tid]), fmaxf(wmax[2][tid], wmax[3][tid]));
+        ws.l[base + tid] = wsum[0][tid] + wsum[1][tid] + wsum[2][tid] + wsum[3][tid];
     }
 }
 
-// One workgroup per stream: merge the splits of every head, then write the
-// new key and value into slot pos mod W (every read of this step is done).
+// One workgroup per (stream, head): merge the splits; the head-0 workgroup
+// then writes the new key and value into slot pos mod W (no workgroup of
+// this launch reads the cache).
 __global__ __launch_bounds__(256) void attn_combine(int Hq, int W, int NS, StepWs ws, const bf16 *k_t,
                                                    const bf16 *v_t, bf16 *kc, bf16 *vc, const int32_t *pos,
                                                    bf16 *o_t)
 {
-    const int b = blockIdx.x, d = threadIdx.x;   // 256 threads = dh
-    for (int h = 0; h < Hq; ++h) {
-        float M = -INFINITY;
-        for (int s = 0; s < NS; ++s) M = fmaxf(M, ws.m[((long)b * NS + s) * 16 + h]);
-        float num = 0.0f, den = 0.0f;
-        for (int s = 0; s < NS; ++s) {
-            const long base = ((long)b * NS + s) * 16 + h;
-            const float wgt = hw_exp2(ws.m[base] - M);   // 0 for an empty split
-            den = fmaf(wgt, ws.l[base], den);
-            num = fmaf(wgt, ws.o[base * 256 + d], num);
-        }
-        o_t[((long)b * Hq + h) * 256 + d] = (bf16)(num / den);
+    const int b = blockIdx.x / Hq, h = blockIdx.x % Hq, d = threadIdx.x;   // 256 threads = dh
+    float M = -INFINITY;
+    for (int s = 0; s < NS; ++s) M = fmaxf(M, ws.m[((long)b * NS + s) * 16 + h]);
+    float num = 0.0f, den = 0.0f;
+    for (int s = 0; s < NS; ++s) {
+        const long base = ((long)b * NS + s) * 16 + h;
+        const float wgt = hw_exp2(ws.m[base] - M);   // 0 for an empty split
+        den = fmaf(wgt, ws.l[base], den);
+        num = fmaf(wgt, ws.o[base * 256 + d], num);
     }
-    const long slot = ((long)b * W + pos[b] % W) * 256 + d;
-    kc[slot] = k_t[(long)b * 256 + d];
-    vc[slot] = v_t[(long)b * 256 + d];
+    o_t[((long)b * Hq + h) * 256 + d] = (bf16)(num / den);
+    if (h == 0) {
+        const long slot = ((long)b * W + pos[b] % W) * 256 + d;
+        kc[slot] = k_t[(long)b * 256 + d];
+        vc[slot] = v_t[(long)b * 256 + d];
+    }
 }
 
 }  // namespace
@@ -535,7 +562,7 @@ void launch_attn_fwd(const rglru_attn_desc &d, const void *q, const void *k, con
             attr = true;
         }
         const long tiles = (d.T * d.Hq + PF_ROWS - 1) / PF_ROWS;
-        attn_prefill_mfma<<<dim3((unsigned)(d.B * tiles)), dim3(256), PF_LDS, s>>>(
+        attn_prefill_mfma<<<dim3((unsigned)(d.B * tiles)), dim3(512), PF_LDS, s>>>(
             (int)d.T, (int)d.Hq, (int)d.W, scale * 1.4426950408889634f, (const bf16 *)q, (const bf16 *)k,
             (const bf16 *)v, (bf16 *)o);
     } else {
@@ -573,7 +600,7 @@ void launch_attn_step(const rglru_attn_desc &d, const void *q_t, const void *k_t
         attn_step_mfma<<<dim3((unsigned)(d.B * NS)), 256, 0, s>>>(
             (int)d.Hq, (int)d.W, NS, scale * 1.4426950408889634f, (const bf16 *)q_t, (const bf16 *)k_t,
             (const bf16 *)v_t, (const bf16 *)kc, (const bf16 *)vc, pos, w);
-        attn_combine<<<dim3((unsigned)d.B), 256, 0, s>>>((int)d.Hq, (int)d.W, NS, w, (const bf16 *)k_t,
+        attn_combine<<<dim3((unsigned)(d.B * d.Hq)), 256, 0, s>>>((int)d.Hq, (int)d.W, NS, w, (const bf16 *)k_t,
                                                          (const bf16 *)v_t, (bf16 *)kc, (bf16 *)vc, pos,
                                                          (bf16 *)o_t);
     } else {
