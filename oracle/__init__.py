@@ -233,3 +233,37 @@ def attn_step(q_t, k_t, v_t, kcache, vcache, pos, scale: float):
                            _p(kcache), _p(vcache), pos.ctypes.data_as(ctypes.POINTER(ctypes.c_long)),
                            _p(o))
     return o
+
+
+# ------------------------------------------------------------ residual layer
+def rmsnorm(x, w, eps=1e-6):
+    """Reading R8: x / sqrt(mean over the last axis of x^2 + eps) * (1 + w)."""
+    x, w = map(_f64, (x, w))
+    D = x.shape[-1]
+    out = np.empty_like(x)
+    lib().oracle_rmsnorm(ctypes.c_long(x.size // D), D, _p(x), _p(w), ctypes.c_double(eps), _p(out))
+    return out
+
+
+def gelu_tanh(v):
+    """GELU, tanh form (reading R8)."""
+    v = _f64(v)
+    out = np.empty_like(v)
+    lib().oracle_gelu_tanh(ctypes.c_long(v.size), _p(v), _p(out))
+    return out
+
+
+def mlp(x, gate_w, up_w, down_w):
+    """Gated MLP (reading R8): down(GELU_tanh(gate x) * (up x)); weights [out][in]."""
+    return linear(gelu_tanh(linear(x, gate_w)) * linear(x, up_w), down_w)
+
+
+def hawk_layer(x, tnorm_w, cnorm_w, proj_in_1, proj_in_2, proj_out, conv_w, conv_b, W_a, b_a, W_x, b_x,
+               Lambda, gate_w, up_w, down_w, h0=None, hist_in=None, c=8.0, eps=1e-6):
+    """Residual layer with the recurrent block as temporal mixer ([L] "Residual
+    Block View"): x~ = x + block(RMSNorm(x)), y = x~ + MLP(RMSNorm(x~)).
+    Returns (y, h_last, hist_out)."""
+    t, h_last, hist_out = block_fwd(rmsnorm(x, tnorm_w, eps), proj_in_1, proj_in_2, proj_out, conv_w, conv_b,
+                                    W_a, b_a, W_x, b_x, Lambda, h0=h0, hist_in=hist_in, c=c)
+    xt = _f64(x) + t
+    return xt + mlp(rmsnorm(xt, cnorm_w, eps), gate_w, up_w, down_w), h_last, hist_out

@@ -28,6 +28,12 @@
  *         RecurrentBlock: Conv1d with padding k-1, groups = width, keep the
  *         first T outputs).
  *  [W]  "Griffin" (wiki note), section "Gated Linear Recurrence".
+ *  [L]  "Griffin" (wiki note), section "Residual Block View": the pre-norm
+ *       residual layer x~ = x + TemporalMix(RMSNorm(x)), y = x~ + MLP(RMSNorm(x~));
+ *       module page "transformer_lens.model_bridge.supported_architectures.
+ *       recurrent_gemma", "Architecture overview": temporal_pre_norm,
+ *       channel_pre_norm, gated MLP gate_proj / up_proj / down_proj with
+ *       GELU-tanh, RMSNorm applying (1 + weight).
  *  [N]  "Griffin" (wiki note), section "Local Attention Path": the window
  *       N(t) = {i : t - w < i <= t} and y_t = sum over N(t) of
  *       softmax_i(q_t . k_i) v_i; [G] "Local Sliding-Window Multi-Query
@@ -50,6 +56,11 @@
  *  R5  the backward is the exact derivative of the forward above (the pages
  *      state no backward); dh_last is an optional extra upstream gradient on
  *      the final state.
+ *  R8  the residual layer (Hawk layer, temporal mixer = the recurrent block):
+ *      RMSNorm(x) = x / sqrt(mean_d x^2 + eps) * (1 + w) with eps = 1e-6 (not
+ *      on the pages); gated MLP = down(GELU_tanh(gate x) * (up x)) without
+ *      biases, GELU_tanh(v) = v/2 (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)));
+ *      the MLP width is the caller's (not on the pages).
  *  R6  the recurrent block ([G] "Non-Linear Multiplicative Gating with GeLU"
  *      and the listing's RecurrentBlock): out = proj_out(y * GeLU(proj_in_2
  *      x)), y the RG-LRU of conv(proj_in_1 x); linear layers without bias,
@@ -499,4 +510,26 @@ void oracle_attn_step(int B, int Hq, int dh, int W, double scale, const double *
     free(keys);
     free(vals);
     free(s);
+}
+
+/* ------------------------------------------------------------ residual layer
+ * [L] "Residual Block View" and the RecurrentGemma module page (R8). */
+
+/* out[m][d] = x[m][d] / sqrt(mean_d x[m][d]^2 + eps) * (1 + w[d]) */
+void oracle_rmsnorm(long M, int D, const double *x, const double *w, double eps, double *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (long m = 0; m < M; ++m) {
+        double ss = 0.0;
+        for (int d = 0; d < D; ++d) ss += x[(size_t)m * D + d] * x[(size_t)m * D + d];
+        const double r = 1.0 / sqrt(ss / D + eps);
+        for (int d = 0; d < D; ++d) out[(size_t)m * D + d] = x[(size_t)m * D + d] * r * (1.0 + w[d]);
+    }
+}
+
+/* GELU, tanh form: v/2 (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))) */
+void oracle_gelu_tanh(long n, const double *v, double *out)
+{
+    const double k = sqrt(2.0 / 3.14159265358979323846);   /* sqrt(2 / pi) */
+    for (long i = 0; i < n; ++i) out[i] = 0.5 * v[i] * (1.0 + tanh(k * (v[i] + 0.044715 * v[i] * v[i] * v[i])));
 }
