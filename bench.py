@@ -14,6 +14,8 @@ The other entry points are timed the same way, each on its own workload, and
 reported under "rows": conv1d, gates and the scan stage alone on the 2B-width
 prefill, the recurrent block around the path on the same shape (three
 projections plus the fused forward with the GeLU merge, d_model = D = 2560),
+the residual layer around it (two RMSNorms, the block, a gated GELU-tanh MLP
+of width 3 d_model, residual adds),
 the fused forward on the 32k-token prefill, 512 decode steps of 256 streams,
 the backward of the 9B-width workload (B = 4, T = 8192, D = 4096), and the
 local sliding-window MQA (10 query heads of 256, window 2048) as prefill on
@@ -43,7 +45,8 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 KERNEL_SOURCES = ("fwd.hip", "common.h", "gatemath.h")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_fused_2b_prefill_pmc.json")
-ALL_ROWS = ("conv1d", "gates", "scan", "block", "long", "decode", "bwd", "attn", "attn_long", "attn_decode")
+ALL_ROWS = ("conv1d", "gates", "scan", "block", "layer", "long", "decode", "bwd", "attn", "attn_long",
+            "attn_decode")
 
 
 def kernel_hash() -> str:
@@ -360,6 +363,38 @@ def main():
         r["torch_linear_x3_ms"] = float(np.mean(tk))
         out["rows"]["block"] = r
         del b_sets, x0, zt, bw
+        torch.cuda.empty_cache()
+
+    if "layer" in rows:
+        # the residual layer around the block: pre-norms, the block with its
+        # residual add, the gated MLP (d_ff = 3 d_model) with its residual add
+        dm, F = D, 3 * D
+        bp = synth.make_block_params(cfg.idx, dm, D, cfg.io)
+        lp = synth.make_layer_params(cfg.idx, dm, F, cfg.io)
+        bw = glr.BlockWeights(dev_t(bp.proj_in_1), dev_t(bp.proj_in_2), dev_t(bp.proj_out))
+        lw = glr.LayerWeights(dev_t(lp.tnorm_w), dev_t(lp.cnorm_w), dev_t(lp.gate_w), dev_t(lp.up_w),
+                              dev_t(lp.down_w))
+        x0 = dev_t(synth.make_activation(cfg.idx, "block_x", (B, T, dm), cfg.io))
+        l_sets = [dict(x=x0 if k == 0 else x0.clone(), o=torch.empty_like(x0)) for k in range(2)]
+        hb = torch.empty((B, D), dtype=torch.float32, device=dev)
+        sb = torch.empty((B, 3, D), dtype=torch.bfloat16, device=dev)
+        glr.workspace(glr.layer_workspace_size(B, T, D, H, dm, lw, glr.BF16), dev, "layer",
+                      (B, T, D, H, dm, F, glr.BF16))
+        _say(f"residual layer, 2B width B={B} T={T} d_model={dm} d_ff={F}")
+
+        def lystep(k):
+            s_ = l_sets[k % 2]
+            glr.layer_fwd(s_["x"], w, bw, lw, out=s_["o"], h_last_out=hb, hist_out_buf=sb)
+        kk, _ = tm.calls(lystep, 10, 2)
+        M = B * T
+        fl = 3 * 2 * M * dm * D + 2 * 2 * 256 * tokch + 3 * 2 * M * dm * F
+        nb = 2 * M * dm * 2 + (3 * D * dm + 3 * F * dm) * 2 + 2 * H * 65536 * 2 + D * 8 * 4 + 2 * dm * 4
+        out["rows"]["layer"] = row(f"rglru_layer_fwd, residual layer at 2B width (B={B} T={T} d_model={dm} "
+                                   f"d_ff={F} bf16): 2 RMSNorms, block, gated MLP, residual adds", kk, tokch,
+                                   nb, flops=fl, bound="mfma",
+                                   note="algorithmic flops: 6 projections (block 3, MLP 3) and the gate "
+                                        "products; tokens_ch counts B*T*D")
+        del l_sets, x0, bw, lw
         torch.cuda.empty_cache()
 
     if "long" in rows:

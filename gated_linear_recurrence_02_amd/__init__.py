@@ -50,6 +50,12 @@ class _AttnDesc(ctypes.Structure):
                 ("scale", ctypes.c_float)]
 
 
+class _Layer(ctypes.Structure):
+    _fields_ = [("tnorm_w", ctypes.c_void_p), ("cnorm_w", ctypes.c_void_p), ("gate_w", ctypes.c_void_p),
+                ("up_w", ctypes.c_void_p), ("down_w", ctypes.c_void_p), ("d_ff", ctypes.c_int64),
+                ("eps", ctypes.c_float)]
+
+
 class _Block(ctypes.Structure):
     _fields_ = [("proj_in_1", ctypes.c_void_p), ("proj_in_2", ctypes.c_void_p),
                 ("proj_out", ctypes.c_void_p)]
@@ -58,7 +64,8 @@ class _Block(ctypes.Structure):
 _lib = None
 SYMBOLS = ("rglru_workspace_size", "rglru_conv1d", "rglru_gates", "rglru_scan_fwd",
            "rglru_step", "rglru_scan_bwd", "rglru_block_workspace_size", "rglru_block_fwd",
-           "rglru_attn_fwd", "rglru_attn_workspace_size", "rglru_attn_step", "rglru_status_string")
+           "rglru_attn_fwd", "rglru_attn_workspace_size", "rglru_attn_step", "rglru_layer_workspace_size",
+           "rglru_layer_fwd", "rglru_status_string")
 
 
 def lib():
@@ -82,6 +89,10 @@ def lib():
         L.rglru_attn_fwd.argtypes = [A, vp, vp, vp, vp, vp, vp, vp]
         L.rglru_attn_workspace_size.argtypes = [A, ctypes.POINTER(sz)]
         L.rglru_attn_step.argtypes = [A, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        LY = ctypes.POINTER(_Layer)
+        L.rglru_layer_workspace_size.argtypes = [D, ctypes.c_int64, LY, ctypes.POINTER(sz)]
+        L.rglru_layer_fwd.argtypes = [D, ctypes.c_int64, W, ctypes.POINTER(_Block), LY, vp, vp, vp, vp, vp, vp, vp,
+                                      sz, vp]
         L.rglru_block_workspace_size.argtypes = [D, ctypes.c_int64, ctypes.POINTER(sz)]
         L.rglru_block_fwd.argtypes = [D, ctypes.c_int64, W, ctypes.POINTER(_Block), vp, vp, vp, vp, vp, vp,
                                       vp, sz, vp]
@@ -428,3 +439,72 @@ def attn_step(q_t: torch.Tensor, k_t: torch.Tensor, v_t: torch.Tensor, kcache: t
     _check(lib().rglru_attn_step(ctypes.byref(d), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(kcache), _ptr(vcache),
                                  _ptr(pos), _ptr(o), _ptr(wsb), wsb.numel(), _stream(dev)), "rglru_attn_step")
     return o
+
+
+# ------------------------------------------------------------ residual layer
+@dataclasses.dataclass
+class LayerWeights:
+    """Device tensors of the residual layer around the block: the two pre-norm
+    weights [d_model] fp32 (applied as 1 + w) and the gated MLP's gate_w,
+    up_w [d_ff][d_model], down_w [d_model][d_ff] (activation dtype)."""
+    tnorm_w: torch.Tensor
+    cnorm_w: torch.Tensor
+    gate_w: torch.Tensor
+    up_w: torch.Tensor
+    down_w: torch.Tensor
+    eps: float = 1e-6
+
+    @property
+    def d_ff(self) -> int:
+        return int(self.gate_w.shape[0])
+
+
+def _layer_struct(lw: LayerWeights, d_model, dtype, dev):
+    F = lw.d_ff
+    _need(lw.tnorm_w, "tnorm_w", dev, torch.float32, (d_model,))
+    _need(lw.cnorm_w, "cnorm_w", dev, torch.float32, (d_model,))
+    _need(lw.gate_w, "gate_w", dev, dtype, (F, d_model))
+    _need(lw.up_w, "up_w", dev, dtype, (F, d_model))
+    _need(lw.down_w, "down_w", dev, dtype, (d_model, F))
+    return _Layer(_ptr(lw.tnorm_w), _ptr(lw.cnorm_w), _ptr(lw.gate_w), _ptr(lw.up_w), _ptr(lw.down_w), F, lw.eps)
+
+
+def layer_workspace_size(B, T, D, H, d_model, lw: LayerWeights, io=BF16, c=8.0) -> int:
+    n = ctypes.c_size_t(0)
+    st = _Layer(None, None, None, None, None, lw.d_ff, lw.eps)
+    _check(lib().rglru_layer_workspace_size(ctypes.byref(_Desc(B, T, D, H, io, c)), d_model, ctypes.byref(st),
+                                            ctypes.byref(n)), "rglru_layer_workspace_size")
+    return int(n.value)
+
+
+def layer_fwd(x: torch.Tensor, w: Weights, bw: BlockWeights, lw: LayerWeights, *, h0=None, hist_in=None,
+              want_hist: bool = True, out=None, h_last_out=None, hist_out_buf=None):
+    """Residual layer: x~ = x + block(RMSNorm(x)), y = x~ + MLP(RMSNorm(x~)).
+    Returns (y, h_last, hist_out or None)."""
+    dev = x.device
+    _need(x, "x", dev)
+    B, T, d_model = x.shape
+    D = int(bw.proj_in_1.shape[0])
+    _need(bw.proj_in_1, "proj_in_1", dev, x.dtype, (D, d_model))
+    _need(bw.proj_in_2, "proj_in_2", dev, x.dtype, (D, d_model))
+    _need(bw.proj_out, "proj_out", dev, x.dtype, (d_model, D))
+    _need(h0, "h0", dev, torch.float32, (B, D))
+    _need(hist_in, "hist_in", dev, x.dtype, (B, 3, D))
+    ws_ = _weights_struct(w, D, x.dtype, dev, conv=True, gates=True)
+    ls = _layer_struct(lw, d_model, x.dtype, dev)
+    y = torch.empty_like(x) if out is None else out
+    h_last = torch.empty((B, D), dtype=torch.float32, device=dev) if h_last_out is None else h_last_out
+    hist_out = None
+    if want_hist:
+        hist_out = hist_out_buf if hist_out_buf is not None else torch.empty((B, 3, D), dtype=x.dtype, device=dev)
+    _need(y, "out", dev, x.dtype, (B, T, d_model))
+    _need(h_last, "h_last_out", dev, torch.float32, (B, D))
+    _need(hist_out, "hist_out_buf", dev, x.dtype, (B, 3, D))
+    d = _Desc(B, T, D, w.H, _io(x), w.c)
+    nbytes = layer_workspace_size(B, T, D, w.H, d_model, lw, _io(x), w.c)
+    wsb = workspace(nbytes, dev, "layer", (B, T, D, w.H, d_model, lw.d_ff, _io(x)))
+    blk = _Block(_ptr(bw.proj_in_1), _ptr(bw.proj_in_2), _ptr(bw.proj_out))
+    _check(lib().rglru_layer_fwd(ctypes.byref(d), d_model, ctypes.byref(ws_), ctypes.byref(blk), ctypes.byref(ls),
+                                 _ptr(x), _ptr(hist_in), _ptr(h0), _ptr(y), _ptr(h_last), _ptr(hist_out),
+                                 _ptr(wsb), wsb.numel(), _stream(dev)), "rglru_layer_fwd")
+    return y, h_last, hist_out

@@ -43,6 +43,17 @@ int check_block(const rglru_desc *d, int64_t d_model)
     return RGLRU_OK;
 }
 
+// residual layer: the block's checks plus the MLP width and the norm epsilon
+int check_layer(const rglru_desc *d, int64_t d_model, const rglru_layer *lw)
+{
+    int st = check_block(d, d_model);
+    if (st) return st;
+    if (lw->d_ff < 1 || lw->d_ff >= 2147483647) return RGLRU_ERR_SHAPE;
+    if ((double)d->B * (double)d->T * (double)lw->d_ff > 9.0e15) return RGLRU_ERR_SHAPE;
+    if (!isfinite(lw->eps) || lw->eps < 0.0f) return RGLRU_ERR_ARG;
+    return RGLRU_OK;
+}
+
 // local attention: shapes of the descriptor (prefill also needs T)
 int check_attn(const rglru_attn_desc *d, bool prefill)
 {
@@ -283,6 +294,48 @@ int rglru_block_fwd(const rglru_desc *desc, int64_t d_model, const rglru_weights
                          {blk->proj_in_1, pw}, {blk->proj_in_2, pw}, {blk->proj_out, pw}};
     if (any_alias(outs, 4, ins, 13)) return RGLRU_ERR_ARG;
     st = launch_block_fwd(d, d_model, *w, *blk, x, hist_in, h0, out, h_last, hist_out, ws, stream);
+    if (st) return st;
+    return launch_status();
+}
+
+int rglru_layer_workspace_size(const rglru_desc *desc, int64_t d_model, const rglru_layer *lw, size_t *bytes)
+{
+    if (!bytes || !lw) return RGLRU_ERR_NULL;
+    int st = check_layer(desc, d_model, lw);
+    if (st) return st;
+    *bytes = layer_layout(desc->B, desc->T, desc->D, d_model, lw->d_ff, esize(*desc)).bytes;
+    return RGLRU_OK;
+}
+
+int rglru_layer_fwd(const rglru_desc *desc, int64_t d_model, const rglru_weights *w, const rglru_block *blk,
+                    const rglru_layer *lw, const void *x, const void *hist_in, const float *h0, void *y,
+                    float *h_last, void *hist_out, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (!lw) return RGLRU_ERR_NULL;
+    int st = check_layer(desc, d_model, lw);
+    if (st) return st;
+    if (!w || !blk || !w->conv_w || !w->W_a || !w->W_x || !w->Lambda || !blk->proj_in_1 || !blk->proj_in_2 ||
+        !blk->proj_out || !lw->tnorm_w || !lw->cnorm_w || !lw->gate_w || !lw->up_w || !lw->down_w || !x || !y)
+        return RGLRU_ERR_NULL;
+    if (!ws) return RGLRU_ERR_WORKSPACE;
+    const void *all[] = {x, hist_in, h0, y, h_last, hist_out, ws, w->conv_w, w->conv_b, w->W_a, w->b_a, w->W_x,
+                         w->b_x, w->Lambda, blk->proj_in_1, blk->proj_in_2, blk->proj_out, lw->tnorm_w,
+                         lw->cnorm_w, lw->gate_w, lw->up_w, lw->down_w};
+    for (const void *p : all)
+        if (p && !aligned16(p)) return RGLRU_ERR_ALIGN;
+    const rglru_desc &d = *desc;
+    const size_t need = layer_layout(d.B, d.T, d.D, d_model, lw->d_ff, esize(d)).bytes;
+    if (ws_bytes < need) return RGLRU_ERR_WORKSPACE;
+    const size_t e = esize(d), io_x = d.B * d.T * d_model * e, hist = d.B * 3 * d.D * e;
+    const size_t sb = d.B * d.D * 4, vec = d.D * 4, wb = d.H * 65536 * e, pw = d.D * d_model * e;
+    const size_t fw = lw->d_ff * d_model * e, nv = d_model * 4;
+    const Range outs[] = {{y, io_x}, {h_last, sb}, {hist_out, hist}, {ws, need}};
+    const Range ins[] = {{x, io_x}, {hist_in, hist}, {h0, sb}, {w->conv_w, vec * 4}, {w->conv_b, vec},
+                         {w->W_a, wb}, {w->b_a, vec}, {w->W_x, wb}, {w->b_x, vec}, {w->Lambda, vec},
+                         {blk->proj_in_1, pw}, {blk->proj_in_2, pw}, {blk->proj_out, pw}, {lw->tnorm_w, nv},
+                         {lw->cnorm_w, nv}, {lw->gate_w, fw}, {lw->up_w, fw}, {lw->down_w, fw}};
+    if (any_alias(outs, 4, ins, 18)) return RGLRU_ERR_ARG;
+    st = launch_layer_fwd(d, d_model, *w, *blk, *lw, x, hist_in, h0, y, h_last, hist_out, ws, stream);
     if (st) return st;
     return launch_status();
 }

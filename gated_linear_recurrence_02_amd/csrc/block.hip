@@ -57,7 +57,127 @@ bool gemm_xwt(rocblas_handle h, int io, int64_t M, int64_t N, int64_t K, const v
                               rocblas_gemm_algo_standard, 0, 0) == rocblas_status_success;
 }
 
+// Y[M][N] = X[M][K] W[N][K]^T + R[M][N] (the residual add rides the GEMM's beta)
+bool gemm_xwt_add(rocblas_handle h, int io, int64_t M, int64_t N, int64_t K, const void *X, const void *W,
+                  const void *R, void *Y)
+{
+    const rocblas_datatype t = io == RGLRU_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
+    const float alpha = 1.0f, beta = 1.0f;
+    return rocblas_gemm_ex_64(h, rocblas_operation_transpose, rocblas_operation_none, N, M, K, &alpha, W, t, K,
+                              X, t, K, &beta, R, t, N, Y, t, N, rocblas_datatype_f32_r,
+                              rocblas_gemm_algo_standard, 0, 0) == rocblas_status_success;
+}
+
 size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------- residual layer
+// Values of one 16-byte piece (8 bf16 or 4 fp32) as floats.
+template <typename T> struct Piece;
+template <> struct Piece<bf16> {
+    static constexpr int N = 8;
+    __device__ static void load(const bf16 *p, float *v)
+    {
+        const bf16x8 q = *(const bf16x8 *)p;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (float)q[i];
+    }
+    __device__ static void store(bf16 *p, const float *v)
+    {
+        bf16x8 q;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = (bf16)v[i];
+        *(bf16x8 *)p = q;
+    }
+};
+template <> struct Piece<float> {
+    static constexpr int N = 4;
+    __device__ static void load(const float *p, float *v)
+    {
+        const f32x4 q = *(const f32x4 *)p;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = q[i];
+    }
+    __device__ static void store(float *p, const float *v) { *(f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]}; }
+};
+
+// RMSNorm of one row per wave: out = x / sqrt(mean x^2 + eps) * (1 + w), fp32
+// sums.  Rows whose width is a multiple of the 16-byte piece and at most
+// 64 x 8 pieces stay in registers between the two passes; other widths read
+// the row again (it is still in cache).
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(long M, int D, const T *x, const float *w, float eps, T *out)
+{
+    constexpr int N = Piece<T>::N, MAXP = 8;
+    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= M) return;
+    const T *xr = x + row * D;
+    T *orow = out + row * D;
+    float ss = 0.0f;
+    if (D % N == 0 && D <= 64 * N * MAXP) {
+        const int np = D / N;
+        float v[MAXP][N];
+#pragma unroll
+        for (int k = 0; k < MAXP; ++k) {
+            const int pc = lane + 64 * k;
+            if (pc < np) {
+                Piece<T>::load(xr + pc * N, v[k]);
+#pragma unroll
+                for (int i = 0; i < N; ++i) ss = fmaf(v[k][i], v[k][i], ss);
+            }
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+        const float r = 1.0f / sqrtf(ss / (float)D + eps);
+#pragma unroll
+        for (int k = 0; k < MAXP; ++k) {
+            const int pc = lane + 64 * k;
+            if (pc < np) {
+                float o[N];
+#pragma unroll
+                for (int i = 0; i < N; ++i) o[i] = v[k][i] * r * (1.0f + w[pc * N + i]);
+                Piece<T>::store(orow + pc * N, o);
+            }
+        }
+        return;
+    }
+    for (int d = lane; d < D; d += 64) {
+        const float v = to_f32(xr[d]);
+        ss = fmaf(v, v, ss);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+    const float r = 1.0f / sqrtf(ss / (float)D + eps);
+    for (int d = lane; d < D; d += 64) orow[d] = from_f32<T>(to_f32(xr[d]) * r * (1.0f + w[d]));
+}
+
+// g <- GELU_tanh(g) * u, in place, one 16-byte piece per thread (the width is
+// a multiple of a piece; the tail thread-range covers the rest element-wise).
+// GELU_tanh(v) = v sigma(2 sqrt(2/pi)(v + 0.044715 v^3)): the tanh form
+// rewritten through 1 + tanh(a) = 2 sigma(2a), which has no cancellation for
+// negative v.
+__device__ __forceinline__ float gelu_tanh(float v)
+{
+    const float a2 = 1.5957691216057308f * fmaf(0.044715f * v, v * v, v);   // 2 sqrt(2/pi) (v + 0.044715 v^3)
+    return v * hw_rcp(1.0f + hw_exp2(-a2 * LOG2E));
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void gelu_tanh_mul_kernel(long n, T *g, const T *u)
+{
+    constexpr int N = Piece<T>::N;
+    const long i = ((long)blockIdx.x * 256 + threadIdx.x) * N;
+    if (i + N <= n) {
+        float gv[N], uv[N];
+        Piece<T>::load(g + i, gv);
+        Piece<T>::load(u + i, uv);
+#pragma unroll
+        for (int k = 0; k < N; ++k) gv[k] = gelu_tanh(gv[k]) * uv[k];
+        Piece<T>::store(g + i, gv);
+    } else {
+        for (long k = i; k < n; ++k) g[k] = from_f32<T>(gelu_tanh(to_f32(g[k])) * to_f32(u[k]));
+    }
+}
 
 }  // namespace
 
@@ -71,9 +191,12 @@ BlockLayout block_layout(int64_t B, int64_t T, int64_t D, size_t esz)
     return L;
 }
 
-int launch_block_fwd(const rglru_desc &d, int64_t d_model, const rglru_weights &w, const rglru_block &blk,
-                     const void *x, const void *hist_in, const float *h0, void *out, float *h_last,
-                     void *hist_out, void *ws, hipStream_t s)
+namespace {
+
+// out = block(x) (+ residual when given: the proj_out GEMM adds it)
+int block_core(const rglru_desc &d, int64_t d_model, const rglru_weights &w, const rglru_block &blk,
+               const void *x, const void *hist_in, const float *h0, void *out, const void *residual,
+               float *h_last, void *hist_out, void *ws, hipStream_t s)
 {
     const size_t esz = d.io == RGLRU_BF16 ? 2 : 4;
     const BlockLayout L = block_layout(d.B, d.T, d.D, esz);
@@ -95,7 +218,85 @@ int launch_block_fwd(const rglru_desc &d, int64_t d_model, const rglru_weights &
         std::lock_guard<std::mutex> lock(blas_mu);
         rocblas_handle h = blas_handle_locked(dev);
         if (!h || rocblas_set_stream(h, s) != rocblas_status_success) return RGLRU_ERR_BLAS;
-        if (!gemm_xwt(h, d.io, M, d_model, d.D, b2, blk.proj_out, out)) return RGLRU_ERR_BLAS;
+        const bool ok = residual ? gemm_xwt_add(h, d.io, M, d_model, d.D, b2, blk.proj_out, residual, out)
+                                 : gemm_xwt(h, d.io, M, d_model, d.D, b2, blk.proj_out, out);
+        if (!ok) return RGLRU_ERR_BLAS;
+    }
+    return RGLRU_OK;
+}
+
+}  // namespace
+
+int launch_block_fwd(const rglru_desc &d, int64_t d_model, const rglru_weights &w, const rglru_block &blk,
+                     const void *x, const void *hist_in, const float *h0, void *out, float *h_last,
+                     void *hist_out, void *ws, hipStream_t s)
+{
+    return block_core(d, d_model, w, blk, x, hist_in, h0, out, nullptr, h_last, hist_out, ws, s);
+}
+
+LayerLayout layer_layout(int64_t B, int64_t T, int64_t D, int64_t d_model, int64_t d_ff, size_t esz)
+{
+    LayerLayout L;
+    L.block = 0;
+    const size_t act = round256((size_t)B * T * d_model * esz), ff = round256((size_t)B * T * d_ff * esz);
+    L.xn = block_layout(B, T, D, esz).bytes;
+    L.xt = L.xn + act;
+    L.g = L.xt + act;
+    L.u = L.g + ff;
+    L.bytes = L.u + ff;
+    return L;
+}
+
+int launch_layer_fwd(const rglru_desc &d, int64_t d_model, const rglru_weights &w, const rglru_block &blk,
+                     const rglru_layer &lw, const void *x, const void *hist_in, const float *h0, void *y,
+                     float *h_last, void *hist_out, void *ws, hipStream_t s)
+{
+    const size_t esz = d.io == RGLRU_BF16 ? 2 : 4;
+    const LayerLayout L = layer_layout(d.B, d.T, d.D, d_model, lw.d_ff, esz);
+    char *base = (char *)ws;
+    void *xn = base + L.xn, *xt = base + L.xt, *g = base + L.g, *u = base + L.u;
+    const long M = d.B * d.T;
+    const unsigned rows_grid = (unsigned)((M + 3) / 4);
+    const long nff = M * lw.d_ff;
+    const long pieces = (nff + (long)(16 / esz) - 1) / (long)(16 / esz);
+    const unsigned ff_grid = (unsigned)((pieces + 255) / 256);
+    // x~ = x + block(RMSNorm(x))
+    if (d.io == RGLRU_BF16)
+        rmsnorm_kernel<bf16><<<rows_grid, 256, 0, s>>>(M, (int)d_model, (const bf16 *)x, lw.tnorm_w, lw.eps,
+                                                        (bf16 *)xn);
+    else
+        rmsnorm_kernel<float><<<rows_grid, 256, 0, s>>>(M, (int)d_model, (const float *)x, lw.tnorm_w, lw.eps,
+                                                         (float *)xn);
+    if (hipGetLastError() != hipSuccess) return RGLRU_ERR_LAUNCH;
+    int st = block_core(d, d_model, w, blk, xn, hist_in, h0, xt, x, h_last, hist_out, base + L.block, s);
+    if (st) return st;
+    // y = x~ + MLP(RMSNorm(x~))
+    if (d.io == RGLRU_BF16)
+        rmsnorm_kernel<bf16><<<rows_grid, 256, 0, s>>>(M, (int)d_model, (const bf16 *)xt, lw.cnorm_w, lw.eps,
+                                                        (bf16 *)xn);
+    else
+        rmsnorm_kernel<float><<<rows_grid, 256, 0, s>>>(M, (int)d_model, (const float *)xt, lw.cnorm_w, lw.eps,
+                                                         (float *)xn);
+    if (hipGetLastError() != hipSuccess) return RGLRU_ERR_LAUNCH;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return RGLRU_ERR_LAUNCH;
+    {
+        std::lock_guard<std::mutex> lock(blas_mu);
+        rocblas_handle h = blas_handle_locked(dev);
+        if (!h || rocblas_set_stream(h, s) != rocblas_status_success) return RGLRU_ERR_BLAS;
+        if (!gemm_xwt(h, d.io, M, lw.d_ff, d_model, xn, lw.gate_w, g)) return RGLRU_ERR_BLAS;
+        if (!gemm_xwt(h, d.io, M, lw.d_ff, d_model, xn, lw.up_w, u)) return RGLRU_ERR_BLAS;
+    }
+    if (d.io == RGLRU_BF16)
+        gelu_tanh_mul_kernel<bf16><<<ff_grid, 256, 0, s>>>(nff, (bf16 *)g, (const bf16 *)u);
+    else
+        gelu_tanh_mul_kernel<float><<<ff_grid, 256, 0, s>>>(nff, (float *)g, (const float *)u);
+    if (hipGetLastError() != hipSuccess) return RGLRU_ERR_LAUNCH;
+    {
+        std::lock_guard<std::mutex> lock(blas_mu);
+        rocblas_handle h = blas_handle_locked(dev);
+        if (!h || rocblas_set_stream(h, s) != rocblas_status_success) return RGLRU_ERR_BLAS;
+        if (!gemm_xwt_add(h, d.io, M, d_model, lw.d_ff, g, lw.down_w, xt, y)) return RGLRU_ERR_BLAS;
     }
     return RGLRU_OK;
 }

@@ -50,6 +50,17 @@ int launch_block_fwd(const rglru_desc &d, int64_t d_model, const rglru_weights &
                      const void *x, const void *hist_in, const float *h0, void *out, float *h_last,
                      void *hist_out, void *ws, hipStream_t s);
 
+// Residual layer (block.hip): byte offsets of its workspace -- the block's
+// workspace, the normed input xn, the residual stream x~, the MLP's gate and
+// up activations -- and the whole size
+struct LayerLayout {
+    size_t block, xn, xt, g, u, bytes;
+};
+LayerLayout layer_layout(int64_t B, int64_t T, int64_t D, int64_t d_model, int64_t d_ff, size_t esz);
+int launch_layer_fwd(const rglru_desc &d, int64_t d_model, const rglru_weights &w, const rglru_block &blk,
+                     const rglru_layer &lw, const void *x, const void *hist_in, const float *h0, void *y,
+                     float *h_last, void *hist_out, void *ws, hipStream_t s);
+
 // local sliding-window MQA (attn.hip)
 bool attn_fast_prefill(const rglru_attn_desc &d);
 bool attn_fast_step(const rglru_attn_desc &d);

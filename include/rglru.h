@@ -226,6 +226,41 @@ int rglru_block_fwd(const rglru_desc *desc, int64_t d_model, const rglru_weights
                     void *out, float *h_last, void *hist_out, void *ws, size_t ws_bytes,
                     hipStream_t stream);
 
+/* Residual layer with the recurrent block as temporal mixer (a Hawk layer):
+ * the pre-norm scaffold of the wiki note "Griffin", section "Residual Block
+ * View", with the norms and MLP of the module page
+ * "transformer_lens.model_bridge.supported_architectures.recurrent_gemma",
+ * "Architecture overview":
+ *     x~ = x + block(RMSNorm_t(x))                  (rglru_block_fwd's block)
+ *     y  = x~ + down(GELU_tanh(gate RMSNorm_c(x~)) * (up RMSNorm_c(x~)))
+ * RMSNorm(v) = v / sqrt(mean v^2 + eps) * (1 + weight); GELU_tanh(v) = v/2
+ * (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))); no biases. */
+typedef struct {
+    const float *tnorm_w;   /* [d_model] fp32, temporal pre-norm weight     */
+    const float *cnorm_w;   /* [d_model] fp32, channel pre-norm weight      */
+    const void *gate_w;     /* [d_ff][d_model] io                           */
+    const void *up_w;       /* [d_ff][d_model] io                           */
+    const void *down_w;     /* [d_model][d_ff] io                           */
+    int64_t d_ff;           /* MLP width, >= 1                              */
+    float eps;              /* RMSNorm epsilon, finite and >= 0             */
+} rglru_layer;
+
+/* Workspace bytes of rglru_layer_fwd: the block's workspace (same rules:
+ * ZERO-FILLED before first use, reused only for the same shapes) followed by
+ * the normed input, the residual stream and the MLP's two activations. */
+int rglru_layer_workspace_size(const rglru_desc *desc, int64_t d_model, const rglru_layer *lw, size_t *bytes);
+
+/* Residual-layer forward.  x, y [B][T][d_model] (io); h0, h_last, hist_in,
+ * hist_out (nullable) are the recurrent block's state and conv history.
+ * Stored intermediates (the normed inputs, b1, b2, the merged product, x~,
+ * the MLP activations) are rounded to io; every sum is fp32.  Five rocBLAS
+ * GEMMs (the residual adds ride the beta of proj_out and down), two RMSNorm
+ * launches, the fused forward with the GeLU merge and one GELU-tanh product
+ * launch.  Same shape limits and errors as rglru_block_fwd, plus d_ff. */
+int rglru_layer_fwd(const rglru_desc *desc, int64_t d_model, const rglru_weights *w, const rglru_block *blk,
+                    const rglru_layer *lw, const void *x, const void *hist_in, const float *h0, void *y,
+                    float *h_last, void *hist_out, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Local sliding-window multi-query attention, Griffin's other temporal mixer
  * (wiki note "Griffin", section "Local Attention Path": token t attends to the

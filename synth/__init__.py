@@ -55,7 +55,8 @@ _THREADS = max(1, min(16, os.cpu_count() or 1))
 TID = dict(u=0, conv_w=1, conv_b=2, W_a=3, W_x=4, lam_u=5, dy=6, h0=7,
            b_a=8, b_x=9, hist=10, dh_last=11,
            block_x=12, proj_in_1=13, proj_in_2=14, proj_out=15,
-           attn_q=16, attn_k=17, attn_v=18, attn_hk=19, attn_hv=20)
+           attn_q=16, attn_k=17, attn_v=18, attn_hk=19, attn_hv=20,
+           tnorm_w=21, cnorm_w=22, gate_w=23, up_w=24, down_w=25)
 
 C_CONST = 8.0
 
@@ -245,3 +246,24 @@ def make_block_params(cfg: int, d_model: int, D: int, io: str) -> BlockParams:
     p2 = store(s_in * normal(seed_for(cfg, "proj_in_2"), 0, D * d_model), io).reshape(D, d_model)
     po = store(s_out * normal(seed_for(cfg, "proj_out"), 0, d_model * D), io).reshape(d_model, D)
     return BlockParams(p1, p2, po)
+
+
+@dataclasses.dataclass
+class LayerParams:
+    """Residual-layer weights around the block: pre-norm weights [d_model] fp32
+    (applied as 1 + w), gated MLP gate_w, up_w [d_ff][d_model], down_w
+    [d_model][d_ff] in the io form."""
+    tnorm_w: np.ndarray
+    cnorm_w: np.ndarray
+    gate_w: np.ndarray
+    up_w: np.ndarray
+    down_w: np.ndarray
+
+
+def make_layer_params(cfg: int, d_model: int, d_ff: int, io: str) -> LayerParams:
+    tn = store(0.1 * normal(seed_for(cfg, "tnorm_w"), 0, d_model), "f32")
+    cn = store(0.1 * normal(seed_for(cfg, "cnorm_w"), 0, d_model), "f32")
+    g = store(normal(seed_for(cfg, "gate_w"), 0, d_ff * d_model) / math.sqrt(d_model), io).reshape(d_ff, d_model)
+    u = store(normal(seed_for(cfg, "up_w"), 0, d_ff * d_model) / math.sqrt(d_model), io).reshape(d_ff, d_model)
+    dn = store(normal(seed_for(cfg, "down_w"), 0, d_model * d_ff) / math.sqrt(d_ff), io).reshape(d_model, d_ff)
+    return LayerParams(tn, cn, g, u, dn)

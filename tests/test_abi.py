@@ -224,3 +224,27 @@ def test_attn_validation(L):
     assert g(ctypes.byref(adesc()), q, k, v, kc, vc, None, o, ws, n.value, s) == ENULL
     assert g(ctypes.byref(adesc()), q, k, v, kc, vc, pos + 2, o, ws, n.value, s) == EALIGN
     assert g(ctypes.byref(adesc()), q, k, v, kc, kc, pos, o, ws, n.value, s) == EARG   # caches overlap
+
+
+def test_layer_validation(L):
+    d = desc()
+    dm = 384
+    lw = glr._Layer(P + 0x6000000, P + 0x6100000, P + 0x7000000, P + 0x8000000, P + 0x9000000, 1024, 1e-6)
+    n = ctypes.c_size_t()
+    assert L.rglru_layer_workspace_size(ctypes.byref(d), dm, ctypes.byref(lw), ctypes.byref(n)) == OK
+    nb, _ = block_ws_size(d, dm)[1], None
+    assert n.value > nb
+    bad = glr._Layer(P, P, P, P, P, 0, 1e-6)
+    assert L.rglru_layer_workspace_size(ctypes.byref(d), dm, ctypes.byref(bad), ctypes.byref(n)) == ESHAPE
+    bad = glr._Layer(P, P, P, P, P, 64, float("nan"))
+    assert L.rglru_layer_workspace_size(ctypes.byref(d), dm, ctypes.byref(bad), ctypes.byref(n)) == EARG
+    w = weights()
+    blk = glr._Block(P + 0x3000000, P + 0x4000000, P + 0x5000000)
+    x, y, ws = P + 0x1000000, P + 0x2000000, P + 0x100000000
+    f = L.rglru_layer_fwd
+    assert f(ctypes.byref(d), dm, ctypes.byref(w), ctypes.byref(blk), None, x, None, None, y, None, None, ws,
+             n.value, None) == ENULL
+    assert f(ctypes.byref(d), dm, ctypes.byref(w), ctypes.byref(blk), ctypes.byref(lw), x, None, None, y, None,
+             None, ws, n.value - 1, None) == EWS
+    assert f(ctypes.byref(d), dm, ctypes.byref(w), ctypes.byref(blk), ctypes.byref(lw), x, None, None, x + 16,
+             None, None, ws, n.value, None) == EARG
