@@ -20,9 +20,15 @@
 // inputs, fp32 accumulation, bf16 output for bf16 I/O; fp32 throughout for
 // fp32 I/O).  Workspace: the scan's carries first (its header must start out
 // zero), then b1 and b2.
+// the solution listing (rocblas_gemm_ex_get_solutions) is in rocBLAS's beta API
+#define ROCBLAS_BETA_FEATURES_API
+#define ROCBLAS_NO_DEPRECATED_WARNINGS
 #include <rocblas/rocblas.h>
 
+#include <map>
 #include <mutex>
+#include <tuple>
+#include <vector>
 
 #include "common.h"
 #include "internal.h"
@@ -45,27 +51,96 @@ rocblas_handle blas_handle_locked(int dev)
     return blas_handles[dev];
 }
 
-// Y[M][N] = X[M][K] W[N][K]^T, all row-major.  Column-major, that is
-// Y^T (N x M, ld N) = W^T (op T of the K x N array W, ld K) * X^T (K x M, ld K).
-bool gemm_xwt(rocblas_handle h, int io, int64_t M, int64_t N, int64_t K, const void *X, const void *W,
-              void *Y)
+// Y[M][N] = X[M][K] W[N][K]^T (+ R[M][N] when R is given, through beta = 1),
+// all row-major.  Column-major, that is Y^T (N x M, ld N) = W^T (op T of the
+// K x N array W, ld K) * X^T (K x M, ld K) (+ R^T).
+//
+// Solution choice: the first product of a shape on a device runs every
+// solution the library lists for it (one warm-up and three timed runs each,
+// on the caller's stream, waiting for them on the host) and keeps the fastest
+// for that shape; the library's default is one of the candidates.
+struct GemmKey {
+    int dev, io, add;
+    int64_t M, N, K;
+    bool operator<(const GemmKey &o) const
+    {
+        return std::tie(dev, io, add, M, N, K) < std::tie(o.dev, o.io, o.add, o.M, o.N, o.K);
+    }
+};
+std::map<GemmKey, int> best_solution;   // guarded by blas_mu
+
+rocblas_status gemm_call(rocblas_handle h, int io, int64_t M, int64_t N, int64_t K, const void *X, const void *W,
+                         const void *R, void *Y, int sol)
 {
     const rocblas_datatype t = io == RGLRU_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
-    const float alpha = 1.0f, beta = 0.0f;
-    return rocblas_gemm_ex_64(h, rocblas_operation_transpose, rocblas_operation_none, N, M, K, &alpha, W,
-                              t, K, X, t, K, &beta, Y, t, N, Y, t, N, rocblas_datatype_f32_r,
-                              rocblas_gemm_algo_standard, 0, 0) == rocblas_status_success;
+    const float alpha = 1.0f, beta = R ? 1.0f : 0.0f;
+    const void *C = R ? R : Y;
+    return rocblas_gemm_ex(h, rocblas_operation_transpose, rocblas_operation_none, (rocblas_int)N,
+                           (rocblas_int)M, (rocblas_int)K, &alpha, W, t, (rocblas_int)K, X, t, (rocblas_int)K, &beta,
+                           C, t, (rocblas_int)N, Y, t, (rocblas_int)N, rocblas_datatype_f32_r,
+                           sol ? rocblas_gemm_algo_solution_index : rocblas_gemm_algo_standard, sol, 0);
 }
 
-// Y[M][N] = X[M][K] W[N][K]^T + R[M][N] (the residual add rides the GEMM's beta)
-bool gemm_xwt_add(rocblas_handle h, int io, int64_t M, int64_t N, int64_t K, const void *X, const void *W,
-                  const void *R, void *Y)
+int pick_solution(rocblas_handle h, hipStream_t s, int dev, int io, int64_t M, int64_t N, int64_t K,
+                  const void *X, const void *W, const void *R, void *Y)
 {
+    const GemmKey key{dev, io, R ? 1 : 0, M, N, K};
+    auto it = best_solution.find(key);
+    if (it != best_solution.end()) return it->second;
     const rocblas_datatype t = io == RGLRU_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
-    const float alpha = 1.0f, beta = 1.0f;
-    return rocblas_gemm_ex_64(h, rocblas_operation_transpose, rocblas_operation_none, N, M, K, &alpha, W, t, K,
-                              X, t, K, &beta, R, t, N, Y, t, N, rocblas_datatype_f32_r,
-                              rocblas_gemm_algo_standard, 0, 0) == rocblas_status_success;
+    const float alpha = 1.0f, beta = R ? 1.0f : 0.0f;
+    const void *C = R ? R : Y;
+    rocblas_int n = 0;
+    std::vector<rocblas_int> cand;
+    if (rocblas_gemm_ex_get_solutions(h, rocblas_operation_transpose, rocblas_operation_none, (rocblas_int)N,
+                                      (rocblas_int)M, (rocblas_int)K, &alpha, W, t, (rocblas_int)K, X, t,
+                                      (rocblas_int)K, &beta, C, t, (rocblas_int)N, Y, t, (rocblas_int)N,
+                                      rocblas_datatype_f32_r, rocblas_gemm_algo_solution_index, 0, nullptr,
+                                      &n) == rocblas_status_success &&
+        n > 0) {
+        cand.resize(n);
+        if (rocblas_gemm_ex_get_solutions(h, rocblas_operation_transpose, rocblas_operation_none, (rocblas_int)N,
+                                          (rocblas_int)M, (rocblas_int)K, &alpha, W, t, (rocblas_int)K, X, t,
+                                          (rocblas_int)K, &beta, C, t, (rocblas_int)N, Y, t, (rocblas_int)N,
+                                          rocblas_datatype_f32_r, rocblas_gemm_algo_solution_index, 0,
+                                          cand.data(), &n) != rocblas_status_success)
+            cand.clear();
+        else
+            cand.resize(n);
+    }
+    int best = 0;
+    float best_ms = -1.0f;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
+        cand.insert(cand.begin(), 0);   // the library's default choice
+        for (const rocblas_int sol : cand) {
+            if (gemm_call(h, io, M, N, K, X, W, R, Y, sol) != rocblas_status_success) continue;
+            (void)hipEventRecord(e0, s);
+            bool ok = true;
+            for (int r = 0; r < 3 && ok; ++r) ok = gemm_call(h, io, M, N, K, X, W, R, Y, sol) == rocblas_status_success;
+            (void)hipEventRecord(e1, s);
+            float ms = 0.0f;
+            if (!ok || hipEventSynchronize(e1) != hipSuccess || hipEventElapsedTime(&ms, e0, e1) != hipSuccess)
+                continue;
+            if (best_ms < 0.0f || ms < best_ms) {
+                best_ms = ms;
+                best = sol;
+            }
+        }
+    }
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    (void)hipGetLastError();   // a candidate the runtime refused leaves no error behind
+    best_solution[key] = best;
+    return best;
+}
+
+// the product with the shape's chosen solution (blas_mu held, stream set)
+bool gemm_run(rocblas_handle h, hipStream_t s, int dev, int io, int64_t M, int64_t N, int64_t K, const void *X,
+              const void *W, const void *R, void *Y)
+{
+    const int sol = pick_solution(h, s, dev, io, M, N, K, X, W, R, Y);
+    return gemm_call(h, io, M, N, K, X, W, R, Y, sol) == rocblas_status_success;
 }
 
 size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -209,8 +284,8 @@ int block_core(const rglru_desc &d, int64_t d_model, const rglru_weights &w, con
         std::lock_guard<std::mutex> lock(blas_mu);
         rocblas_handle h = blas_handle_locked(dev);
         if (!h || rocblas_set_stream(h, s) != rocblas_status_success) return RGLRU_ERR_BLAS;
-        if (!gemm_xwt(h, d.io, M, d.D, d_model, x, blk.proj_in_1, b1)) return RGLRU_ERR_BLAS;
-        if (!gemm_xwt(h, d.io, M, d.D, d_model, x, blk.proj_in_2, b2)) return RGLRU_ERR_BLAS;
+        if (!gemm_run(h, s, dev, d.io, M, d.D, d_model, x, blk.proj_in_1, nullptr, b1)) return RGLRU_ERR_BLAS;
+        if (!gemm_run(h, s, dev, d.io, M, d.D, d_model, x, blk.proj_in_2, nullptr, b2)) return RGLRU_ERR_BLAS;
     }
     launch_scan_fwd_merge(d, w, b1, b2, hist_in, h0, b2, h_last, hist_out, base + L.scan, s);
     if (hipGetLastError() != hipSuccess) return RGLRU_ERR_LAUNCH;
@@ -218,9 +293,7 @@ int block_core(const rglru_desc &d, int64_t d_model, const rglru_weights &w, con
         std::lock_guard<std::mutex> lock(blas_mu);
         rocblas_handle h = blas_handle_locked(dev);
         if (!h || rocblas_set_stream(h, s) != rocblas_status_success) return RGLRU_ERR_BLAS;
-        const bool ok = residual ? gemm_xwt_add(h, d.io, M, d_model, d.D, b2, blk.proj_out, residual, out)
-                                 : gemm_xwt(h, d.io, M, d_model, d.D, b2, blk.proj_out, out);
-        if (!ok) return RGLRU_ERR_BLAS;
+        if (!gemm_run(h, s, dev, d.io, M, d_model, d.D, b2, blk.proj_out, residual, out)) return RGLRU_ERR_BLAS;
     }
     return RGLRU_OK;
 }
@@ -284,8 +357,8 @@ int launch_layer_fwd(const rglru_desc &d, int64_t d_model, const rglru_weights &
         std::lock_guard<std::mutex> lock(blas_mu);
         rocblas_handle h = blas_handle_locked(dev);
         if (!h || rocblas_set_stream(h, s) != rocblas_status_success) return RGLRU_ERR_BLAS;
-        if (!gemm_xwt(h, d.io, M, lw.d_ff, d_model, xn, lw.gate_w, g)) return RGLRU_ERR_BLAS;
-        if (!gemm_xwt(h, d.io, M, lw.d_ff, d_model, xn, lw.up_w, u)) return RGLRU_ERR_BLAS;
+        if (!gemm_run(h, s, dev, d.io, M, lw.d_ff, d_model, xn, lw.gate_w, nullptr, g)) return RGLRU_ERR_BLAS;
+        if (!gemm_run(h, s, dev, d.io, M, lw.d_ff, d_model, xn, lw.up_w, nullptr, u)) return RGLRU_ERR_BLAS;
     }
     if (d.io == RGLRU_BF16)
         gelu_tanh_mul_kernel<bf16><<<ff_grid, 256, 0, s>>>(nff, (bf16 *)g, (const bf16 *)u);
@@ -296,7 +369,7 @@ int launch_layer_fwd(const rglru_desc &d, int64_t d_model, const rglru_weights &
         std::lock_guard<std::mutex> lock(blas_mu);
         rocblas_handle h = blas_handle_locked(dev);
         if (!h || rocblas_set_stream(h, s) != rocblas_status_success) return RGLRU_ERR_BLAS;
-        if (!gemm_xwt_add(h, d.io, M, d_model, lw.d_ff, g, lw.down_w, xt, y)) return RGLRU_ERR_BLAS;
+        if (!gemm_run(h, s, dev, d.io, M, d_model, lw.d_ff, g, lw.down_w, xt, y)) return RGLRU_ERR_BLAS;
     }
     return RGLRU_OK;
 }

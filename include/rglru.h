@@ -22,9 +22,12 @@
  * Pointers.  Every tensor pointer is DEVICE memory owned by the caller.  The
  *   library never synchronises the host: a return of RGLRU_OK means the work
  *   was enqueued on `stream`.  It allocates nothing and keeps no global state,
- *   with one exception: rglru_block_fwd creates one rocBLAS handle per device
- *   on its first call there (rocBLAS allocates its own device memory) and
- *   keeps it until the process ends.
+ *   with one exception: rglru_block_fwd and rglru_layer_fwd create one rocBLAS
+ *   handle per device on their first call there (rocBLAS allocates its own
+ *   device memory) and keep it until the process ends; and the first product
+ *   of each GEMM shape on a device times every solution rocBLAS lists for it
+ *   (on the caller's stream, waiting on the host) and keeps the fastest, so
+ *   that first call blocks until the timing runs are done.
  * Layouts.  Row-major, channel fastest:
  *     activations u, x, r, i, y, dy, du   [B][T][D]   (dtype desc->io)
  *     conv history hist                   [B][3][D]   (dtype desc->io)
