@@ -193,3 +193,18 @@ def test_decode_full_size_sampled():
                                okc, ovc, starts[b:b + 1], 1.0 / 16)
         _cmp(f"o_t[{b}]", o[b:b + 1], ref, TOL["bf16"])
         assert np.array_equal(from_dev(kc[b:b + 1]), okc)
+
+
+@pytest.mark.parametrize("io,dh", [("bf16", 256), ("f32", 32)])
+def test_prefill_single_token_and_ring_fill(io, dh):
+    # T = 1 and T < W: o equals v for the lone token; the ring receives it in slot 0
+    B, Hq, W = 3, 4, 16
+    q, k, v = _qkv(B, 1, Hq, dh, io, tag=6)
+    dt = torch.bfloat16 if io == "bf16" else torch.float32
+    kc = torch.zeros((B, W, dh), dtype=dt, device=DEV)
+    vc = torch.zeros_like(kc)
+    o = glr.attn_fwd(to_dev(q, DEV), to_dev(k, DEV), to_dev(v, DEV), W, dh ** -0.5, kcache=kc, vcache=vc)
+    torch.cuda.synchronize()
+    _cmp("o", from_dev(o), np.repeat(synth.widen(v)[:, :, None, :], Hq, axis=2), TOL[io])
+    assert np.array_equal(from_dev(kc[:, 0]), synth.widen(k[:, 0]))
+    assert np.all(from_dev(kc[:, 1:]) == 0.0)

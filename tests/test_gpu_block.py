@@ -149,3 +149,13 @@ def test_block_projection_weights_in_one_buffer(swap):
     ro, rh, _ = _oracle_block(prob, bp, x, 0, 1)
     _cmp(f"out (swap={swap})", from_dev(out), ro, TOL["f32"])
     _cmp(f"h_last (swap={swap})", from_dev(hl), rh, TOL["f32"])
+
+
+def test_block_single_token_with_state():
+    # T = 1: the conv reads only the history; one chunk of one token
+    prob, bp, x = _block_setup(0, 3, 1, 64, with_state=True)
+    out, hl, ho = _run(prob, bp, x, True)
+    ro, rh, rhist = _oracle_block(prob, bp, x, 0, 3, with_state=True)
+    _cmp("out", out, ro, TOL["f32"])
+    _cmp("h_last", hl, rh, TOL["f32"])
+    _cmp("hist_out", ho, rhist, TOL["f32"])
