@@ -178,90 +178,105 @@ __global__ __launch_bounds__(256) void attn_fill_cache(int B, int T_, int W, int
 }
 
 // ------------------------------------------------------------ MFMA prefill
-constexpr int PF_ROWS = 128;            // flattened (token, head) rows per workgroup (8 waves x 16)
-constexpr int PF_KEYS = 64;             // keys per tile
-constexpr int PF_KSTRIDE = 264;         // bf16 per K row in LDS (528 B, conflict-free b128 reads)
-constexpr int PF_VSTRIDE = 72;          // bf16 per V^T row (144 B, conflict-free b128 reads)
-constexpr int PF_KBYTES = PF_KEYS * PF_KSTRIDE * 2;   // 33,792
-constexpr int PF_VBYTES = 256 * PF_VSTRIDE * 2;       // 36,864
-constexpr int PF_STAGE = PF_KBYTES + PF_VBYTES;
-constexpr int PF_LDS = 2 * PF_STAGE;                  // 141,312
-
-// The staged pieces of one key tile.  Threads 0..255 carry 8 pieces (128 B)
-// of one K row; threads 256..511 a block of 8 keys x 8 dh of V, transposed in
-// registers before the LDS write so that V^T rows hold consecutive keys.
-// Lane-to-block maps keep each 16-lane group's LDS writes in distinct banks.
-struct PfStage {
-    u32x4 kp[8];
-    u32x4 vp[8];
+// A workgroup of NW waves owns 16 NW flattened (token, head) rows and walks its
+// windows' keys in tiles of KT (32 or 64).
+constexpr int PF_KSTRIDE = 264;   // bf16 per K row in LDS (528 B, conflict-free b128 reads)
+template <int KT> struct PfTile {
+    static constexpr int VSTRIDE = KT + 8;                 // bf16 per V^T row
+    static constexpr int KBYTES = KT * PF_KSTRIDE * 2;
+    static constexpr int VBYTES = 256 * VSTRIDE * 2;
+    static constexpr int STAGE = KBYTES + VBYTES;
+    static constexpr int LDS = 2 * STAGE;
 };
 
+// The staged pieces of one key tile.  The first half of the threads carry 8
+// pieces (128 B) of one K row each, the second half a block of 8 keys x 8 dh
+// of V, transposed in registers before the LDS write so that V^T rows hold
+// consecutive keys.
+// (one array for both halves: separate ones would meet at the branch join
+// as copies that wait for the loads)
+struct PfStage {
+    u32x4 r[8];
+};
+
+template <int NW, int KT>
 __device__ __forceinline__ void pf_load(PfStage &st, const bf16 *k, const bf16 *v, long kv0, int key0, int T_,
                                         int tid)
 {
-    if (tid < 256) {
+    constexpr int HALF = 32 * NW;
+    // the split is by whole waves; a scalar branch keeps each wave on one side
+    // (with both sides under an exec mask the two register sets alias and
+    // every load would be waited for at once)
+    if (__builtin_amdgcn_readfirstlane(tid >> 6) < NW / 2) {
+        // keys past the end read the last row instead: real, finite values
+        // whose weights the mask makes 0 (loads stay unconditional, so no
+        // branch makes the wave wait for them here)
         const int row = tid >> 2, seg = tid & 3;   // 64 dh per thread
         const int key = key0 + row;
-        const u32x4 *src = (const u32x4 *)(k + (kv0 + (key < T_ ? key : 0)) * 256 + 64 * seg);
+        const u32x4 *src = (const u32x4 *)(k + (kv0 + (key < T_ ? key : T_ - 1)) * 256 + 64 * seg);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) st.kp[i] = key < T_ ? src[i] : u32x4{0, 0, 0, 0};
+        for (int i = 0; i < 8; ++i) st.r[i] = src[i];
     } else {
-        const int t2 = tid - 256, kg = t2 & 7, dg = t2 >> 3;   // keys 8kg.., dh 8dg..
+        const int t2 = tid - HALF, kg = t2 % (KT / 8), dg = t2 / (KT / 8);   // keys 8kg.., dh 8dg..
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int key = key0 + 8 * kg + i;
-            const u32x4 *src = (const u32x4 *)(v + (kv0 + (key < T_ ? key : 0)) * 256 + 8 * dg);
-            st.vp[i] = key < T_ ? *src : u32x4{0, 0, 0, 0};
+            st.r[i] = *(const u32x4 *)(v + (kv0 + (key < T_ ? key : T_ - 1)) * 256 + 8 * dg);
         }
     }
 }
 
+template <int NW, int KT>
 __device__ __forceinline__ void pf_store(const PfStage &st, char *stage, int tid)
 {
-    if (tid < 256) {
+    constexpr int HALF = 32 * NW;
+    if (__builtin_amdgcn_readfirstlane(tid >> 6) < NW / 2) {
         const int row = tid >> 2, seg = tid & 3;
         // key 32j + 8a + 4u + i goes to LDS row 32j + 16u + 4a + i, so that the
         // 16 keys one score tile reads together sit in 16 consecutive rows
         const int lrow = (row & 0x23) | ((row & 0x4) << 2) | ((row & 0x18) >> 1);
         u32x4 *dst = (u32x4 *)(stage + (lrow * PF_KSTRIDE + 64 * seg) * 2);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dst[i] = st.kp[i];
+        for (int i = 0; i < 8; ++i) dst[i] = st.r[i];
     } else {
-        const int t2 = tid - 256, kg = t2 & 7, dg = t2 >> 3;
-        // vp[i] holds key 8kg+i, dh 8dg..8dg+7 (dword c = dh pair 2c, 2c+1);
+        const int t2 = tid - HALF, kg = t2 % (KT / 8), dg = t2 / (KT / 8);
+        // r[i] holds key 8kg+i, dh 8dg..8dg+7 (dword c = dh pair 2c, 2c+1);
         // V^T row 8dg + j receives keys 8kg..8kg+7 of dh 8dg + j
-        char *vt = stage + PF_KBYTES;
+        char *vt = stage + PfTile<KT>::KBYTES;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
             const int c = j >> 1;
             u32x4 o;
-            o[0] = __builtin_amdgcn_perm(st.vp[1][c], st.vp[0][c], sel);
-            o[1] = __builtin_amdgcn_perm(st.vp[3][c], st.vp[2][c], sel);
-            o[2] = __builtin_amdgcn_perm(st.vp[5][c], st.vp[4][c], sel);
-            o[3] = __builtin_amdgcn_perm(st.vp[7][c], st.vp[6][c], sel);
-            *(u32x4 *)(vt + ((8 * dg + j) * PF_VSTRIDE + 8 * kg) * 2) = o;
+            o[0] = __builtin_amdgcn_perm(st.r[1][c], st.r[0][c], sel);
+            o[1] = __builtin_amdgcn_perm(st.r[3][c], st.r[2][c], sel);
+            o[2] = __builtin_amdgcn_perm(st.r[5][c], st.r[4][c], sel);
+            o[3] = __builtin_amdgcn_perm(st.r[7][c], st.r[6][c], sel);
+            *(u32x4 *)(vt + ((8 * dg + j) * PfTile<KT>::VSTRIDE + 8 * kg) * 2) = o;
         }
     }
 }
 
 // 16 query rows per wave on v_mfma_f32_16x16x32_bf16.  In the score tiles
-// (keys x queries, four of 16 keys per 64-key tile) A row r of tile st is key
+// (keys x queries, KT/16 of 16 keys per tile) A row r of tile st is key
 // 32(st/2) + 8(r/4) + 4(st%2) + r%4, so that lane (n, g) -- query n = lane%16,
-// g = lane/16 -- ends up with keys 32j + 8g .. +7 for j = 0, 1: exactly the
-// k-slots it supplies as the B operand of step j of O^T += V^T P^T, whose A
-// operand then reads 8 consecutive keys of a V^T row.
-__global__ __launch_bounds__(512) void attn_prefill_mfma(int T_, int Hq, int W, float scale_log2e,
-                                                         const bf16 *q, const bf16 *k, const bf16 *v, bf16 *o)
+// g = lane/16 -- ends up with keys 32j + 8g .. +7 of each 32-key step j:
+// exactly the k-slots it supplies as the B operand of step j of
+// O^T += V^T P^T, whose A operand then reads 8 consecutive keys of a V^T row.
+template <int NW, int KT>
+__global__ __launch_bounds__(64 * NW, 2) void attn_prefill_mfma(int T_, int Hq, int W, float scale_log2e,
+                                                             const bf16 *q, const bf16 *k, const bf16 *v, bf16 *o)
 {
+    constexpr int ROWS = 16 * NW, NST = KT / 16, NJ = KT / 32;
+    using TL = PfTile<KT>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int n = lane & 15, g = lane >> 4;
     const long rows_per_b = (long)T_ * Hq;
-    const long tiles_per_b = (rows_per_b + PF_ROWS - 1) / PF_ROWS;
+    const long tiles_per_b = (rows_per_b + ROWS - 1) / ROWS;
     const int b = (int)(blockIdx.x / tiles_per_b);
-    const long f0 = (blockIdx.x % tiles_per_b) * PF_ROWS;   // first flattened row of the workgroup
-    const long kv0 = (long)b * T_;                          // first key row of stream b
+    const long f0 = (blockIdx.x % tiles_per_b) * ROWS;   // first flattened row of the workgroup
+    const long kv0 = (long)b * T_;                       // first key row of stream b
 
     // this lane's query row
     const long f = f0 + 16 * wave + n;
@@ -275,10 +290,10 @@ __global__ __launch_bounds__(512) void attn_prefill_mfma(int T_, int Hq, int W, 
     }
 
     // keys of the union of the workgroup's windows
-    const long f_last = (f0 + PF_ROWS - 1 < rows_per_b ? f0 + PF_ROWS - 1 : rows_per_b - 1);
+    const long f_last = (f0 + ROWS - 1 < rows_per_b ? f0 + ROWS - 1 : rows_per_b - 1);
     const int t_first = (int)(f0 / Hq), t_last = (int)(f_last / Hq);
     const int k_lo = t_first - W + 1 < 0 ? 0 : t_first - W + 1;
-    const int tile0 = k_lo / PF_KEYS, tile1 = t_last / PF_KEYS;
+    const int tile0 = k_lo / KT, tile1 = t_last / KT;
 
     f32x4_t acc[16];
 #pragma unroll
@@ -286,41 +301,39 @@ __global__ __launch_bounds__(512) void attn_prefill_mfma(int T_, int Hq, int W, 
     float m = -INFINITY, l = 0.0f;
 
     // tile i is computed from LDS while tile i+1 is on its way from memory
-    // (the second wave of each SIMD covers the wait)
     PfStage st;
-    pf_load(st, k, v, kv0, tile0 * PF_KEYS, T_, tid);
-    pf_store(st, smem + (tile0 & 1) * PF_STAGE, tid);
+    pf_load<NW, KT>(st, k, v, kv0, tile0 * KT, T_, tid);
+    pf_store<NW, KT>(st, smem + (tile0 & 1) * TL::STAGE, tid);
     __syncthreads();
 
-    // A row of this lane in score tile st: key 32(st/2) + 8(n/4) + 4(st%2) + n%4,
-    // held in LDS row 32(st/2) + 16(st%2) + n
     for (int tile = tile0; tile <= tile1; ++tile) {
-        if (tile < tile1) pf_load(st, k, v, kv0, (tile + 1) * PF_KEYS, T_, tid);
-        const char *stage = smem + (tile & 1) * PF_STAGE;
+        if (tile < tile1) pf_load<NW, KT>(st, k, v, kv0, (tile + 1) * KT, T_, tid);
+        const char *stage = smem + (tile & 1) * TL::STAGE;
 
-        // S^T = K Q^T over dh = 256, four tiles of 16 keys
-        f32x4_t sa[4] = {};
+        // S^T = K Q^T over dh = 256, NST tiles of 16 keys (A row of this lane
+        // in tile st: LDS row 32(st/2) + 16(st%2) + n)
+        f32x4_t sa[NST] = {};
         {
             const bf16 *kr = (const bf16 *)stage + n * PF_KSTRIDE + 8 * g;
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-                for (int st4 = 0; st4 < 4; ++st4) {
-                    const int off = (32 * (st4 >> 1) + 16 * (st4 & 1)) * PF_KSTRIDE;
+                for (int s4 = 0; s4 < NST; ++s4) {
+                    const int off = (32 * (s4 >> 1) + 16 * (s4 & 1)) * PF_KSTRIDE;
                     const bf16x8 a = *(const bf16x8 *)(kr + off + 32 * ks);
-                    sa[st4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], sa[st4], 0, 0, 0);
+                    sa[s4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], sa[s4], 0, 0, 0);
                 }
         }
         // this lane's keys: 32j + 8g + e, e = 4(st%2) + i, j = st/2
-        float sv[16];
+        float sv[4 * NST];
 #pragma unroll
-        for (int st4 = 0; st4 < 4; ++st4)
+        for (int s4 = 0; s4 < NST; ++s4)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sv[8 * (st4 >> 1) + 4 * (st4 & 1) + i] = sa[st4][i];
+            for (int i = 0; i < 4; ++i) sv[8 * (s4 >> 1) + 4 * (s4 & 1) + i] = sa[s4][i];
         float mt = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int key = tile * PF_KEYS + 32 * (e >> 3) + 8 * g + (e & 7);
+        for (int e = 0; e < 4 * NST; ++e) {
+            const int key = tile * KT + 32 * (e >> 3) + 8 * g + (e & 7);
             const bool ok = key <= t && key > t - W;
             sv[e] = ok ? sv[e] * scale_log2e : -INFINITY;
             mt = fmaxf(mt, sv[e]);
@@ -334,9 +347,9 @@ __global__ __launch_bounds__(512) void attn_prefill_mfma(int T_, int Hq, int W, 
         const float mu = mn == -INFINITY ? 0.0f : mn;
         const float alpha = hw_exp2(m - mu);   // 0 while m is -inf
         float ls = 0.0f;
-        bf16x8 pb[2];
+        bf16x8 pb[NJ];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
+        for (int e = 0; e < 4 * NST; ++e) {
             const float pr = hw_exp2(sv[e] - mu);
             ls += pr;
             pb[e >> 3][e & 7] = (bf16)pr;
@@ -351,18 +364,18 @@ __global__ __launch_bounds__(512) void attn_prefill_mfma(int T_, int Hq, int W, 
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[i][r] *= alpha;
         }
-        // O^T += V^T P^T: 16 dh tiles, two 32-key steps each
+        // O^T += V^T P^T: 16 dh tiles, NJ 32-key steps each
         {
-            const bf16 *vt = (const bf16 *)(stage + PF_KBYTES) + n * PF_VSTRIDE + 8 * g;
+            const bf16 *vt = (const bf16 *)(stage + TL::KBYTES) + n * TL::VSTRIDE + 8 * g;
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < NJ; ++j)
 #pragma unroll
                 for (int dt = 0; dt < 16; ++dt) {
-                    const bf16x8 a = *(const bf16x8 *)(vt + 16 * dt * PF_VSTRIDE + 32 * j);
+                    const bf16x8 a = *(const bf16x8 *)(vt + 16 * dt * TL::VSTRIDE + 32 * j);
                     acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[j], acc[dt], 0, 0, 0);
                 }
         }
-        if (tile < tile1) pf_store(st, smem + ((tile + 1) & 1) * PF_STAGE, tid);
+        if (tile < tile1) pf_store<NW, KT>(st, smem + ((tile + 1) & 1) * TL::STAGE, tid);
         __syncthreads();
     }
 
@@ -379,6 +392,10 @@ __global__ __launch_bounds__(512) void attn_prefill_mfma(int T_, int Hq, int W, 
         }
     }
 }
+
+// the launch shape: workgroups of 4 waves (64 rows) and 32-key tiles, 75 KB of
+// LDS, so that two workgroups share a CU and drift out of phase
+constexpr int PF_NW = 4, PF_KT = 32;
 
 // -------------------------------------------------------------- MFMA decode
 constexpr int DS_SLOTS = 256;   // ring slots per workgroup
@@ -555,14 +572,15 @@ void launch_attn_fwd(const rglru_attn_desc &d, const void *q, const void *k, con
 {
     const float scale = d.scale;
     if (attn_fast_prefill(d)) {
+        constexpr int lds = PfTile<PF_KT>::LDS;
         static bool attr = false;
         if (!attr) {
-            (void)hipFuncSetAttribute((const void *)&attn_prefill_mfma,
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, PF_LDS);
+            (void)hipFuncSetAttribute((const void *)&attn_prefill_mfma<PF_NW, PF_KT>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
             attr = true;
         }
-        const long tiles = (d.T * d.Hq + PF_ROWS - 1) / PF_ROWS;
-        attn_prefill_mfma<<<dim3((unsigned)(d.B * tiles)), dim3(512), PF_LDS, s>>>(
+        const long tiles = (d.T * d.Hq + 16 * PF_NW - 1) / (16 * PF_NW);
+        attn_prefill_mfma<PF_NW, PF_KT><<<dim3((unsigned)(d.B * tiles)), dim3(64 * PF_NW), lds, s>>>(
             (int)d.T, (int)d.Hq, (int)d.W, scale * 1.4426950408889634f, (const bf16 *)q, (const bf16 *)k,
             (const bf16 *)v, (bf16 *)o);
     } else {
