@@ -420,9 +420,12 @@ __global__ __launch_bounds__(256) void attn_step_mfma(int Hq, int W, int NS, flo
     __shared__ float wsum[4][16];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int b = blockIdx.x / NS, sp = blockIdx.x % NS;
-    const long p = pos[b];
-    const int cur = (int)(p % W);
+    const int p = pos[b];
+    const int cur = p % W;
     const int n16 = lane & 15, kg = lane >> 4;
+    // a slot s < W holds a position of the window iff it has been written,
+    // i.e. s <= p (the slot's position is p - ((p - s) mod W), which is >= 0
+    // exactly then)
 
     // q^T as B operand: lane holds head n16, dh 32*ks + 8*kg .. +8
     bf16x8 qb[8];
@@ -438,19 +441,20 @@ __global__ __launch_bounds__(256) void attn_step_mfma(int Hq, int W, int NS, flo
     for (int st = 0; st < 4; ++st) {
         const int slot_a = sp * DS_SLOTS + 64 * wave + 16 * st + n16;   // A-operand row of this lane
         const bool a_ok = slot_a < W;
-        const bf16 *kr = slot_a == cur ? k_t + (long)b * 256 : kc + ((long)b * W + (a_ok ? slot_a : 0)) * 256;
+        // rows past the ring read its last slot: whatever it holds only enters
+        // scores that the mask below replaces, and the loads need no branch
+        const bf16 *kr = slot_a == cur ? k_t + (long)b * 256 : kc + ((long)b * W + (a_ok ? slot_a : W - 1)) * 256;
         f32x4_t acc = {};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            const bf16x8 a = a_ok ? *(const bf16x8 *)(kr + 32 * ks + 8 * kg) : bf16x8{};
+            const bf16x8 a = *(const bf16x8 *)(kr + 32 * ks + 8 * kg);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], acc, 0, 0, 0);
         }
         // lane holds head n16 for slots 4*kg + i of the 16
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int slot = sp * DS_SLOTS + 64 * wave + 16 * st + 4 * kg + i;
-            const long ppos = p - ((p - slot) % W + W) % W;   // position held by the slot
-            const bool ok = slot < W && ppos >= 0 && n16 < Hq;
+            const bool ok = slot < W && slot <= p && n16 < Hq;
             sc[st][i] = ok ? acc[i] * scale_log2e : -INFINITY;
             mx = fmaxf(mx, sc[st][i]);
         }
@@ -489,10 +493,10 @@ __global__ __launch_bounds__(256) void attn_step_mfma(int Hq, int W, int NS, flo
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int slot = sp * DS_SLOTS + 64 * ch + 8 * sg + i;
-            const long ppos = p - ((p - slot) % W + W) % W;
-            const bool ok = slot < W && ppos >= 0;
-            const bf16 *vr = slot == cur ? v_t + (long)b * 256 : vc + ((long)b * W + (ok ? slot : 0)) * 256;
-            r[i] = ok ? *(const u32x4 *)(vr + 8 * dg) : u32x4{0, 0, 0, 0};
+            const bool ok = slot < W && slot <= p;
+            const bf16 *vr = slot == cur ? v_t + (long)b * 256 : vc + ((long)b * W + (slot < W ? slot : W - 1)) * 256;
+            const u32x4 val = *(const u32x4 *)(vr + 8 * dg);   // unconditional; zeroed below if unused
+            r[i] = ok ? val : u32x4{0, 0, 0, 0};
         }
         __syncthreads();   // the previous chunk's V^T has been read (first pass: P^T is complete)
 #pragma unroll
