@@ -508,3 +508,17 @@ def layer_fwd(x: torch.Tensor, w: Weights, bw: BlockWeights, lw: LayerWeights, *
                                  _ptr(x), _ptr(hist_in), _ptr(h0), _ptr(y), _ptr(h_last), _ptr(hist_out),
                                  _ptr(wsb), wsb.numel(), _stream(dev)), "rglru_layer_fwd")
     return y, h_last, hist_out
+
+
+def hawk_stack_fwd(x: torch.Tensor, layers, *, states=None):
+    """A Hawk stack: residual layers (each a (Weights, BlockWeights,
+    LayerWeights) triple) applied in order, each one rglru_layer_fwd call.
+    states: optional per-layer (h0, hist_in) pairs carried in (decode-style
+    continuation); returns (y, [(h_last, hist_out) per layer])."""
+    out_states = []
+    y = x
+    for idx, (w, bw, lw) in enumerate(layers):
+        h0, hist = (None, None) if states is None else states[idx]
+        y, h_last, hist_out = layer_fwd(y, w, bw, lw, h0=h0, hist_in=hist)
+        out_states.append((h_last, hist_out))
+    return y, out_states

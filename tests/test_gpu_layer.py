@@ -113,3 +113,35 @@ def test_layer_full_size_prefix():
     y, _, _ = _run(prob, bp, lp, x, False)
     ry, _, _ = _ref(prob, bp, lp, x, 5, 6, T=160, stored=True)
     _cmp("y[5, :160]", y[5:6, :160], ry, TOL_LAYER_BF16)
+
+
+def test_hawk_stack_two_layers_split_with_state():
+    # two layers in a row, over 40 tokens and over 25 + 15 tokens with each
+    # layer's state carried between the calls; both against the oracle
+    cfgs = (0, 0)
+    dm, F, B, T = 96, 160, 2, 40
+    layers_dev, layers_ref = [], []
+    for li, cfg in enumerate(cfgs):
+        prob = make_problem(cfg, B=B, T=1, param_cfg=cfg)
+        bp = synth.make_block_params(cfg, dm, prob.D, prob.io)
+        lp = synth.make_layer_params(cfg + 40 + li, dm, F, prob.io)
+        layers_dev.append((prob.weights(DEV),
+                           glr.BlockWeights(to_dev(bp.proj_in_1, DEV), to_dev(bp.proj_in_2, DEV),
+                                            to_dev(bp.proj_out, DEV)),
+                           glr.LayerWeights(to_dev(lp.tnorm_w, DEV), to_dev(lp.cnorm_w, DEV), to_dev(lp.gate_w, DEV),
+                                            to_dev(lp.up_w, DEV), to_dev(lp.down_w, DEV))))
+        layers_ref.append((prob, bp, lp))
+    x = synth.make_activation(0, "block_x", (B, T, dm), "f32")
+    ref = synth.widen(x)
+    for prob, bp, lp in layers_ref:
+        W = synth.widen
+        ref, _, _ = oracle.hawk_layer(ref, W(lp.tnorm_w), W(lp.cnorm_w), W(bp.proj_in_1), W(bp.proj_in_2),
+                                      W(bp.proj_out), **prob.oracle_params(), gate_w=W(lp.gate_w),
+                                      up_w=W(lp.up_w), down_w=W(lp.down_w), c=8.0)
+    xd = to_dev(x, DEV)
+    y, _ = glr.hawk_stack_fwd(xd, layers_dev)
+    y1, st1 = glr.hawk_stack_fwd(xd[:, :25].contiguous(), layers_dev)
+    y2, _ = glr.hawk_stack_fwd(xd[:, 25:].contiguous(), layers_dev, states=st1)
+    torch.cuda.synchronize()
+    _cmp("stack y", from_dev(y), ref, TOL["f32"])
+    _cmp("stack split y", np.concatenate([from_dev(y1), from_dev(y2)], axis=1), ref, TOL["f32"])
