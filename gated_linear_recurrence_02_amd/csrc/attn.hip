@@ -183,6 +183,7 @@ __global__ __launch_bounds__(256) void attn_fill_cache(int B, int T_, int W, int
 constexpr int PF_KSTRIDE = 264;   // bf16 per K row in LDS (528 B, conflict-free b128 reads)
 template <int KT> struct PfTile {
     static constexpr int VSTRIDE = KT + 8;                 // bf16 per V^T row
+    __device__ static int vrow(int r) { return r * VSTRIDE * 2; }   // byte offset of V^T row r
     static constexpr int KBYTES = KT * PF_KSTRIDE * 2;
     static constexpr int VBYTES = 256 * VSTRIDE * 2;
     static constexpr int STAGE = KBYTES + VBYTES;
@@ -199,6 +200,15 @@ struct PfStage {
     u32x4 r[8];
 };
 
+// K row and 64-dh segment carried by staging thread t (t < 4 KT): each
+// aligned group of 8 threads takes rows {0-3, 8-11} + offset of one segment,
+// whose LDS rows (permuted below) fall in 8 different bank groups
+template <int KT> __device__ __forceinline__ int pf_krow(int t)
+{
+    return (t & 3) | (((t >> 3) & 1) << 2) | (((t >> 2) & 1) << 3) | (t & (KT - 16));
+}
+template <int KT> __device__ __forceinline__ int pf_kseg(int t) { return t / KT; }
+
 template <int NW, int KT>
 __device__ __forceinline__ void pf_load(PfStage &st, const bf16 *k, const bf16 *v, long kv0, int key0, int T_,
                                         int tid)
@@ -211,7 +221,7 @@ __device__ __forceinline__ void pf_load(PfStage &st, const bf16 *k, const bf16 *
         // keys past the end read the last row instead: real, finite values
         // whose weights the mask makes 0 (loads stay unconditional, so no
         // branch makes the wave wait for them here)
-        const int row = tid >> 2, seg = tid & 3;   // 64 dh per thread
+        const int row = pf_krow<KT>(tid), seg = pf_kseg<KT>(tid);   // 64 dh per thread
         const int key = key0 + row;
         const u32x4 *src = (const u32x4 *)(k + (kv0 + (key < T_ ? key : T_ - 1)) * 256 + 64 * seg);
 #pragma unroll
@@ -231,7 +241,7 @@ __device__ __forceinline__ void pf_store(const PfStage &st, char *stage, int tid
 {
     constexpr int HALF = 32 * NW;
     if (__builtin_amdgcn_readfirstlane(tid >> 6) < NW / 2) {
-        const int row = tid >> 2, seg = tid & 3;
+        const int row = pf_krow<KT>(tid), seg = pf_kseg<KT>(tid);
         // key 32j + 8a + 4u + i goes to LDS row 32j + 16u + 4a + i, so that the
         // 16 keys one score tile reads together sit in 16 consecutive rows
         const int lrow = (row & 0x23) | ((row & 0x4) << 2) | ((row & 0x18) >> 1);
@@ -252,7 +262,7 @@ __device__ __forceinline__ void pf_store(const PfStage &st, char *stage, int tid
             o[1] = __builtin_amdgcn_perm(st.r[3][c], st.r[2][c], sel);
             o[2] = __builtin_amdgcn_perm(st.r[5][c], st.r[4][c], sel);
             o[3] = __builtin_amdgcn_perm(st.r[7][c], st.r[6][c], sel);
-            *(u32x4 *)(vt + ((8 * dg + j) * PfTile<KT>::VSTRIDE + 8 * kg) * 2) = o;
+            *(u32x4 *)(vt + PfTile<KT>::vrow(8 * dg + j) + 16 * kg) = o;
         }
     }
 }
@@ -366,12 +376,12 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_prefill_mfma(int T_, int Hq, 
         }
         // O^T += V^T P^T: 16 dh tiles, NJ 32-key steps each
         {
-            const bf16 *vt = (const bf16 *)(stage + TL::KBYTES) + n * TL::VSTRIDE + 8 * g;
+            const char *vt = stage + TL::KBYTES + 16 * g;
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
 #pragma unroll
                 for (int dt = 0; dt < 16; ++dt) {
-                    const bf16x8 a = *(const bf16x8 *)(vt + 16 * dt * TL::VSTRIDE + 32 * j);
+                    const bf16x8 a = *(const bf16x8 *)(vt + TL::vrow(16 * dt + n) + 64 * j);
                     acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[j], acc[dt], 0, 0, 0);
                 }
         }
