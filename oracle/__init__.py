@@ -267,3 +267,34 @@ def hawk_layer(x, tnorm_w, cnorm_w, proj_in_1, proj_in_2, proj_out, conv_w, conv
                                     W_a, b_a, W_x, b_x, Lambda, h0=h0, hist_in=hist_in, c=c)
     xt = _f64(x) + t
     return xt + mlp(rmsnorm(xt, cnorm_w, eps), gate_w, up_w, down_w), h_last, hist_out
+
+
+# ------------------------------------------------------------ attention layer
+def rope(x, positions, rot, base=10000.0):
+    """Rotary embedding (reading R9): x [..][H][dh] with positions [..] (one per
+    row); pairs (j, j + rot/2), j < rot/2, turn by pos * base^(-2j/rot)."""
+    x = np.array(x, dtype=np.float64, order="C", copy=True)
+    H, dh = x.shape[-2], x.shape[-1]
+    pos = np.ascontiguousarray(np.broadcast_to(positions, x.shape[:-2]).reshape(-1), dtype=np.int64)
+    lib().oracle_rope(ctypes.c_long(pos.size), H, dh, int(rot), ctypes.c_double(base),
+                      pos.ctypes.data_as(ctypes.POINTER(ctypes.c_long)), _p(x))
+    return x
+
+
+def attn_layer(x, tnorm_w, cnorm_w, wq, wk, wv, wo, gate_w, up_w, down_w, Hq, window, scale, rot,
+               base=10000.0, pos0=0, eps=1e-6):
+    """Residual layer with local MQA as temporal mixer (readings R8, R9):
+    x~ = x + o_proj(attn(RoPE(q), RoPE(k), v)), y = x~ + MLP(RMSNorm(x~)).
+    wq [Hq*dh][d_model], wk, wv [dh][d_model], wo [d_model][Hq*dh]; token t has
+    position pos0 + t.  Returns y."""
+    x = _f64(x)
+    B, T, dm = x.shape
+    dh = wk.shape[0]
+    xn = rmsnorm(x, tnorm_w, eps)
+    pos = pos0 + np.arange(T)[None, :].repeat(B, axis=0)
+    q = rope(linear(xn, wq).reshape(B, T, Hq, dh), pos, rot, base)
+    k = rope(linear(xn, wk).reshape(B, T, 1, dh), pos, rot, base).reshape(B, T, dh)
+    v = linear(xn, wv)
+    o = attn_fwd(q, k, v, window, scale).reshape(B, T, Hq * dh)
+    xt = x + linear(o, wo)
+    return xt + mlp(rmsnorm(xt, cnorm_w, eps), gate_w, up_w, down_w)

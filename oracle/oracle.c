@@ -61,6 +61,13 @@
  *      on the pages); gated MLP = down(GELU_tanh(gate x) * (up x)) without
  *      biases, GELU_tanh(v) = v/2 (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)));
  *      the MLP width is the caller's (not on the pages).
+ *  R9  the attention residual layer: q, k, v are bias-free projections of
+ *      RMSNorm(x) (Hq query heads, one key and one value head); rotary
+ *      embedding ([G] "Local Sliding-Window Multi-Query Attention (MQA)":
+ *      standard RoPE on queries and keys; module page: partial rotary) turns
+ *      dimension pairs (j, j + rot/2), j < rot/2, of each head by the angle
+ *      p * base^(-2j/rot) at position p, leaving dimensions >= rot as they are;
+ *      the output projection is bias-free; the MLP half is that of R8.
  *  R6  the recurrent block ([G] "Non-Linear Multiplicative Gating with GeLU"
  *      and the listing's RecurrentBlock): out = proj_out(y * GeLU(proj_in_2
  *      x)), y the RG-LRU of conv(proj_in_1 x); linear layers without bias,
@@ -532,4 +539,23 @@ void oracle_gelu_tanh(long n, const double *v, double *out)
 {
     const double k = sqrt(2.0 / 3.14159265358979323846);   /* sqrt(2 / pi) */
     for (long i = 0; i < n; ++i) out[i] = 0.5 * v[i] * (1.0 + tanh(k * (v[i] + 0.044715 * v[i] * v[i] * v[i])));
+}
+
+/* ------------------------------------------------------------ rotary embedding
+ * (R9) x [M][H][dh] in place: row m has position pos[m]; pairs (j, j + rot/2)
+ * for j < rot/2 turn by pos * base^(-2j/rot). */
+void oracle_rope(long M, int H, int dh, int rot, double base, const long *pos, double *x)
+{
+    const int half = rot / 2;
+    for (long m = 0; m < M; ++m)
+        for (int h = 0; h < H; ++h) {
+            double *v = x + ((size_t)m * H + h) * dh;
+            for (int j = 0; j < half; ++j) {
+                const double ang = (double)pos[m] * pow(base, -2.0 * j / rot);
+                const double c = cos(ang), s = sin(ang);
+                const double a = v[j], b = v[j + half];
+                v[j] = a * c - b * s;
+                v[j + half] = a * s + b * c;
+            }
+        }
 }
