@@ -19,7 +19,9 @@ of width 3 d_model, residual adds),
 the fused forward on the 32k-token prefill, 512 decode steps of 256 streams,
 the backward of the 9B-width workload (B = 4, T = 8192, D = 4096), and the
 local sliding-window MQA (10 query heads of 256, window 2048) as prefill on
-the 2B-width and 32k-token shapes and as a decode step of 256 streams.
+the 2B-width and 32k-token shapes and as a decode step of 256 streams, and
+Griffin's attention residual layer around it (projections, rotary embedding,
+gated MLP).
 
 Prints ONE JSON line: tokens*channels/s for the whole job, the dominant
 kernel's achieved algorithmic HBM bandwidth against the 8 TB/s peak (kernel
@@ -46,7 +48,7 @@ PEAK_BF16_TFLOPS = 2500.0
 KERNEL_SOURCES = ("fwd.hip", "common.h", "gatemath.h")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_fused_2b_prefill_pmc.json")
 ALL_ROWS = ("conv1d", "gates", "scan", "block", "layer", "long", "decode", "bwd", "attn", "attn_long",
-            "attn_decode")
+            "attn_decode", "attn_layer")
 
 
 def kernel_hash() -> str:
@@ -509,6 +511,32 @@ def main():
                                                   "o_t, the new key/value written; two launches (splits, "
                                                   "combine)")
         del kc, vc, qd, kd, vd, od
+        torch.cuda.empty_cache()
+
+    if "attn_layer" in rows:
+        # Griffin's attention residual layer at the 2B width: q/k/v projections,
+        # rotary embedding on half of each head (partial rotary), the local
+        # MQA, output projection with the residual, gated MLP (d_ff = 3 d_model)
+        dm, F = D, 3 * D
+        ap = synth.make_attn_proj(cfg.idx, dm, AH, ADH, cfg.io)
+        lp = synth.make_layer_params(cfg.idx, dm, F, cfg.io)
+        apd = glr.AttnProjWeights(dev_t(ap.wq), dev_t(ap.wk), dev_t(ap.wv), dev_t(ap.wo))
+        lw = glr.LayerWeights(dev_t(lp.tnorm_w), dev_t(lp.cnorm_w), dev_t(lp.gate_w), dev_t(lp.up_w),
+                              dev_t(lp.down_w))
+        x0 = dev_t(synth.make_activation(cfg.idx, "block_x", (B, T, dm), cfg.io))
+        a_sets = [dict(x=x0 if k == 0 else x0.clone(), o=torch.empty_like(x0)) for k in range(2)]
+        _say(f"attention residual layer, 2B width B={B} T={T} Hq={AH} dh={ADH} W={AW} d_ff={F}")
+        kk, _ = tm.calls(lambda k: glr.attn_layer_fwd(a_sets[k % 2]["x"], apd, lw, AH, AW, scale=1.0 / 16,
+                                                      rot=ADH // 2, out=a_sets[k % 2]["o"]), 10, 2)
+        M = B * T
+        fl = 2 * M * dm * (AH * ADH + 2 * ADH) + 2 * M * AH * ADH * dm + attn_flops(B, T) + 3 * 2 * M * dm * F
+        nb = 2 * M * dm * 2 + (AH * ADH * dm * 2 + 2 * ADH * dm + 3 * F * dm) * 2 + 2 * dm * 4
+        out["rows"]["attn_layer"] = row(f"rglru_attn_layer_fwd, attention residual layer at 2B width (B={B} "
+                                        f"T={T} Hq={AH} dh={ADH} W={AW} d_ff={F} bf16)", kk, M * dm, nb,
+                                        flops=fl, bound="mfma",
+                                        note="algorithmic flops: q/k/v/o and MLP projections and the "
+                                             "windowed attention; tokens_ch counts B*T*d_model")
+        del a_sets, x0, apd, lw
         torch.cuda.empty_cache()
 
     if not args.no_cpu:

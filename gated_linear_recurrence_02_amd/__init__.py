@@ -56,6 +56,10 @@ class _Layer(ctypes.Structure):
                 ("eps", ctypes.c_float)]
 
 
+class _AttnProj(ctypes.Structure):
+    _fields_ = [("wq", ctypes.c_void_p), ("wk", ctypes.c_void_p), ("wv", ctypes.c_void_p), ("wo", ctypes.c_void_p)]
+
+
 class _Block(ctypes.Structure):
     _fields_ = [("proj_in_1", ctypes.c_void_p), ("proj_in_2", ctypes.c_void_p),
                 ("proj_out", ctypes.c_void_p)]
@@ -65,7 +69,8 @@ _lib = None
 SYMBOLS = ("rglru_workspace_size", "rglru_conv1d", "rglru_gates", "rglru_scan_fwd",
            "rglru_step", "rglru_scan_bwd", "rglru_block_workspace_size", "rglru_block_fwd",
            "rglru_attn_fwd", "rglru_attn_workspace_size", "rglru_attn_step", "rglru_layer_workspace_size",
-           "rglru_layer_fwd", "rglru_status_string")
+           "rglru_layer_fwd", "rglru_attn_layer_workspace_size", "rglru_attn_layer_fwd",
+           "rglru_status_string")
 
 
 def lib():
@@ -93,6 +98,9 @@ def lib():
         L.rglru_layer_workspace_size.argtypes = [D, ctypes.c_int64, LY, ctypes.POINTER(sz)]
         L.rglru_layer_fwd.argtypes = [D, ctypes.c_int64, W, ctypes.POINTER(_Block), LY, vp, vp, vp, vp, vp, vp, vp,
                                       sz, vp]
+        L.rglru_attn_layer_workspace_size.argtypes = [A, ctypes.c_int64, LY, ctypes.POINTER(sz)]
+        L.rglru_attn_layer_fwd.argtypes = [A, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_int64,
+                                           ctypes.POINTER(_AttnProj), LY, vp, vp, vp, vp, vp, sz, vp]
         L.rglru_block_workspace_size.argtypes = [D, ctypes.c_int64, ctypes.POINTER(sz)]
         L.rglru_block_fwd.argtypes = [D, ctypes.c_int64, W, ctypes.POINTER(_Block), vp, vp, vp, vp, vp, vp,
                                       vp, sz, vp]
@@ -522,3 +530,48 @@ def hawk_stack_fwd(x: torch.Tensor, layers, *, states=None):
         y, h_last, hist_out = layer_fwd(y, w, bw, lw, h0=h0, hist_in=hist)
         out_states.append((h_last, hist_out))
     return y, out_states
+
+
+# ------------------------------------------------------------ attention layer
+@dataclasses.dataclass
+class AttnProjWeights:
+    """Attention layer projections (activation dtype, [out][in]): wq
+    [Hq*dh][d_model], wk, wv [dh][d_model], wo [d_model][Hq*dh]."""
+    wq: torch.Tensor
+    wk: torch.Tensor
+    wv: torch.Tensor
+    wo: torch.Tensor
+
+
+def attn_layer_fwd(x: torch.Tensor, ap: AttnProjWeights, lw: LayerWeights, Hq: int, window: int, *,
+                   scale: Optional[float] = None, rot: Optional[int] = None, rope_base: float = 10000.0,
+                   pos0: int = 0, kcache=None, vcache=None, out=None):
+    """Attention residual layer: x~ = x + attn(RoPE(q), RoPE(k), v) wo^T,
+    y = x~ + MLP(RMSNorm(x~)), with q, k, v projections of RMSNorm(x).
+    rot defaults to dh (full rotary); positions are pos0 + t.  Returns y."""
+    dev = x.device
+    _need(x, "x", dev)
+    B, T, d_model = x.shape
+    dh = int(ap.wk.shape[0])
+    _need(ap.wq, "wq", dev, x.dtype, (Hq * dh, d_model))
+    _need(ap.wk, "wk", dev, x.dtype, (dh, d_model))
+    _need(ap.wv, "wv", dev, x.dtype, (dh, d_model))
+    _need(ap.wo, "wo", dev, x.dtype, (d_model, Hq * dh))
+    if (kcache is None) != (vcache is None):
+        raise ValueError("kcache and vcache go together")
+    _need(kcache, "kcache", dev, x.dtype, (B, window, dh))
+    _need(vcache, "vcache", dev, x.dtype, (B, window, dh))
+    ls = _layer_struct(lw, d_model, x.dtype, dev)
+    y = torch.empty_like(x) if out is None else out
+    _need(y, "out", dev, x.dtype, (B, T, d_model))
+    sc = dh ** -0.5 if scale is None else float(scale)
+    d = _AttnDesc(B, T, Hq, dh, window, _io(x), sc)
+    n = ctypes.c_size_t(0)
+    _check(lib().rglru_attn_layer_workspace_size(ctypes.byref(d), d_model, ctypes.byref(ls), ctypes.byref(n)),
+           "rglru_attn_layer_workspace_size")
+    wsb = workspace(int(n.value), dev, "attn_layer")
+    pr = _AttnProj(_ptr(ap.wq), _ptr(ap.wk), _ptr(ap.wv), _ptr(ap.wo))
+    _check(lib().rglru_attn_layer_fwd(ctypes.byref(d), d_model, dh if rot is None else int(rot), rope_base, pos0,
+                                      ctypes.byref(pr), ctypes.byref(ls), _ptr(x), _ptr(y), _ptr(kcache),
+                                      _ptr(vcache), _ptr(wsb), wsb.numel(), _stream(dev)), "rglru_attn_layer_fwd")
+    return y

@@ -72,6 +72,18 @@ int check_attn(const rglru_attn_desc *d, bool prefill)
     return RGLRU_OK;
 }
 
+// attention layer: the prefill's checks plus the model and MLP widths
+int check_attn_layer(const rglru_attn_desc *d, int64_t d_model, const rglru_layer *lw)
+{
+    int st = check_attn(d, true);
+    if (st) return st;
+    if (d_model < 1 || d_model > MAX_DIM || lw->d_ff < 1 || lw->d_ff >= 2147483647) return RGLRU_ERR_SHAPE;
+    if (d->B * d->T >= 2147483647 || d->Hq * d->dh >= 2147483647) return RGLRU_ERR_SHAPE;
+    if ((double)d->B * d->T * (double)(d_model > lw->d_ff ? d_model : lw->d_ff) > 9.0e15) return RGLRU_ERR_SHAPE;
+    if (!isfinite(lw->eps) || lw->eps < 0.0f) return RGLRU_ERR_ARG;
+    return RGLRU_OK;
+}
+
 struct Range {
     const void *p;
     size_t bytes;
@@ -336,6 +348,49 @@ int rglru_layer_fwd(const rglru_desc *desc, int64_t d_model, const rglru_weights
                          {lw->cnorm_w, nv}, {lw->gate_w, fw}, {lw->up_w, fw}, {lw->down_w, fw}};
     if (any_alias(outs, 4, ins, 18)) return RGLRU_ERR_ARG;
     st = launch_layer_fwd(d, d_model, *w, *blk, *lw, x, hist_in, h0, y, h_last, hist_out, ws, stream);
+    if (st) return st;
+    return launch_status();
+}
+
+int rglru_attn_layer_workspace_size(const rglru_attn_desc *desc, int64_t d_model, const rglru_layer *lw,
+                                    size_t *bytes)
+{
+    if (!bytes || !lw) return RGLRU_ERR_NULL;
+    int st = check_attn_layer(desc, d_model, lw);
+    if (st) return st;
+    *bytes = attn_layer_layout(*desc, d_model, lw->d_ff).bytes;
+    return RGLRU_OK;
+}
+
+int rglru_attn_layer_fwd(const rglru_attn_desc *desc, int64_t d_model, int32_t rot, float rope_base, int64_t pos0,
+                         const rglru_attn_proj *ap, const rglru_layer *lw, const void *x, void *y, void *kcache,
+                         void *vcache, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (!ap || !lw) return RGLRU_ERR_NULL;
+    int st = check_attn_layer(desc, d_model, lw);
+    if (st) return st;
+    const rglru_attn_desc &d = *desc;
+    if (rot < 0 || rot > d.dh || rot % 2 != 0 || !(rope_base > 1.0f) || !isfinite(rope_base)) return RGLRU_ERR_ARG;
+    if (pos0 < 0 || pos0 + d.T >= 2147483647) return RGLRU_ERR_SHAPE;
+    if (!ap->wq || !ap->wk || !ap->wv || !ap->wo || !lw->tnorm_w || !lw->cnorm_w || !lw->gate_w || !lw->up_w ||
+        !lw->down_w || !x || !y)
+        return RGLRU_ERR_NULL;
+    if ((kcache == nullptr) != (vcache == nullptr)) return RGLRU_ERR_ARG;
+    if (!ws) return RGLRU_ERR_WORKSPACE;
+    const void *all[] = {x, y, kcache, vcache, ws, ap->wq, ap->wk, ap->wv, ap->wo, lw->tnorm_w, lw->cnorm_w,
+                         lw->gate_w, lw->up_w, lw->down_w};
+    for (const void *p : all)
+        if (p && !aligned16(p)) return RGLRU_ERR_ALIGN;
+    const size_t need = attn_layer_layout(d, d_model, lw->d_ff).bytes;
+    if (ws_bytes < need) return RGLRU_ERR_WORKSPACE;
+    const size_t e = d.io == RGLRU_BF16 ? 2 : 4, io_x = d.B * d.T * d_model * e, cb = d.B * d.W * d.dh * e;
+    const size_t wqb = d.Hq * d.dh * d_model * e, wkb = d.dh * d_model * e, fw = lw->d_ff * d_model * e,
+                 nv = d_model * 4;
+    const Range outs[] = {{y, io_x}, {kcache, cb}, {vcache, cb}, {ws, need}};
+    const Range ins[] = {{x, io_x}, {ap->wq, wqb}, {ap->wk, wkb}, {ap->wv, wkb}, {ap->wo, wqb},
+                         {lw->tnorm_w, nv}, {lw->cnorm_w, nv}, {lw->gate_w, fw}, {lw->up_w, fw}, {lw->down_w, fw}};
+    if (any_alias(outs, 4, ins, 10)) return RGLRU_ERR_ARG;
+    st = launch_attn_layer_fwd(d, d_model, rot, rope_base, pos0, *ap, *lw, x, y, kcache, vcache, ws, stream);
     if (st) return st;
     return launch_status();
 }

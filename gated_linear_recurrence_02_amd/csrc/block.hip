@@ -320,6 +320,143 @@ LayerLayout layer_layout(int64_t B, int64_t T, int64_t D, int64_t d_model, int64
     return L;
 }
 
+namespace {
+
+int rmsnorm_launch(int io, long M, int64_t D, const void *x, const float *w, float eps, void *out, hipStream_t s)
+{
+    const unsigned grid = (unsigned)((M + 3) / 4);
+    if (io == RGLRU_BF16)
+        rmsnorm_kernel<bf16><<<grid, 256, 0, s>>>(M, (int)D, (const bf16 *)x, w, eps, (bf16 *)out);
+    else
+        rmsnorm_kernel<float><<<grid, 256, 0, s>>>(M, (int)D, (const float *)x, w, eps, (float *)out);
+    return hipGetLastError() == hipSuccess ? RGLRU_OK : RGLRU_ERR_LAUNCH;
+}
+
+// y = x~ + down(GELU_tanh(gate RMSNorm(x~)) * up RMSNorm(x~)); xn, g, u are scratch
+int mlp_tail(int io, long M, int64_t d_model, const rglru_layer &lw, const void *xt, void *xn, void *g, void *u,
+             void *y, hipStream_t s)
+{
+    const size_t esz = io == RGLRU_BF16 ? 2 : 4;
+    int st = rmsnorm_launch(io, M, d_model, xt, lw.cnorm_w, lw.eps, xn, s);
+    if (st) return st;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return RGLRU_ERR_LAUNCH;
+    {
+        std::lock_guard<std::mutex> lock(blas_mu);
+        rocblas_handle h = blas_handle_locked(dev);
+        if (!h || rocblas_set_stream(h, s) != rocblas_status_success) return RGLRU_ERR_BLAS;
+        if (!gemm_run(h, s, dev, io, M, lw.d_ff, d_model, xn, lw.gate_w, nullptr, g)) return RGLRU_ERR_BLAS;
+        if (!gemm_run(h, s, dev, io, M, lw.d_ff, d_model, xn, lw.up_w, nullptr, u)) return RGLRU_ERR_BLAS;
+    }
+    const long nff = M * lw.d_ff;
+    const long pieces = (nff + (long)(16 / esz) - 1) / (long)(16 / esz);
+    const unsigned ff_grid = (unsigned)((pieces + 255) / 256);
+    if (io == RGLRU_BF16)
+        gelu_tanh_mul_kernel<bf16><<<ff_grid, 256, 0, s>>>(nff, (bf16 *)g, (const bf16 *)u);
+    else
+        gelu_tanh_mul_kernel<float><<<ff_grid, 256, 0, s>>>(nff, (float *)g, (const float *)u);
+    if (hipGetLastError() != hipSuccess) return RGLRU_ERR_LAUNCH;
+    {
+        std::lock_guard<std::mutex> lock(blas_mu);
+        rocblas_handle h = blas_handle_locked(dev);
+        if (!h || rocblas_set_stream(h, s) != rocblas_status_success) return RGLRU_ERR_BLAS;
+        if (!gemm_run(h, s, dev, io, M, d_model, lw.d_ff, g, lw.down_w, xt, y)) return RGLRU_ERR_BLAS;
+    }
+    return RGLRU_OK;
+}
+
+// Rotary embedding in place on x [M][H][dh]: row m has position pos0 + m % T;
+// pairs (j, j + rot/2) turn by pos * base^(-2j/rot).  The angle is formed
+// and reduced modulo 2 pi in double, so large positions keep their accuracy.
+template <typename T>
+__global__ __launch_bounds__(256) void rope_kernel(long M, int T_, int H, int dh, int rot, double log2_base,
+                                                   long pos0, T *x)
+{
+    const int half = rot / 2;
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= M * H * half) return;
+    const int j = (int)(i % half);
+    const long mh = i / half;   // row * H + head
+    const long m = mh / H;
+    const double pos = (double)(pos0 + m % T_);
+    double ang = pos * exp2(-2.0 * j / rot * log2_base);
+    ang -= 6.283185307179586 * floor(ang / 6.283185307179586);
+    float sn, cs;
+    sincosf((float)ang, &sn, &cs);
+    T *v = x + mh * dh;
+    const float a = to_f32(v[j]), b = to_f32(v[j + half]);
+    v[j] = from_f32<T>(a * cs - b * sn);
+    v[j + half] = from_f32<T>(a * sn + b * cs);
+}
+
+}  // namespace
+
+AttnLayerLayout attn_layer_layout(const rglru_attn_desc &d, int64_t d_model, int64_t d_ff)
+{
+    const size_t esz = d.io == RGLRU_BF16 ? 2 : 4;
+    const size_t M = d.B * d.T;
+    AttnLayerLayout L;
+    L.xn = 0;
+    L.q = L.xn + round256(M * d_model * esz);
+    L.k = L.q + round256(M * d.Hq * d.dh * esz);
+    L.v = L.k + round256(M * d.dh * esz);
+    L.o = L.v + round256(M * d.dh * esz);
+    L.xt = L.o + round256(M * d.Hq * d.dh * esz);
+    L.g = L.xt + round256(M * d_model * esz);
+    L.u = L.g + round256(M * d_ff * esz);
+    L.bytes = L.u + round256(M * d_ff * esz);
+    return L;
+}
+
+int launch_attn_layer_fwd(const rglru_attn_desc &d, int64_t d_model, int rot, float rope_base, int64_t pos0,
+                          const rglru_attn_proj &ap, const rglru_layer &lw, const void *x, void *y, void *kc,
+                          void *vc, void *ws, hipStream_t s)
+{
+    const AttnLayerLayout L = attn_layer_layout(d, d_model, lw.d_ff);
+    char *base = (char *)ws;
+    void *xn = base + L.xn, *q = base + L.q, *k = base + L.k, *v = base + L.v, *o = base + L.o,
+         *xt = base + L.xt, *g = base + L.g, *u = base + L.u;
+    const long M = d.B * d.T;
+    const int64_t HD = d.Hq * d.dh;
+    int st = rmsnorm_launch(d.io, M, d_model, x, lw.tnorm_w, lw.eps, xn, s);
+    if (st) return st;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return RGLRU_ERR_LAUNCH;
+    {
+        std::lock_guard<std::mutex> lock(blas_mu);
+        rocblas_handle h = blas_handle_locked(dev);
+        if (!h || rocblas_set_stream(h, s) != rocblas_status_success) return RGLRU_ERR_BLAS;
+        if (!gemm_run(h, s, dev, d.io, M, HD, d_model, xn, ap.wq, nullptr, q)) return RGLRU_ERR_BLAS;
+        if (!gemm_run(h, s, dev, d.io, M, d.dh, d_model, xn, ap.wk, nullptr, k)) return RGLRU_ERR_BLAS;
+        if (!gemm_run(h, s, dev, d.io, M, d.dh, d_model, xn, ap.wv, nullptr, v)) return RGLRU_ERR_BLAS;
+    }
+    if (rot > 0) {
+        const double l2b = log2((double)rope_base);
+        const long nq = M * d.Hq * (rot / 2), nk = M * (rot / 2);
+        if (d.io == RGLRU_BF16) {
+            rope_kernel<bf16><<<(unsigned)((nq + 255) / 256), 256, 0, s>>>(M, (int)d.T, (int)d.Hq, (int)d.dh, rot,
+                                                                          l2b, pos0, (bf16 *)q);
+            rope_kernel<bf16><<<(unsigned)((nk + 255) / 256), 256, 0, s>>>(M, (int)d.T, 1, (int)d.dh, rot, l2b,
+                                                                          pos0, (bf16 *)k);
+        } else {
+            rope_kernel<float><<<(unsigned)((nq + 255) / 256), 256, 0, s>>>(M, (int)d.T, (int)d.Hq, (int)d.dh, rot,
+                                                                           l2b, pos0, (float *)q);
+            rope_kernel<float><<<(unsigned)((nk + 255) / 256), 256, 0, s>>>(M, (int)d.T, 1, (int)d.dh, rot, l2b,
+                                                                           pos0, (float *)k);
+        }
+        if (hipGetLastError() != hipSuccess) return RGLRU_ERR_LAUNCH;
+    }
+    launch_attn_fwd(d, q, k, v, o, kc, vc, s);
+    if (hipGetLastError() != hipSuccess) return RGLRU_ERR_LAUNCH;
+    {
+        std::lock_guard<std::mutex> lock(blas_mu);
+        rocblas_handle h = blas_handle_locked(dev);
+        if (!h || rocblas_set_stream(h, s) != rocblas_status_success) return RGLRU_ERR_BLAS;
+        if (!gemm_run(h, s, dev, d.io, M, d_model, HD, o, ap.wo, x, xt)) return RGLRU_ERR_BLAS;
+    }
+    return mlp_tail(d.io, M, d_model, lw, xt, xn, g, u, y, s);
+}
+
 int launch_layer_fwd(const rglru_desc &d, int64_t d_model, const rglru_weights &w, const rglru_block &blk,
                      const rglru_layer &lw, const void *x, const void *hist_in, const float *h0, void *y,
                      float *h_last, void *hist_out, void *ws, hipStream_t s)
@@ -329,49 +466,13 @@ int launch_layer_fwd(const rglru_desc &d, int64_t d_model, const rglru_weights &
     char *base = (char *)ws;
     void *xn = base + L.xn, *xt = base + L.xt, *g = base + L.g, *u = base + L.u;
     const long M = d.B * d.T;
-    const unsigned rows_grid = (unsigned)((M + 3) / 4);
-    const long nff = M * lw.d_ff;
-    const long pieces = (nff + (long)(16 / esz) - 1) / (long)(16 / esz);
-    const unsigned ff_grid = (unsigned)((pieces + 255) / 256);
     // x~ = x + block(RMSNorm(x))
-    if (d.io == RGLRU_BF16)
-        rmsnorm_kernel<bf16><<<rows_grid, 256, 0, s>>>(M, (int)d_model, (const bf16 *)x, lw.tnorm_w, lw.eps,
-                                                        (bf16 *)xn);
-    else
-        rmsnorm_kernel<float><<<rows_grid, 256, 0, s>>>(M, (int)d_model, (const float *)x, lw.tnorm_w, lw.eps,
-                                                         (float *)xn);
-    if (hipGetLastError() != hipSuccess) return RGLRU_ERR_LAUNCH;
-    int st = block_core(d, d_model, w, blk, xn, hist_in, h0, xt, x, h_last, hist_out, base + L.block, s);
+    int st = rmsnorm_launch(d.io, M, d_model, x, lw.tnorm_w, lw.eps, xn, s);
+    if (st) return st;
+    st = block_core(d, d_model, w, blk, xn, hist_in, h0, xt, x, h_last, hist_out, base + L.block, s);
     if (st) return st;
     // y = x~ + MLP(RMSNorm(x~))
-    if (d.io == RGLRU_BF16)
-        rmsnorm_kernel<bf16><<<rows_grid, 256, 0, s>>>(M, (int)d_model, (const bf16 *)xt, lw.cnorm_w, lw.eps,
-                                                        (bf16 *)xn);
-    else
-        rmsnorm_kernel<float><<<rows_grid, 256, 0, s>>>(M, (int)d_model, (const float *)xt, lw.cnorm_w, lw.eps,
-                                                         (float *)xn);
-    if (hipGetLastError() != hipSuccess) return RGLRU_ERR_LAUNCH;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return RGLRU_ERR_LAUNCH;
-    {
-        std::lock_guard<std::mutex> lock(blas_mu);
-        rocblas_handle h = blas_handle_locked(dev);
-        if (!h || rocblas_set_stream(h, s) != rocblas_status_success) return RGLRU_ERR_BLAS;
-        if (!gemm_run(h, s, dev, d.io, M, lw.d_ff, d_model, xn, lw.gate_w, nullptr, g)) return RGLRU_ERR_BLAS;
-        if (!gemm_run(h, s, dev, d.io, M, lw.d_ff, d_model, xn, lw.up_w, nullptr, u)) return RGLRU_ERR_BLAS;
-    }
-    if (d.io == RGLRU_BF16)
-        gelu_tanh_mul_kernel<bf16><<<ff_grid, 256, 0, s>>>(nff, (bf16 *)g, (const bf16 *)u);
-    else
-        gelu_tanh_mul_kernel<float><<<ff_grid, 256, 0, s>>>(nff, (float *)g, (const float *)u);
-    if (hipGetLastError() != hipSuccess) return RGLRU_ERR_LAUNCH;
-    {
-        std::lock_guard<std::mutex> lock(blas_mu);
-        rocblas_handle h = blas_handle_locked(dev);
-        if (!h || rocblas_set_stream(h, s) != rocblas_status_success) return RGLRU_ERR_BLAS;
-        if (!gemm_run(h, s, dev, d.io, M, d_model, lw.d_ff, g, lw.down_w, xt, y)) return RGLRU_ERR_BLAS;
-    }
-    return RGLRU_OK;
+    return mlp_tail(d.io, M, d_model, lw, xt, xn, g, u, y, s);
 }
 
 }  // namespace rglru

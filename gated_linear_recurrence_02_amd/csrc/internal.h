@@ -61,6 +61,16 @@ int launch_layer_fwd(const rglru_desc &d, int64_t d_model, const rglru_weights &
                      const rglru_layer &lw, const void *x, const void *hist_in, const float *h0, void *y,
                      float *h_last, void *hist_out, void *ws, hipStream_t s);
 
+// Attention residual layer (block.hip): workspace offsets of xn, q, k, v, o,
+// x~ and the MLP activations
+struct AttnLayerLayout {
+    size_t xn, q, k, v, o, xt, g, u, bytes;
+};
+AttnLayerLayout attn_layer_layout(const rglru_attn_desc &d, int64_t d_model, int64_t d_ff);
+int launch_attn_layer_fwd(const rglru_attn_desc &d, int64_t d_model, int rot, float rope_base, int64_t pos0,
+                          const rglru_attn_proj &ap, const rglru_layer &lw, const void *x, void *y, void *kc,
+                          void *vc, void *ws, hipStream_t s);
+
 // local sliding-window MQA (attn.hip)
 bool attn_fast_prefill(const rglru_attn_desc &d);
 bool attn_fast_step(const rglru_attn_desc &d);

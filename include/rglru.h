@@ -309,6 +309,35 @@ int rglru_attn_step(const rglru_attn_desc *desc, const void *q_t, const void *k_
                     void *kcache, void *vcache, const int32_t *pos, void *o_t, void *ws, size_t ws_bytes,
                     hipStream_t stream);
 
+/* Attention residual layer (Griffin's third block kind): the scaffold of
+ * rglru_layer_fwd with local MQA as temporal mixer,
+ *     q = RoPE(RMSNorm_t(x) wq^T), k = RoPE(RMSNorm_t(x) wk^T), v = RMSNorm_t(x) wv^T
+ *     x~ = x + attn(q, k, v) wo^T            (rglru_attn_fwd, window desc->W)
+ *     y  = x~ + gated MLP(RMSNorm_c(x~))     (as in rglru_layer_fwd)
+ * The rotary embedding (page "Griffin Guide", "Local Sliding-Window
+ * Multi-Query Attention (MQA)": standard RoPE on queries and keys; module
+ * page: partial rotary) turns dimension pairs (j, j + rot/2), j < rot/2, of
+ * every head by p * rope_base^(-2j/rot) at position p = pos0 + t; dimensions
+ * >= rot are left as they are.  Projections are bias-free, stored [out][in]
+ * in desc->io.  x, y [B][T][d_model].  kcache / vcache (both or neither)
+ * receive the rotated keys and the values of the last W positions in ring
+ * order, as rglru_attn_fwd.  Shapes as rglru_attn_fwd and rglru_layer_fwd;
+ * 0 <= rot <= dh, rot even; rope_base > 1; 0 <= pos0, pos0 + T < 2^31. */
+typedef struct {
+    const void *wq;   /* [Hq*dh][d_model] */
+    const void *wk;   /* [dh][d_model]    */
+    const void *wv;   /* [dh][d_model]    */
+    const void *wo;   /* [d_model][Hq*dh] */
+} rglru_attn_proj;
+
+/* Workspace bytes of rglru_attn_layer_fwd (no initialisation needed). */
+int rglru_attn_layer_workspace_size(const rglru_attn_desc *desc, int64_t d_model, const rglru_layer *lw,
+                                    size_t *bytes);
+
+int rglru_attn_layer_fwd(const rglru_attn_desc *desc, int64_t d_model, int32_t rot, float rope_base, int64_t pos0,
+                         const rglru_attn_proj *ap, const rglru_layer *lw, const void *x, void *y, void *kcache,
+                         void *vcache, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Short English text of a status code (static storage). */
 const char *rglru_status_string(int status);
 

@@ -56,7 +56,8 @@ TID = dict(u=0, conv_w=1, conv_b=2, W_a=3, W_x=4, lam_u=5, dy=6, h0=7,
            b_a=8, b_x=9, hist=10, dh_last=11,
            block_x=12, proj_in_1=13, proj_in_2=14, proj_out=15,
            attn_q=16, attn_k=17, attn_v=18, attn_hk=19, attn_hv=20,
-           tnorm_w=21, cnorm_w=22, gate_w=23, up_w=24, down_w=25)
+           tnorm_w=21, cnorm_w=22, gate_w=23, up_w=24, down_w=25,
+           wq=26, wk=27, wv=28, wo=29)
 
 C_CONST = 8.0
 
@@ -267,3 +268,22 @@ def make_layer_params(cfg: int, d_model: int, d_ff: int, io: str) -> LayerParams
     u = store(normal(seed_for(cfg, "up_w"), 0, d_ff * d_model) / math.sqrt(d_model), io).reshape(d_ff, d_model)
     dn = store(normal(seed_for(cfg, "down_w"), 0, d_model * d_ff) / math.sqrt(d_ff), io).reshape(d_model, d_ff)
     return LayerParams(tn, cn, g, u, dn)
+
+
+@dataclasses.dataclass
+class AttnProj:
+    """Attention layer projections [out][in] in the io form: wq [Hq*dh][d_model],
+    wk, wv [dh][d_model], wo [d_model][Hq*dh]."""
+    wq: np.ndarray
+    wk: np.ndarray
+    wv: np.ndarray
+    wo: np.ndarray
+
+
+def make_attn_proj(cfg: int, d_model: int, Hq: int, dh: int, io: str) -> AttnProj:
+    s_in, s_o = 1.0 / math.sqrt(d_model), 1.0 / math.sqrt(Hq * dh)
+    wq = store(s_in * normal(seed_for(cfg, "wq"), 0, Hq * dh * d_model), io).reshape(Hq * dh, d_model)
+    wk = store(s_in * normal(seed_for(cfg, "wk"), 0, dh * d_model), io).reshape(dh, d_model)
+    wv = store(s_in * normal(seed_for(cfg, "wv"), 0, dh * d_model), io).reshape(dh, d_model)
+    wo = store(s_o * normal(seed_for(cfg, "wo"), 0, d_model * Hq * dh), io).reshape(d_model, Hq * dh)
+    return AttnProj(wq, wk, wv, wo)
