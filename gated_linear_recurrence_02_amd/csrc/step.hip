@@ -11,19 +11,23 @@
 // kernel is shaped for parallelism and latency, not reuse: one workgroup
 // (8 waves) per (16 streams, 256-channel block), 160 workgroups at B = 256,
 // D = 2560.
-//   1. the gate weights the lane needs and its own outputs' state, history
-//      and input -- 2 channels x 4 streams -- start loading first;
+//   1. every load is issued at once, in the order the values are needed:
+//      the conv's inputs and taps, the gate weights the lane needs, then its
+//      own outputs' state and gate biases -- 2 channels x 4 streams;
 //   2. every thread computes the conv of 8 channels of one stream of the
-//      block's input tile (16 streams x 256 channels) into LDS;
+//      block's input tile (16 streams x 256 channels) into LDS (bf16 for
+//      the matrix cores, fp32 for the update), and the first 256 threads the
+//      decay constant of one channel; after the barrier the same thread
+//      writes its 8 channels of history back, shifted by one token;
 //   3. bf16: wave w computes the gate products of output channels
 //      32w .. 32w+31 (two 16-channel tiles) for the 16 streams with
 //      v_mfma_f32_16x16x32_bf16 (A = x tile rows, B = W rows read from
 //      memory), which leaves lane l with streams 4(l/16)+i of channels
 //      32w + 16t + l%16; fp32: the same outputs by fp32 FMAs;
 //   4. gates, decay, normalisation and the state update for those 8
-//      elements; state, output and history are rewritten in place.
+//      elements; state and output are rewritten in place.
 // A workgroup reads and rewrites the history of its own (streams, block)
-// only, after the barrier that ends the reads of step 2.
+// only, after the barrier that ends the reads of step 1.
 #include "common.h"
 #include "gatemath.h"
 #include "internal.h"
@@ -148,56 +152,87 @@ __global__ __launch_bounds__(512) void step_kernel(int B, int D, float c, const 
                                                    T *hist, float *hstate, T *y_t)
 {
     constexpr int S = XTile<T>::STRIDE;
-    __shared__ __attribute__((aligned(16))) T Xs[SB * S];
-    const int sb0 = blockIdx.x * SB, g = blockIdx.y;
+    constexpr int S32 = XTile<float>::STRIDE;
+    __shared__ __attribute__((aligned(16))) T Xs[SB * S];          // conv output, MFMA operand
+    __shared__ __attribute__((aligned(16))) float X32[SB * S32];   // the same in fp32
+    __shared__ float ncs_s[256];   // -c softplus(-Lambda) of the block's channels
+    // Workgroup id -> (stream tile, block), block-major over the XCDs:
+    // consecutive ids go round-robin to the 8 XCDs, so ids that share id % 8
+    // get consecutive (block, tile) pairs and each XCD's L2 holds the gate
+    // weights of two or three blocks rather than all of them.  The map is a
+    // permutation of the ids whatever the hardware does.
+    const int nwg = gridDim.x, ntile = (B + SB - 1) / SB;
+    const int xcd = blockIdx.x % 8, loc = blockIdx.x / 8;
+    const int pair = xcd * (nwg / 8) + (xcd < nwg % 8 ? xcd : nwg % 8) + loc;
+    const int sb0 = (pair % ntile) * SB, g = pair / ntile;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // optional per-channel vectors: a null one reads a valid array and is
+    // replaced by zeros, so that no load sits behind a branch
+    const float *cbp = cb ? cb : Lambda, *bap = ba ? ba : Lambda, *bxp = bx ? bx : Lambda;
 
-    // 1. the gate weights of the lane's outputs, then the lane's outputs'
-    //    state, history and input (stored values, converted when used):
-    //    element e = 4t + i is stream sb0 + 4(l/16) + i of channel
-    //    oc0 + 16t + l%16 of the block
+    // 1. every load, in the order the values are needed: the conv's inputs
+    //    and taps (8 channels of one stream per thread), the gate weights of
+    //    the lane's outputs, then the lane's outputs' state and gate biases
+    //    -- element e = 4t + i is stream sb0 + 4(l/16) + i of channel
+    //    oc0 + 16t + l%16 of the block.  Streams past B read stream B - 1 and
+    //    are not stored.
+    const int cg = tid & 31, sl = tid >> 5;
+    const long sc = sb0 + sl < B ? sb0 + sl : B - 1;
+    const int dc = g * 256 + 8 * cg;
+    float a0[8], a1[8], a2[8], a3[8];
+    load8(hist + (sc * 3 + 0) * D + dc, a0);
+    load8(hist + (sc * 3 + 1) * D + dc, a1);
+    load8(hist + (sc * 3 + 2) * D + dc, a2);
+    load8(u_t + sc * D + dc, a3);
+    f32x4 taps[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) taps[e] = *(const f32x4 *)(cw + 4 * (long)(dc + e));
+    float cbv[8];
+    load8(cbp + dc, cbv);
+    const float lam = Lambda[g * 256 + (tid & 255)];   // used by the first 256 threads
+
     const int oc0 = 32 * wave;
     WOps<T> wop;
     load_wops(wop, Wa + (size_t)g * 65536, Wx + (size_t)g * 65536, oc0, lane);
     float hv[8];
-    T h0v[8], h1v[8], h2v[8], uv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const int s = sb0 + 4 * (lane >> 4) + (e & 3);
-        const int d = g * 256 + oc0 + 16 * (e >> 2) + (lane & 15);
-        const bool ok = s < B;
-        const long sd = ok ? (long)s * D + d : d;   // a valid address either way
-        hv[e] = hstate[sd];
-        h0v[e] = hist[((ok ? (long)s : 0) * 3 + 0) * D + d];
-        h1v[e] = hist[((ok ? (long)s : 0) * 3 + 1) * D + d];
-        h2v[e] = hist[((ok ? (long)s : 0) * 3 + 2) * D + d];
-        uv[e] = u_t[sd];
+        const int s0 = sb0 + 4 * (lane >> 4) + (e & 3);
+        const long s = s0 < B ? s0 : B - 1;
+        hv[e] = hstate[s * D + g * 256 + oc0 + 16 * (e >> 2) + (lane & 15)];
     }
+    float bav[2], bxv[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int d = g * 256 + oc0 + 16 * t + (lane & 15);
+        bav[t] = bap[d];
+        bxv[t] = bxp[d];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep every request ahead of the first wait
 
-    // 2. conv of the input tile: 8 channels of one stream per thread
+    // 2. conv of the input tile into LDS; the decay constants of the block
     {
-        const int cg = tid & 31, sl = tid >> 5, s = sb0 + sl;
-        const int dc = g * 256 + 8 * cg;
         float x[8];
-        if (s < B) {
-            float a0[8], a1[8], a2[8], a3[8];
-            load8(hist + ((long)s * 3 + 0) * D + dc, a0);
-            load8(hist + ((long)s * 3 + 1) * D + dc, a1);
-            load8(hist + ((long)s * 3 + 2) * D + dc, a2);
-            load8(u_t + (long)s * D + dc, a3);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const f32x4 t = *(const f32x4 *)(cw + 4 * (long)(dc + e));
-                const float bias = cb ? cb[dc + e] : 0.0f;
-                x[e] = fmaf(t[3], a3[e], fmaf(t[2], a2[e], fmaf(t[1], a1[e], fmaf(t[0], a0[e], bias))));
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+        for (int e = 0; e < 8; ++e) {
+            const f32x4 t = taps[e];
+            const float bias = cb ? cbv[e] : 0.0f;
+            x[e] = fmaf(t[3], a3[e], fmaf(t[2], a2[e], fmaf(t[1], a1[e], fmaf(t[0], a0[e], bias))));
         }
         store8(Xs + sl * S + 8 * cg, x);
+        store8(X32 + sl * S32 + 8 * cg, x);
+        const float ncs = -c * softplus_acc(-lam);
+        if (tid < 256) ncs_s[tid] = ncs;
     }
-    __syncthreads();   // the tile is complete and every read of the history is done
+    __syncthreads();   // the tiles are complete and every read of the history is done
+
+    // the history moves one token on: the thread that read 8 channels of a
+    // stream writes them back one position earlier, with the new input last
+    if (sb0 + sl < B) {
+        store8(hist + (sc * 3 + 0) * D + dc, a1);
+        store8(hist + (sc * 3 + 1) * D + dc, a2);
+        store8(hist + (sc * 3 + 2) * D + dc, a3);
+    }
 
     // 3. gate pre-activations of the lane's outputs
     float za[8], zx[8];
@@ -206,19 +241,16 @@ __global__ __launch_bounds__(512) void step_kernel(int B, int D, float c, const 
     // 4. gates, decay, normalisation, state update
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        const int d = g * 256 + oc0 + 16 * t + (lane & 15);
-        const f32x4 cwd = *(const f32x4 *)(cw + 4 * (long)d);
-        const float bd = cb ? cb[d] : 0.0f;
-        const float ncs = -c * softplus_acc(-Lambda[d]);
-        const float bav = ba ? ba[d] : 0.0f, bxv = bx ? bx[d] : 0.0f;
-        const float kba = -LOG2E * bav, kbx = -LOG2E * bxv, kdec = LOG2E * ncs;
+        const int ch = oc0 + 16 * t + (lane & 15);
+        const int d = g * 256 + ch;
+        const float ncs = ncs_s[ch];
+        const float bat = ba ? bav[t] : 0.0f, bxt = bx ? bxv[t] : 0.0f;
+        const float kba = -LOG2E * bat, kbx = -LOG2E * bxt, kdec = LOG2E * ncs;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = 4 * t + i;
-            const int s = sb0 + 4 * (lane >> 4) + i;
-            if (s >= B) continue;
-            const float x = fmaf(cwd[3], to_f32(uv[e]),
-                                 fmaf(cwd[2], to_f32(h2v[e]), fmaf(cwd[1], to_f32(h1v[e]), fmaf(cwd[0], to_f32(h0v[e]), bd))));
+            const int sr = 4 * (lane >> 4) + i, s = sb0 + sr;
+            const float x = X32[sr * S32 + ch];
             float a, bb;
             if constexpr (sizeof(T) == 2) {
                 const float rr = hw_rcp(1.0f + hw_exp2(fmaf(za[e], -LOG2E, kba)));
@@ -226,18 +258,17 @@ __global__ __launch_bounds__(512) void step_kernel(int B, int D, float c, const 
                 a = hw_exp2(rr * kdec);
                 bb = hw_sqrt(fmaf(-a, a, 1.0f)) * ii * x;
             } else {
-                const float rr = sigmoid_acc(za[e] + bav);
-                const float ii = sigmoid_acc(zx[e] + bxv);
+                const float rr = sigmoid_acc(za[e] + bat);
+                const float ii = sigmoid_acc(zx[e] + bxt);
                 const float l = ncs * rr;
                 a = expf(l);
                 bb = sqrtf(-expm1f(2.0f * l)) * ii * x;
             }
             const float hn = fmaf(a, hv[e], bb);
-            hstate[(long)s * D + d] = hn;
-            y_t[(long)s * D + d] = from_f32<T>(hn);
-            hist[((long)s * 3 + 0) * D + d] = h1v[e];
-            hist[((long)s * 3 + 1) * D + d] = h2v[e];
-            hist[((long)s * 3 + 2) * D + d] = uv[e];
+            if (s < B) {
+                hstate[(long)s * D + d] = hn;
+                y_t[(long)s * D + d] = from_f32<T>(hn);
+            }
         }
     }
 }
@@ -246,7 +277,7 @@ template <typename T>
 void launch_step_t(const rglru_desc &d, const rglru_weights &w, const void *u_t, void *hist,
                    float *h, void *y_t, hipStream_t s)
 {
-    const dim3 grid((unsigned)((d.B + SB - 1) / SB), (unsigned)d.H);
+    const dim3 grid((unsigned)(((d.B + SB - 1) / SB) * d.H));
     hipLaunchKernelGGL((step_kernel<T>), grid, dim3(512), 0, s, (int)d.B, (int)d.D, d.c,
                        (const T *)u_t, w.conv_w, w.conv_b, (const T *)w.W_a, w.b_a,
                        (const T *)w.W_x, w.b_x, w.Lambda, (T *)hist, h, (T *)y_t);
