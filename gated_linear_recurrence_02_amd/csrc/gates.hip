@@ -14,7 +14,8 @@
 // matrix cores; tiles alternate between two LDS buffers.  Lane l of wave w
 // gets channel 32w + l%32 of rows 16(l/32) .. +15 back from the MFMA output
 // layout; r and i go through an LDS output tile ([token][channel]) and leave
-// in 16-byte pieces rather than as 2-byte stores.
+// in 16-byte nontemporal stores rather than as 2-byte stores (streaming them
+// past the caches measured 5% faster at 2B width).
 // fp32: one workgroup per (tile, block); the tile is staged in LDS and the
 // products run on fp32 FMAs.
 #include "common.h"
@@ -24,6 +25,8 @@
 namespace rglru {
 
 namespace {
+
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));   // nontemporal stores
 
 template <typename T>
 __global__ __launch_bounds__(512) void gates_kernel(long rows, int D, const T *x, const T *Wa,
@@ -135,8 +138,10 @@ __global__ __launch_bounds__(512) void gates_kernel_w(long rows, int D, int G, i
         for (int h = 0; h < 2; ++h) {
             const long row = q * 32 + lr + 16 * h;
             if (row < rows) {
-                *(uint4 *)(r + row * D + g * 256 + lc) = *(const uint4 *)(&Os[0][(lr + 16 * h) * OS + lc]);
-                *(uint4 *)(i + row * D + g * 256 + lc) = *(const uint4 *)(&Os[1][(lr + 16 * h) * OS + lc]);
+                __builtin_nontemporal_store(*(const nt_u32x4 *)(&Os[0][(lr + 16 * h) * OS + lc]),
+                                            (nt_u32x4 *)(r + row * D + g * 256 + lc));
+                __builtin_nontemporal_store(*(const nt_u32x4 *)(&Os[1][(lr + 16 * h) * OS + lc]),
+                                            (nt_u32x4 *)(i + row * D + g * 256 + lc));
             }
         }
     }
