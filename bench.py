@@ -97,9 +97,28 @@ def cpu_baseline(prob, budget_s: float):
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    return dict(value=done / dt, unit="tokens*ch/s", cores=oracle.num_threads(), kind="oracle",
+    cores = oracle.num_threads()
+    # the tiny fp32 configuration (B=1 T=256 D=256) on one thread, for scale
+    c0 = synth.CONFIGS[0]
+    p0 = synth.make_params(0, c0.D, c0.H, c0.io)
+    u0 = synth.widen(synth.make_activation(0, "u", (c0.B, c0.T, c0.D), c0.io))
+    op0 = {k: synth.widen(getattr(p0, k)) for k in ("conv_w", "conv_b", "W_a", "b_a", "W_x", "b_x", "Lambda")}
+    oracle.set_threads(1)
+    try:
+        t1 = time.perf_counter()
+        reps = 0
+        while reps < 3 or time.perf_counter() - t1 < 0.5:
+            oracle.fwd(u0, **op0)
+            reps += 1
+        dt1 = (time.perf_counter() - t1) / reps
+    finally:
+        oracle.set_threads(cores)
+    return dict(value=done / dt, unit="tokens*ch/s", cores=cores, kind="oracle",
                 sample=f"{n} of {len(slices)} (stream, 256-channel block) slices of the 2B-width "
-                       f"prefill workload ({done} tokens*ch), double precision, {dt:.1f} s")
+                       f"prefill workload ({done} tokens*ch), double precision, {dt:.1f} s",
+                single_thread_tiny=dict(value=u0.size / dt1, unit="tokens*ch/s", cores=1,
+                                        sample="B=1 T=256 D=256 fp32 configuration, whole, "
+                                               f"{dt1 * 1e3:.1f} ms per call"))
 
 
 class Timer:
@@ -165,6 +184,60 @@ def copy_calibration(torch, dev, n=10):
                       "kernel_ms": ms, "gbs": 2 * nbytes / (ms * 1e-3) / 1e9}), flush=True)
 
 
+def micro(torch, dev):
+    """Ceilings on this GPU: vector-ALU rates (FMA and the transcendentals the
+    gate math uses), bf16 MFMA rate and plain copy bandwidth, from the kernels
+    of librglru_micro.so, each timed with HIP events on the launch stream."""
+    import ctypes
+
+    import numpy as np
+    path = os.path.join(ROOT, "gated_linear_recurrence_02_amd", "librglru_micro.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is not built; run gated_linear_recurrence_02_amd/build.py")
+    L = ctypes.CDLL(path)
+    L.rglru_micro_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.rglru_micro_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.rglru_micro_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                   ctypes.c_void_p]
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    tm = Timer(torch, stream)
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = 8 * ncu   # 8 workgroups of 4 waves per CU: 8 waves per SIMD
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    res = {"cus": ncu, "clock_for_cycles_ghz": 2.4}
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(f"micro kernel launch failed: hip error {rc}")
+
+    iters = 2048
+    for kind, name in enumerate(("fma", "exp2", "rcp", "sqrt", "exp2+fma")):
+        kms, _ = tm.calls(lambda k: check(L.rglru_micro_valu(kind, blocks, iters, out.data_ptr(), sp)), 5, 2)
+        ms = float(np.median(kms))
+        wave_instr_per_simd = blocks * 4 * iters * 8 / (ncu * 4)
+        ns = ms * 1e6 / wave_instr_per_simd
+        res[f"valu_{name}"] = {"lane_ops_per_s": blocks * 256 * iters * 8 / (ms * 1e-3),
+                               "ns_per_wave_instr_per_simd": ns, "cycles_at_2p4ghz": ns * 2.4}
+    kms, _ = tm.calls(lambda k: check(L.rglru_micro_mfma(blocks, 1024, out.data_ptr(), sp)), 5, 2)
+    ms = float(np.median(kms))
+    flops = blocks * 4 * 1024 * 4 * 32768
+    res["mfma_bf16_32x32x16"] = {"tflops": flops / (ms * 1e-3) / 1e12,
+                                 "frac_of_2500": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for cb in (ncu * 4, ncu * 16):
+        kms, _ = tm.calls(lambda k: check(L.rglru_micro_copy(src.data_ptr(), dst.data_ptr(), nbytes, cb, sp)),
+                          10, 2)
+        ms = float(np.median(kms))
+        res[f"copy_1gib_{cb}_workgroups"] = {"gbs": 2 * nbytes / (ms * 1e-3) / 1e9,
+                                             "frac_of_8000": 2 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    if not torch.equal(src, dst):
+        raise RuntimeError("copy microbenchmark: destination differs from source")
+    print(json.dumps({"micro": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,6 +248,8 @@ def main():
     ap.add_argument("--rows", default=",".join(ALL_ROWS),
                     help="comma-separated extra rows to time (empty for the headline only): "
                          + ",".join(ALL_ROWS))
+    ap.add_argument("--micro", action="store_true",
+                    help="run the ALU, MFMA and copy microbenchmarks and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device copy and exit")
     args = ap.parse_args()
@@ -196,6 +271,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.copy_calibration:
         copy_calibration(torch, dev)
+        return
+    if args.micro:
+        micro(torch, dev)
         return
     glr.lib()
     stream = torch.cuda.current_stream(dev)
@@ -543,6 +621,8 @@ def main():
         _say(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(dict(B=B, T=T, D=D, H=H, params=params, u=u_host),
                                            args.cpu_seconds)
+        # the whole-job rate over the oracle's, both on the headline workload
+        out["cpu_baseline"]["gpu_over_oracle"] = out["value"] / out["cpu_baseline"]["value"]
     print(json.dumps(out), flush=True)
 
 

@@ -1,4 +1,5 @@
-"""Build librglru.so (all HIP sources in csrc/) for gfx950 with hipcc.
+"""Build librglru.so (all HIP sources in csrc/) and the microbenchmark library
+librglru_micro.so (micro/micro.hip) for gfx950 with hipcc.
 
 Every source is compiled with packed-FP32 instructions disabled
 (-Xclang -target-feature -Xclang -packed-fp32-ops); the host pass warns that
@@ -15,6 +16,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "librglru.so")
+MICRO_OUT = os.path.join(HERE, "librglru_micro.so")
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -46,8 +48,15 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, OUT)
+    # the microbenchmarks bench.py --micro runs: a library of their own
+    msrc = os.path.join(HERE, "micro", "micro.hip")
+    mtmp = MICRO_OUT + ".tmp"
+    r = subprocess.run([HIPCC, *FLAGS, "-shared", msrc, "-o", mtmp], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {msrc}:\n{r.stdout}\n{r.stderr}")
+    os.replace(mtmp, MICRO_OUT)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT} and {MICRO_OUT}")
     return OUT
 
 

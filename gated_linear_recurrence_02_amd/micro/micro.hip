@@ -1,0 +1,104 @@
+// micro.hip -- microbenchmarks of the ceilings the path's kernels are held
+// against on this GPU: vector-ALU throughput of plain FMAs and of the
+// transcendental instructions the gate and decay math uses (exp2, rcp,
+// sqrt), bf16 matrix-core throughput, and plain device copy bandwidth.
+// Built into its own library (librglru_micro.so), not part of librglru.so;
+// bench.py --micro launches these and times them with HIP events.
+//
+// Each kernel writes one value per thread so that nothing is optimised away;
+// the values themselves mean nothing.
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 8 independent chains per thread, `iters` rounds; KIND 0 fma, 1 exp2,
+// 2 rcp, 3 sqrt, 4 exp2 and fma alternating
+template <int KIND>
+__global__ __launch_bounds__(256) void valu_kernel(float *out, int iters, float s)
+{
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = s * (float)(threadIdx.x + j);
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (KIND == 0) v[j] = __builtin_fmaf(v[j], s, 0.5f);
+            if (KIND == 1) v[j] = __builtin_amdgcn_exp2f(v[j]);
+            if (KIND == 2) v[j] = __builtin_amdgcn_rcpf(v[j]);
+            if (KIND == 3) v[j] = __builtin_amdgcn_sqrtf(v[j]);
+            if (KIND == 4) v[j] = (j & 1) ? __builtin_amdgcn_exp2f(v[j]) : __builtin_fmaf(v[j], s, 0.5f);
+        }
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += v[j];
+    out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+// 4 independent v_mfma_f32_32x32x16_bf16 chains per wave, `iters` rounds
+__global__ __launch_bounds__(256) void mfma_kernel(float *out, int iters)
+{
+    bf16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = (__bf16)(0.001f * (float)(threadIdx.x + e));
+        b[e] = (__bf16)(0.002f * (float)(threadIdx.x - e));
+    }
+    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int i = 0; i < iters; ++i) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc += c0[e] + c1[e] + c2[e] + c3[e];
+    out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+// grid-stride copy of n 16-byte pieces
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4 *src, u32x4 *dst, size_t n)
+{
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += stride) dst[k] = src[k];
+}
+
+}  // namespace
+
+// kind: 0 fma, 1 exp2, 2 rcp, 3 sqrt, 4 exp2/fma alternating.  out holds
+// blocks * 256 floats.  Returns a hipError_t value.
+extern "C" int rglru_micro_valu(int kind, int blocks, int iters, float *out, hipStream_t s)
+{
+    if (kind < 0 || kind > 4 || blocks < 1 || iters < 1 || !out) return (int)hipErrorInvalidValue;
+    const dim3 g((unsigned)blocks), b(256);
+    if (kind == 0) valu_kernel<0><<<g, b, 0, s>>>(out, iters, 1.0001f);
+    else if (kind == 1) valu_kernel<1><<<g, b, 0, s>>>(out, iters, 1.0001f);
+    else if (kind == 2) valu_kernel<2><<<g, b, 0, s>>>(out, iters, 1.0001f);
+    else if (kind == 3) valu_kernel<3><<<g, b, 0, s>>>(out, iters, 1.0001f);
+    else valu_kernel<4><<<g, b, 0, s>>>(out, iters, 1.0001f);
+    return (int)hipGetLastError();
+}
+
+// 4 * iters MFMAs of 32768 flops per wave; out holds blocks * 256 floats
+extern "C" int rglru_micro_mfma(int blocks, int iters, float *out, hipStream_t s)
+{
+    if (blocks < 1 || iters < 1 || !out) return (int)hipErrorInvalidValue;
+    mfma_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(out, iters);
+    return (int)hipGetLastError();
+}
+
+// copies `bytes` (a multiple of 16; both pointers 16-byte aligned)
+extern "C" int rglru_micro_copy(const void *src, void *dst, size_t bytes, int blocks, hipStream_t s)
+{
+    if (!src || !dst || bytes % 16 || ((uintptr_t)src | (uintptr_t)dst) % 16 || blocks < 1)
+        return (int)hipErrorInvalidValue;
+    copy_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>((const u32x4 *)src, (u32x4 *)dst, bytes / 16);
+    return (int)hipGetLastError();
+}
