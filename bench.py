@@ -173,6 +173,18 @@ def row(workload, kms, tokch, nbytes, flops=None, note=None, bound="hbm"):
 
 
 def copy_calibration(torch, dev, n=10):
+    # MFMA waves and FMA waves on the same SIMDs: alone and together
+    L.rglru_micro_mix.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    mblocks = 2 * ncu
+    mout = torch.empty(mblocks * 512, dtype=torch.float32, device=dev)
+    mix = {}
+    for mode, name in enumerate(("mfma_alone", "fma_alone", "together")):
+        kms, _ = tm.calls(lambda k: check(L.rglru_micro_mix(mode, mblocks, 512, 2048, mout.data_ptr(), sp)), 5, 2)
+        mix[name + "_ms"] = float(np.median(kms))
+    mix["together_over_max"] = mix["together_ms"] / max(mix["mfma_alone_ms"], mix["fma_alone_ms"])
+    mix["together_over_sum"] = mix["together_ms"] / (mix["mfma_alone_ms"] + mix["fma_alone_ms"])
+    res["mfma_fma_coexecution"] = mix
     nbytes = 1 << 30
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -224,6 +236,18 @@ def micro(torch, dev):
     flops = blocks * 4 * 1024 * 4 * 32768
     res["mfma_bf16_32x32x16"] = {"tflops": flops / (ms * 1e-3) / 1e12,
                                  "frac_of_2500": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    # MFMA waves and FMA waves on the same SIMDs: alone and together
+    L.rglru_micro_mix.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    mblocks = 2 * ncu
+    mout = torch.empty(mblocks * 512, dtype=torch.float32, device=dev)
+    mix = {}
+    for mode, name in enumerate(("mfma_alone", "fma_alone", "together")):
+        kms, _ = tm.calls(lambda k: check(L.rglru_micro_mix(mode, mblocks, 512, 2048, mout.data_ptr(), sp)), 5, 2)
+        mix[name + "_ms"] = float(np.median(kms))
+    mix["together_over_max"] = mix["together_ms"] / max(mix["mfma_alone_ms"], mix["fma_alone_ms"])
+    mix["together_over_sum"] = mix["together_ms"] / (mix["mfma_alone_ms"] + mix["fma_alone_ms"])
+    res["mfma_fma_coexecution"] = mix
     nbytes = 1 << 30
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)

@@ -63,6 +63,45 @@ __global__ __launch_bounds__(256) void mfma_kernel(float *out, int iters)
     out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+// co-execution: 8-wave workgroups, waves w and w + 4 share a SIMD.  mode 0:
+// waves 0..3 run MFMA chains, waves 4..7 return at once; mode 1: waves 4..7
+// run FMA chains, waves 0..3 return; mode 2: both at once.  If the matrix
+// cores and the vector ALU of a SIMD serve two waves at the same time, mode
+// 2 takes about as long as the slower of modes 0 and 1.
+__global__ __launch_bounds__(512) void mix_kernel(float *out, int mfma_iters, int fma_iters, int mode)
+{
+    const int wave = threadIdx.x >> 6;
+    float acc = 0.0f;
+    if (wave < 4 && mode != 1) {
+        bf16x8 a, b;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            a[e] = (__bf16)(0.001f * (float)(threadIdx.x + e));
+            b[e] = (__bf16)(0.002f * (float)(threadIdx.x - e));
+        }
+        f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+        for (int i = 0; i < mfma_iters; ++i) {
+            c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+            c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+            c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc += c0[e] + c1[e] + c2[e] + c3[e];
+    } else if (wave >= 4 && mode != 0) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = 1.0001f * (float)(threadIdx.x + j);
+        for (int i = 0; i < fma_iters; ++i) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = __builtin_fmaf(v[j], 1.0001f, 0.5f);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc += v[j];
+    }
+    out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
 // grid-stride copy of n 16-byte pieces
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4 *src, u32x4 *dst, size_t n)
 {
@@ -91,6 +130,15 @@ extern "C" int rglru_micro_mfma(int blocks, int iters, float *out, hipStream_t s
 {
     if (blocks < 1 || iters < 1 || !out) return (int)hipErrorInvalidValue;
     mfma_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(out, iters);
+    return (int)hipGetLastError();
+}
+
+// mode 0 MFMA waves only, 1 FMA waves only, 2 both; out holds blocks * 512 floats
+extern "C" int rglru_micro_mix(int mode, int blocks, int mfma_iters, int fma_iters, float *out, hipStream_t s)
+{
+    if (mode < 0 || mode > 2 || blocks < 1 || mfma_iters < 1 || fma_iters < 1 || !out)
+        return (int)hipErrorInvalidValue;
+    mix_kernel<<<dim3((unsigned)blocks), dim3(512), 0, s>>>(out, mfma_iters, fma_iters, mode);
     return (int)hipGetLastError();
 }
 
