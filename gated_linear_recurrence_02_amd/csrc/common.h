@@ -98,14 +98,18 @@ __device__ __forceinline__ float look_back(const uint64_t *aggA, const uint64_t 
                                            float accA = 1.0f, float accX = 0.0f)
 {
     uint32_t spins = 0;
+    // chunk indices and the stride fit 32 bits: one 32x32->64 multiply-add
+    // per chunk word offset instead of a full 64-bit product
+    const uint32_t st = (uint32_t)stride;
     while (k >= 0) {
         uint64_t wi[LB_BATCH], wa[LB_BATCH], wx[LB_BATCH];
 #pragma unroll
         for (int j = 0; j < LB_BATCH; ++j) {
-            const long kk = k - j >= 0 ? k - j : 0;
-            wi[j] = load_word(incl + kk * stride);
-            wa[j] = load_word(aggA + kk * stride);
-            wx[j] = load_word(aggX + kk * stride);
+            const int kk = max((int)k - j, 0);
+            const uint64_t o = (uint64_t)(uint32_t)kk * st;
+            wi[j] = load_word(incl + o);
+            wa[j] = load_word(aggA + o);
+            wx[j] = load_word(aggX + o);
         }
         int j = 0;
 #pragma unroll

@@ -299,8 +299,19 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
 
             float za[16], zx[16];
             if constexpr (MODE != 2) {
+                if constexpr (sizeof(T) == 2) {   // two tokens per conversion
+                    typedef __attribute__((ext_vector_type(2))) float f32x2v;
+                    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
 #pragma unroll
-                for (int k = 0; k < 16; ++k) Xs[(16 * half + k) * S + ch] = from_f32<T>(x[k]);
+                    for (int k = 0; k < 16; k += 2) {
+                        const bf16x2v pr = __builtin_convertvector(f32x2v{x[k], x[k + 1]}, bf16x2v);
+                        Xs[(16 * half + k) * S + ch] = pr.x;
+                        Xs[(16 * half + k + 1) * S + ch] = pr.y;
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) Xs[(16 * half + k) * S + ch] = from_f32<T>(x[k]);
+                }
                 __syncthreads();
                 if constexpr (WREG) {
                     const int r = lane & 31, kg = lane >> 5;
@@ -461,8 +472,20 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
             if (y && dv) {
                 T *dst = y + (row_b + tb) * p.D + d;
                 if ((c + 1) * CHUNK <= p.T) {
+                    if constexpr (sizeof(T) == 2) {
+                        // two tokens per conversion (the pair's halves go to two rows)
+                        typedef __attribute__((ext_vector_type(2))) float f32x2v;
+                        typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
 #pragma unroll
-                    for (int k = 0; k < 16; ++k) dst[(long)k * p.D] = from_f32<T>(zl[k]);
+                        for (int k = 0; k < 16; k += 2) {
+                            const bf16x2v pr = __builtin_convertvector(f32x2v{zl[k], zl[k + 1]}, bf16x2v);
+                            dst[(long)k * p.D] = pr.x;
+                            dst[(long)(k + 1) * p.D] = pr.y;
+                        }
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < 16; ++k) dst[(long)k * p.D] = from_f32<T>(zl[k]);
+                    }
                 } else {
 #pragma unroll
                     for (int k = 0; k < 16; ++k)
