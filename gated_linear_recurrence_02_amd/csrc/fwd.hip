@@ -186,6 +186,10 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
     const float bxv = (MODE != 2 && dv && p.bx) ? p.bx[d] : 0.0f;
     // fast-path forms: 2^(-log2e (z + b)) and 2^(log2e ncs r)
     const float kba = -LOG2E * bav, kbx = -LOG2E * bxv, kdec = LOG2E * ncs;
+    // a_t = 2^(kdec r_t) with r_t = 1 / (1 + e_t) is 2^(1 / ((1 + e_t) / kdec)):
+    // with 1 / kdec precomputed that is one FMA, no product.  A zero or tiny
+    // kdec takes +-FLT_MAX, which still gives a_t = 1 (never 0 * inf)
+    const float ikdec = kdec != 0.0f ? fminf(fmaxf(1.0f / kdec, -3.4e38f), 3.4e38f) : -3.4e38f;
 
     // gate weights of rows 32*wave .. +31 of block g, as MFMA B operands
     bf16x8 wa[WREG ? 16 : 1], wx[WREG ? 16 : 1];
@@ -373,12 +377,19 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
                         if (MODE == 2) {
                             rr = za[k];
                             ii = zx[k];
-                        } else {
+                        } else if (RI) {
                             rr = hw_rcp(1.0f + hw_exp2(fmaf(za[k], -LOG2E, kba)));
+                            ii = hw_rcp(1.0f + hw_exp2(fmaf(zx[k], -LOG2E, kbx)));
+                        } else {   // r_t itself is not needed, only a_t
+                            rr = 0.0f;
                             ii = hw_rcp(1.0f + hw_exp2(fmaf(zx[k], -LOG2E, kbx)));
                         }
                         if constexpr (RI) put_ri(k, rr, ii);
-                        a = hw_exp2(rr * kdec);
+                        if (MODE == 2 || RI) a = hw_exp2(rr * kdec);
+                        else {
+                            const float er = hw_exp2(fmaf(za[k], -LOG2E, kba));
+                            a = hw_exp2(hw_rcp(fmaf(er, ikdec, ikdec)));
+                        }
                         bb = hw_sqrt(fmaf(-a, a, 1.0f)) * ii * x[k];
                     } else {
                         float rr, ii;
