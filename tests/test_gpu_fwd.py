@@ -115,6 +115,23 @@ def test_mode_a_ragged_lengths_with_state(T):
     assert np.array_equal(ho.cpu().view(torch.int16).numpy().view(np.uint16), want)
 
 
+def test_mode_a_bf16_extreme_decay_constants():
+    # Lambda far out on both sides: softplus(-Lambda) underflowing to zero
+    # (a_t = 1, the state carried unchanged), a normal but tiny decay
+    # constant, one at the edge of the float range, and a_t ~ 0 (h_t ~ i_t x_t)
+    prob = make_problem(1, B=2, T=100, with_state=True)
+    lam = prob.params.Lambda
+    K = prob.D // prob.H
+    for h, v in [(0, 120.0), (1, 60.0), (2, 88.5), (3, -20.0), (4, 30.0)]:
+        lam[h * K:(h + 1) * K] = v
+    _say("mode A bf16, B=2 T=100, Lambda blocks 120, 60, 88.5, -20, 30, with state")
+    y, hl, _ = _run_fwd(prob, h0=prob.h0, hist=prob.hist)
+    for b, h in [(0, 0), (1, 1), (0, 2), (1, 3), (0, 4), (1, 7)]:
+        ry, rh, _ = _oracle_slice(prob, b, h, prob.h0, prob.hist)
+        _cmp(f"y[b={b},h={h}]", prob.slice_block(from_dev(y), b, h), ry, TOL["bf16"])
+        _cmp(f"h_last[b={b},h={h}]", prob.slice_block(from_dev(hl), b, h), rh, TOL["bf16"])
+
+
 def test_mode_b_equals_conv_then_mode_b_oracle():
     prob = make_problem(1, B=2, T=200)
     _say("mode B: B=2 T=200 D=2560 bf16 (x = conv output from rglru_conv1d)")
