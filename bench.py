@@ -99,7 +99,7 @@ def cpu_baseline(prob, budget_s: float):
     dt = time.perf_counter() - t0
     cores = oracle.num_threads()
     # the tiny fp32 configuration (B=1 T=256 D=256) on one thread, for scale
-    c0 = synth.CONFIGS[0]
+    c0 = synth.TINY
     p0 = synth.make_params(0, c0.D, c0.H, c0.io)
     u0 = synth.widen(synth.make_activation(0, "u", (c0.B, c0.T, c0.D), c0.io))
     op0 = {k: synth.widen(getattr(p0, k)) for k in ("conv_w", "conv_b", "W_a", "b_a", "W_x", "b_x", "Lambda")}
@@ -316,7 +316,7 @@ def main():
         return p, w
 
     # ------------------------------------------------ headline: fused forward
-    cfg = synth.CONFIGS[1]
+    cfg = synth.PREFILL_2B
     B, T, D, H = cfg.B, cfg.T, cfg.D, cfg.H
     params, w = weights(cfg)
     u_host = synth.make_u(cfg)
@@ -502,7 +502,7 @@ def main():
         torch.cuda.empty_cache()
 
     if "long" in rows:
-        c2 = synth.CONFIGS[2]
+        c2 = synth.PREFILL_32K
         _, w2 = weights(c2)
         u2 = dev_t(synth.make_u(c2))
         l_sets = [dict(u=u2 if k == 0 else u2.clone(), y=torch.empty_like(u2),
@@ -523,7 +523,7 @@ def main():
         torch.cuda.empty_cache()
 
     if "decode" in rows:
-        c3 = synth.CONFIGS[3]
+        c3 = synth.DECODE_256
         _, w3 = weights(c3)
         n3 = c3.B * c3.D
         # the decode stream [steps][B][D]; call k reads the slice synth.make_decode_u(c3, k)
@@ -547,7 +547,7 @@ def main():
         torch.cuda.empty_cache()
 
     if "bwd" in rows:
-        c4 = synth.CONFIGS[4]
+        c4 = synth.FWD_BWD_9B
         _, w4 = weights(c4)
         u4 = dev_t(synth.make_u(c4))
         dy4 = dev_t(synth.make_dy(c4))

@@ -177,6 +177,9 @@ CONFIGS = [
     Config(4, "9B-width forward+backward", 4, 8192, 4096, 16, "bf16"),
 ]
 
+# the same workloads by name (the index stays the seed component)
+TINY, PREFILL_2B, PREFILL_32K, DECODE_256, FWD_BWD_9B = CONFIGS
+
 
 def lambda_from_uniform(u01: np.ndarray, c: float = C_CONST) -> np.ndarray:
     """Lambda = logit(u^(1/c)) with u = 0.9 + 0.099 * u01 (float64)."""

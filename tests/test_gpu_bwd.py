@@ -79,7 +79,7 @@ def test_bwd_fp32_ragged_with_all_optional_inputs():
 
 def test_bwd_fd_slice_of_9b_workload():
     # the finite-difference slice: batch 0, the first 16 tokens, 9B-width parameters
-    cfg = synth.CONFIGS[4]
+    cfg = synth.FWD_BWD_9B
     prob = make_problem(4, B=1, T=16)
     h0 = synth.store(synth.normal(synth.seed_for(4, "h0"), 0, cfg.D), "f32").reshape(1, cfg.D)
     dy = synth.make_activation(4, "dy", (1, 16, cfg.D), "bf16")
@@ -103,7 +103,7 @@ def test_bwd_bf16_ragged(T):
 
 
 def test_bwd_config4_full_size():
-    cfg = synth.CONFIGS[4]
+    cfg = synth.FWD_BWD_9B
     prob = make_problem(4)
     dy = synth.make_dy(cfg)
     _say("bwd bf16 full size: B=4 T=8192 D=4096 H=16")

@@ -31,7 +31,7 @@ def _cmp(name, got, ref, tol):
 
 
 def _decode_run(steps, B=None, sample_streams=(0, 1, 77, 255), sample_heads=(0, 9)):
-    cfg = synth.CONFIGS[3]
+    cfg = synth.DECODE_256
     B = cfg.B if B is None else B
     D, H = cfg.D, cfg.H
     params = synth.make_params(cfg.idx, D, H, cfg.io)
@@ -93,7 +93,7 @@ def test_steps_equal_prefill_on_gpu():
 def test_decode_fp32_tiny_width():
     # fp32 I/O on the tiny workload's parameters (D = 256, one block),
     # 20 streams with a nonzero starting history and state, 10 steps
-    cfg = synth.CONFIGS[0]
+    cfg = synth.TINY
     B, D, steps = 20, cfg.D, 10
     params = synth.make_params(cfg.idx, D, cfg.H, "f32")
     w = glr.Weights(conv_w=to_dev(params.conv_w, DEV), W_a=to_dev(params.W_a, DEV),

@@ -60,7 +60,7 @@ def _check_fd(prob, dy, dh_last, entries):
 
 
 def _slice_problem():
-    cfg = synth.CONFIGS[4]
+    cfg = synth.FWD_BWD_9B
     K = cfg.K
     p = synth.make_params(cfg.idx, cfg.D, cfg.H, cfg.io)
     # batch 0, tokens < 16, head 0 of the 9B-width workload's seeded tensors
