@@ -16,7 +16,8 @@ prefill, the recurrent block around the path on the same shape (three
 projections plus the fused forward with the GeLU merge, d_model = D = 2560),
 the residual layer around it (two RMSNorms, the block, a gated GELU-tanh MLP
 of width 3 d_model, residual adds),
-the fused forward on the 32k-token prefill, 512 decode steps of 256 streams,
+the fused forward on the 32k-token prefill and on the 9B-width workload
+(B = 4, T = 8192, D = 4096), 512 decode steps of 256 streams,
 the backward of the 9B-width workload (B = 4, T = 8192, D = 4096), and the
 local sliding-window MQA (10 query heads of 256, window 2048) as prefill on
 the 2B-width and 32k-token shapes and as a decode step of 256 streams, and
@@ -47,7 +48,7 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 KERNEL_SOURCES = ("fwd.hip", "common.h", "gatemath.h")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "fwd_fused_2b_prefill_pmc.json")
-ALL_ROWS = ("conv1d", "gates", "scan", "block", "layer", "long", "decode", "bwd", "attn", "attn_long",
+ALL_ROWS = ("conv1d", "gates", "scan", "block", "layer", "long", "fwd9b", "decode", "bwd", "attn", "attn_long",
             "attn_decode", "attn_layer")
 
 
@@ -173,18 +174,10 @@ def row(workload, kms, tokch, nbytes, flops=None, note=None, bound="hbm"):
 
 
 def copy_calibration(torch, dev, n=10):
-    # MFMA waves and FMA waves on the same SIMDs: alone and together
-    L.rglru_micro_mix.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-                                  ctypes.c_void_p]
-    mblocks = 2 * ncu
-    mout = torch.empty(mblocks * 512, dtype=torch.float32, device=dev)
-    mix = {}
-    for mode, name in enumerate(("mfma_alone", "fma_alone", "together")):
-        kms, _ = tm.calls(lambda k: check(L.rglru_micro_mix(mode, mblocks, 512, 2048, mout.data_ptr(), sp)), 5, 2)
-        mix[name + "_ms"] = float(np.median(kms))
-    mix["together_over_max"] = mix["together_ms"] / max(mix["mfma_alone_ms"], mix["fma_alone_ms"])
-    mix["together_over_sum"] = mix["together_ms"] / (mix["mfma_alone_ms"] + mix["fma_alone_ms"])
-    res["mfma_fma_coexecution"] = mix
+    """A plain 1 GiB device copy (torch's copy kernel), timed with HIP events.
+    Run under rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE), its per-dispatch
+    readings against the known 1 GiB read and written give the scale factors
+    that turn the counters of the fused forward into HBM bytes."""
     nbytes = 1 << 30
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -520,6 +513,28 @@ def main():
         out["rows"]["long"] = row(f"rglru_scan_fwd mode A, long prefill (B=1 T={c2.T} D={c2.D} bf16)",
                                   kk, t2, fwd_bytes(c2.B, c2.T, c2.D, c2.H, 2))
         del l_sets, u2
+        torch.cuda.empty_cache()
+
+    if "fwd9b" in rows:
+        c4 = synth.FWD_BWD_9B
+        _, w4 = weights(c4)
+        u4 = dev_t(synth.make_u(c4))
+        f_sets = [dict(u=u4 if k == 0 else u4.clone(), y=torch.empty_like(u4),
+                       h=torch.empty((c4.B, c4.D), dtype=torch.float32, device=dev),
+                       hist=torch.empty((c4.B, 3, c4.D), dtype=torch.bfloat16, device=dev))
+                  for k in range(2)]
+        glr.workspace(glr.workspace_size(c4.B, c4.T, c4.D, c4.H, glr.BF16, glr.OP_SCAN_FWD), dev)
+        _say(f"fused forward, 9B width B={c4.B} T={c4.T} D={c4.D}")
+
+        def f4step(k):
+            s = f_sets[k % 2]
+            glr.scan_fwd(s["u"], w4, out=s["y"], h_last_out=s["h"], hist_out_buf=s["hist"])
+        kk, _ = tm.calls(f4step, 20, 3)
+        t4 = c4.B * c4.T * c4.D
+        out["rows"]["fwd9b"] = row(f"rglru_scan_fwd mode A, 9B width (B={c4.B} T={c4.T} D={c4.D} bf16)",
+                                   kk, t4, fwd_bytes(c4.B, c4.T, c4.D, c4.H, 2),
+                                   flops=2 * 2 * 256 * t4)
+        del f_sets, u4
         torch.cuda.empty_cache()
 
     if "decode" in rows:

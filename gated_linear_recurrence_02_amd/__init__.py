@@ -66,7 +66,7 @@ class _Block(ctypes.Structure):
 
 
 _lib = None
-SYMBOLS = ("rglru_workspace_size", "rglru_conv1d", "rglru_gates", "rglru_scan_fwd",
+SYMBOLS = ("rglru_workspace_size", "rglru_workspace_status", "rglru_conv1d", "rglru_gates", "rglru_scan_fwd",
            "rglru_step", "rglru_scan_bwd", "rglru_block_workspace_size", "rglru_block_fwd",
            "rglru_attn_fwd", "rglru_attn_workspace_size", "rglru_attn_step", "rglru_layer_workspace_size",
            "rglru_layer_fwd", "rglru_attn_layer_workspace_size", "rglru_attn_layer_fwd",
@@ -85,6 +85,7 @@ def lib():
         L.rglru_status_string.restype = ctypes.c_char_p
         L.rglru_status_string.argtypes = [ctypes.c_int]
         L.rglru_workspace_size.argtypes = [D, ctypes.c_int, ctypes.POINTER(sz)]
+        L.rglru_workspace_status.argtypes = [vp, sz, vp]
         L.rglru_conv1d.argtypes = [D, vp, vp, vp, vp, vp, vp, vp]
         L.rglru_gates.argtypes = [D, W, vp, vp, vp, vp]
         L.rglru_scan_fwd.argtypes = [D, W, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -200,17 +201,17 @@ def block_workspace_size(B, T, D, H, d_model, io=BF16, c=8.0) -> int:
 
 def workspace(nbytes: int, device, kind: str = "fwd", key=None) -> torch.Tensor:
     """A zero-filled workspace of at least nbytes, one cached buffer per device
-    and kind ("fwd", "bwd", "block").
+    and kind ("fwd", "bwd", "block", ...).
 
     The library restores the workspace header at the end of every call, so the
     cached buffer can be reused by calls that run one after another (one
-    stream).  A forward-scan workspace holds only counters and tagged carry
-    words, so it serves calls of any shape.  The backward's and the block's
-    also keep plain data, which must not sit where a later call of another
-    layout expects carry words: when `key` (the layout: shape and dtype)
-    differs from the previous call's, the buffer is zero-filled again, on the
-    current stream, before it is handed out.  Calls that may overlap need
-    workspaces of their own."""
+    stream).  A forward-scan workspace holds only counters (at fixed offsets)
+    and tagged carry words, so it serves forward calls of any shape.  The
+    backward's and the block's also keep plain data, which must not sit where
+    a later call of another layout expects carry words: when `key` (the
+    layout: shape and dtype) differs from the previous call's, the buffer is
+    zero-filled again, on the current stream, before it is handed out.  Calls
+    that may overlap need workspaces of their own."""
     device = torch.device(device)
     ent = _ws_cache.get((device, kind))
     if ent is None or ent[0].numel() < nbytes:
@@ -220,6 +221,18 @@ def workspace(nbytes: int, device, kind: str = "fwd", key=None) -> torch.Tensor:
         ent[0].zero_()
         ent[1] = key
     return ent[0]
+
+
+def workspace_status(device, kind: str = "fwd") -> None:
+    """Wait for the current stream and raise RGLRUError if a chunk-carry wait
+    of a call that used the cached workspace of this kind gave up (its
+    outputs hold NaN); the report is cleared (rglru_workspace_status)."""
+    device = torch.device(device)
+    ent = _ws_cache.get((device, kind))
+    if ent is None:
+        return
+    _check(lib().rglru_workspace_status(_ptr(ent[0]), ent[0].numel(), _stream(device)),
+           "rglru_workspace_status")
 
 
 # ----------------------------------------------------------------- entry points

@@ -27,6 +27,7 @@ int check_desc(const rglru_desc *d, bool need_k256)
     const int64_t NC = (d->T + 31) / 32, G = (d->D + 255) / 256;
     if ((double)d->B * NC * G >= 2147483647.0) return RGLRU_ERR_SHAPE;   // work units fit a grid
     if (need_k256 && d->D / d->H != 256) return RGLRU_ERR_SHAPE;
+    if (G > MAX_CLAIM_GROUPS) return RGLRU_ERR_SHAPE;   // claim counters of the chunked scans
     if (!isfinite(d->c)) return RGLRU_ERR_ARG;
     return RGLRU_OK;
 }
@@ -129,8 +130,24 @@ const char *rglru_status_string(int status)
     case RGLRU_ERR_LAUNCH: return "HIP launch error";
     case RGLRU_ERR_ARG: return "inconsistent arguments";
     case RGLRU_ERR_BLAS: return "a rocBLAS call failed";
+    case RGLRU_ERR_TIMEOUT: return "a chunk-carry wait of an earlier call on this workspace gave up (its outputs hold NaN)";
     default: return "unknown status";
     }
+}
+
+int rglru_workspace_status(const void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (!ws) return RGLRU_ERR_NULL;
+    if (!aligned16(ws)) return RGLRU_ERR_ALIGN;
+    if (ws_bytes < 256) return RGLRU_ERR_WORKSPACE;
+    if (hipStreamSynchronize(stream) != hipSuccess) return RGLRU_ERR_LAUNCH;
+    uint32_t flag = 0;
+    char *word = (char *)ws + WS_ERROR_OFFSET;
+    if (hipMemcpy(&flag, word, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess) return RGLRU_ERR_LAUNCH;
+    if (flag == 0) return RGLRU_OK;
+    const uint32_t zero = 0;
+    if (hipMemcpy(word, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return RGLRU_ERR_LAUNCH;
+    return RGLRU_ERR_TIMEOUT;
 }
 
 int rglru_workspace_size(const rglru_desc *desc, int op, size_t *bytes)

@@ -6,9 +6,11 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "../../include/rglru.h"
+#include "internal.h"
 
 namespace rglru {
 
@@ -48,6 +50,7 @@ struct WsHeader {
     uint32_t pad[50];
 };
 static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
+static_assert(offsetof(WsHeader, error) == WS_ERROR_OFFSET, "timeout word where the host reads it");
 
 constexpr int CHUNK = 32;               // tokens per chunk (one 32-row MFMA tile)
 constexpr uint32_t SPIN_LIMIT = 1u << 22;
@@ -73,22 +76,32 @@ __device__ __forceinline__ bool get_word(const uint64_t *p, uint32_t tag, float 
 // the kernel ends), and acquire/release at agent scope would write back and
 // invalidate the whole L2 on every call.
 
-// Walk back from chunk `k` (the chunk just before the caller's) until a chunk
-// with a published inclusive state is found, composing published aggregates
-// on the way; chunk -1's end state is `h_before_first`.  (accA, accX) is the
-// composition of the chunks after k already walked over (identity by
-// default).  Words are indexed base + k * stride; chunks are numbered in the order the scan runs (a
-// reverse scan numbers them from the end of the sequence).  Returns the state
-// at the end of chunk k.  The words of LB_BATCH predecessors are loaded
-// together, so a walk over many published aggregates costs one memory round
-// trip per LB_BATCH chunks.  The walk only waits on chunks that were handed
-// out before the caller's chunk, so it ends once their aggregates are
-// published; a wait that exceeds SPIN_LIMIT polls flags the header and
-// returns NaN rather than hanging.  Two chunks per round: the words of one
-// round stay in registers across the wait, and at 4 chunks (24 registers)
-// the fused forward measured 3% slower at 2B width and 2% at 32k tokens
-// (1 chunk: 1% slower than 2); by the time a chunk's back half runs, its
-// predecessor has usually published its inclusive state.
+// Walk back from chunk `k` (the chunk just before the caller's) to the newest
+// chunk j <= k whose inclusive (end) state is published, passing over chunks
+// whose aggregate is published; chunk -1's end state is `h_before_first`.
+// Words are indexed base + k * stride; chunks are numbered in the order the
+// scan runs (a reverse scan numbers them from the end of the sequence).
+// Returns the state at the end of chunk k.
+//
+// The result is the same whatever the walk finds, bit for bit: every
+// inclusive state is the serial recurrence over chunk aggregates,
+//     e(-1) = h_before_first,   e(m) = fma(A_m, e(m-1), X_m),
+// and the aggregates of chunks j+1 .. k are folded onto e(j) forward, in chunk
+// order, with the same fma, so the same operations run on the same values
+// however far back the walk had to go (a look-back that composed the
+// aggregates backward would group the products differently from run to run).
+//
+// The words of LB_BATCH predecessors are loaded together.  When the walk ends
+// inside the first round, the aggregates are already in registers; a longer
+// walk loads them again (they are published, so the second load returns the
+// same words).  The walk only waits on chunks that were handed out before the
+// caller's chunk, so it ends once their aggregates are published; a wait
+// that exceeds SPIN_LIMIT flags the header and returns NaN rather than
+// hanging.  Two chunks per round: the words of one round stay in registers
+// across the wait, and at 4 chunks (24 registers) the fused forward measured
+// 3% slower at 2B width and 2% at 32k tokens (1 chunk: 1% slower than 2); by
+// the time a chunk's back half runs, its predecessor has usually published
+// its inclusive state.
 constexpr int LB_BATCH = 2;
 
 __device__ __forceinline__ uint64_t load_word(const uint64_t *p)
@@ -96,42 +109,61 @@ __device__ __forceinline__ uint64_t load_word(const uint64_t *p)
     return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ bool tagged(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
+__device__ __forceinline__ float word_val(uint64_t w) { return __uint_as_float((uint32_t)w); }
+
 __device__ __forceinline__ float look_back(const uint64_t *aggA, const uint64_t *aggX,
                                            const uint64_t *incl, long k, long stride,
-                                           float h_before_first, uint32_t tag, WsHeader *hdr,
-                                           float accA = 1.0f, float accX = 0.0f)
+                                           float h_before_first, uint32_t tag, WsHeader *hdr)
 {
     uint32_t spins = 0;
     // chunk indices and the stride fit 32 bits: one 32x32->64 multiply-add
     // per chunk word offset instead of a full 64-bit product
     const uint32_t st = (uint32_t)stride;
-    while (k >= 0) {
+    long j = k;                  // newest chunk not yet walked over
+    long jf = -1;                // chunk whose inclusive state starts the fold
+    float base = h_before_first;
+    while (j >= 0) {
         uint64_t wi[LB_BATCH], wa[LB_BATCH], wx[LB_BATCH];
 #pragma unroll
-        for (int j = 0; j < LB_BATCH; ++j) {
-            const int kk = max((int)k - j, 0);
+        for (int q = 0; q < LB_BATCH; ++q) {
+            const int kk = max((int)j - q, 0);
             const uint64_t o = (uint64_t)(uint32_t)kk * st;
-            wi[j] = load_word(incl + o);
-            wa[j] = load_word(aggA + o);
-            wx[j] = load_word(aggX + o);
+            wi[q] = load_word(incl + o);
+            wa[q] = load_word(aggA + o);
+            wx[q] = load_word(aggX + o);
         }
-        int j = 0;
+        int passed = 0;          // chunks of this round walked over
+        bool done = false;
 #pragma unroll
-        for (int jj = 0; jj < LB_BATCH; ++jj) {
-            if (j != jj) continue;             // an earlier slot stopped the walk
-            if (k - jj < 0) return fmaf(accA, h_before_first, accX);
-            if ((uint32_t)(wi[jj] >> 32) == tag) return fmaf(accA, __uint_as_float((uint32_t)wi[jj]), accX);
-            if ((uint32_t)(wa[jj] >> 32) == tag && (uint32_t)(wx[jj] >> 32) == tag) {
-                accX = fmaf(accA, __uint_as_float((uint32_t)wx[jj]), accX);
-                accA = accA * __uint_as_float((uint32_t)wa[jj]);
-                ++j;
+        for (int q = 0; q < LB_BATCH; ++q) {
+            if (done || passed != q) continue;   // an earlier slot ended the round
+            if (j - q < 0) {
+                done = true;                     // reached the start: fold onto h_before_first
+            } else if (tagged(wi[q], tag)) {
+                done = true;
+                jf = j - q;
+                base = word_val(wi[q]);
+            } else if (tagged(wa[q], tag) && tagged(wx[q], tag)) {
+                ++passed;
             }
         }
-        k -= j;
-        if (j == 0) {
-            // chunk k has not published yet: every chunk publishes its aggregate
+        if (!done && j - passed < 0) done = true;   // passed chunk 0
+        if (done) {
+            if (j == k) {   // short walk: the aggregates to fold are in hand
+                float s = base;
+#pragma unroll
+                for (int q = LB_BATCH - 1; q >= 0; --q)   // chunks k - q, oldest first
+                    if (q < passed) s = fmaf(word_val(wa[q]), s, word_val(wx[q]));
+                return s;
+            }
+            break;
+        }
+        j -= passed;
+        if (passed == 0) {
+            // chunk j has not published yet: every chunk publishes its aggregate
             // before its inclusive state, so poll that one word before reloading
-            while ((uint32_t)(load_word(aggX + k * stride) >> 32) != tag) {
+            while (!tagged(load_word(aggX + (uint64_t)(uint32_t)j * st), tag)) {
                 if (++spins > SPIN_LIMIT) {
                     __hip_atomic_store(&hdr->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     return __builtin_nanf("");
@@ -140,7 +172,21 @@ __device__ __forceinline__ float look_back(const uint64_t *aggA, const uint64_t 
             }
         }
     }
-    return fmaf(accA, h_before_first, accX);
+    // a walk longer than the first round: fold chunks jf+1 .. k, 4 at a time
+    float s = base;
+    for (long m = jf + 1; m <= k; m += 4) {
+        uint64_t a4[4], x4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint64_t o = (uint64_t)(uint32_t)min(m + q, k) * st;
+            a4[q] = load_word(aggA + o);
+            x4[q] = load_word(aggX + o);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (m + q <= k) s = fmaf(word_val(a4[q]), s, word_val(x4[q]));
+    }
+    return s;
 }
 
 // Finish of a persistent launch: workgroups count themselves in one of 8
@@ -211,8 +257,12 @@ __device__ __forceinline__ void finish_claimed(WsHeader *hdr, uint32_t *claims, 
     }
 }
 
-// Workspace bytes of the claim counters of `n` groups (a multiple of 256).
-inline size_t claim_bytes(int64_t n) { return (size_t)((n * 4 + 255) / 256) * 256; }
+// The claim counters sit in a region of fixed size right after the header,
+// one 32-bit counter per group, for up to MAX_CLAIM_GROUPS groups.  Its size
+// does not depend on the shape, so the carry words of one call can never
+// land where a later call of another shape keeps its counters: a forward
+// workspace serves calls of any shape.
+constexpr size_t CLAIM_REGION_BYTES = (size_t)MAX_CLAIM_GROUPS * 4;
 
 // Element `e` of an array whose base is the same for the whole wave: the
 // 32-bit byte offset lets the compiler use scalar-base addressing.

@@ -41,6 +41,8 @@
 // on anything, processes its units in claim order, and every wait is for a
 // unit of the same block with a smaller index, which was claimed earlier by a
 // running workgroup; by induction on the unit index every wait ends.
+#include <stdlib.h>
+
 #include <mutex>
 #include <type_traits>
 
@@ -584,8 +586,14 @@ void launch_mode(FwdParams p, hipStream_t s)
     static_assert(32 * 264 * 2 + 512 * PSTRIDE * 4 + 2 * ST_BYTES + 2 * GT_BYTES + 16 <= 160 * 1024,
                   "LDS budget (bf16)");
     const LaunchShape ls = fwd_shape<T, MODE>();
-    // workgroups per block: fill the resident slots, never more than the units
+    // workgroups per block: fill the resident slots, never more than the units;
+    // RGLRU_FWD_GROUP_WORKGROUPS (a positive integer) caps the count, which
+    // changes nothing in the results (work is claimed in order at run time)
     long wpg = ((long)ls.ncu * ls.occ) / p.G;
+    if (const char *cap = getenv("RGLRU_FWD_GROUP_WORKGROUPS")) {
+        const long c = atol(cap);
+        if (c > 0 && c < wpg) wpg = c;
+    }
     if (wpg < 1) wpg = 1;
     if (wpg > p.units) wpg = p.units;
     const long grid = (long)p.G * wpg;
@@ -637,7 +645,7 @@ void run_fwd(const rglru_desc &d, const rglru_weights &w, int mode, const void *
     p.hdr = (WsHeader *)ws;
     p.claim = (uint32_t *)((char *)ws + sizeof(WsHeader));
     const size_t nw = (size_t)d.B * p.NC * d.D;
-    p.aggA = (uint64_t *)((char *)ws + sizeof(WsHeader) + claim_bytes(p.G));
+    p.aggA = (uint64_t *)((char *)ws + sizeof(WsHeader) + CLAIM_REGION_BYTES);
     p.aggX = p.aggA + nw;
     p.incl = p.aggX + nw;
     if (d.io == RGLRU_BF16) launch_t<bf16>(p, mode, s);
@@ -649,7 +657,8 @@ void run_fwd(const rglru_desc &d, const rglru_weights &w, int mode, const void *
 size_t fwd_workspace_bytes(int64_t B, int64_t T, int64_t D)
 {
     const int64_t NC = (T + CHUNK - 1) / CHUNK, G = (D + 255) / 256;
-    return sizeof(WsHeader) + claim_bytes(G) + 3 * (size_t)B * NC * D * sizeof(uint64_t);
+    (void)G;
+    return sizeof(WsHeader) + CLAIM_REGION_BYTES + 3 * (size_t)B * NC * D * sizeof(uint64_t);
 }
 
 void launch_scan_fwd(const rglru_desc &d, const rglru_weights &w, int mode, const void *in,

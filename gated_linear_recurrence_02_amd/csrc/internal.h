@@ -10,6 +10,13 @@
 
 namespace rglru {
 
+// Largest number of 256-channel groups a chunked scan serves: its workspace
+// keeps one claim counter per group in a region of fixed size.
+constexpr int MAX_CLAIM_GROUPS = 4096;
+// Byte offset of the look-back timeout word in the header that starts every
+// scan workspace (the forward's, the backward's, the block's and the layer's).
+constexpr size_t WS_ERROR_OFFSET = 12;
+
 size_t fwd_workspace_bytes(int64_t B, int64_t T, int64_t D);
 // esz: bytes per activation element (2 for bf16 I/O, 4 for fp32)
 size_t bwd_workspace_bytes(int64_t B, int64_t T, int64_t D, int64_t H, size_t esz);

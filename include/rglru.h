@@ -20,8 +20,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * Pointers.  Every tensor pointer is DEVICE memory owned by the caller.  The
- *   library never synchronises the host: a return of RGLRU_OK means the work
- *   was enqueued on `stream`.  It allocates nothing and keeps no global state,
+ *   library does not synchronise the host (rglru_workspace_status, a report
+ *   the caller asks for, aside): a return of RGLRU_OK means the work was
+ *   enqueued on `stream`.  It allocates nothing and keeps no global state,
  *   with one exception: rglru_block_fwd and rglru_layer_fwd create one rocBLAS
  *   handle per device on their first call there (rocBLAS allocates its own
  *   device memory) and keep it until the process ends; and the first product
@@ -42,7 +43,7 @@
  * Dtypes.  desc->io is RGLRU_F32 or RGLRU_BF16 (activations, history and gate
  *   weights).  State, biases, Lambda, conv weights and every accumulation are
  *   fp32.
- * Shapes.  B, T, D, H >= 1, D % H == 0.  Every call that evaluates the gates
+ * Shapes.  B, T, D, H >= 1, D % H == 0, D <= 1048576.  Every call that evaluates the gates
  *   (rglru_gates, rglru_scan_fwd without r/i, rglru_step, rglru_scan_bwd)
  *   needs K = D / H = 256, the block width of the MFMA gate kernels.
  *   rglru_conv1d and the scan-only mode of rglru_scan_fwd accept any D.
@@ -53,21 +54,22 @@
  * Work distribution.  The forward scans are persistent kernels that claim
  *   their work units from counters in the workspace at run time; they need
  *   no co-residency guarantee and may share the device with other work.  A
- *   look-back wait that never sees its data (which only a corrupted or
+ *   chunk-carry wait that never sees its data (which only a corrupted or
  *   concurrently reused workspace can cause) gives up after a bounded spin,
- *   sets an error word in the workspace header and yields NaN.  The
- *   backward's own kernels never wait on one another's workgroups.
+ *   sets a timeout word in the workspace header and yields NaN; the call has
+ *   returned RGLRU_OK by then (it only enqueues), so rglru_workspace_status
+ *   reports it afterwards.  The backward's own kernels never wait on one
+ *   another's workgroups.
  * Aliasing.  Outputs must not overlap inputs, except hist and h of
  *   rglru_step, which are read and rewritten in place by design.
- * Determinism.  rglru_conv1d, rglru_gates and rglru_step are bitwise
- *   repeatable, and so are the reverse scan and the reductions of
- *   rglru_scan_bwd (fixed order, no floating-point atomics).  The chunked
- *   forward scan of rglru_scan_fwd, which the backward also runs first,
- *   combines chunk carries through a decoupled look-back whose path depends
- *   on timing (a chunk may compose a different number of published
- *   aggregates), so repeated calls can differ in the last bits of the
- *   carried state and, through it, of y and the gradients; the difference is
- *   rounding only (the same products, grouped differently).
+ * Determinism.  Every call is bitwise repeatable: identical inputs on the
+ *   same device give identical outputs, whatever the timing of the
+ *   workgroups.  The chunked scans carry state between 32-token chunks
+ *   through published words; a chunk folds the aggregates of the chunks
+ *   after the newest published end state onto it in chunk order, which
+ *   reproduces the serial recurrence over chunk aggregates exactly, however
+ *   far back it had to look.  The backward's reverse scan and reductions run
+ *   in a fixed order with no floating-point atomics.
  * Numerics.  NaN and Inf in the inputs propagate; they are not trapped.
  */
 #ifndef RGLRU_H
@@ -92,7 +94,9 @@ typedef enum {
     RGLRU_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than required       */
     RGLRU_ERR_LAUNCH = -6,     /* the HIP runtime reported a launch error       */
     RGLRU_ERR_ARG = -7,        /* inconsistent arguments (mode, aliasing)       */
-    RGLRU_ERR_BLAS = -8        /* a rocBLAS call of rglru_block_fwd failed      */
+    RGLRU_ERR_BLAS = -8,       /* a rocBLAS call of rglru_block_fwd failed      */
+    RGLRU_ERR_TIMEOUT = -9     /* rglru_workspace_status: a chunk-carry wait of
+                                  an earlier call gave up (outputs hold NaN)    */
 } rglru_status;
 
 /* Problem description.  c is the decay-exponent scale (8 on the pages). */
@@ -119,14 +123,29 @@ enum { RGLRU_OP_SCAN_FWD = 0, RGLRU_OP_SCAN_BWD = 1 };
  * (op RGLRU_OP_SCAN_BWD) needs for `desc`.  The workspace carries the chunk
  * carries of the chunked scan and a small header of counters; it must be
  * ZERO-FILLED before its first use and is left ready for the next call
- * (every call restores the header).  Its layout depends on the op and on
- * desc: the carry words of one layout can fall where another layout keeps
- * plain data, which a later look-back could take for a published carry.  So
- * reuse a workspace without zero-filling it again only for calls with the same
- * op and the same desc (B, T, D, H, io).  One workspace must not be used by
- * two calls that can run at the same time.  Errors: RGLRU_ERR_NULL, _SHAPE,
+ * (every call restores the header).  A forward workspace holds only the
+ * header, claim counters in a region of fixed size and tagged carry words
+ * (stale words carry an earlier call's tag), so one zero-filled buffer of
+ * the largest size needed serves forward calls of any shape one after
+ * another.  The backward's workspace also keeps plain data (states, gate
+ * values, staging) where a later call of another layout could look for
+ * carry words, so reuse it without zero-filling it again only for calls with
+ * the same desc (B, T, D, H, io).  One workspace must not be used by two
+ * calls that can run at the same time.  The chunked scans serve at most 4096
+ * groups of 256 channels (D <= 1048576).  Errors: RGLRU_ERR_NULL, _SHAPE,
  * _DTYPE, _ARG (unknown op). */
 int rglru_workspace_size(const rglru_desc *desc, int op, size_t *bytes);
+
+/* Timeout report of the scan workspace `ws` (any of the forward's, the
+ * backward's, the recurrent block's or the residual layer's, all of which
+ * start with the same header): WAITS for the work enqueued on `stream`, reads
+ * the header's timeout word and clears it.  Returns RGLRU_OK if no
+ * chunk-carry wait of a call that used `ws` has given up since the last
+ * report, RGLRU_ERR_TIMEOUT if one has (that call's outputs hold NaN),
+ * RGLRU_ERR_NULL / _ALIGN / _WORKSPACE (ws_bytes < 256) for bad arguments and
+ * RGLRU_ERR_LAUNCH if the runtime reports an error.  This is the one call of
+ * the library that synchronises the host; it allocates nothing. */
+int rglru_workspace_status(const void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* a1 -- causal depthwise Conv1D of width 4 with bias (section "Temporal
  * Filtering via Separable 1D Convolutions"; the listing's Conv1d with

@@ -13,7 +13,7 @@ import gated_linear_recurrence_02_amd as glr
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rglru.h")
 
-OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, ELAUNCH, EARG, EBLAS = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, ELAUNCH, EARG, EBLAS, ETIMEOUT = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 P = 0x7F0000000000          # a 16-byte aligned fake device address (never dereferenced)
 
 
@@ -53,9 +53,16 @@ def ws_size(d, op=glr.OP_SCAN_FWD):
 
 
 def test_status_strings(L):
-    for rc in (OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, ELAUNCH, EARG, EBLAS):
-        assert L.rglru_status_string(rc)
+    for rc in (OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, ELAUNCH, EARG, EBLAS, ETIMEOUT):
+        assert L.rglru_status_string(rc) != b"unknown status"
     assert L.rglru_status_string(123) == b"unknown status"
+
+
+def test_workspace_status_validation(L):
+    # argument checks come before any device call
+    assert L.rglru_workspace_status(None, 4096, None) == ENULL
+    assert L.rglru_workspace_status(ctypes.c_void_p(0x1008), 4096, None) == EALIGN
+    assert L.rglru_workspace_status(ctypes.c_void_p(0x1000), 255, None) == EWS
 
 
 def test_workspace_size(L):
@@ -67,9 +74,15 @@ def test_workspace_size(L):
     assert ws_size(desc(T=0))[0] == ESHAPE
     assert ws_size(desc(), op=9)[0] == EARG
     assert ws_size(desc(D=768, H=2), op=glr.OP_SCAN_BWD)[0] == ESHAPE   # K = 384
-    # the backward addresses rows with 32-bit offsets: D <= 2^24
-    assert ws_size(desc(B=1, T=1, D=(1 << 24) + 256, H=(1 << 16) + 1), op=glr.OP_SCAN_BWD)[0] == ESHAPE
-    assert ws_size(desc(B=1, T=1, D=1 << 24, H=1 << 16), op=glr.OP_SCAN_BWD)[0] == OK
+    # the chunked scans keep one claim counter per 256-channel group in a
+    # region of fixed size: at most 4096 groups (D <= 2^20), for both ops
+    for op in (glr.OP_SCAN_FWD, glr.OP_SCAN_BWD):
+        assert ws_size(desc(B=1, T=1, D=(1 << 20) + 256, H=(1 << 12) + 1), op=op)[0] == ESHAPE
+        assert ws_size(desc(B=1, T=1, D=1 << 20, H=1 << 12), op=op)[0] == OK
+    # the forward's workspace: a fixed prefix (header + claim region) then
+    # 3 tagged words per (stream, chunk, channel)
+    n1, n2 = ws_size(desc(B=1, T=32, D=256, H=1))[1], ws_size(desc(B=1, T=32, D=512, H=2))[1]
+    assert n2 - n1 == 3 * 256 * 8
     # the backward's workspace depends on the I/O type (fp16 r and fp32 i for bf16)
     assert ws_size(desc(io=glr.BF16), op=glr.OP_SCAN_BWD)[1] < ws_size(desc(io=glr.F32), op=glr.OP_SCAN_BWD)[1]
     assert L.rglru_workspace_size(None, 0, None) == ENULL

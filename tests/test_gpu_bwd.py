@@ -72,9 +72,8 @@ def test_bwd_fp32_ragged_with_all_optional_inputs():
     _say("bwd fp32: B=2 T=70 D=256, h0, history and dh_last given")
     g = _run(prob, dy, prob.h0, prob.hist, dh)
     ref = _oracle_block(prob, dy, 0, prob.h0, prob.hist, dh)
-    # fp32 products and sums; 1e-5 as for the forward, looser factor 10 for the
-    # gradient's cancellation in a h_{t-1} - (a^2/beta) i x
-    _compare_block(prob, g, ref, 0, 1e-4)
+    # fp32 products and sums: the fp32 bar of 1e-5 (measured at most 5.9e-6)
+    _compare_block(prob, g, ref, 0, TOL["f32"])
 
 
 def test_bwd_fd_slice_of_9b_workload():
@@ -106,9 +105,9 @@ def test_bwd_config4_full_size():
     cfg = synth.FWD_BWD_9B
     prob = make_problem(4)
     dy = synth.make_dy(cfg)
-    _say("bwd bf16 full size: B=4 T=8192 D=4096 H=16")
+    _say("bwd bf16 full size: B=4 T=8192 D=4096 H=16, every block")
     g = _run(prob, dy)
-    for h in (0, 11):
+    for h in range(prob.H):
         ref = _oracle_block(prob, dy, h)
         _compare_block(prob, g, ref, h, TOL["bf16"])
 
@@ -131,7 +130,7 @@ def test_bwd_ranges_cross_stream_boundaries():
 def test_bwd_tiny_lengths(T):
     # one partial chunk, shorter than the conv window for T < 3 (history rows
     # feed every token), fp32 and bf16
-    for cfg, tol in ((0, 1e-4), (1, TOL["bf16"])):
+    for cfg, tol in ((0, TOL["f32"]), (1, TOL["bf16"])):
         prob = make_problem(cfg, B=2, T=T, with_state=True)
         D = prob.D
         dy = synth.make_activation(cfg, "dy", (2, T, D), prob.io)
@@ -143,12 +142,9 @@ def test_bwd_tiny_lengths(T):
 
 
 def test_bwd_repeat_with_workspace_reuse():
-    # the same call twice with a forward of another shape in between (one shared
-    # workspace): the reverse scan and reductions are fixed-order, the state
-    # pass's look-back may regroup products, so the repeat agrees to rounding:
-    # fp32 gradients to 1e-5, du (stored in bf16) to one bf16 step at its
-    # largest magnitude (2^-7 relative), since a last-bit change in fp32 can
-    # move an element across a bf16 rounding boundary
+    # the same call twice with a forward of another shape in between (one
+    # shared forward workspace, the backward's own re-zeroed for its layout):
+    # every gradient is bitwise repeatable
     prob = make_problem(1, B=3, T=100, with_state=True)
     dy = synth.make_activation(1, "dy", (3, 100, 2560), "bf16")
     _say("bwd bf16: B=3 T=100 D=2560, repeated with a forward in between")
@@ -158,7 +154,5 @@ def test_bwd_repeat_with_workspace_reuse():
     torch.cuda.synchronize()
     g2 = _run(prob, dy, prob.h0, prob.hist)
     for n in NAMES:
-        a, b = from_dev(g1[n]), from_dev(g2[n])
-        e = oracle.rel_err(b, a)
-        _say(f"  {n}: repeat difference {e:.3e}")
-        assert e <= (2.0 ** -7 if n == "du" else 1e-5), n
+        assert torch.equal(g1[n], g2[n]), f"{n} differs between two identical calls"
+    glr.workspace_status(DEV, "bwd")

@@ -15,7 +15,7 @@ import torch
 import gated_linear_recurrence_02_amd as glr
 import oracle
 import synth
-from problems import TOL, from_dev, make_problem, to_dev
+from problems import TOL, Problem, from_dev, make_problem, to_dev
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -191,28 +191,49 @@ def test_mode_c_scan_only_any_width():
 
 
 # ---------------------------------------------------- full-size workloads
-def test_config1_full_size_sampled_slices():
+def test_config1_full_size_every_block():
+    # every 256-channel block on one stream (stream h % B), the first and the
+    # last block also on the other ends of the batch
     prob = make_problem(1)
     _say("config 1 full size: B=8 T=2048 D=2560 bf16, mode A")
     y, hl, _ = _run_fwd(prob)
-    yn = from_dev(y)
+    yn, hn = from_dev(y), from_dev(hl)
     assert np.all(np.isfinite(yn))
-    for b, h in [(0, 0), (3, 7), (7, 9)]:
+    for b, h in [(h % prob.B, h) for h in range(prob.H)] + [(7, 0), (3, 9)]:
         ry, rh, _ = _oracle_slice(prob, b, h)
         _cmp(f"y[b={b},h={h}]", prob.slice_block(yn, b, h), ry, TOL["bf16"])
-        _cmp(f"h_last[b={b},h={h}]", prob.slice_block(from_dev(hl), b, h), rh, TOL["bf16"])
+        _cmp(f"h_last[b={b},h={h}]", prob.slice_block(hn, b, h), rh, TOL["bf16"])
+    glr.workspace_status(DEV)
 
 
-def test_config2_full_size_sampled_slices():
+def test_config2_full_size_every_block():
     prob = make_problem(2)
-    _say("config 2 full size: B=1 T=32768 D=2560 bf16, mode A")
+    _say("config 2 full size: B=1 T=32768 D=2560 bf16, mode A, every block")
     y, hl, _ = _run_fwd(prob)
-    yn = from_dev(y)
+    yn, hn = from_dev(y), from_dev(hl)
     assert np.all(np.isfinite(yn))
-    for b, h in [(0, 0), (0, 6)]:
+    for h in range(prob.H):
+        ry, rh, _ = _oracle_slice(prob, 0, h)
+        _cmp(f"y[h={h}]", prob.slice_block(yn, 0, h), ry, TOL["bf16"])
+        _cmp(f"h_last[h={h}]", prob.slice_block(hn, 0, h), rh, TOL["bf16"])
+    glr.workspace_status(DEV)
+
+
+def test_config4_forward_full_size():
+    # the 9B-width workload's forward (B=4 T=8192 D=4096 H=16): blocks 0, 8
+    # and 15 over all streams, every other block on one stream
+    prob = make_problem(4)
+    _say("config 4 forward full size: B=4 T=8192 D=4096 H=16 bf16, mode A")
+    y, hl, _ = _run_fwd(prob)
+    yn, hn = from_dev(y), from_dev(hl)
+    assert np.all(np.isfinite(yn))
+    cases = [(b, h) for h in (0, 8, 15) for b in range(prob.B)]
+    cases += [(h % prob.B, h) for h in range(prob.H) if h not in (0, 8, 15)]
+    for b, h in cases:
         ry, rh, _ = _oracle_slice(prob, b, h)
-        _cmp(f"y[h={h}]", prob.slice_block(yn, b, h), ry, TOL["bf16"])
-        _cmp(f"h_last[h={h}]", prob.slice_block(from_dev(hl), b, h), rh, TOL["bf16"])
+        _cmp(f"y[b={b},h={h}]", prob.slice_block(yn, b, h), ry, TOL["bf16"])
+        _cmp(f"h_last[b={b},h={h}]", prob.slice_block(hn, b, h), rh, TOL["bf16"])
+    glr.workspace_status(DEV)
 
 
 # ------------------------------------------------------- self-consistency
@@ -233,30 +254,86 @@ def test_split_equals_whole_on_gpu():
 
 
 def test_repeatable():
-    # conv, gates and the decode step are bitwise repeatable; the chunked scan's
-    # look-back may stop at a different published chunk from run to run, which
-    # changes only the rounding of the carried state
+    # every entry point is bitwise repeatable, the chunked scan included: a
+    # chunk folds the aggregates after the newest published end state onto it
+    # in chunk order, which is the serial recurrence whatever the timing
     prob = make_problem(1, B=2, T=500)
     w = prob.weights(DEV)
     u = to_dev(prob.u, DEV)
     x1, _ = glr.conv1d(u, w.conv_w, w.conv_b, H=prob.H)
     x2, _ = glr.conv1d(u, w.conv_w, w.conv_b, H=prob.H)
     r1, i1 = glr.gates(x1, w)
-    r2, i2 = glr.gates(x1, w)
+    r2, i2 = glr.gates(x2, w)
     y1, h1, _ = glr.scan_fwd(u, w)
-    y2, h2, _ = glr.scan_fwd(u, w)
-    torch.cuda.synchronize()
+    y1, h1 = y1.clone(), h1.clone()
     assert torch.equal(x1, x2) and torch.equal(r1, r2) and torch.equal(i1, i2)
-    _cmp("run-to-run y", from_dev(y2), from_dev(y1), 1e-2)
-    _cmp("run-to-run h_last", from_dev(h2), from_dev(h1), 1e-5)
+    for k in range(5):
+        y2, h2, _ = glr.scan_fwd(u, w)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2) and torch.equal(h1, h2), f"scan differs on repeat {k}"
+    # the long prefill, where a chunk looks back over many in-flight chunks
+    prob2 = make_problem(2, T=8192)
+    u2, w2 = to_dev(prob2.u, DEV), prob2.weights(DEV)
+    ya, ha, _ = glr.scan_fwd(u2, w2)
+    ya, ha = ya.clone(), ha.clone()
+    for k in range(3):
+        yb, hb, _ = glr.scan_fwd(u2, w2)
+        torch.cuda.synchronize()
+        assert torch.equal(ya, yb) and torch.equal(ha, hb), f"long scan differs on repeat {k}"
+    glr.workspace_status(DEV)
+
+
+@pytest.mark.parametrize("mode", ["A", "C"])
+def test_results_independent_of_grid(mode, monkeypatch):
+    # the persistent forward claims its units at run time; one workgroup per
+    # 256-channel group (every wait then on the same workgroup's earlier
+    # units) and three must give the same bits as the full grid
+    prob = make_problem(1, B=4, T=700, with_state=True)
+    w = prob.weights(DEV)
+    u = to_dev(prob.u, DEV)
+    h0, hist = to_dev(prob.h0, DEV), to_dev(prob.hist, DEV)
+    if mode == "C":
+        x, _ = glr.conv1d(u, w.conv_w, w.conv_b, hist, H=prob.H)
+        r, i = glr.gates(x, w)
+        wc = glr.Weights(conv_w=None, W_a=None, W_x=None, Lambda=w.Lambda)
+        run = lambda: glr.scan_fwd(x, wc, r=r, i=i, h0=h0)
+    else:
+        run = lambda: glr.scan_fwd(u, w, h0=h0, hist_in=hist)
+    y0, h0_, _ = run()
+    y0, h0_ = y0.clone(), h0_.clone()
+    for cap in ("1", "3"):
+        monkeypatch.setenv("RGLRU_FWD_GROUP_WORKGROUPS", cap)
+        _say(f"mode {mode}, B=4 T=700 D=2560, {cap} workgroup(s) per group")
+        y1, h1, _ = run()
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y1) and torch.equal(h0_, h1), f"results depend on the grid ({cap})"
+    monkeypatch.delenv("RGLRU_FWD_GROUP_WORKGROUPS")
+    ry, rh, _ = _oracle_slice(prob, 3, 5, prob.h0, prob.hist)
+    _cmp("y[b=3,h=5]", prob.slice_block(from_dev(y0), 3, 5), ry, TOL["bf16"])
+    glr.workspace_status(DEV)
 
 
 def test_workspace_reused_across_shapes():
-    # the header is restored by every call, so one zeroed buffer serves calls of any size
+    # one zeroed forward workspace serves calls of any shape one after another:
+    # the claim counters sit at fixed offsets, carry words carry their call's tag
     for T in (40, 1000, 7, 333):
         prob = make_problem(1, B=1, T=T)
         y, hl, _ = _run_fwd(prob)
         ry, rh, _ = _oracle_slice(prob, 0, 2)
         _cmp(f"T={T} y", prob.slice_block(from_dev(y), 0, 2), ry, TOL["bf16"])
+    # a narrow call, then a call with 65 blocks on the same buffer: block 64's
+    # counter lies past the 64 counters a narrow layout would have reserved
+    for D, H, T in ((256, 1, 300), (16640, 65, 130)):
+        p = synth.make_params(1, D, H, "bf16")
+        u = synth.make_activation(1, "u", (2, T, D), "bf16")
+        prob = Problem(1, 2, T, D, H, "bf16", p, u, None, None)
+        y, hl, _ = _run_fwd(prob)
+        yn, hn = from_dev(y), from_dev(hl)
+        assert np.all(np.isfinite(yn))
+        for b, h in sorted({(0, 0), (1, H - 1), (0, H // 2)}):
+            ry, rh, _ = _oracle_slice(prob, b, h)
+            _cmp(f"D={D} y[b={b},h={h}]", prob.slice_block(yn, b, h), ry, TOL["bf16"])
+            _cmp(f"D={D} h_last[b={b},h={h}]", prob.slice_block(hn, b, h), rh, TOL["bf16"])
+    glr.workspace_status(DEV)
     hdr = glr._ws_cache[(torch.device(DEV), "fwd")][0][:16].cpu().numpy().view(np.uint32)
     assert hdr[0] == 0 and hdr[1] == 0 and hdr[3] == 0     # counters reset, no look-back timeout
