@@ -241,6 +241,22 @@ def micro(torch, dev):
     mix["together_over_max"] = mix["together_ms"] / max(mix["mfma_alone_ms"], mix["fma_alone_ms"])
     mix["together_over_sum"] = mix["together_ms"] / (mix["mfma_alone_ms"] + mix["fma_alone_ms"])
     res["mfma_fma_coexecution"] = mix
+    # one wave per SIMD issuing its own MFMAs and independent FMAs in one loop
+    L.rglru_micro_interleave.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+    iblocks = ncu
+    iout = torch.empty(iblocks * 256, dtype=torch.float32, device=dev)
+    inter = {}
+    for fpm in (4, 8, 16):
+        r = {}
+        for mode, name in enumerate(("mfma_alone", "fma_alone", "together")):
+            kms, _ = tm.calls(lambda k: check(L.rglru_micro_interleave(mode, iblocks, 2048, fpm, iout.data_ptr(),
+                                                                        sp)), 5, 2)
+            r[name + "_ms"] = float(np.median(kms))
+        r["together_over_max"] = r["together_ms"] / max(r["mfma_alone_ms"], r["fma_alone_ms"])
+        r["together_over_sum"] = r["together_ms"] / (r["mfma_alone_ms"] + r["fma_alone_ms"])
+        inter[f"fma_per_4_mfma_{8 * fpm}"] = r
+    res["same_wave_interleave_1_wave_per_simd"] = inter
     nbytes = 1 << 30
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)

@@ -2,8 +2,9 @@
 librglru_micro.so (micro/micro.hip) for gfx950 with hipcc.
 
 Every source is compiled with packed-FP32 instructions disabled
-(-Xclang -target-feature -Xclang -packed-fp32-ops); the host pass warns that
-it does not know the feature, which is harmless.
+(-Xclang -target-feature -Xclang -packed-fp32-ops; the host pass warns that
+it does not know the feature, which is harmless) and without the atomic
+optimizer (see FLAGS).
 """
 from __future__ import annotations
 
@@ -23,7 +24,11 @@ ARCH = "gfx950"
 
 FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-Wno-unused-command-line-argument"]
+         "-Wno-unused-command-line-argument",
+         # thread 0 alone claims work units: the atomic optimizer's wave-wide
+         # rewrite reads the result at once, which waits for every vector
+         # memory operation issued before it (prefetches included)
+         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 
 
 def _compile(src: str) -> str:

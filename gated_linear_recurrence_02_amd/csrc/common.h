@@ -71,6 +71,23 @@ __device__ __forceinline__ bool get_word(const uint64_t *p, uint32_t tag, float 
     return (uint32_t)(w >> 32) == tag;
 }
 
+// Workgroup barrier that orders LDS only: the fences are restricted to the
+// local address space, so the barrier waits for this wave's LDS operations
+// (lgkmcnt) but not for its global stores and loads in flight (a plain
+// __syncthreads() also drains vmcnt, i.e. waits for every outstanding store
+// to reach memory and for every prefetch to land).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8): every LDS operation done and at most N vector memory
+// operations outstanding
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
 // Every atomic here is relaxed on purpose: no data is published through the
 // counters (each carry word holds its own tag, outputs are read only after
 // the kernel ends), and acquire/release at agent scope would write back and

@@ -665,6 +665,10 @@ void launch_scan_fwd(const rglru_desc &d, const rglru_weights &w, int mode, cons
                      const void *r, const void *i, const void *hist_in, const float *h0, void *y,
                      float *h_last, void *hist_out, void *ws, hipStream_t s)
 {
+    if (mode == 0 && fused_fwd_applies(d)) {
+        launch_fused_fwd(d, w, in, hist_in, h0, y, h_last, hist_out, ws, s);
+        return;
+    }
     run_fwd(d, w, mode, in, r, i, hist_in, h0, y, h_last, hist_out, nullptr, nullptr, nullptr, ws, s);
 }
 

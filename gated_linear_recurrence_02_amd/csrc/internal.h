@@ -32,6 +32,13 @@ void launch_scan_fwd(const rglru_desc &d, const rglru_weights &w, int mode, cons
                      const void *r, const void *i, const void *hist_in, const float *h0, void *y,
                      float *h_last, void *hist_out, void *ws, hipStream_t s);
 
+// mode A, bf16 I/O, K = 256, B T D 2 < 2^31: the one-wave-per-SIMD fused
+// forward (fused.hip), taken only with RGLRU_FWD_FUSED=1 in the environment;
+// fused_fwd_applies says whether a call takes it.
+bool fused_fwd_applies(const rglru_desc &d);
+void launch_fused_fwd(const rglru_desc &d, const rglru_weights &w, const void *u, const void *hist_in,
+                      const float *h0, void *y, float *h_last, void *hist_out, void *ws, hipStream_t s);
+
 // mode A forward that stores no outputs but the state before every 32-token
 // chunk ([B][NC][D] fp32) and the gate values r, i of every token (layout of
 // GateStore in common.h) -- the first pass of the backward

@@ -102,6 +102,58 @@ __global__ __launch_bounds__(512) void mix_kernel(float *out, int mfma_iters, in
     out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+// Same-wave interleaving: 4-wave workgroups (one wave per SIMD when one
+// workgroup runs per CU); each round issues 4 independent
+// v_mfma_f32_32x32x16_bf16 (mode 0 and 2) and 8 independent chains of FPM
+// FMAs (mode 1 and 2), scheduled as one MFMA followed by 2 FPM FMAs, four
+// times.  If a wave's vector ALU work issues while its own MFMAs execute,
+// mode 2 takes about as long as the slower of modes 0 and 1.
+template <int MODE, int FPM>
+__global__ __launch_bounds__(256) void interleave_kernel(float *out, int iters)
+{
+    bf16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = (__bf16)(0.001f * (float)(threadIdx.x + e));
+        b[e] = (__bf16)(0.002f * (float)(threadIdx.x - e));
+    }
+    f32x16 c[4] = {};
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = 1.0001f * (float)(threadIdx.x + j);
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (MODE != 1) c[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[q], 0, 0, 0);
+            if (MODE != 0) {
+#pragma unroll
+                for (int f = 0; f < FPM / 4; ++f) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) v[j] = __builtin_fmaf(v[j], 1.0001f, 0.5f);
+                }
+            }
+            if (MODE == 2) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 2 * FPM, 0);  // then 2 FPM VALU
+            }
+        }
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc += c[q][e];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc += v[j];
+    out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+template <int FPM>
+void launch_interleave(int mode, dim3 g, float *out, int iters, hipStream_t s)
+{
+    if (mode == 0) interleave_kernel<0, FPM><<<g, dim3(256), 0, s>>>(out, iters);
+    else if (mode == 1) interleave_kernel<1, FPM><<<g, dim3(256), 0, s>>>(out, iters);
+    else interleave_kernel<2, FPM><<<g, dim3(256), 0, s>>>(out, iters);
+}
 // grid-stride copy of n 16-byte pieces
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4 *src, u32x4 *dst, size_t n)
 {
@@ -142,6 +194,18 @@ extern "C" int rglru_micro_mix(int mode, int blocks, int mfma_iters, int fma_ite
     return (int)hipGetLastError();
 }
 
+// mode 0 MFMA only, 1 FMA only, 2 both in one wave; 8 fpm FMAs per round of
+// 4 MFMAs, fpm in {4, 8, 16}; out holds blocks * 256 floats
+extern "C" int rglru_micro_interleave(int mode, int blocks, int iters, int fpm, float *out, hipStream_t s)
+{
+    if (mode < 0 || mode > 2 || blocks < 1 || iters < 1 || !out || (fpm != 4 && fpm != 8 && fpm != 16))
+        return (int)hipErrorInvalidValue;
+    const dim3 g((unsigned)blocks);
+    if (fpm == 4) launch_interleave<4>(mode, g, out, iters, s);
+    else if (fpm == 8) launch_interleave<8>(mode, g, out, iters, s);
+    else launch_interleave<16>(mode, g, out, iters, s);
+    return (int)hipGetLastError();
+}
 // copies `bytes` (a multiple of 16; both pointers 16-byte aligned)
 extern "C" int rglru_micro_copy(const void *src, void *dst, size_t bytes, int blocks, hipStream_t s)
 {

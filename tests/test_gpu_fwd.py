@@ -337,3 +337,36 @@ def test_workspace_reused_across_shapes():
     glr.workspace_status(DEV)
     hdr = glr._ws_cache[(torch.device(DEV), "fwd")][0][:16].cpu().numpy().view(np.uint32)
     assert hdr[0] == 0 and hdr[1] == 0 and hdr[3] == 0     # counters reset, no look-back timeout
+
+
+# --------------------------------------- opt-in one-wave-per-SIMD kernel
+def test_fused_opt_in_kernel(monkeypatch):
+    # RGLRU_FWD_FUSED=1 sends mode A bf16 to the second, one-wave-per-SIMD
+    # forward; it answers to the same oracle, at full size, on ragged lengths
+    # with state, and gives the same bits for any grid
+    monkeypatch.setenv("RGLRU_FWD_FUSED", "1")
+    prob = make_problem(1)
+    _say("fused kernel, config 1 full size: B=8 T=2048 D=2560 bf16")
+    y, hl, _ = _run_fwd(prob)
+    yn, hn = from_dev(y), from_dev(hl)
+    for b, h in [(0, 0), (7, 9), (3, 4), (5, 6)]:
+        ry, rh, _ = _oracle_slice(prob, b, h)
+        _cmp(f"y[b={b},h={h}]", prob.slice_block(yn, b, h), ry, TOL["bf16"])
+        _cmp(f"h_last[b={b},h={h}]", prob.slice_block(hn, b, h), rh, TOL["bf16"])
+    for T in (1, 3, 33, 130):
+        prob = make_problem(1, B=2, T=T, with_state=True)
+        _say(f"fused kernel, ragged T={T}, B=2, h0 and history given")
+        y, hl, ho = _run_fwd(prob, h0=prob.h0, hist=prob.hist)
+        for b, h in [(0, 0), (1, 9)]:
+            ry, rh, _ = _oracle_slice(prob, b, h, prob.h0, prob.hist)
+            _cmp(f"y[b={b},h={h}]", prob.slice_block(from_dev(y), b, h), ry, TOL["bf16"])
+            _cmp(f"h_last[b={b},h={h}]", prob.slice_block(from_dev(hl), b, h), rh, TOL["bf16"])
+        want = np.concatenate([prob.hist, prob.u], axis=1)[:, -3:, :]
+        assert np.array_equal(ho.cpu().view(torch.int16).numpy().view(np.uint16), want)
+    prob = make_problem(1, B=4, T=700)
+    y0, h0_, _ = _run_fwd(prob)
+    y0, h0_ = y0.clone(), h0_.clone()
+    monkeypatch.setenv("RGLRU_FWD_GROUP_WORKGROUPS", "1")
+    y1, h1, _ = _run_fwd(prob)
+    assert torch.equal(y0, y1) and torch.equal(h0_, h1), "fused results depend on the grid"
+    glr.workspace_status(DEV)
