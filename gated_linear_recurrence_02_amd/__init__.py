@@ -65,8 +65,12 @@ class _Block(ctypes.Structure):
                 ("proj_out", ctypes.c_void_p)]
 
 
+# size of the scratch behind rglru_scan_fwd_noalloc (RGLRU_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
 _lib = None
 SYMBOLS = ("rglru_workspace_size", "rglru_workspace_status", "rglru_conv1d", "rglru_gates", "rglru_scan_fwd",
+           "rglru_scan_fwd_noalloc",
            "rglru_step", "rglru_scan_bwd", "rglru_block_workspace_size", "rglru_block_fwd",
            "rglru_attn_fwd", "rglru_attn_workspace_size", "rglru_attn_step", "rglru_layer_workspace_size",
            "rglru_layer_fwd", "rglru_attn_layer_workspace_size", "rglru_attn_layer_fwd",
@@ -89,6 +93,7 @@ def lib():
         L.rglru_conv1d.argtypes = [D, vp, vp, vp, vp, vp, vp, vp]
         L.rglru_gates.argtypes = [D, W, vp, vp, vp, vp]
         L.rglru_scan_fwd.argtypes = [D, W, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.rglru_scan_fwd_noalloc.argtypes = [D, W, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.rglru_step.argtypes = [D, W, vp, vp, vp, vp, vp]
         L.rglru_scan_bwd.argtypes = [D, W, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         A = ctypes.POINTER(_AttnDesc)
@@ -281,6 +286,20 @@ def scan_fwd(inp: torch.Tensor, w: Weights, *, r=None, i=None, h0=None, hist_in=
     """Forward scan.  Mode A (conv=True, no r/i): inp is pre-conv u.  Mode B
     (conv=False, no r/i): inp is x.  Mode C (r and i given): inp is x, scan only.
     Returns (y, h_last, hist_out or None)."""
+    return _scan_fwd(inp, w, r, i, h0, hist_in, conv, want_hist, out, h_last_out, hist_out_buf, False)
+
+
+def scan_fwd_noalloc(inp: torch.Tensor, w: Weights, *, r=None, i=None, h0=None, hist_in=None,
+                     conv: bool = True, want_hist: bool = True, out=None, h_last_out=None,
+                     hist_out_buf=None):
+    """scan_fwd through rglru_scan_fwd_noalloc: the chunk carries live in the
+    library's fixed per-device scratch instead of a workspace (calls on one
+    device must not overlap).  Outputs not passed in are allocated here, by
+    the binding; the library call allocates nothing."""
+    return _scan_fwd(inp, w, r, i, h0, hist_in, conv, want_hist, out, h_last_out, hist_out_buf, True)
+
+
+def _scan_fwd(inp, w, r, i, h0, hist_in, conv, want_hist, out, h_last_out, hist_out_buf, noalloc):
     dev = inp.device
     _need(inp, "in", dev)
     B, T, D = inp.shape
@@ -303,12 +322,14 @@ def scan_fwd(inp: torch.Tensor, w: Weights, *, r=None, i=None, h0=None, hist_in=
     _need(h_last, "h_last_out", dev, torch.float32, (B, D))
     _need(hist_out, "hist_out_buf", dev, inp.dtype, (B, 3, D))
     d = _Desc(B, T, D, H, _io(inp), w.c)
+    args = (ctypes.byref(d), ctypes.byref(ws_), _ptr(inp), _ptr(r), _ptr(i),
+            _ptr(hist_in) if use_conv else None, _ptr(h0), _ptr(y), _ptr(h_last), _ptr(hist_out))
+    if noalloc:
+        _check(lib().rglru_scan_fwd_noalloc(*args, _stream(dev)), "rglru_scan_fwd_noalloc")
+        return y, h_last, hist_out
     nbytes = workspace_size(B, T, D, H, _io(inp), OP_SCAN_FWD, w.c)
     wsb = workspace(nbytes, dev)
-    _check(lib().rglru_scan_fwd(ctypes.byref(d), ctypes.byref(ws_), _ptr(inp), _ptr(r), _ptr(i),
-                                _ptr(hist_in) if use_conv else None, _ptr(h0), _ptr(y),
-                                _ptr(h_last), _ptr(hist_out), _ptr(wsb), wsb.numel(), _stream(dev)),
-           "rglru_scan_fwd")
+    _check(lib().rglru_scan_fwd(*args, _ptr(wsb), wsb.numel(), _stream(dev)), "rglru_scan_fwd")
     return y, h_last, hist_out
 
 

@@ -4,9 +4,15 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "internal.h"
 
 using namespace rglru;
+
+// Workspace of rglru_scan_fwd_noalloc, one copy per device (file scope).
+constexpr size_t NOALLOC_SCRATCH_BYTES = RGLRU_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -114,6 +120,82 @@ int launch_status()
     return hipGetLastError() == hipSuccess ? RGLRU_OK : RGLRU_ERR_LAUNCH;
 }
 
+// Checks of the forward scan's arguments, shared by rglru_scan_fwd (own_ws:
+// the caller's workspace ws of ws_bytes) and rglru_scan_fwd_noalloc (the
+// library's scratch, which no caller buffer can overlap).  *mode receives
+// 0, 1 or 2 for modes A, B, C.
+int check_scan_fwd(const rglru_desc *desc, const rglru_weights *w, const void *in, const void *r,
+                   const void *i, const void *hist_in, const float *h0, const void *y, const float *h_last,
+                   const void *hist_out, bool own_ws, const void *ws, size_t ws_bytes, int *mode)
+{
+    if (!desc || !w) return RGLRU_ERR_NULL;
+    if ((r == nullptr) != (i == nullptr)) return RGLRU_ERR_ARG;
+    const int m = r ? 2 : (w->conv_w ? 0 : 1);
+    if (m == 2 && w->conv_w) return RGLRU_ERR_ARG;
+    if (m != 0 && (hist_in || hist_out)) return RGLRU_ERR_ARG;
+    int st = check_desc(desc, m != 2);
+    if (st) return st;
+    if (!in || !y || !w->Lambda) return RGLRU_ERR_NULL;
+    if (m != 2 && (!w->W_a || !w->W_x)) return RGLRU_ERR_NULL;
+    if (own_ws && !ws) return RGLRU_ERR_WORKSPACE;
+    const void *all[] = {in, r, i, hist_in, h0, y, h_last, hist_out, ws, w->conv_w, w->conv_b,
+                         w->W_a, w->b_a, w->W_x, w->b_x, w->Lambda};
+    for (const void *p : all)
+        if (p && !aligned16(p)) return RGLRU_ERR_ALIGN;
+    const rglru_desc &d = *desc;
+    const size_t need = fwd_workspace_bytes(d.B, d.T, d.D);
+    if (own_ws && ws_bytes < need) return RGLRU_ERR_WORKSPACE;
+    if (!own_ws && need > NOALLOC_SCRATCH_BYTES) return RGLRU_ERR_SCRATCH;
+    const size_t act = d.B * d.T * d.D * esize(d), hist = d.B * 3 * d.D * esize(d);
+    const size_t st_b = d.B * d.D * 4, vec = d.D * 4;
+    const size_t wb = m == 2 ? 0 : d.H * 65536 * esize(d);
+    const Range outs[] = {{y, act}, {h_last, st_b}, {hist_out, hist}, {ws, own_ws ? need : 0}};
+    const Range ins[] = {{in, act}, {r, act}, {i, act}, {hist_in, hist}, {h0, st_b},
+                         {w->conv_w, m == 0 ? vec * 4 : 0}, {w->conv_b, m == 0 ? vec : 0},
+                         {w->W_a, wb}, {w->W_x, wb}, {w->b_a, m == 2 ? 0 : vec},
+                         {w->b_x, m == 2 ? 0 : vec}, {w->Lambda, vec}};
+    if (any_alias(outs, 4, ins, 12)) return RGLRU_ERR_ARG;
+    *mode = m;
+    return RGLRU_OK;
+}
+
+// ------------------------------------------- scratch of rglru_scan_fwd_noalloc
+// The forward scan's workspace for callers that cannot allocate: one array per
+// device, loaded with the library's code object and held until the process
+// ends.  In host code the name `scratch` is only a stand-in for the symbol;
+// the device address of each device's copy comes from hipGetSymbolAddress,
+// taken once per device and cleared once (a plain fill kernel, so that a
+// captured first call records no memset).  Every later call leaves the
+// header as it found it and tags its carry words with its own launch number,
+// so no call clears anything again.
+constexpr int NOALLOC_MAX_DEVICES = 64;
+
+__global__ void __launch_bounds__(256) scratch_clear_kernel(uint4 *p, size_t n16)
+{
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < n16; k += stride)
+        p[k] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+int noalloc_scratch(hipStream_t stream, void **out)
+{
+    static std::mutex mu;
+    static void *ptr[NOALLOC_MAX_DEVICES];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return RGLRU_ERR_LAUNCH;
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return RGLRU_ERR_ARG;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return RGLRU_ERR_LAUNCH;
+        scratch_clear_kernel<<<dim3(1024), dim3(256), 0, stream>>>((uint4 *)p, NOALLOC_SCRATCH_BYTES / 16);
+        if (hipGetLastError() != hipSuccess) return RGLRU_ERR_LAUNCH;
+        ptr[dev] = p;
+    }
+    *out = ptr[dev];
+    return RGLRU_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -130,6 +212,7 @@ const char *rglru_status_string(int status)
     case RGLRU_ERR_LAUNCH: return "HIP launch error";
     case RGLRU_ERR_ARG: return "inconsistent arguments";
     case RGLRU_ERR_BLAS: return "a rocBLAS call failed";
+    case RGLRU_ERR_SCRATCH: return "problem needs more than the fixed scratch of rglru_scan_fwd_noalloc";
     case RGLRU_ERR_TIMEOUT: return "a chunk-carry wait of an earlier call on this workspace gave up (its outputs hold NaN)";
     default: return "unknown status";
     }
@@ -203,33 +286,24 @@ int rglru_scan_fwd(const rglru_desc *desc, const rglru_weights *w, const void *i
                    const void *i, const void *hist_in, const float *h0, void *y, float *h_last,
                    void *hist_out, void *ws, size_t ws_bytes, hipStream_t stream)
 {
-    if (!desc || !w) return RGLRU_ERR_NULL;
-    if ((r == nullptr) != (i == nullptr)) return RGLRU_ERR_ARG;
-    const int mode = r ? 2 : (w->conv_w ? 0 : 1);
-    if (mode == 2 && w->conv_w) return RGLRU_ERR_ARG;
-    if (mode != 0 && (hist_in || hist_out)) return RGLRU_ERR_ARG;
-    int st = check_desc(desc, mode != 2);
+    int mode = 0;
+    const int st = check_scan_fwd(desc, w, in, r, i, hist_in, h0, y, h_last, hist_out, true, ws, ws_bytes, &mode);
     if (st) return st;
-    if (!in || !y || !w->Lambda) return RGLRU_ERR_NULL;
-    if (mode != 2 && (!w->W_a || !w->W_x)) return RGLRU_ERR_NULL;
-    if (!ws) return RGLRU_ERR_WORKSPACE;
-    const void *all[] = {in, r, i, hist_in, h0, y, h_last, hist_out, ws, w->conv_w, w->conv_b,
-                         w->W_a, w->b_a, w->W_x, w->b_x, w->Lambda};
-    for (const void *p : all)
-        if (p && !aligned16(p)) return RGLRU_ERR_ALIGN;
-    const rglru_desc &d = *desc;
-    const size_t need = fwd_workspace_bytes(d.B, d.T, d.D);
-    if (ws_bytes < need) return RGLRU_ERR_WORKSPACE;
-    const size_t act = d.B * d.T * d.D * esize(d), hist = d.B * 3 * d.D * esize(d);
-    const size_t st_b = d.B * d.D * 4, vec = d.D * 4;
-    const size_t wb = mode == 2 ? 0 : d.H * 65536 * esize(d);
-    const Range outs[] = {{y, act}, {h_last, st_b}, {hist_out, hist}, {ws, need}};
-    const Range ins[] = {{in, act}, {r, act}, {i, act}, {hist_in, hist}, {h0, st_b},
-                         {w->conv_w, mode == 0 ? vec * 4 : 0}, {w->conv_b, mode == 0 ? vec : 0},
-                         {w->W_a, wb}, {w->W_x, wb}, {w->b_a, mode == 2 ? 0 : vec},
-                         {w->b_x, mode == 2 ? 0 : vec}, {w->Lambda, vec}};
-    if (any_alias(outs, 4, ins, 12)) return RGLRU_ERR_ARG;
-    launch_scan_fwd(d, *w, mode, in, r, i, hist_in, h0, y, h_last, hist_out, ws, stream);
+    launch_scan_fwd(*desc, *w, mode, in, r, i, hist_in, h0, y, h_last, hist_out, ws, stream);
+    return launch_status();
+}
+
+int rglru_scan_fwd_noalloc(const rglru_desc *desc, const rglru_weights *w, const void *in, const void *r,
+                           const void *i, const void *hist_in, const float *h0, void *y, float *h_last,
+                           void *hist_out, hipStream_t stream)
+{
+    int mode = 0;
+    int st = check_scan_fwd(desc, w, in, r, i, hist_in, h0, y, h_last, hist_out, false, nullptr, 0, &mode);
+    if (st) return st;
+    void *ws = nullptr;
+    st = noalloc_scratch(stream, &ws);
+    if (st) return st;
+    launch_scan_fwd(*desc, *w, mode, in, r, i, hist_in, h0, y, h_last, hist_out, ws, stream);
     return launch_status();
 }
 

@@ -95,8 +95,10 @@ typedef enum {
     RGLRU_ERR_LAUNCH = -6,     /* the HIP runtime reported a launch error       */
     RGLRU_ERR_ARG = -7,        /* inconsistent arguments (mode, aliasing)       */
     RGLRU_ERR_BLAS = -8,       /* a rocBLAS call of rglru_block_fwd failed      */
-    RGLRU_ERR_TIMEOUT = -9     /* rglru_workspace_status: a chunk-carry wait of
+    RGLRU_ERR_TIMEOUT = -9,    /* rglru_workspace_status: a chunk-carry wait of
                                   an earlier call gave up (outputs hold NaN)    */
+    RGLRU_ERR_SCRATCH = -10    /* rglru_scan_fwd_noalloc: the call needs more
+                                  than RGLRU_NOALLOC_SCRATCH_BYTES              */
 } rglru_status;
 
 /* Problem description.  c is the decay-exponent scale (8 on the pages). */
@@ -185,6 +187,27 @@ int rglru_scan_fwd(const rglru_desc *desc, const rglru_weights *w, const void *i
                    const void *r, const void *i, const void *hist_in, const float *h0,
                    void *y, float *h_last, void *hist_out, void *ws, size_t ws_bytes,
                    hipStream_t stream);
+
+/* rglru_scan_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same modes, arguments, checks,
+ * results and determinism as rglru_scan_fwd, with the chunk carries kept in
+ * a scratch array of RGLRU_NOALLOC_SCRATCH_BYTES (64 MiB) that the library
+ * holds on each device it runs on until the process ends.  The call
+ * allocates nothing; its first call on a device resolves that device's copy
+ * of the array and clears it with a kernel on `stream`.  Every call on one
+ * device shares the array: calls that can run at the same time on one
+ * device (other streams, other host threads) RACE and must be serialised by
+ * the caller.  The scratch has no timeout report; a chunk-carry wait that
+ * gives up (possible only when calls overlap) leaves NaN in the outputs.
+ * Extra error: RGLRU_ERR_SCRATCH when rglru_workspace_size(desc,
+ * RGLRU_OP_SCAN_FWD) -- 16640 + 24 B ceil(T/32) D bytes -- exceeds
+ * RGLRU_NOALLOC_SCRATCH_BYTES, i.e. B ceil(T/32) D > 2795509: the 32k-token
+ * prefill at D = 2560 (2621440) fits, B = 4, T = 8192, D = 4096 does not. */
+#define RGLRU_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int rglru_scan_fwd_noalloc(const rglru_desc *desc, const rglru_weights *w, const void *in,
+                           const void *r, const void *i, const void *hist_in, const float *h0,
+                           void *y, float *h_last, void *hist_out, hipStream_t stream);
 
 /* a6 -- one decode step for B independent streams (the listing's RGLRU.step,
  * with the conv history carried in front): desc->T must be 1.

@@ -14,6 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rglru.h")
 
 OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, ELAUNCH, EARG, EBLAS, ETIMEOUT = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+ESCRATCH = -10
 P = 0x7F0000000000          # a 16-byte aligned fake device address (never dereferenced)
 
 
@@ -53,7 +54,7 @@ def ws_size(d, op=glr.OP_SCAN_FWD):
 
 
 def test_status_strings(L):
-    for rc in (OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, ELAUNCH, EARG, EBLAS, ETIMEOUT):
+    for rc in (OK, ENULL, ESHAPE, EDTYPE, EALIGN, EWS, ELAUNCH, EARG, EBLAS, ETIMEOUT, ESCRATCH):
         assert L.rglru_status_string(rc) != b"unknown status"
     assert L.rglru_status_string(123) == b"unknown status"
 
@@ -130,6 +131,30 @@ def test_scan_fwd_validation(L):
     d300 = desc(D=300, H=1)
     _, n3 = ws_size(d300)
     assert f(ctypes.byref(d300), ctypes.byref(w), u, None, None, None, None, y, None, None, ws, n3, s) == ESHAPE
+
+
+def test_scan_fwd_noalloc_validation(L):
+    # the same checks as rglru_scan_fwd, and a size limit in place of the
+    # workspace size: 16640 + 24 B ceil(T/32) D bytes must fit the scratch
+    d = desc()
+    w = weights()
+    s = None
+    u, y, r = P + 0x1000000, P + 0x2000000, P + 0x3000000
+    f = L.rglru_scan_fwd_noalloc
+    assert f(ctypes.byref(d), ctypes.byref(w), u, r, None, None, None, y, None, None, s) == EARG
+    assert f(ctypes.byref(d), ctypes.byref(w), u, None, None, None, None, None, None, None, s) == ENULL
+    assert f(ctypes.byref(d), ctypes.byref(w), u + 8, None, None, None, None, y, None, None, s) == EALIGN
+    assert f(ctypes.byref(d), ctypes.byref(w), u, None, None, None, None, u, None, None, s) == EARG
+    assert f(None, ctypes.byref(w), u, None, None, None, None, y, None, None, s) == ENULL
+    fits = desc(B=1, T=1091 * 32, D=2560, H=10)
+    rc, n = ws_size(fits)
+    assert rc == OK and n == 16640 + 24 * 1091 * 2560 <= glr.NOALLOC_SCRATCH_BYTES
+    over = desc(B=1, T=1092 * 32, D=2560, H=10)
+    rc, n = ws_size(over)
+    assert rc == OK and n > glr.NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(over), ctypes.byref(w), u, None, None, None, None, y, None, None, s) == ESCRATCH
+    big = desc(B=4, T=8192, D=4096, H=16)
+    assert f(ctypes.byref(big), ctypes.byref(w), u, None, None, None, None, y, None, None, s) == ESCRATCH
 
 
 def test_step_validation(L):
