@@ -189,6 +189,61 @@ def copy_calibration(torch, dev, n=10):
                       "kernel_ms": ms, "gbs": 2 * nbytes / (ms * 1e-3) / 1e9}), flush=True)
 
 
+# kernels that the counter summaries cover: (label, regular expression for the
+# kernel name as rocprofv3 reports it, demangled "<__bf16, 0>" or mangled
+# "IDF16bLi0E" for the bf16 template arguments)
+PROFILED_KERNELS = (
+    ("fused forward, mode A (rglru_scan_fwd)", r"(?<![a-z_])fwd_kernel(<__bf16, 0>|IDF16bLi0E)"),
+    ("backward pass 1: states, r, i (mode-3 forward)", r"(?<![a-z_])fwd_kernel(<__bf16, 3>|IDF16bLi3E)"),
+    ("backward pass 3: reverse aggregates", r"rev_agg_kernel(<__bf16>|IDF16b)"),
+    ("backward pass 4: unit kernel", r"bwd_unit_kernel(<__bf16>|IDF16b)"),
+    ("backward pass 6: dW", r"dw_kernel_bf16"),
+    ("decode step (rglru_step)", r"step_kernel(<__bf16>|IDF16b)"),
+)
+
+
+def summarize(args):
+    """Summaries of rocprofv3 output kept in profiles/ (no GPU needed)."""
+    from gated_linear_recurrence_02_amd import profiling
+    import synth
+    if args.summarize_traffic:
+        d = args.summarize_traffic
+        match = PROFILED_KERNELS[0][1]
+        cfg = synth.PREFILL_2B
+        t = profiling.traffic(os.path.join(d, "fetch"), os.path.join(d, "write"), os.path.join(d, "copy_fetch"),
+                              os.path.join(d, "copy_write"), match, 1 << 30)
+        alg = fwd_bytes(cfg.B, cfg.T, cfg.D, cfg.H, 2)
+        out = {"kernel": "fwd_kernel<bf16, mode A>",
+               "workload": f"2B-width prefill B={cfg.B} T={cfg.T} D={cfg.D} bf16",
+               "kernel_source_hash": kernel_hash(),
+               "commands": {
+                   "fetch": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --kernel-trace "
+                            "--output-format csv -d <out>/fetch -- python3 <repo>/bench.py --steps 5 --warmup 1 "
+                            "--no-cpu --rows=",
+                   "write": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --kernel-trace "
+                            "--output-format csv -d <out>/write -- python3 <repo>/bench.py --steps 5 --warmup 1 "
+                            "--no-cpu --rows=",
+                   "copy_fetch": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --kernel-trace "
+                                 "--output-format csv -d <out>/copy_fetch -- python3 <repo>/bench.py "
+                                 "--copy-calibration",
+                   "copy_write": "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --kernel-trace "
+                                 "--output-format csv -d <out>/copy_write -- python3 <repo>/bench.py "
+                                 "--copy-calibration",
+                   "summary": "python3 <repo>/bench.py --summarize-traffic <out>"},
+               **t,
+               "algorithmic_bytes_per_launch": alg,
+               "traffic_over_algorithmic": round(t["hbm_bytes_per_launch"] / alg, 3),
+               "note": "FETCH_SIZE/WRITE_SIZE count traffic between L2 and the fabric (Infinity Cache hits "
+                       "included); each is scaled by what the same counter reads for torch's copy of 1 GiB. "
+                       "kernel_source_hash covers the sources of the kernel; bench.py reports traffic only "
+                       "while it matches."}
+        print(json.dumps(out, indent=1))
+    if args.summarize_counters:
+        print(profiling.counter_table(args.summarize_counters, PROFILED_KERNELS))
+    if args.summarize_trace:
+        print(profiling.trace_table(args.summarize_trace))
+
+
 def micro(torch, dev):
     """Ceilings on this GPU: vector-ALU rates (FMA and the transcendentals the
     gate math uses), bf16 MFMA rate and plain copy bandwidth, from the kernels
@@ -285,7 +340,20 @@ def main():
                     help="run the ALU, MFMA and copy microbenchmarks and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device copy and exit")
+    ap.add_argument("--summarize-traffic", metavar="DIR",
+                    help="print the HBM traffic summary of the headline kernel from rocprofv3 CSV output "
+                         "under DIR/fetch, DIR/write (FETCH_SIZE / WRITE_SIZE runs of this script) and "
+                         "DIR/copy_fetch, DIR/copy_write (the same runs of --copy-calibration), then exit")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print per-kernel calls and durations from rocprofv3 --kernel-trace --stats CSV "
+                         "output under DIR, then exit")
+    ap.add_argument("--summarize-counters", metavar="DIR", nargs="+",
+                    help="print the per-kernel means of every counter found in rocprofv3 --pmc CSV "
+                         "output under the DIRs (one per counter pass), then exit")
     args = ap.parse_args()
+    if args.summarize_traffic or args.summarize_counters or args.summarize_trace:
+        summarize(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               f"(this build runs and reports a single MI355X)", file=sys.stderr)
