@@ -94,7 +94,7 @@ def lib():
         L.rglru_gates.argtypes = [D, W, vp, vp, vp, vp]
         L.rglru_scan_fwd.argtypes = [D, W, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.rglru_scan_fwd_noalloc.argtypes = [D, W, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-        L.rglru_step.argtypes = [D, W, vp, vp, vp, vp, vp]
+        L.rglru_step.argtypes = [D, W, vp, vp, vp, vp, vp, vp]
         L.rglru_scan_bwd.argtypes = [D, W, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         A = ctypes.POINTER(_AttnDesc)
         L.rglru_attn_fwd.argtypes = [A, vp, vp, vp, vp, vp, vp, vp]
@@ -333,19 +333,24 @@ def _scan_fwd(inp, w, r, i, h0, hist_in, conv, want_hist, out, h_last_out, hist_
     return y, h_last, hist_out
 
 
-def step(u_t: torch.Tensor, w: Weights, hist: torch.Tensor, h: torch.Tensor, y_out=None):
-    """One decode step; hist [B][3][D] and h [B][D] are updated in place.  Returns y_t."""
+def step(u_t: torch.Tensor, w: Weights, h: torch.Tensor, hist_in=None, hist_out=None, y_out=None):
+    """One decode step.  h [B][D] (fp32) is updated in place; the conv history
+    goes from hist_in [B][3][D] (None: zeros) to hist_out (allocated if None;
+    must not overlap hist_in -- alternate two buffers).  Returns (y_t, hist_out)."""
     dev = u_t.device
     _need(u_t, "u_t", dev)
     B, D = u_t.shape
-    _need(hist, "hist", dev, u_t.dtype, (B, 3, D))
+    _need(hist_in, "hist_in", dev, u_t.dtype, (B, 3, D))
     _need(h, "h", dev, torch.float32, (B, D))
     ws_ = _weights_struct(w, D, u_t.dtype, dev, conv=True, gates=True)
     y_t = torch.empty_like(u_t) if y_out is None else y_out
+    if hist_out is None:
+        hist_out = torch.empty((B, 3, D), dtype=u_t.dtype, device=dev)
+    _need(hist_out, "hist_out", dev, u_t.dtype, (B, 3, D))
     d = _Desc(B, 1, D, w.H, _io(u_t), w.c)
-    _check(lib().rglru_step(ctypes.byref(d), ctypes.byref(ws_), _ptr(u_t), _ptr(hist), _ptr(h),
-                            _ptr(y_t), _stream(dev)), "rglru_step")
-    return y_t
+    _check(lib().rglru_step(ctypes.byref(d), ctypes.byref(ws_), _ptr(u_t), _ptr(hist_in), _ptr(hist_out),
+                            _ptr(h), _ptr(y_t), _stream(dev)), "rglru_step")
+    return y_t, hist_out
 
 
 def scan_bwd(u: torch.Tensor, w: Weights, dy: torch.Tensor, *, h0=None, hist_in=None,

@@ -307,26 +307,27 @@ int rglru_scan_fwd_noalloc(const rglru_desc *desc, const rglru_weights *w, const
     return launch_status();
 }
 
-int rglru_step(const rglru_desc *desc, const rglru_weights *w, const void *u_t, void *hist, float *h,
-               void *y_t, hipStream_t stream)
+int rglru_step(const rglru_desc *desc, const rglru_weights *w, const void *u_t, const void *hist_in,
+               void *hist_out, float *h, void *y_t, hipStream_t stream)
 {
     int st = check_desc(desc, true);
     if (st) return st;
     if (desc->T != 1) return RGLRU_ERR_SHAPE;
-    if (!w || !w->conv_w || !w->W_a || !w->W_x || !w->Lambda || !u_t || !hist || !h || !y_t)
-        return RGLRU_ERR_NULL;
-    const void *all[] = {u_t, hist, h, y_t, w->conv_w, w->conv_b, w->W_a, w->b_a, w->W_x, w->b_x, w->Lambda};
+    if (!w || !w->conv_w || !w->W_a || !w->W_x || !w->Lambda || !u_t || !h || !y_t) return RGLRU_ERR_NULL;
+    const void *all[] = {u_t, hist_in, hist_out, h, y_t, w->conv_w, w->conv_b, w->W_a, w->b_a, w->W_x, w->b_x,
+                         w->Lambda};
     for (const void *p : all)
         if (p && !aligned16(p)) return RGLRU_ERR_ALIGN;
     const rglru_desc &d = *desc;
     const size_t row = d.B * d.D * esize(d), hb = d.B * 3 * d.D * esize(d), sb = d.B * d.D * 4;
     const size_t vec = d.D * 4, wb = d.H * 65536 * esize(d);
-    // hist and h are in/out by design; they must not overlap each other, y_t or any input
-    const Range outs[] = {{y_t, row}, {hist, hb}, {h, sb}};
-    const Range ins[] = {{u_t, row}, {w->conv_w, vec * 4}, {w->conv_b, vec}, {w->W_a, wb},
+    // h is read and rewritten in place by design; no output may overlap another
+    // output or an input (hist_out and hist_in included)
+    const Range outs[] = {{y_t, row}, {hist_out, hb}, {h, sb}};
+    const Range ins[] = {{u_t, row}, {hist_in, hb}, {w->conv_w, vec * 4}, {w->conv_b, vec}, {w->W_a, wb},
                          {w->b_a, vec}, {w->W_x, wb}, {w->b_x, vec}, {w->Lambda, vec}};
-    if (any_alias(outs, 3, ins, 8)) return RGLRU_ERR_ARG;
-    launch_step(d, *w, u_t, hist, h, y_t, stream);
+    if (any_alias(outs, 3, ins, 9)) return RGLRU_ERR_ARG;
+    launch_step(d, *w, u_t, hist_in, hist_out, h, y_t, stream);
     return launch_status();
 }
 

@@ -94,8 +94,8 @@ void launch_attn_fwd(const rglru_attn_desc &d, const void *q, const void *k, con
 void launch_attn_step(const rglru_attn_desc &d, const void *q_t, const void *k_t, const void *v_t, void *kc,
                       void *vc, const int32_t *pos, void *o_t, void *ws, hipStream_t s);
 
-void launch_step(const rglru_desc &d, const rglru_weights &w, const void *u_t, void *hist,
-                 float *h, void *y_t, hipStream_t s);
+void launch_step(const rglru_desc &d, const rglru_weights &w, const void *u_t, const void *hist_in,
+                 void *hist_out, float *h, void *y_t, hipStream_t s);
 
 void launch_scan_bwd(const rglru_desc &d, const rglru_weights &w, const void *u, const void *hist_in,
                      const float *h0, const void *dy, const float *dh_last, void *du, float *dcw,

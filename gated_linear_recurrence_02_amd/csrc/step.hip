@@ -7,29 +7,35 @@
 // evaluated on the carried 3-token history.
 //
 // A decode step is small (B x D elements, ~18 MB touched at B = 256,
-// D = 2560, most of it resident in L2 / Infinity Cache between calls), so the
-// kernel is shaped for parallelism and latency, not reuse: one workgroup
-// (8 waves) per (16 streams, 256-channel block), 160 workgroups at B = 256,
-// D = 2560.
-//   1. every load is issued at once, in the order the values are needed:
-//      the conv's inputs and taps, the gate weights the lane needs, then its
-//      own outputs' state and gate biases -- 2 channels x 4 streams;
-//   2. every thread computes the conv of 8 channels of one stream of the
-//      block's input tile (16 streams x 256 channels) into LDS (bf16 for
-//      the matrix cores, fp32 for the update), and the first 256 threads the
-//      decay constant of one channel; after the barrier the same thread
-//      writes its 8 channels of history back, shifted by one token;
-//   3. bf16: wave w computes the gate products of output channels
-//      32w .. 32w+31 (two 16-channel tiles) for the 16 streams with
-//      v_mfma_f32_16x16x32_bf16 (A = x tile rows, B = W rows read from
-//      memory), which leaves lane l with streams 4(l/16)+i of channels
-//      32w + 16t + l%16; fp32: the same outputs by fp32 FMAs;
-//   4. gates, decay, normalisation and the state update for those 8
-//      elements; state and output are rewritten in place.
-// A workgroup reads and rewrites the history of its own (streams, block)
-// only, after the barrier that ends the reads of step 1.
+// D = 2560, most of it resident in L2 / Infinity Cache between calls) and
+// its time is latency: one global round trip, two barriers, a short
+// matrix-core phase and the elementwise update.  One workgroup of 8 waves
+// per (64 streams, 256-channel block g, 64 output channels oc0 .. oc0+63
+// of the block): 4 x 10 x 4 = 160 workgroups at B = 256, D = 2560, one per
+// CU.
+//   1. every load is issued at once: the conv inputs of the 64 streams x
+//      256 input channels of the block (history rows and the new token), the
+//      block's conv taps and bias and the 64 rows of W_a and W_x of the
+//      workgroup's outputs (both staged into LDS with global_load_lds, whole
+//      1 KB pieces), and for each lane's own outputs the state and gate
+//      biases;
+//   2. after the first barrier: the conv of the input tile into LDS (bf16,
+//      the matrix-core B operand; fp32 for the workgroup's own 64 channels,
+//      which the update uses), the history of the own channels moved one
+//      token on into hist_out, and -c softplus(-Lambda) of the own channels;
+//   3. after the second: wave w computes the gate pre-activations of the 16
+//      channels 16 (w % 4) .. +15 x the 32 streams 32 (w / 4) .. +31 with
+//      v_mfma_f32_16x16x32_bf16 (fp32 I/O: the same outputs by fp32 FMAs);
+//   4. gates, decay, normalisation, state update: 16-byte state loads and
+//      stores, h rewritten in place, y stored.
+// The 4 workgroups of one (streams, block) pair read the same inputs; the
+// blockIdx -> work map puts them on one XCD so that its L2 serves the
+// repeats.  History in and out are separate buffers: the other workgroups
+// of the pair still read the old history of the channels whose new history
+// a workgroup writes.
+#include <mutex>
+
 #include "common.h"
-#include "gatemath.h"
 #include "internal.h"
 
 namespace rglru {
@@ -38,258 +44,376 @@ namespace {
 
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4v;
 
-constexpr int SB = 16;   // streams per workgroup
+constexpr int SS = 64;            // streams per workgroup
+constexpr int SC = 64;            // output channels per workgroup
+constexpr int NSLICE = 256 / SC;  // workgroups per (streams, block) pair
+constexpr int NT = 512;           // threads per workgroup
 
-__device__ __forceinline__ void load8(const bf16 *p, float v[8])
-{
-    const bf16x8 q = *(const bf16x8 *)p;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (float)q[e];
-}
-
-__device__ __forceinline__ void load8(const float *p, float v[8])
-{
-    const f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        v[e] = a[e];
-        v[4 + e] = b[e];
-    }
-}
-
-__device__ __forceinline__ void store8(bf16 *p, const float v[8])
-{
-    bf16x8 q;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) q[e] = (bf16)v[e];
-    *(bf16x8 *)p = q;
-}
-
-__device__ __forceinline__ void store8(float *p, const float v[8])
-{
-    *(f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
-    *(f32x4 *)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
-}
-
-// B operands of the lane's gate products: rows oc0 + 16t + l%16 of W_a and
-// W_x, K-steps of 32 (lane group l/16 holds 8 consecutive inputs of a step);
-// requested at kernel start so that their latency overlaps steps 1 and 2
-template <typename T> struct WOps {
-    bf16x8 a[2][8], x[2][8];
+// LDS of one workgroup: the conv output tile (streams x 256 input channels,
+// rows padded by 16 bytes), (bf16) the 2 x 64 weight rows and the fp32 conv
+// output of the own channels, -c softplus(-Lambda) of the own channels, and
+// the conv taps and bias of the block's 256 channels.  The weight rows are
+// 512 bytes, unpadded, with the 16-byte slots of row r XOR-swizzled by
+// r & 15, so that the 16 rows one operand read touches hit 16 different
+// slots.
+template <typename T> struct StepLds {
+    static constexpr int V = 16 / sizeof(T);       // elements per 16-byte vector
+    static constexpr int XS = 256 + V;             // padded row stride
+    static constexpr int X32S = SC + 4;
+    T x[SS * XS];
+    bf16 w[sizeof(T) == 2 ? 2 * SC * 256 : 8];
+    float x32[sizeof(T) == 2 ? SS * X32S : 4];
+    float ncs[SC];
+    f32x4 taps[256];
+    float cb[256];
 };
-template <> struct WOps<float> {};
 
-__device__ __forceinline__ void load_wops(WOps<bf16> &w, const bf16 *Wa_h, const bf16 *Wx_h, int oc0, int lane)
-{
-    const int m = lane & 15, kq = lane >> 4;
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-        const bf16 *wa = Wa_h + (size_t)(oc0 + 16 * ct + m) * 256 + 8 * kq;
-        const bf16 *wx = Wx_h + (size_t)(oc0 + 16 * ct + m) * 256 + 8 * kq;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            w.a[ct][ks] = *(const bf16x8 *)(wa + 32 * ks);
-            w.x[ct][ks] = *(const bf16x8 *)(wx + 32 * ks);
-        }
-    }
-}
-__device__ __forceinline__ void load_wops(WOps<float> &, const float *, const float *, int, int) {}
+template <typename T> struct StepParams {
+    int B, D;
+    float c;
+    const T *u_t, *hist_in;
+    T *hist_out;
+    const float *cw, *cb;
+    const T *Wa, *Wx;
+    const float *ba, *bx, *Lambda;
+    float *h;
+    T *y;
+};
 
-// gate pre-activations of the lane's 8 outputs -- streams 4(l/16)+i (i < 4)
-// of channels oc0 + 16t + l%16 (t < 2) -- bf16: two 16-channel tiles x
-// 8 K-steps x 2 gates on the matrix cores; element e = 4t + i
-__device__ __forceinline__ void step_gates(const bf16 *Xs, const WOps<bf16> &w, const bf16 *, const bf16 *,
-                                           int, int lane, float za[8], float zx[8])
+template <typename T> struct Vec;
+template <> struct Vec<bf16> { typedef bf16x8 type; };
+template <> struct Vec<float> { typedef f32x4 type; };
+
+template <typename T>
+__device__ __forceinline__ void to_f32(const typename Vec<T>::type &q, float *v)
 {
-    constexpr int S = XTile<bf16>::STRIDE;
-    const int m = lane & 15, kq = lane >> 4;
-    const bf16 *xrow = Xs + m * S + 8 * kq;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-        f32x4v A = {}, X = {};
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const bf16x8 av = *(const bf16x8 *)(xrow + 32 * ks);
-            A = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, w.a[ct][ks], A, 0, 0, 0);
-            X = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, w.x[ct][ks], X, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            za[4 * ct + i] = A[i];
-            zx[4 * ct + i] = X[i];
-        }
-    }
+    for (int e = 0; e < StepLds<T>::V; ++e) v[e] = (float)q[e];
 }
 
-// fp32: the same outputs with fp32 FMAs in input-channel order
-__device__ __forceinline__ void step_gates(const float *Xs, const WOps<float> &, const float *Wa_h,
-                                           const float *Wx_h, int oc0, int lane, float za[8], float zx[8])
+typedef __attribute__((address_space(3))) void lds_void;
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int nt_u32x2 __attribute__((ext_vector_type(2)));
+
+// Outputs are streamed past L2 (nontemporal): nothing in the step reads
+// them again, and dirty lines left in L2 would be written back at the end
+// of every step.
+template <typename V16> __device__ __forceinline__ void nt_store16(void *dst, const V16 &v)
 {
-    constexpr int S = XTile<float>::STRIDE;
-    const int m = lane & 15, kq = lane >> 4;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) za[e] = zx[e] = 0.0f;
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-        const float *wa = Wa_h + (size_t)(oc0 + 16 * ct + m) * 256;
-        const float *wx = Wx_h + (size_t)(oc0 + 16 * ct + m) * 256;
-        for (int k = 0; k < 256; ++k) {
-            const float a = wa[k], x = wx[k];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float xv = Xs[(4 * kq + i) * S + k];
-                za[4 * ct + i] = fmaf(a, xv, za[4 * ct + i]);
-                zx[4 * ct + i] = fmaf(x, xv, zx[4 * ct + i]);
-            }
-        }
-    }
+    static_assert(sizeof(V16) == 16, "16-byte store");
+    __builtin_nontemporal_store(__builtin_bit_cast(nt_u32x4, v), (nt_u32x4 *)dst);
+}
+template <typename V8> __device__ __forceinline__ void nt_store8(void *dst, const V8 &v)
+{
+    static_assert(sizeof(V8) == 8, "8-byte store");
+    __builtin_nontemporal_store(__builtin_bit_cast(nt_u32x2, v), (nt_u32x2 *)dst);
+}
+
+// softplus(v) = max(v, 0) + log1p(e^-|v|) for the bf16 path, from the
+// hardware exp2 and reciprocal: e^-|v| with the rounding of |v| log2(e)
+// corrected to first order, then log1p(z) = 2 atanh(s), s = z / (2 + z)
+// <= 1/3, by its odd series to s^15 (truncation below 2^-29 relative).
+// Relative error a few ulp, uniformly in v.
+__device__ __forceinline__ float softplus_fast(float v)
+{
+    constexpr float LOG2E_LO = 1.925963033500011e-8f;   // log2(e) - LOG2E
+    constexpr float LN2 = 0.6931471805599453f;
+    const float x = -fabsf(v);
+    const float t = x * LOG2E;
+    const float err = fmaf(x, LOG2E, -t) + x * LOG2E_LO;   // x log2(e) - t
+    const float z = hw_exp2(t) * fmaf(err, LN2, 1.0f);
+    const float sv = z * hw_rcp(2.0f + z);
+    const float s2 = sv * sv;
+    float q = 2.0f / 15.0f;
+    q = fmaf(q, s2, 2.0f / 13.0f);
+    q = fmaf(q, s2, 2.0f / 11.0f);
+    q = fmaf(q, s2, 2.0f / 9.0f);
+    q = fmaf(q, s2, 2.0f / 7.0f);
+    q = fmaf(q, s2, 2.0f / 5.0f);
+    q = fmaf(q, s2, 2.0f / 3.0f);
+    q = fmaf(q, s2, 2.0f);
+    return fmaxf(v, 0.0f) + sv * q;
 }
 
 template <typename T>
-__global__ __launch_bounds__(512) void step_kernel(int B, int D, float c, const T *u_t, const float *cw,
-                                                   const float *cb, const T *Wa, const float *ba,
-                                                   const T *Wx, const float *bx, const float *Lambda,
-                                                   T *hist, float *hstate, T *y_t)
+__global__ __launch_bounds__(NT) void step_kernel(StepParams<T> p)
 {
-    constexpr int S = XTile<T>::STRIDE;
-    constexpr int S32 = XTile<float>::STRIDE;
-    __shared__ __attribute__((aligned(16))) T Xs[SB * S];          // conv output, MFMA operand
-    __shared__ __attribute__((aligned(16))) float X32[SB * S32];   // the same in fp32
-    __shared__ float ncs_s[256];   // -c softplus(-Lambda) of the block's channels
-    // Workgroup id -> (stream tile, block), block-major over the XCDs:
-    // consecutive ids go round-robin to the 8 XCDs, so ids that share id % 8
-    // get consecutive (block, tile) pairs and each XCD's L2 holds the gate
-    // weights of two or three blocks rather than all of them.  The map is a
-    // permutation of the ids whatever the hardware does.
-    const int nwg = gridDim.x, ntile = (B + SB - 1) / SB;
+    typedef typename Vec<T>::type vec;
+    constexpr int V = StepLds<T>::V, XS = StepLds<T>::XS, X32S = StepLds<T>::X32S;
+    constexpr int NG = 256 / V;         // channel groups of one stream row
+    constexpr int RS = NT / NG;         // stream rows one pass of the workgroup covers
+    constexpr int SPT = SS / RS;        // streams per thread in the conv
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    StepLds<T> &L = *reinterpret_cast<StepLds<T> *>(smem);
+
+    const int B = p.B, D = p.D;
+    // Workgroup id -> (stream tile, block, channel slice).  Consecutive ids
+    // go round-robin to the 8 XCDs; `lin` renumbers them so that ids sharing
+    // an XCD get consecutive numbers, and the slices of one (tile, block)
+    // pair have consecutive numbers.  A permutation of the ids whatever the
+    // hardware does.
+    const int nwg = gridDim.x, ntile = (B + SS - 1) / SS;
     const int xcd = blockIdx.x % 8, loc = blockIdx.x / 8;
-    const int pair = xcd * (nwg / 8) + (xcd < nwg % 8 ? xcd : nwg % 8) + loc;
-    const int sb0 = (pair % ntile) * SB, g = pair / ntile;
+    const int lin = xcd * (nwg / 8) + (xcd < nwg % 8 ? xcd : nwg % 8) + loc;
+    const int pair = lin / NSLICE, oc0 = (lin % NSLICE) * SC;
+    const int sb0 = (pair % ntile) * SS, g = pair / ntile;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    // optional per-channel vectors: a null one reads a valid array and is
-    // replaced by zeros, so that no load sits behind a branch
-    const float *cbp = cb ? cb : Lambda, *bap = ba ? ba : Lambda, *bxp = bx ? bx : Lambda;
+    const int m = lane & 15, kq = lane >> 4;
+    const long gb = (long)g * 256;
 
-    // 1. every load, in the order the values are needed: the conv's inputs
-    //    and taps (8 channels of one stream per thread), the gate weights of
-    //    the lane's outputs, then the lane's outputs' state and gate biases
-    //    -- element e = 4t + i is stream sb0 + 4(l/16) + i of channel
-    //    oc0 + 16t + l%16 of the block.  Streams past B read stream B - 1 and
-    //    are not stored.
-    const int cg = tid & 31, sl = tid >> 5;
-    const long sc = sb0 + sl < B ? sb0 + sl : B - 1;
-    const int dc = g * 256 + 8 * cg;
-    float a0[8], a1[8], a2[8], a3[8];
-    load8(hist + (sc * 3 + 0) * D + dc, a0);
-    load8(hist + (sc * 3 + 1) * D + dc, a1);
-    load8(hist + (sc * 3 + 2) * D + dc, a2);
-    load8(u_t + sc * D + dc, a3);
-    f32x4 taps[8];
+    // 1. loads, all issued before the first wait.
+    //  - conv taps and bias of the block's channels into LDS (one 1 KB wave
+    //    instruction each: wave w < 4 the taps of channels 64w .. 64w+63,
+    //    wave 4 the bias);
+    if (wave < 4)
+        __builtin_amdgcn_global_load_lds((const void *)(p.cw + 4 * (gb + tid)), (lds_void *)(L.taps + 64 * wave),
+                                         16, 0, 0);
+    if (p.cb) {
+        if (wave == 4)
+            __builtin_amdgcn_global_load_lds((const void *)(p.cb + gb + 4 * lane), (lds_void *)L.cb, 16, 0, 0);
+    } else if (tid < 256) {
+        L.cb[tid] = 0.0f;
+    }
+    //  - conv inputs: thread t covers channels V cg .. V cg + V-1 of streams
+    //    sb0 + sl + RS j (j < SPT); streams past B read stream B-1 and store
+    //    nothing;
+    const int cg = tid % NG, sl = tid / NG;
+    const long dc = gb + V * cg;
+    vec hv[SPT][4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) taps[e] = *(const f32x4 *)(cw + 4 * (long)(dc + e));
-    float cbv[8];
-    load8(cbp + dc, cbv);
-    const float lam = Lambda[g * 256 + (tid & 255)];   // used by the first 256 threads
-
-    const int oc0 = 32 * wave;
-    WOps<T> wop;
-    load_wops(wop, Wa + (size_t)g * 65536, Wx + (size_t)g * 65536, oc0, lane);
-    float hv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int s0 = sb0 + 4 * (lane >> 4) + (e & 3);
+    for (int j = 0; j < SPT; ++j) {
+        const int s0 = sb0 + sl + RS * j;
         const long s = s0 < B ? s0 : B - 1;
-        hv[e] = hstate[s * D + g * 256 + oc0 + 16 * (e >> 2) + (lane & 15)];
-    }
-    float bav[2], bxv[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int d = g * 256 + oc0 + 16 * t + (lane & 15);
-        bav[t] = bap[d];
-        bxv[t] = bxp[d];
-    }
-    __builtin_amdgcn_sched_barrier(0);   // keep every request ahead of the first wait
-
-    // 2. conv of the input tile into LDS; the decay constants of the block
-    {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const f32x4 t = taps[e];
-            const float bias = cb ? cbv[e] : 0.0f;
-            x[e] = fmaf(t[3], a3[e], fmaf(t[2], a2[e], fmaf(t[1], a1[e], fmaf(t[0], a0[e], bias))));
+        for (int r = 0; r < 3; ++r) {
+            if (p.hist_in) hv[j][r] = *(const vec *)(p.hist_in + (s * 3 + r) * D + dc);
+            else hv[j][r] = vec{};
         }
-        store8(Xs + sl * S + 8 * cg, x);
-        store8(X32 + sl * S32 + 8 * cg, x);
-        const float ncs = -c * softplus_acc(-lam);
-        if (tid < 256) ncs_s[tid] = ncs;
+        hv[j][3] = *(const vec *)(p.u_t + s * D + dc);
     }
-    __syncthreads();   // the tiles are complete and every read of the history is done
-
-    // the history moves one token on: the thread that read 8 channels of a
-    // stream writes them back one position earlier, with the new input last
-    if (sb0 + sl < B) {
-        store8(hist + (sc * 3 + 0) * D + dc, a1);
-        store8(hist + (sc * 3 + 1) * D + dc, a2);
-        store8(hist + (sc * 3 + 2) * D + dc, a3);
+    //  - bf16: the weight rows oc0 .. oc0+63 of block g, both gates, in 64
+    //    wave instructions of two rows each, 8 per wave: instruction n stages
+    //    rows 2(n % 32), +1 of gate n / 32; lane l the slot l % 32 of row
+    //    2(n % 32) + l / 32, which holds column vector slot ^ (row & 15);
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int n = 8 * k + wave, gate = n >> 5, r = 2 * (n & 31) + (lane >> 5);
+            const int cv = (lane & 31) ^ (r & 15);
+            const T *src = (gate ? p.Wx : p.Wa) + (size_t)g * 65536 + (size_t)(oc0 + r) * 256 + 8 * cv;
+            __builtin_amdgcn_global_load_lds((const void *)src, (lds_void *)(L.w + (gate * SC + 2 * (n & 31)) * 256),
+                                             16, 0, 0);
+        }
     }
+    //  - the lane's outputs: channels oc0 + 16 ct + 4 kq + r (ct = wave % 4,
+    //    r < 4) of the block for streams sb0 + 16 st + m (st = 2 (wave / 4)
+    //    and + 1): state and gate biases as 16-byte vectors; Lambda of
+    //    channel oc0 + tid (tid < SC)
+    const int ct = wave & 3, st0 = 2 * (wave >> 2);
+    const int cl = 16 * ct + 4 * kq;   // first channel of the lane in the slice
+    const long dl = gb + oc0 + cl;
+    f32x4 hs[2];
+    long srow[2];
+    int so[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        so[st] = sb0 + 16 * (st0 + st) + m;
+        srow[st] = (long)(so[st] < B ? so[st] : B - 1) * D;
+        hs[st] = *(const f32x4 *)(p.h + srow[st] + dl);
+    }
+    const f32x4 bav = p.ba ? *(const f32x4 *)(p.ba + dl) : f32x4{};
+    const f32x4 bxv = p.bx ? *(const f32x4 *)(p.bx + dl) : f32x4{};
+    const float lam = tid < SC ? p.Lambda[gb + oc0 + tid] : 0.0f;
+    // every staged byte has landed (and the conv inputs with it)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 
-    // 3. gate pre-activations of the lane's outputs
-    float za[8], zx[8];
-    step_gates(Xs, wop, Wa + (size_t)g * 65536, Wx + (size_t)g * 65536, oc0, lane, za, zx);
+    // 2. conv into LDS; the own channels' history moved on into hist_out;
+    //    the decay constants of the own channels
+    const bool own = V * cg >= oc0 && V * cg < oc0 + SC;
+    {
+        f32x4 taps[V];
+        float cbv[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            taps[e] = L.taps[V * cg + e];
+            cbv[e] = L.cb[V * cg + e];
+        }
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) {
+            const int sr = sl + RS * j;
+            float a[4][V], x[V];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) to_f32<T>(hv[j][r], a[r]);
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                const f32x4 t = taps[e];
+                x[e] = fmaf(t[3], a[3][e], fmaf(t[2], a[2][e], fmaf(t[1], a[1][e], fmaf(t[0], a[0][e], cbv[e]))));
+            }
+            vec q;
+#pragma unroll
+            for (int e = 0; e < V; ++e) q[e] = from_f32<T>(x[e]);
+            *(vec *)(L.x + sr * XS + V * cg) = q;
+            if constexpr (sizeof(T) == 2) {
+                if (own) {
+                    float *dst = L.x32 + sr * X32S + (V * cg - oc0);
+                    *(f32x4 *)dst = f32x4{x[0], x[1], x[2], x[3]};
+                    *(f32x4 *)(dst + 4) = f32x4{x[4], x[5], x[6], x[7]};
+                }
+            }
+            if (own && p.hist_out && sb0 + sr < B) {
+                const long s = sb0 + sr;
+                nt_store16(p.hist_out + (s * 3 + 0) * D + dc, hv[j][1]);
+                nt_store16(p.hist_out + (s * 3 + 1) * D + dc, hv[j][2]);
+                nt_store16(p.hist_out + (s * 3 + 2) * D + dc, hv[j][3]);
+            }
+        }
+    }
+    if (tid < SC) L.ncs[tid] = -p.c * (sizeof(T) == 2 ? softplus_fast(-lam) : softplus_acc(-lam));
+    // LDS only: the history stores need not have completed
+    lds_barrier();
+
+    // 3. gate pre-activations z[st][r]: channel cl + r of the slice, stream
+    //    16 (st0 + st) + m of the tile (weight rows = A operand, conv outputs
+    //    = B)
+    float za[2][4], zx[2][4];
+    if constexpr (sizeof(T) == 2) {
+        f32x4v A[2] = {}, X[2] = {};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const int slot = (kq + 4 * ks) ^ m;   // row 16 ct + m: swizzled by m
+            const bf16x8 wa = *(const bf16x8 *)(L.w + (16 * ct + m) * 256 + 8 * slot);
+            const bf16x8 wx = *(const bf16x8 *)(L.w + (SC + 16 * ct + m) * 256 + 8 * slot);
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const bf16x8 xv = *(const bf16x8 *)(L.x + (16 * (st0 + st) + m) * XS + 8 * kq + 32 * ks);
+                A[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xv, A[st], 0, 0, 0);
+                X[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wx, xv, X[st], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                za[st][r] = A[st][r];
+                zx[st][r] = X[st][r];
+            }
+    } else {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) za[st][r] = zx[st][r] = 0.0f;
+        const size_t wrow = (size_t)g * 65536 + (size_t)(oc0 + cl) * 256;
+        for (int k = 0; k < 256; k += 4) {
+            f32x4 xv[2], wav[4], wxv[4];
+#pragma unroll
+            for (int st = 0; st < 2; ++st) xv[st] = *(const f32x4 *)(L.x + (16 * (st0 + st) + m) * XS + k);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                wav[r] = *(const f32x4 *)(p.Wa + wrow + (size_t)r * 256 + k);
+                wxv[r] = *(const f32x4 *)(p.Wx + wrow + (size_t)r * 256 + k);
+            }
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        za[st][r] = fmaf(wav[r][kk], xv[st][kk], za[st][r]);
+                        zx[st][r] = fmaf(wxv[r][kk], xv[st][kk], zx[st][r]);
+                    }
+        }
+    }
 
     // 4. gates, decay, normalisation, state update
+    const f32x4 ncs = *(const f32x4 *)(L.ncs + cl);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int ch = oc0 + 16 * t + (lane & 15);
-        const int d = g * 256 + ch;
-        const float ncs = ncs_s[ch];
-        const float bat = ba ? bav[t] : 0.0f, bxt = bx ? bxv[t] : 0.0f;
-        const float kba = -LOG2E * bat, kbx = -LOG2E * bxt, kdec = LOG2E * ncs;
+    for (int st = 0; st < 2; ++st) {
+        const int sr = 16 * (st0 + st) + m;
+        f32x4 xs;
+        if constexpr (sizeof(T) == 2) xs = *(const f32x4 *)(L.x32 + sr * X32S + cl);
+        else xs = *(const f32x4 *)(L.x + sr * XS + oc0 + cl);
+        f32x4 hn;
+        vec yq{};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = 4 * t + i;
-            const int sr = 4 * (lane >> 4) + i, s = sb0 + sr;
-            const float x = X32[sr * S32 + ch];
+        for (int r = 0; r < 4; ++r) {
             float a, bb;
             if constexpr (sizeof(T) == 2) {
-                const float rr = hw_rcp(1.0f + hw_exp2(fmaf(za[e], -LOG2E, kba)));
-                const float ii = hw_rcp(1.0f + hw_exp2(fmaf(zx[e], -LOG2E, kbx)));
-                a = hw_exp2(rr * kdec);
-                bb = hw_sqrt(fmaf(-a, a, 1.0f)) * ii * x;
+                const float rr = hw_rcp(1.0f + hw_exp2((za[st][r] + bav[r]) * -LOG2E));
+                const float ii = hw_rcp(1.0f + hw_exp2((zx[st][r] + bxv[r]) * -LOG2E));
+                a = hw_exp2(rr * (LOG2E * ncs[r]));
+                bb = hw_sqrt(fmaf(-a, a, 1.0f)) * ii * xs[r];
             } else {
-                const float rr = sigmoid_acc(za[e] + bat);
-                const float ii = sigmoid_acc(zx[e] + bxt);
-                const float l = ncs * rr;
+                const float rr = sigmoid_acc(za[st][r] + bav[r]);
+                const float ii = sigmoid_acc(zx[st][r] + bxv[r]);
+                const float l = ncs[r] * rr;
                 a = expf(l);
-                bb = sqrtf(-expm1f(2.0f * l)) * ii * x;
+                bb = sqrtf(-expm1f(2.0f * l)) * ii * xs[r];
             }
-            const float hn = fmaf(a, hv[e], bb);
-            if (s < B) {
-                hstate[(long)s * D + d] = hn;
-                y_t[(long)s * D + d] = from_f32<T>(hn);
+            hn[r] = fmaf(a, hs[st][r], bb);
+            yq[r] = from_f32<T>(hn[r]);
+        }
+        if (so[st] < B) {
+            nt_store16(p.h + srow[st] + dl, hn);
+            if constexpr (sizeof(T) == 2) {
+                typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+                nt_store8(p.y + srow[st] + dl, bf16x4{yq[0], yq[1], yq[2], yq[3]});
+            } else {
+                nt_store16(p.y + srow[st] + dl, f32x4{yq[0], yq[1], yq[2], yq[3]});
             }
         }
     }
 }
 
-template <typename T>
-void launch_step_t(const rglru_desc &d, const rglru_weights &w, const void *u_t, void *hist,
-                   float *h, void *y_t, hipStream_t s)
+// the kernels' LDS exceeds the default limit: raise it once per device
+template <typename T> void step_lds_attribute()
 {
-    const dim3 grid((unsigned)(((d.B + SB - 1) / SB) * d.H));
-    hipLaunchKernelGGL((step_kernel<T>), grid, dim3(512), 0, s, (int)d.B, (int)d.D, d.c,
-                       (const T *)u_t, w.conv_w, w.conv_b, (const T *)w.W_a, w.b_a,
-                       (const T *)w.W_x, w.b_x, w.Lambda, (T *)hist, h, (T *)y_t);
+    static std::mutex mu;
+    static bool done[64];
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (dev < 0 || dev >= 64) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!done[dev]) {
+        // a failure here surfaces through the launch and hipGetLastError
+        (void)hipFuncSetAttribute((const void *)&step_kernel<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)sizeof(StepLds<T>));
+        done[dev] = true;
+    }
+}
+
+template <typename T>
+void launch_step_t(const rglru_desc &d, const rglru_weights &w, const void *u_t, const void *hist_in,
+                   void *hist_out, float *h, void *y_t, hipStream_t s)
+{
+    StepParams<T> p;
+    p.B = (int)d.B;
+    p.D = (int)d.D;
+    p.c = d.c;
+    p.u_t = (const T *)u_t;
+    p.hist_in = (const T *)hist_in;
+    p.hist_out = (T *)hist_out;
+    p.cw = w.conv_w;
+    p.cb = w.conv_b;
+    p.Wa = (const T *)w.W_a;
+    p.Wx = (const T *)w.W_x;
+    p.ba = w.b_a;
+    p.bx = w.b_x;
+    p.Lambda = w.Lambda;
+    p.h = h;
+    p.y = (T *)y_t;
+    step_lds_attribute<T>();
+    const dim3 grid((unsigned)(((d.B + SS - 1) / SS) * d.H * NSLICE));
+    step_kernel<T><<<grid, dim3(NT), sizeof(StepLds<T>), s>>>(p);
 }
 
 }  // namespace
 
-void launch_step(const rglru_desc &d, const rglru_weights &w, const void *u_t, void *hist,
-                 float *h, void *y_t, hipStream_t s)
+void launch_step(const rglru_desc &d, const rglru_weights &w, const void *u_t, const void *hist_in,
+                 void *hist_out, float *h, void *y_t, hipStream_t s)
 {
-    if (d.io == RGLRU_BF16) launch_step_t<bf16>(d, w, u_t, hist, h, y_t, s);
-    else launch_step_t<float>(d, w, u_t, hist, h, y_t, s);
+    if (d.io == RGLRU_BF16) launch_step_t<bf16>(d, w, u_t, hist_in, hist_out, h, y_t, s);
+    else launch_step_t<float>(d, w, u_t, hist_in, hist_out, h, y_t, s);
 }
 
 }  // namespace rglru

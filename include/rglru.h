@@ -60,8 +60,8 @@
  *   returned RGLRU_OK by then (it only enqueues), so rglru_workspace_status
  *   reports it afterwards.  The backward's own kernels never wait on one
  *   another's workgroups.
- * Aliasing.  Outputs must not overlap inputs, except hist and h of
- *   rglru_step, which are read and rewritten in place by design.
+ * Aliasing.  Outputs must not overlap inputs, except h of rglru_step,
+ *   which is read and rewritten in place by design.
  * Determinism.  Every call is bitwise repeatable: identical inputs on the
  *   same device give identical outputs, whatever the timing of the
  *   workgroups.  The chunked scans carry state between 32-token chunks
@@ -211,14 +211,20 @@ int rglru_scan_fwd_noalloc(const rglru_desc *desc, const rglru_weights *w, const
 
 /* a6 -- one decode step for B independent streams (the listing's RGLRU.step,
  * with the conv history carried in front): desc->T must be 1.
- *     x = conv_b + conv_w[0] hist[0] + conv_w[1] hist[1] + conv_w[2] hist[2]
- *                + conv_w[3] u_t
- *     h <- a h + sqrt(1 - a^2) i x,   y_t = h,   hist <- (hist[1], hist[2], u_t)
- * hist [B][3][D] (io) and h [B][D] (fp32) are updated in place.  Reads every
- * field of w (conv_b, b_a, b_x nullable).  K = 256.  512 consecutive calls
- * equal one rglru_scan_fwd (mode A) over the same 512 tokens. */
+ *     x = conv_b + conv_w[0] hist_in[0] + conv_w[1] hist_in[1]
+ *                + conv_w[2] hist_in[2] + conv_w[3] u_t
+ *     h <- a h + sqrt(1 - a^2) i x,   y_t = h,
+ *     hist_out <- (hist_in[1], hist_in[2], u_t)
+ * hist_in / hist_out [B][3][D] (io; hist_in NULL means zeros, hist_out NULL
+ * drops the new history) are separate buffers that must not overlap -- the
+ * caller alternates two of them between steps, as with rglru_scan_fwd's --
+ * and h [B][D] (fp32) is read and rewritten in place.  Reads every field of
+ * w (conv_b, b_a, b_x nullable).  K = 256.  512 consecutive calls equal one
+ * rglru_scan_fwd (mode A) over the same 512 tokens, the history copies bit
+ * for bit.  Extra error: RGLRU_ERR_ARG if hist_out overlaps hist_in or any
+ * other argument. */
 int rglru_step(const rglru_desc *desc, const rglru_weights *w, const void *u_t,
-               void *hist, float *h, void *y_t, hipStream_t stream);
+               const void *hist_in, void *hist_out, float *h, void *y_t, hipStream_t stream);
 
 /* a7 -- backward of mode A: gradients of L = <dy, y> + <dh_last, h_last>
  * with respect to u, conv_w, conv_b, W_a, b_a, W_x, b_x, Lambda and h0 (the

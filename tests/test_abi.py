@@ -161,13 +161,16 @@ def test_step_validation(L):
     d = desc(T=2)
     w = weights()
     s = None
-    args = (P + 0x1000000, P + 0x2000000, P + 0x3000000, P + 0x4000000, s)
-    assert L.rglru_step(ctypes.byref(d), ctypes.byref(w), *args) == ESHAPE
+    u, hi, ho, h, y = P + 0x1000000, P + 0x2000000, P + 0x3000000, P + 0x4000000, P + 0x5000000
+    assert L.rglru_step(ctypes.byref(d), ctypes.byref(w), u, hi, ho, h, y, s) == ESHAPE
     d = desc(T=1)
-    assert L.rglru_step(ctypes.byref(d), ctypes.byref(weights(conv=False)), *args) == ENULL
-    # h aliasing the history
-    assert L.rglru_step(ctypes.byref(d), ctypes.byref(w), P + 0x1000000, P + 0x2000000, P + 0x2000000,
-                        P + 0x4000000, s) == EARG
+    assert L.rglru_step(ctypes.byref(d), ctypes.byref(weights(conv=False)), u, hi, ho, h, y, s) == ENULL
+    assert L.rglru_step(ctypes.byref(d), ctypes.byref(w), u, hi, ho, None, y, s) == ENULL
+    assert L.rglru_step(ctypes.byref(d), ctypes.byref(w), u, hi + 8, ho, h, y, s) == EALIGN
+    # the new history written over the old one, h over the history, y over h
+    assert L.rglru_step(ctypes.byref(d), ctypes.byref(w), u, hi, hi, h, y, s) == EARG
+    assert L.rglru_step(ctypes.byref(d), ctypes.byref(w), u, hi, ho, ho, y, s) == EARG
+    assert L.rglru_step(ctypes.byref(d), ctypes.byref(w), u, hi, ho, h, h, s) == EARG
 
 
 def test_scan_bwd_validation(L):

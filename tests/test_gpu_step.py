@@ -39,13 +39,16 @@ def _decode_run(steps, B=None, sample_streams=(0, 1, 77, 255), sample_heads=(0, 
                     W_x=to_dev(params.W_x, DEV), Lambda=to_dev(params.Lambda, DEV),
                     conv_b=to_dev(params.conv_b, DEV), b_a=to_dev(params.b_a, DEV),
                     b_x=to_dev(params.b_x, DEV))
-    hist = torch.zeros((B, 3, D), dtype=torch.bfloat16, device=DEV)
+    # two history buffers, alternated; the first step reads no history (zeros)
+    hists = [torch.full((B, 3, D), 7.0, dtype=torch.bfloat16, device=DEV) for _ in range(2)]
     h = torch.zeros((B, D), dtype=torch.float32, device=DEV)
     us, ys = [], []
     for s in range(steps):
         u_s = synth.make_activation(cfg.idx, "u", (cfg.B, D), cfg.io, start=s * cfg.B * D)[:B]
         us.append(u_s)
-        ys.append(glr.step(to_dev(u_s, DEV), w, hist, h).clone())
+        y, _ = glr.step(to_dev(u_s, DEV), w, h, None if s == 0 else hists[s % 2], hists[(s + 1) % 2])
+        ys.append(y)
+    hist = hists[steps % 2]
     torch.cuda.synchronize()
     u_seq = np.stack(us, axis=1)                      # [B][steps][D] stored bf16
     y_seq = torch.stack(ys, dim=1)                    # [B][steps][D]
@@ -78,9 +81,11 @@ def test_decode_full_512_steps():
     _decode_run(512)
 
 
-def test_decode_ragged_stream_count():
-    _say("decode: B=45 (not a multiple of 32), 6 steps")
-    _decode_run(6, B=45, sample_streams=(0, 31, 32, 44))
+@pytest.mark.parametrize("B", [45, 130])
+def test_decode_ragged_stream_count(B):
+    # a partial tile of 64 streams (45), and two full tiles plus a partial one (130)
+    _say(f"decode: B={B} (not a multiple of 64), 6 steps")
+    _decode_run(6, B=B, sample_streams=(0, 31, 44, 63, 64, 127, 128, 129))
 
 
 def test_steps_equal_prefill_on_gpu():
@@ -103,10 +108,14 @@ def test_decode_fp32_tiny_width():
     hist0 = synth.make_activation(cfg.idx, "hist", (B, 3, D), "f32")
     h00 = synth.store(synth.normal(synth.seed_for(cfg.idx, "h0"), 0, B * D), "f32").reshape(B, D)
     u_seq = synth.make_activation(cfg.idx, "u", (B, steps, D), "f32")
-    hist = to_dev(hist0, DEV)
+    hists = [to_dev(hist0, DEV), torch.empty((B, 3, D), dtype=torch.float32, device=DEV)]
     h = to_dev(h00, DEV)
     _say(f"decode fp32: B={B} D={D}, {steps} steps with history and state")
-    ys = [glr.step(to_dev(np.ascontiguousarray(u_seq[:, s]), DEV), w, hist, h).clone() for s in range(steps)]
+    ys = []
+    for s in range(steps):
+        y, _ = glr.step(to_dev(np.ascontiguousarray(u_seq[:, s]), DEV), w, h, hists[s % 2], hists[(s + 1) % 2])
+        ys.append(y)
+    hist = hists[steps % 2]
     torch.cuda.synchronize()
     op = dict(conv_w=synth.widen(params.conv_w), conv_b=synth.widen(params.conv_b),
               W_a=synth.widen(params.W_a), b_a=synth.widen(params.b_a),
@@ -116,3 +125,44 @@ def test_decode_fp32_tiny_width():
     _cmp("y", from_dev(torch.stack(ys, dim=1)), ry, TOL["f32"])
     _cmp("h", from_dev(h), rh, TOL["f32"])
     assert np.array_equal(hist.cpu().numpy(), u_seq[:, -3:, :])
+
+
+def test_decode_graph_replays_equal_eager():
+    # 16 steps captured in a HIP graph: each replay, with eager work and a
+    # synchronisation between replays, gives what the eager steps gave
+    cfg = synth.DECODE_256
+    B, D, H, steps = 64, cfg.D, cfg.H, 16
+    params = synth.make_params(cfg.idx, D, H, cfg.io)
+    w = glr.Weights(conv_w=to_dev(params.conv_w, DEV), W_a=to_dev(params.W_a, DEV),
+                    W_x=to_dev(params.W_x, DEV), Lambda=to_dev(params.Lambda, DEV),
+                    conv_b=to_dev(params.conv_b, DEV), b_a=to_dev(params.b_a, DEV),
+                    b_x=to_dev(params.b_x, DEV))
+    u = to_dev(synth.make_activation(cfg.idx, "u", (steps, B, D), cfg.io), DEV)
+    y = torch.empty_like(u)
+    h = torch.zeros((B, D), dtype=torch.float32, device=DEV)
+    hists = [torch.zeros((B, 3, D), dtype=torch.bfloat16, device=DEV) for _ in range(2)]
+
+    def run():
+        for k in range(steps):
+            glr.step(u[k], w, h, hists[k % 2], hists[(k + 1) % 2], y[k])
+
+    run()
+    torch.cuda.synchronize()
+    y_ref, h_ref, hist_ref = y.clone(), h.clone(), hists[steps % 2].clone()
+    gs = torch.cuda.Stream()
+    gs.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(gs):
+        with torch.cuda.graph(graph, stream=gs):
+            run()
+    torch.cuda.current_stream().wait_stream(gs)
+    for rep in range(3):
+        h.zero_()
+        for hb in hists:
+            hb.zero_()
+        y.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref) and torch.equal(h, h_ref), f"replay {rep} differs"
+        assert torch.equal(hists[steps % 2], hist_ref), f"replay {rep}: history differs"
