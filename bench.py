@@ -527,7 +527,7 @@ def main():
         # block's intermediates)
         nb = 2 * M * dm * 2 + 3 * D * dm * 2 + 2 * H * 65536 * 2 + D * 8 * 4 + B * D * 4 + B * 3 * D * 2
         r = row(f"rglru_block_fwd, 2B width (B={B} T={T} D=d_model={D} bf16): 3 projections "
-                "(rocBLAS) + fused forward with the GeLU merge", kk, tokch, nb,
+                "(hand-written MFMA GEMM) + fused forward with the GeLU merge", kk, tokch, nb,
                 flops=gemm_flops + 2 * 2 * 256 * tokch, bound="mfma",
                 note="algorithmic flops: the three projections (3 x 2 M d_model D) and the gate "
                      "products; tokens_ch counts B*T*D")

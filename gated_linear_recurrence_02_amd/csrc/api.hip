@@ -38,8 +38,8 @@ int check_desc(const rglru_desc *d, bool need_k256)
     return RGLRU_OK;
 }
 
-// the recurrent block: the scan's checks plus the GEMM sizes (rocBLAS takes
-// 64-bit sizes; each dimension is kept below 2^31 all the same)
+// the recurrent block: the scan's checks plus the GEMM sizes (each GEMM
+// dimension below 2^31)
 int check_block(const rglru_desc *d, int64_t d_model)
 {
     int st = check_desc(d, true);
@@ -211,7 +211,7 @@ const char *rglru_status_string(int status)
     case RGLRU_ERR_WORKSPACE: return "workspace missing or too small";
     case RGLRU_ERR_LAUNCH: return "HIP launch error";
     case RGLRU_ERR_ARG: return "inconsistent arguments";
-    case RGLRU_ERR_BLAS: return "a rocBLAS call failed";
+    case RGLRU_ERR_BLAS: return "reserved status (not returned)";
     case RGLRU_ERR_SCRATCH: return "problem needs more than the fixed scratch of rglru_scan_fwd_noalloc";
     case RGLRU_ERR_TIMEOUT: return "a chunk-carry wait of an earlier call on this workspace gave up (its outputs hold NaN)";
     default: return "unknown status";

@@ -7,28 +7,19 @@
 // and a bias-free output projection back to d_model.  The residual add belongs
 // to the decoder layer, outside the block.
 //
-//   b1 = x proj_in_1^T        [B*T][D]    rocBLAS GEMM
-//   b2 = x proj_in_2^T        [B*T][D]    rocBLAS GEMM
+//   b1 = x proj_in_1^T        [B*T][D]    GEMM (gemm.hip)
+//   b2 = x proj_in_2^T        [B*T][D]    GEMM
 //   z  = RG-LRU(conv(b1)) * GeLU(b2)      the fused forward, mode 4 (the merge
 //                                         happens where y would be stored; z
 //                                         overwrites b2 in place: every element
 //                                         of b2 is read by the lane that writes
 //                                         z there, before it writes)
-//   out = z proj_out^T        [B*T][d_model]  rocBLAS GEMM
+//   out = z proj_out^T        [B*T][d_model]  GEMM
 //
-// The projections are plain dense GEMMs, so they go to the library (bf16
+// The projections are dense GEMMs on the matrix cores (gemm.hip: bf16
 // inputs, fp32 accumulation, bf16 output for bf16 I/O; fp32 throughout for
 // fp32 I/O).  Workspace: the scan's carries first (its header must start out
 // zero), then b1 and b2.
-// the solution listing (rocblas_gemm_ex_get_solutions) is in rocBLAS's beta API
-#define ROCBLAS_BETA_FEATURES_API
-#define ROCBLAS_NO_DEPRECATED_WARNINGS
-#include <rocblas/rocblas.h>
-
-#include <map>
-#include <mutex>
-#include <tuple>
-#include <vector>
 
 #include "common.h"
 #include "internal.h"
@@ -36,112 +27,6 @@
 namespace rglru {
 
 namespace {
-
-// One rocBLAS handle per device, made on first use with that device current.
-// Calls that share a device share its handle; the stream is set and the GEMM
-// enqueued under the lock, so concurrent callers never see each other's stream.
-std::mutex blas_mu;
-rocblas_handle blas_handles[64];
-
-rocblas_handle blas_handle_locked(int dev)
-{
-    if (dev < 0 || dev >= 64) return nullptr;
-    if (!blas_handles[dev] && rocblas_create_handle(&blas_handles[dev]) != rocblas_status_success)
-        blas_handles[dev] = nullptr;
-    return blas_handles[dev];
-}
-
-// Y[M][N] = X[M][K] W[N][K]^T (+ R[M][N] when R is given, through beta = 1),
-// all row-major.  Column-major, that is Y^T (N x M, ld N) = W^T (op T of the
-// K x N array W, ld K) * X^T (K x M, ld K) (+ R^T).
-//
-// Solution choice: the first product of a shape on a device runs every
-// solution the library lists for it (one warm-up and three timed runs each,
-// on the caller's stream, waiting for them on the host) and keeps the fastest
-// for that shape; the library's default is one of the candidates.
-struct GemmKey {
-    int dev, io, add;
-    int64_t M, N, K;
-    bool operator<(const GemmKey &o) const
-    {
-        return std::tie(dev, io, add, M, N, K) < std::tie(o.dev, o.io, o.add, o.M, o.N, o.K);
-    }
-};
-std::map<GemmKey, int> best_solution;   // guarded by blas_mu
-
-rocblas_status gemm_call(rocblas_handle h, int io, int64_t M, int64_t N, int64_t K, const void *X, const void *W,
-                         const void *R, void *Y, int sol)
-{
-    const rocblas_datatype t = io == RGLRU_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
-    const float alpha = 1.0f, beta = R ? 1.0f : 0.0f;
-    const void *C = R ? R : Y;
-    return rocblas_gemm_ex(h, rocblas_operation_transpose, rocblas_operation_none, (rocblas_int)N,
-                           (rocblas_int)M, (rocblas_int)K, &alpha, W, t, (rocblas_int)K, X, t, (rocblas_int)K, &beta,
-                           C, t, (rocblas_int)N, Y, t, (rocblas_int)N, rocblas_datatype_f32_r,
-                           sol ? rocblas_gemm_algo_solution_index : rocblas_gemm_algo_standard, sol, 0);
-}
-
-int pick_solution(rocblas_handle h, hipStream_t s, int dev, int io, int64_t M, int64_t N, int64_t K,
-                  const void *X, const void *W, const void *R, void *Y)
-{
-    const GemmKey key{dev, io, R ? 1 : 0, M, N, K};
-    auto it = best_solution.find(key);
-    if (it != best_solution.end()) return it->second;
-    const rocblas_datatype t = io == RGLRU_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
-    const float alpha = 1.0f, beta = R ? 1.0f : 0.0f;
-    const void *C = R ? R : Y;
-    rocblas_int n = 0;
-    std::vector<rocblas_int> cand;
-    if (rocblas_gemm_ex_get_solutions(h, rocblas_operation_transpose, rocblas_operation_none, (rocblas_int)N,
-                                      (rocblas_int)M, (rocblas_int)K, &alpha, W, t, (rocblas_int)K, X, t,
-                                      (rocblas_int)K, &beta, C, t, (rocblas_int)N, Y, t, (rocblas_int)N,
-                                      rocblas_datatype_f32_r, rocblas_gemm_algo_solution_index, 0, nullptr,
-                                      &n) == rocblas_status_success &&
-        n > 0) {
-        cand.resize(n);
-        if (rocblas_gemm_ex_get_solutions(h, rocblas_operation_transpose, rocblas_operation_none, (rocblas_int)N,
-                                          (rocblas_int)M, (rocblas_int)K, &alpha, W, t, (rocblas_int)K, X, t,
-                                          (rocblas_int)K, &beta, C, t, (rocblas_int)N, Y, t, (rocblas_int)N,
-                                          rocblas_datatype_f32_r, rocblas_gemm_algo_solution_index, 0,
-                                          cand.data(), &n) != rocblas_status_success)
-            cand.clear();
-        else
-            cand.resize(n);
-    }
-    int best = 0;
-    float best_ms = -1.0f;
-    hipEvent_t e0 = nullptr, e1 = nullptr;
-    if (hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
-        cand.insert(cand.begin(), 0);   // the library's default choice
-        for (const rocblas_int sol : cand) {
-            if (gemm_call(h, io, M, N, K, X, W, R, Y, sol) != rocblas_status_success) continue;
-            (void)hipEventRecord(e0, s);
-            bool ok = true;
-            for (int r = 0; r < 3 && ok; ++r) ok = gemm_call(h, io, M, N, K, X, W, R, Y, sol) == rocblas_status_success;
-            (void)hipEventRecord(e1, s);
-            float ms = 0.0f;
-            if (!ok || hipEventSynchronize(e1) != hipSuccess || hipEventElapsedTime(&ms, e0, e1) != hipSuccess)
-                continue;
-            if (best_ms < 0.0f || ms < best_ms) {
-                best_ms = ms;
-                best = sol;
-            }
-        }
-    }
-    if (e0) (void)hipEventDestroy(e0);
-    if (e1) (void)hipEventDestroy(e1);
-    (void)hipGetLastError();   // a candidate the runtime refused leaves no error behind
-    best_solution[key] = best;
-    return best;
-}
-
-// the product with the shape's chosen solution (blas_mu held, stream set)
-bool gemm_run(rocblas_handle h, hipStream_t s, int dev, int io, int64_t M, int64_t N, int64_t K, const void *X,
-              const void *W, const void *R, void *Y)
-{
-    const int sol = pick_solution(h, s, dev, io, M, N, K, X, W, R, Y);
-    return gemm_call(h, io, M, N, K, X, W, R, Y, sol) == rocblas_status_success;
-}
 
 size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -278,22 +163,16 @@ int block_core(const rglru_desc &d, int64_t d_model, const rglru_weights &w, con
     char *base = (char *)ws;
     void *b1 = base + L.b1, *b2 = base + L.b2;
     const int64_t M = d.B * d.T;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return RGLRU_ERR_LAUNCH;
     {
-        std::lock_guard<std::mutex> lock(blas_mu);
-        rocblas_handle h = blas_handle_locked(dev);
-        if (!h || rocblas_set_stream(h, s) != rocblas_status_success) return RGLRU_ERR_BLAS;
-        if (!gemm_run(h, s, dev, d.io, M, d.D, d_model, x, blk.proj_in_1, nullptr, b1)) return RGLRU_ERR_BLAS;
-        if (!gemm_run(h, s, dev, d.io, M, d.D, d_model, x, blk.proj_in_2, nullptr, b2)) return RGLRU_ERR_BLAS;
+        int st;
+        if ((st = launch_gemm(d.io, M, d.D, d_model, x, blk.proj_in_1, nullptr, b1, s)) != RGLRU_OK) return st;
+        if ((st = launch_gemm(d.io, M, d.D, d_model, x, blk.proj_in_2, nullptr, b2, s)) != RGLRU_OK) return st;
     }
     launch_scan_fwd_merge(d, w, b1, b2, hist_in, h0, b2, h_last, hist_out, base + L.scan, s);
     if (hipGetLastError() != hipSuccess) return RGLRU_ERR_LAUNCH;
     {
-        std::lock_guard<std::mutex> lock(blas_mu);
-        rocblas_handle h = blas_handle_locked(dev);
-        if (!h || rocblas_set_stream(h, s) != rocblas_status_success) return RGLRU_ERR_BLAS;
-        if (!gemm_run(h, s, dev, d.io, M, d_model, d.D, b2, blk.proj_out, residual, out)) return RGLRU_ERR_BLAS;
+        int st;
+        if ((st = launch_gemm(d.io, M, d_model, d.D, b2, blk.proj_out, residual, out, s)) != RGLRU_OK) return st;
     }
     return RGLRU_OK;
 }
@@ -339,14 +218,10 @@ int mlp_tail(int io, long M, int64_t d_model, const rglru_layer &lw, const void 
     const size_t esz = io == RGLRU_BF16 ? 2 : 4;
     int st = rmsnorm_launch(io, M, d_model, xt, lw.cnorm_w, lw.eps, xn, s);
     if (st) return st;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return RGLRU_ERR_LAUNCH;
     {
-        std::lock_guard<std::mutex> lock(blas_mu);
-        rocblas_handle h = blas_handle_locked(dev);
-        if (!h || rocblas_set_stream(h, s) != rocblas_status_success) return RGLRU_ERR_BLAS;
-        if (!gemm_run(h, s, dev, io, M, lw.d_ff, d_model, xn, lw.gate_w, nullptr, g)) return RGLRU_ERR_BLAS;
-        if (!gemm_run(h, s, dev, io, M, lw.d_ff, d_model, xn, lw.up_w, nullptr, u)) return RGLRU_ERR_BLAS;
+        int st;
+        if ((st = launch_gemm(io, M, lw.d_ff, d_model, xn, lw.gate_w, nullptr, g, s)) != RGLRU_OK) return st;
+        if ((st = launch_gemm(io, M, lw.d_ff, d_model, xn, lw.up_w, nullptr, u, s)) != RGLRU_OK) return st;
     }
     const long nff = M * lw.d_ff;
     const long pieces = (nff + (long)(16 / esz) - 1) / (long)(16 / esz);
@@ -357,10 +232,8 @@ int mlp_tail(int io, long M, int64_t d_model, const rglru_layer &lw, const void 
         gelu_tanh_mul_kernel<float><<<ff_grid, 256, 0, s>>>(nff, (float *)g, (const float *)u);
     if (hipGetLastError() != hipSuccess) return RGLRU_ERR_LAUNCH;
     {
-        std::lock_guard<std::mutex> lock(blas_mu);
-        rocblas_handle h = blas_handle_locked(dev);
-        if (!h || rocblas_set_stream(h, s) != rocblas_status_success) return RGLRU_ERR_BLAS;
-        if (!gemm_run(h, s, dev, io, M, d_model, lw.d_ff, g, lw.down_w, xt, y)) return RGLRU_ERR_BLAS;
+        int st;
+        if ((st = launch_gemm(io, M, d_model, lw.d_ff, g, lw.down_w, xt, y, s)) != RGLRU_OK) return st;
     }
     return RGLRU_OK;
 }
@@ -420,15 +293,11 @@ int launch_attn_layer_fwd(const rglru_attn_desc &d, int64_t d_model, int rot, fl
     const int64_t HD = d.Hq * d.dh;
     int st = rmsnorm_launch(d.io, M, d_model, x, lw.tnorm_w, lw.eps, xn, s);
     if (st) return st;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return RGLRU_ERR_LAUNCH;
     {
-        std::lock_guard<std::mutex> lock(blas_mu);
-        rocblas_handle h = blas_handle_locked(dev);
-        if (!h || rocblas_set_stream(h, s) != rocblas_status_success) return RGLRU_ERR_BLAS;
-        if (!gemm_run(h, s, dev, d.io, M, HD, d_model, xn, ap.wq, nullptr, q)) return RGLRU_ERR_BLAS;
-        if (!gemm_run(h, s, dev, d.io, M, d.dh, d_model, xn, ap.wk, nullptr, k)) return RGLRU_ERR_BLAS;
-        if (!gemm_run(h, s, dev, d.io, M, d.dh, d_model, xn, ap.wv, nullptr, v)) return RGLRU_ERR_BLAS;
+        int st;
+        if ((st = launch_gemm(d.io, M, HD, d_model, xn, ap.wq, nullptr, q, s)) != RGLRU_OK) return st;
+        if ((st = launch_gemm(d.io, M, d.dh, d_model, xn, ap.wk, nullptr, k, s)) != RGLRU_OK) return st;
+        if ((st = launch_gemm(d.io, M, d.dh, d_model, xn, ap.wv, nullptr, v, s)) != RGLRU_OK) return st;
     }
     if (rot > 0) {
         const double l2b = log2((double)rope_base);
@@ -449,10 +318,8 @@ int launch_attn_layer_fwd(const rglru_attn_desc &d, int64_t d_model, int rot, fl
     launch_attn_fwd(d, q, k, v, o, kc, vc, s);
     if (hipGetLastError() != hipSuccess) return RGLRU_ERR_LAUNCH;
     {
-        std::lock_guard<std::mutex> lock(blas_mu);
-        rocblas_handle h = blas_handle_locked(dev);
-        if (!h || rocblas_set_stream(h, s) != rocblas_status_success) return RGLRU_ERR_BLAS;
-        if (!gemm_run(h, s, dev, d.io, M, d_model, HD, o, ap.wo, x, xt)) return RGLRU_ERR_BLAS;
+        int st;
+        if ((st = launch_gemm(d.io, M, d_model, HD, o, ap.wo, x, xt, s)) != RGLRU_OK) return st;
     }
     return mlp_tail(d.io, M, d_model, lw, xt, xn, g, u, y, s);
 }

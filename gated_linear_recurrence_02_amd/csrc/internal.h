@@ -52,6 +52,12 @@ void launch_scan_fwd_merge(const rglru_desc &d, const rglru_weights &w, const vo
                            const void *hist_in, const float *h0, void *z, float *h_last, void *hist_out,
                            void *ws, hipStream_t s);
 
+// Y[M][N] = X[M][K] W[N][K]^T (+ R when not null), row-major, fp32
+// accumulation, io types (gemm.hip); returns an rglru_status
+int launch_gemm(int io, int64_t M, int64_t N, int64_t K, const void *X, const void *W, const void *R, void *Y,
+                hipStream_t s);
+bool gemm_uses_mfma(int io, int64_t M, int64_t N, int64_t K);
+
 // Recurrent block: byte offsets inside its workspace (scan carries at 0,
 // then the two projections b1 and b2) and the whole size
 struct BlockLayout {
@@ -59,7 +65,7 @@ struct BlockLayout {
 };
 BlockLayout block_layout(int64_t B, int64_t T, int64_t D, size_t esz);
 
-// returns an rglru_status (the GEMMs report their own failures)
+// returns an rglru_status
 int launch_block_fwd(const rglru_desc &d, int64_t d_model, const rglru_weights &w, const rglru_block &blk,
                      const void *x, const void *hist_in, const float *h0, void *out, float *h_last,
                      void *hist_out, void *ws, hipStream_t s);

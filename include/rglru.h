@@ -22,13 +22,9 @@
  * Pointers.  Every tensor pointer is DEVICE memory owned by the caller.  The
  *   library does not synchronise the host (rglru_workspace_status, a report
  *   the caller asks for, aside): a return of RGLRU_OK means the work was
- *   enqueued on `stream`.  It allocates nothing and keeps no global state,
- *   with one exception: rglru_block_fwd and rglru_layer_fwd create one rocBLAS
- *   handle per device on their first call there (rocBLAS allocates its own
- *   device memory) and keep it until the process ends; and the first product
- *   of each GEMM shape on a device times every solution rocBLAS lists for it
- *   (on the caller's stream, waiting on the host) and keeps the fastest, so
- *   that first call blocks until the timing runs are done.
+ *   enqueued on `stream`.  It allocates nothing (rglru_scan_fwd_noalloc's
+ *   fixed scratch, loaded with the library, aside) and keeps no state
+ *   between calls beyond what the caller's buffers hold.
  * Layouts.  Row-major, channel fastest:
  *     activations u, x, r, i, y, dy, du   [B][T][D]   (dtype desc->io)
  *     conv history hist                   [B][3][D]   (dtype desc->io)
@@ -94,7 +90,7 @@ typedef enum {
     RGLRU_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than required       */
     RGLRU_ERR_LAUNCH = -6,     /* the HIP runtime reported a launch error       */
     RGLRU_ERR_ARG = -7,        /* inconsistent arguments (mode, aliasing)       */
-    RGLRU_ERR_BLAS = -8,       /* a rocBLAS call of rglru_block_fwd failed      */
+    RGLRU_ERR_BLAS = -8,       /* reserved (no call returns it)                 */
     RGLRU_ERR_TIMEOUT = -9,    /* rglru_workspace_status: a chunk-carry wait of
                                   an earlier call gave up (outputs hold NaN)    */
     RGLRU_ERR_SCRATCH = -10    /* rglru_scan_fwd_noalloc: the call needs more
@@ -266,11 +262,12 @@ int rglru_block_workspace_size(const rglru_desc *desc, int64_t d_model, size_t *
  * block has no biases and no residual add (that is the decoder layer's).
  * x and out are [B][T][d_model] in desc->io; h0, h_last, hist_in, hist_out
  * (nullable) are the state and conv history of branch 1, as in
- * rglru_scan_fwd.  The three projections are rocBLAS GEMMs with fp32
- * accumulation; b1 and b2 are rounded to io, and so is the merged product
- * that feeds proj_out.  Reads every field of w (conv_b, b_a, b_x nullable).
- * K = 256; 1 <= d_model <= 2^30 and B*T, D, d_model each below 2^31 for the
- * GEMMs.  Extra error: RGLRU_ERR_BLAS when a rocBLAS call fails (work enqueued
+ * rglru_scan_fwd.  The three projections are the library's own GEMMs (bf16:
+ * on the matrix cores when the inner dimension is a multiple of 64) with
+ * fp32 accumulation; b1 and b2 are rounded to io, and so is the merged
+ * product that feeds proj_out.  Reads every field of w (conv_b, b_a, b_x
+ * nullable).  K = 256; 1 <= d_model <= 2^30 and B*T, D, d_model each below
+ * 2^31 for the GEMMs.  A launch error is RGLRU_ERR_LAUNCH (work enqueued
  * before it stays enqueued). */
 int rglru_block_fwd(const rglru_desc *desc, int64_t d_model, const rglru_weights *w,
                     const rglru_block *blk, const void *x, const void *hist_in, const float *h0,
@@ -304,10 +301,10 @@ int rglru_layer_workspace_size(const rglru_desc *desc, int64_t d_model, const rg
 /* Residual-layer forward.  x, y [B][T][d_model] (io); h0, h_last, hist_in,
  * hist_out (nullable) are the recurrent block's state and conv history.
  * Stored intermediates (the normed inputs, b1, b2, the merged product, x~,
- * the MLP activations) are rounded to io; every sum is fp32.  Five rocBLAS
- * GEMMs (the residual adds ride the beta of proj_out and down), two RMSNorm
- * launches, the fused forward with the GeLU merge and one GELU-tanh product
- * launch.  Same shape limits and errors as rglru_block_fwd, plus d_ff. */
+ * the MLP activations) are rounded to io; every sum is fp32.  Five GEMMs
+ * (the residual adds happen in the epilogues of proj_out and down), two
+ * RMSNorm launches, the fused forward with the GeLU merge and one GELU-tanh
+ * product launch.  Same shape limits and errors as rglru_block_fwd, plus d_ff. */
 int rglru_layer_fwd(const rglru_desc *desc, int64_t d_model, const rglru_weights *w, const rglru_block *blk,
                     const rglru_layer *lw, const void *x, const void *hist_in, const float *h0, void *y,
                     float *h_last, void *hist_out, void *ws, size_t ws_bytes, hipStream_t stream);
