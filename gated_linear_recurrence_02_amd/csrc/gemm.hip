@@ -128,6 +128,16 @@ __global__ __launch_bounds__(GT) void gemm_nt_mfma(GemmArgs a)
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j], acc[i][j], 0,
                                                                         0, 0);
+            // the next step's 6 operand reads between this step's 8 products
+            if (ks + 1 < 4) {
+#pragma unroll
+                for (int t = 0; t < 6; ++t) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
