@@ -3,8 +3,8 @@ librglru_micro.so (micro/micro.hip) for gfx950 with hipcc.
 
 Every source is compiled with packed-FP32 instructions disabled
 (-Xclang -target-feature -Xclang -packed-fp32-ops; the host pass warns that
-it does not know the feature, which is harmless) and without the atomic
-optimizer (see FLAGS).
+it does not know the feature, which is harmless); fused.hip also without the
+atomic optimizer (see FILE_FLAGS).
 """
 from __future__ import annotations
 
@@ -24,16 +24,18 @@ ARCH = "gfx950"
 
 FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-Wno-unused-command-line-argument",
-         # thread 0 alone claims work units: the atomic optimizer's wave-wide
-         # rewrite reads the result at once, which waits for every vector
-         # memory operation issued before it (prefetches included)
-         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
+         "-Wno-unused-command-line-argument"]
+# fused.hip only: there thread 0 alone claims work units while the wave's
+# prefetches are in flight, and the atomic optimizer's wave-wide rewrite
+# reads the result at once, which waits for every vector memory operation
+# issued before it.  The 8-wave forward measured 5% slower with the
+# optimizer off, so the other sources keep it.
+FILE_FLAGS = {"fused.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
