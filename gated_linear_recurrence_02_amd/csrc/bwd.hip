@@ -199,10 +199,18 @@ __global__ __launch_bounds__(256) void rev_agg_kernel(int B, int T_, int D, int 
 #pragma unroll
         for (int k = 0; k < 32; ++k) g_[k] = k < nt ? to_f32(dyp[(long)k * D]) : 0.0f;
     }
+    // a_t itself: bf16 I/O takes the hardware 2^x (within an ulp of the
+    // unit kernel's 1 + (e^l - 1), which it needs for 1 - a^2; the carries
+    // only multiply by a), fp32 I/O the same form as the unit kernel
+    const float kdec = LOG2E * ncs;
     float e = 0.0f, Rr = 1.0f;
 #pragma unroll
     for (int k = 31; k >= 0; --k) {
-        const float ak = k < nt ? 1.0f + expm1_neg(ncs * (float)rv[k]) : 1.0f;
+        float ak = 1.0f;
+        if (k < nt) {
+            if constexpr (sizeof(T) == 2) ak = hw_exp2(kdec * (float)rv[k]);
+            else ak = 1.0f + expm1_neg(ncs * (float)rv[k]);
+        }
         e = ak * (g_[k] + e);
         Rr *= ak;
     }
