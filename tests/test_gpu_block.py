@@ -107,6 +107,22 @@ def test_block_bf16_2b_width_short():
     _cmp("hist_out", ho, rhist, TOL["bf16"])
 
 
+@pytest.mark.parametrize("T,d_model", [(70, 200), (33, 320)])
+def test_block_bf16_ragged_projection_shapes(T, d_model):
+    # the projections' edge cases on the matrix-core GEMM and its fallback:
+    # d_model = 200 sends proj_in (inner size 200) to the generic kernel and
+    # gives proj_out a partial 256-column tile; d_model = 320 runs proj_in on
+    # the matrix cores (inner size 5 x 64) and proj_out over a full and a
+    # partial column tile; B T = 140 / 66 rows are one partial row tile
+    prob, bp, x = _block_setup(1, 2, T, d_model, with_state=True)
+    _say(f"block bf16: B=2 T={T} D={prob.D} d_model={d_model}, with state")
+    out, hl, ho = _run(prob, bp, x, True)
+    ro, rh, rhist = _oracle_block_stored(prob, bp, x, 0, 2, with_state=True)
+    _cmp("out", out, ro, TOL["bf16"])
+    _cmp("h_last", hl, rh, TOL["bf16"])
+    _cmp("hist_out", ho, rhist, TOL["bf16"])
+
+
 def test_block_prefill_split_equals_whole():
     # two calls that hand over (h_last, hist_out) equal one call over the whole
     # sequence, and both equal the oracle
