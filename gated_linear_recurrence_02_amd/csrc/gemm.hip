@@ -174,7 +174,9 @@ __global__ __launch_bounds__(256) void gemm_nt_generic(GemmArgs a)
     T *Y = (T *)a.Y;
     const int M = a.M, N = a.N, K = a.K;
     const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-    const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+    const int ntn = (N + 63) / 64;   // one-dimensional grid: M may exceed 65535 tiles
+    const long m0 = (long)(blockIdx.x / ntn) * 64;
+    const int n0 = (int)(blockIdx.x % ntn) * 64;
     float acc[4][4] = {};
     for (int k0 = 0; k0 < K; k0 += 16) {
 #pragma unroll
@@ -204,7 +206,8 @@ __global__ __launch_bounds__(256) void gemm_nt_generic(GemmArgs a)
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int row = m0 + 4 * ty + i, col = n0 + 4 * tx + j;
+            const long row = m0 + 4 * ty + i;
+            const int col = n0 + 4 * tx + j;
             if (row < M && col < N) {
                 const size_t o = (size_t)row * N + col;
                 float v = acc[i][j];
@@ -252,7 +255,7 @@ int launch_gemm(int io, int64_t M, int64_t N, int64_t K, const void *X, const vo
         const long tiles = ((M + TBM - 1) / TBM) * ((N + TBN - 1) / TBN);
         gemm_nt_mfma<<<dim3((unsigned)tiles), dim3(GT), 2 * TBUF * 2, s>>>(a);
     } else {
-        const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
+        const dim3 grid((unsigned)(((N + 63) / 64) * ((M + 63) / 64)));
         if (io == RGLRU_BF16) gemm_nt_generic<bf16><<<grid, dim3(256), 0, s>>>(a);
         else gemm_nt_generic<float><<<grid, dim3(256), 0, s>>>(a);
     }
