@@ -18,6 +18,7 @@ namespace {
 
 constexpr int64_t MAX_DIM = (int64_t)1 << 30;
 constexpr int64_t BWD_MAX_D = (int64_t)1 << 24;   // 32-bit row offsets in the backward
+constexpr int64_t BWD_MAX_B = 65535;               // streams: one grid row each in the carry scan
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -338,7 +339,7 @@ int rglru_scan_bwd(const rglru_desc *desc, const rglru_weights *w, const void *u
 {
     int st = check_desc(desc, true);
     if (st) return st;
-    if (desc->D > BWD_MAX_D) return RGLRU_ERR_SHAPE;
+    if (desc->D > BWD_MAX_D || desc->B > BWD_MAX_B) return RGLRU_ERR_SHAPE;
     if (!w || !w->conv_w || !w->W_a || !w->W_x || !w->Lambda || !u || !dy || !du || !dconv_w ||
         !dconv_b || !dW_a || !db_a || !dW_x || !db_x || !dLambda)
         return RGLRU_ERR_NULL;

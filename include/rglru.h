@@ -228,8 +228,9 @@ int rglru_step(const rglru_desc *desc, const rglru_weights *w, const void *u_t,
  * above).  dh_last, h0, hist_in and dh0 are nullable.  du is io; every other
  * gradient is fp32 and is WRITTEN, not accumulated.  The gradient of hist_in
  * is not produced.  Reads every field of w.  K = 256; D <= 2^24 (its
- * kernels address a chunk's rows with 32-bit offsets).  The workspace size
- * depends on desc->io. */
+ * kernels address a chunk's rows with 32-bit offsets) and B <= 65535 (the
+ * carry scan runs one grid row per stream); otherwise RGLRU_ERR_SHAPE.  The
+ * workspace size depends on desc->io. */
 int rglru_scan_bwd(const rglru_desc *desc, const rglru_weights *w, const void *u,
                    const void *hist_in, const float *h0, const void *dy,
                    const float *dh_last, void *du, float *dconv_w, float *dconv_b,

@@ -191,6 +191,8 @@ def test_scan_bwd_validation(L):
     bad = list(good)
     bad[5] = u                                               # du == u
     assert f(ctypes.byref(d), ctypes.byref(w), *bad, ws, n, s) == EARG
+    many = desc(B=65536, T=1)                                # one stream past the carry scan's grid
+    assert f(ctypes.byref(many), ctypes.byref(w), *good, ws, n, s) == ESHAPE
 
 
 def block_ws_size(d, d_model):
