@@ -83,6 +83,19 @@ __device__ __forceinline__ void lds_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Workgroup barrier for LDS written by ds_* instructions only.  In a kernel
+// that also fills LDS through global_load_lds, the compiler's local-memory
+// fences wait for every vector memory operation (such a fill completes with
+// vmcnt), and __syncthreads() does as well; both would stall on stores and
+// requests meant to stay in flight.  This form waits for the wave's LDS
+// operations and keeps the compiler from moving memory accesses across it;
+// LDS that a global_load_lds fills may be read after it only once every
+// wave has waited for that fill (s_waitcnt vmcnt) before the barrier.
+__device__ __forceinline__ void ds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8): every LDS operation done and at most N vector memory
 // operations outstanding
@@ -239,6 +252,22 @@ __device__ __forceinline__ void finish_persistent(WsHeader *hdr)
 __device__ __forceinline__ uint32_t claim_next(uint32_t *ctr)
 {
     return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The same claim with the counter's address passed through a vector
+// register.  LLVM's atomic optimizer rewrites atomics on a uniform address
+// into one wave-wide operation whose result is read at once, and that read
+// waits for every vector memory operation the wave issued before the atomic
+// (its stores included).  With the address in a VGPR the rewrite does not
+// apply and the result is waited for only where it is used.
+__device__ __forceinline__ uint32_t claim_next_late(uint32_t *ctr)
+{
+    uintptr_t a = (uintptr_t)ctr;
+    asm volatile("" : "+v"(a));
+    // a global (not flat) atomic: a flat one would also count against lgkmcnt
+    // and hold up the wave's LDS waits until it returns
+    typedef __attribute__((address_space(1))) uint32_t global_u32;
+    return __hip_atomic_fetch_add((global_u32 *)a, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // End of a launch whose work was claimed from `nclaims` counters: called by

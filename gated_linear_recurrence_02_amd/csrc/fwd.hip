@@ -209,13 +209,17 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
     const uint32_t units = (uint32_t)p.units;
     Pend pd = {0, 0, 0.f, 0.f, 0.f, 0.f};
     bool have_pend = false;
+    // wave-uniform: some half-1 lane of this wave has a channel, so the wave
+    // runs the back half's branch (and its wait for the tile requests)
+    const bool half1_live = g * 256 + wave * 32 < p.D;
+    bool tile_waited = false;
     // Unit u_m of this workgroup travels through claim slot m & 1: thread 0
-    // claims u_{n+2} during iteration n and stores it at the end of the
+    // claims u_{n+2} at the start of iteration n and stores it later in the
     // iteration; every thread reads u_{n+1} after the first barrier of
     // iteration n.  The parity of n also selects the stage buffer.
     __syncthreads();
     uint32_t j = s_unit[0];
-    uint32_t t0_next = s_unit[1];   // thread 0 only: the latest unit it claimed
+    uint32_t my_claim = 0xFFFFFFFFu;   // thread 0 only: the unit claimed this iteration
     int it = 0;
     ScanIn<T> sin;   // mode C: inputs of unit j
     if constexpr (MODE == 2) scan_in_load(sin, p, j, d, half);
@@ -231,14 +235,30 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
     for (;;) {
         const bool have = j < units;
         if (!have && !have_pend) break;
-        uint32_t my_claim = 0xFFFFFFFFu;
-        if (tid == 0 && t0_next < units) my_claim = claim_next(claim);
+        // thread 0 claims every iteration (a unit number past the last one
+        // means no unit); only thread 0 writes the register, so no other wave
+        // waits for the claim's return before reusing it
+        if (tid == 0) my_claim = claim_next_late(claim);
+        auto publish_claim = [&]() {   // u_{n+2}, read after the first barrier of the next iteration
+            // every thread takes the value (only thread 0's is used) through an
+            // empty asm, which keeps the wait for the claim's return here
+            uint32_t v = my_claim;
+            asm volatile("" : "+v"(v));
+            if (tid == 0) s_unit[it & 1] = v;
+        };
 
         float hl[16], P[16];
         Pend cur = {0, 0, 0.f, 0.f, 0.f, 0.f};
-        if constexpr (STAGE) __builtin_amdgcn_s_waitcnt(0);   // this wave's tile loads have landed
-        __syncthreads();   // ... and every wave's; the other stage buffer, the x tile and
-                           // the claim slot read last time are free again
+        if constexpr (STAGE) {
+            // this wave's tile requests have landed (waited for in the last
+            // back half where one ran), and every wave's; the other stage
+            // buffer, the x tile and the claim slot read last time are free
+            // again.  The last back half's stores stay in flight.
+            if (!tile_waited) __builtin_amdgcn_s_waitcnt(0);
+            ds_barrier();
+        } else {
+            __syncthreads();
+        }
         const uint32_t jn = s_unit[(it + 1) & 1];   // u_{n+1}
         ScanIn<T> sin_next;   // mode C: inputs of the next unit, requested now
         if constexpr (MODE == 2) scan_in_load(sin_next, p, jn, d, half);
@@ -318,7 +338,10 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
 #pragma unroll
                     for (int k = 0; k < 16; ++k) Xs[(16 * half + k) * S + ch] = from_f32<T>(x[k]);
                 }
-                __syncthreads();
+                // orders the x tile only; the next unit's tile requests (into
+                // the other stage buffer) and the last back half's stores stay
+                // in flight
+                ds_barrier();
                 if constexpr (WREG) {
                     const int r = lane & 31, kg = lane >> 5;
                     const bf16 *xrow = (const bf16 *)Xs + tile_row_token(r) * S + 8 * kg;
@@ -346,6 +369,12 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
                     zx[k] = ok ? to_f32(sin.i[k]) : 0.0f;
                 }
             }
+
+            // u_{n+2} into its claim slot (read after the next iteration's
+            // first barrier) now, while the wave has few memory operations in
+            // flight: waiting for the claim's return later would also wait for
+            // the stores issued after it
+            if constexpr (STAGE) publish_claim();
 
             // gates, decay, normalisation, local scan from zero; interior
             // chunks take a copy of the loop without the end-of-sequence test
@@ -445,6 +474,9 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
                 hchunk = c == 0 ? hbefore
                                 : look_back(p.aggA + base, p.aggX + base, p.incl + base, c - 1, p.D,
                                             hbefore, tag, p.hdr);
+                // the tile requests of this iteration's front were issued before
+                // the look-back's loads, so this wait costs little
+                if constexpr (STAGE) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
                 put_word(p.incl + widx, fmaf(pd.Ach, hchunk, pd.Xch), tag);
                 if (p.hstart_out) p.hstart_out[widx] = hchunk;
             }
@@ -527,12 +559,10 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
             }
             pd = cur;
         }
+        tile_waited = have_pend && half1_live;
         have_pend = have;
         if constexpr (MODE == 2) sin = sin_next;
-        if (tid == 0) {   // u_{n+2}, read after the first barrier of the next iteration
-            s_unit[it & 1] = my_claim;
-            t0_next = my_claim;
-        }
+        if (!STAGE || !have) publish_claim();
         j = jn;
         ++it;
     }
