@@ -29,7 +29,8 @@
 //          3. gates, decay, normalisation; local scan from h = 0 keeping the
 //             running state and running decay product per token;
 //          4. the halves combine across lanes l, l^32 into the unit's affine
-//             aggregate (A, X), which is published at once;
+//             aggregate (A, X), published right after the look-back of step
+//             5 for the previous unit (at once if there is none);
 //   back   5. one unit later: the unit's start state from the decoupled
 //             look-back over earlier chunks of the same (b, g), its end state
 //             published, and y_t = local state + running product * start
@@ -37,10 +38,14 @@
 // The running state and product of the unit waiting for its back half sit in
 // LDS, so the look-back of unit j overlaps the front of the next unit.
 //
-// Forward progress: a workgroup publishes a unit's aggregate before it waits
-// on anything, processes its units in claim order, and every wait is for a
-// unit of the same block with a smaller index, which was claimed earlier by a
-// running workgroup; by induction on the unit index every wait ends.
+// Forward progress: a workgroup processes its units in claim order, every
+// wait is a look-back for a unit's start state, and it waits only for units
+// of the same block with a smaller index, which were claimed earlier by
+// running workgroups.  Take the smallest unit whose look-back has not ended:
+// each unit it waits for has either published its end state already, or sits
+// in a workgroup that is not waiting (any wait there would be for a still
+// smaller unit), which goes on to publish that unit's aggregate and end state.
+// So the smallest waiting look-back always ends, and by induction every one.
 #include <stdlib.h>
 
 #include <mutex>
@@ -249,6 +254,11 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
 
         float hl[16], P[16];
         Pend cur = {0, 0, 0.f, 0.f, 0.f, 0.f};
+        auto publish_agg = [&](const Pend &u) {   // half-1 lanes with a channel
+            const long widx = ((long)u.b * p.NC + u.c) * p.D + d;
+            put_word(p.aggA + widx, u.Ach, tag);
+            put_word(p.aggX + widx, u.Xch, tag);
+        };
         if constexpr (STAGE) {
             // this wave's tile requests have landed (waited for in the last
             // back half where one ran), and every wave's; the other stage
@@ -449,16 +459,12 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
             if (full && dv) scan16(std::false_type{});
             else scan16(std::true_type{});
 
-            // chunk aggregate, published before anything waits
+            // chunk aggregate; published here only when no back half follows
             cur.A0 = __shfl_xor(P[15], 32);
             cur.X0 = __shfl_xor(hl[15], 32);
             cur.Ach = P[15] * cur.A0;
             cur.Xch = fmaf(P[15], cur.X0, hl[15]);
-            if (half == 1 && dv) {
-                const long widx = ((long)b * p.NC + c) * p.D + d;
-                put_word(p.aggA + widx, cur.Ach, tag);
-                put_word(p.aggX + widx, cur.Xch, tag);
-            }
+            if (!have_pend && half == 1 && dv) publish_agg(cur);
         }
 
         if (have_pend) {
@@ -477,6 +483,10 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
                 // the tile requests of this iteration's front were issued before
                 // the look-back's loads, so this wait costs little
                 if constexpr (STAGE) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+                // the current unit's aggregate goes out after the look-back's
+                // loads: issued before them, these stores would have had to
+                // complete before the loads could be waited for
+                if (have) publish_agg(cur);
                 put_word(p.incl + widx, fmaf(pd.Ach, hchunk, pd.Xch), tag);
                 if (p.hstart_out) p.hstart_out[widx] = hchunk;
             }
