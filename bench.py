@@ -356,7 +356,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              f"(this build runs and reports a single MI355X)", file=sys.stderr)
+              f"(the library runs on and reports a single MI355X; the sharding plan is "
+              f"described but not implemented)", file=sys.stderr)
         sys.exit(2)
     rows = [r for r in args.rows.split(",") if r]
     for r in rows:
