@@ -138,6 +138,22 @@ def test_mode_a_ragged_lengths_with_state(T):
     assert np.array_equal(ho.cpu().view(torch.int16).numpy().view(np.uint16), want)
 
 
+@pytest.mark.parametrize("B,T", [(48, 40), (130, 33)])
+def test_mode_a_many_short_streams_with_state(B, T):
+    # many streams, two chunks each (the second ragged): the claims run
+    # through every stream's first chunk (unstaged, history-fed) before any
+    # second chunk, whose look-back then finds its one predecessor
+    prob = make_problem(1, B=B, T=T, with_state=True)
+    _say(f"B={B} T={T}, D=2560 bf16, h0 and history given")
+    y, hl, ho = _run_fwd(prob, h0=prob.h0, hist=prob.hist)
+    for b, h in [(0, 0), (B // 2, 5), (B - 1, 9)]:
+        ry, rh, rho = _oracle_slice(prob, b, h, prob.h0, prob.hist)
+        _cmp(f"y[b={b},h={h}]", prob.slice_block(from_dev(y), b, h), ry, TOL["bf16"])
+        _cmp(f"h_last[b={b},h={h}]", prob.slice_block(from_dev(hl), b, h), rh, TOL["bf16"])
+    want = np.concatenate([prob.hist, prob.u], axis=1)[:, -3:, :]
+    assert np.array_equal(ho.cpu().view(torch.int16).numpy().view(np.uint16), want)
+
+
 def test_mode_a_bf16_extreme_decay_constants():
     # Lambda far out on both sides: softplus(-Lambda) underflowing to zero
     # (a_t = 1, the state carried unchanged), a normal but tiny decay
