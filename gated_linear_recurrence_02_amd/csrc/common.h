@@ -122,9 +122,11 @@ constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 
 // aggregates backward would group the products differently from run to run).
 //
 // The words of LB_BATCH predecessors are loaded together.  When the walk ends
-// inside the first round, the aggregates are already in registers; a longer
-// walk loads them again (they are published, so the second load returns the
-// same words).  The walk only waits on chunks that were handed out before the
+// inside the first round, the aggregates are already in registers; later
+// rounds take LB_WIDE chunks and load only the tag halves of their
+// aggregates, and a longer walk then loads the aggregates' values for the
+// fold, eight chunks per round trip (they are published, so these loads
+// return the published values).  The walk only waits on chunks that were handed out before the
 // caller's chunk, so it ends once their aggregates are published; a wait
 // that exceeds SPIN_LIMIT flags the header and returns NaN rather than
 // hanging.  Two chunks per round: the words of one round stay in registers
@@ -133,10 +135,24 @@ constexpr int waitcnt_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 
 // the time a chunk's back half runs, its predecessor has usually published
 // its inclusive state.
 constexpr int LB_BATCH = 2;
+constexpr int LB_WIDE = 3;   // chunks per later round (tag halves of the aggregates only)
 
 __device__ __forceinline__ uint64_t load_word(const uint64_t *p)
 {
     return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// the tag half of a word (the high 32 bits)
+__device__ __forceinline__ uint32_t load_tag(const uint64_t *p)
+{
+    return __hip_atomic_load((uint32_t *)const_cast<uint64_t *>(p) + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// the value half of a word already known to be published
+__device__ __forceinline__ float load_value(const uint64_t *p)
+{
+    return __uint_as_float(__hip_atomic_load((uint32_t *)const_cast<uint64_t *>(p), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT));
 }
 
 __device__ __forceinline__ bool tagged(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
@@ -154,40 +170,69 @@ __device__ __forceinline__ float look_back(const uint64_t *aggA, const uint64_t 
     long jf = -1;                // chunk whose inclusive state starts the fold
     float base = h_before_first;
     while (j >= 0) {
-        uint64_t wi[LB_BATCH], wa[LB_BATCH], wx[LB_BATCH];
-#pragma unroll
-        for (int q = 0; q < LB_BATCH; ++q) {
-            const int kk = max((int)j - q, 0);
-            const uint64_t o = (uint64_t)(uint32_t)kk * st;
-            wi[q] = load_word(incl + o);
-            wa[q] = load_word(aggA + o);
-            wx[q] = load_word(aggX + o);
-        }
         int passed = 0;          // chunks of this round walked over
         bool done = false;
+        if (j == k) {
+            // a round at the caller's predecessor: whole words, so that a
+            // walk ending here folds the aggregates in hand
+            uint64_t wi[LB_BATCH], wa[LB_BATCH], wx[LB_BATCH];
 #pragma unroll
-        for (int q = 0; q < LB_BATCH; ++q) {
-            if (done || passed != q) continue;   // an earlier slot ended the round
-            if (j - q < 0) {
-                done = true;                     // reached the start: fold onto h_before_first
-            } else if (tagged(wi[q], tag)) {
-                done = true;
-                jf = j - q;
-                base = word_val(wi[q]);
-            } else if (tagged(wa[q], tag) && tagged(wx[q], tag)) {
-                ++passed;
+            for (int q = 0; q < LB_BATCH; ++q) {
+                const int kk = max((int)j - q, 0);
+                const uint64_t o = (uint64_t)(uint32_t)kk * st;
+                wi[q] = load_word(incl + o);
+                wa[q] = load_word(aggA + o);
+                wx[q] = load_word(aggX + o);
             }
-        }
-        if (!done && j - passed < 0) done = true;   // passed chunk 0
-        if (done) {
-            if (j == k) {   // short walk: the aggregates to fold are in hand
+#pragma unroll
+            for (int q = 0; q < LB_BATCH; ++q) {
+                if (done || passed != q) continue;   // an earlier slot ended the round
+                if (j - q < 0) {
+                    done = true;                     // reached the start: fold onto h_before_first
+                } else if (tagged(wi[q], tag)) {
+                    done = true;
+                    jf = j - q;
+                    base = word_val(wi[q]);
+                } else if (tagged(wa[q], tag) && tagged(wx[q], tag)) {
+                    ++passed;
+                }
+            }
+            if (!done && j - passed < 0) done = true;   // passed chunk 0
+            if (done) {   // short walk: the aggregates to fold are in hand
                 float s = base;
 #pragma unroll
                 for (int q = LB_BATCH - 1; q >= 0; --q)   // chunks k - q, oldest first
                     if (q < passed) s = fmaf(word_val(wa[q]), s, word_val(wx[q]));
                 return s;
             }
-            break;
+        } else {
+            // later rounds: LB_WIDE chunks, of the aggregates only the tag
+            // halves (their values are loaded by the fold below)
+            uint64_t wi[LB_WIDE];
+            uint32_t ta[LB_WIDE], tx[LB_WIDE];
+#pragma unroll
+            for (int q = 0; q < LB_WIDE; ++q) {
+                const int kk = max((int)j - q, 0);
+                const uint64_t o = (uint64_t)(uint32_t)kk * st;
+                wi[q] = load_word(incl + o);
+                ta[q] = load_tag(aggA + o);
+                tx[q] = load_tag(aggX + o);
+            }
+#pragma unroll
+            for (int q = 0; q < LB_WIDE; ++q) {
+                if (done || passed != q) continue;
+                if (j - q < 0) {
+                    done = true;
+                } else if (tagged(wi[q], tag)) {
+                    done = true;
+                    jf = j - q;
+                    base = word_val(wi[q]);
+                } else if (ta[q] == tag && tx[q] == tag) {
+                    ++passed;
+                }
+            }
+            if (!done && j - passed < 0) done = true;
+            if (done) break;
         }
         j -= passed;
         if (passed == 0) {
@@ -202,19 +247,21 @@ __device__ __forceinline__ float look_back(const uint64_t *aggA, const uint64_t 
             }
         }
     }
-    // a walk longer than the first round: fold chunks jf+1 .. k, 4 at a time
+    // a walk longer than the first round: fold chunks jf+1 .. k, 8 at a time.
+    // Their words are published and never change again within the launch,
+    // so only the value halves (the low 32 bits) are loaded
     float s = base;
-    for (long m = jf + 1; m <= k; m += 4) {
-        uint64_t a4[4], x4[4];
+    for (long m = jf + 1; m <= k; m += 8) {
+        float a8[8], x8[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < 8; ++q) {
             const uint64_t o = (uint64_t)(uint32_t)min(m + q, k) * st;
-            a4[q] = load_word(aggA + o);
-            x4[q] = load_word(aggX + o);
+            a8[q] = load_value(aggA + o);
+            x8[q] = load_value(aggX + o);
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (m + q <= k) s = fmaf(word_val(a4[q]), s, word_val(x4[q]));
+        for (int q = 0; q < 8; ++q)
+            if (m + q <= k) s = fmaf(a8[q], s, x8[q]);
     }
     return s;
 }
