@@ -34,7 +34,9 @@
 //   back   5. one unit later: the unit's start state from the decoupled
 //             look-back over earlier chunks of the same (b, g), its end state
 //             published, and y_t = local state + running product * start
-//             state stored.
+//             state stored.  In bf16 mode A the words that look-back reads
+//             first were requested into LDS before the unit's gate products
+//             (lb_prefetch), so a short walk usually finds them there.
 // The running state and product of the unit waiting for its back half sit in
 // LDS, so the look-back of unit j overlaps the front of the next unit.
 //
@@ -75,7 +77,7 @@ __device__ __forceinline__ bool stageable(int c, int T) { return c > 0 && (c + 1
 
 // OPQ: the lane's part of the address is rebuilt at every call instead of
 // being kept live (as a 64-bit pointer) across the caller's loop -- fewer
-// spilled registers in mode 4, a little slower where registers suffice
+// spilled registers in modes A and 4, a little slower where registers suffice
 template <int NBLK = ST_BLOCKS, bool OPQ = false>
 __device__ __forceinline__ void stage_issue(const bf16 *in, long row0, int D, int g, char *dst,
                                             int wave, int lane)
@@ -99,6 +101,7 @@ __device__ __forceinline__ float stage_read(const char *buf, int r, int ch)
 
 struct FwdParams {
     int B, T, D, NC, G, units;
+    int lbp;   // mode A: prefetch the look-back words (walks expected to be short)
     float c;
     const void *in, *r, *i;
     const float *cw, *cb;
@@ -115,6 +118,88 @@ struct FwdParams {
     uint32_t *claim;
     uint64_t *aggA, *aggX, *incl;
 };
+
+// Look-back prefetch (bf16 mode A).  Before a unit's gate products the
+// wave asks the LDS-DMA path for the words the pending chunk's look-back reads
+// first, for the wave's 32 channels: the inclusive states of chunks c-1, c-2
+// and c-3 and both aggregate halves of c-1 and c-2.  They land in the wave's
+// 2 KB slot while the products and the elementwise work run, so that the back
+// half usually finds the start state there instead of paying a round trip to
+// memory; a word not yet published when it was copied sends the lane to
+// look_back.  Slot layout: array k (0 incl c-1, 1 aggA c-1, 2 aggX c-1,
+// 3 incl c-2, 4 aggA c-2, 5 aggX c-2, 6 incl c-3) at k * 256 bytes, channel n
+// of the wave at n * 8 within it.
+constexpr int LBP_BYTES = 2048;
+
+// Two DMA instructions of 16 bytes per lane (two channels' words): lanes
+// 16q .. 16q+15 fill array q of the instruction's half of the slot.  Chunks
+// before the first read chunk 0 (in bounds; never used).  The words are read
+// at agent coherence (sc1), as look_back reads them.
+__device__ __forceinline__ void lb_prefetch(const FwdParams &p, int b, int c, int g, int wave, int lane,
+                                            char *slot)
+{
+    // the lane's part is rebuilt at every call rather than kept live across
+    // the caller's loop, where registers are short
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int q = ln >> 4;
+    const long ch0 = (long)g * 256 + wave * 32 + 2 * (ln & 15);
+    const long row = (long)b * p.NC;
+    // the three arrays sit one after another in the workspace (aggA, aggX,
+    // incl; see run_fwd), so a lane picks its array by an offset from one
+    // scalar base rather than by selecting a pointer per lane
+    const long nw = (long)p.B * p.NC * p.D;
+    const int k1 = q == 0 ? 2 : q == 1 ? 0 : q == 2 ? 1 : 2;   // incl, aggA, aggX, incl
+    const int c1 = q == 3 ? c - 2 : c - 1;
+    const int k2 = q == 0 ? 0 : q == 1 ? 1 : 2;                 // aggA, aggX, incl, incl
+    const int c2 = q < 2 ? c - 2 : c - 3;
+    const uint64_t *s1 = p.aggA + k1 * nw, *s2 = p.aggA + k2 * nw;
+    __builtin_amdgcn_global_load_lds((const void *)(s1 + (row + max(c1, 0)) * p.D + ch0),
+                                     (__attribute__((address_space(3))) void *)slot, 16, 0, 16);
+    __builtin_amdgcn_global_load_lds((const void *)(s2 + (row + max(c2, 0)) * p.D + ch0),
+                                     (__attribute__((address_space(3))) void *)(slot + 1024), 16, 0, 16);
+}
+
+// The state before the chunk after chunk k (k >= 0) from the prefetched
+// words of channel n, when they reach back to a published inclusive state or
+// to the sequence start; false sends the caller to look_back.  The fold is
+// look_back's, term for term (aggregates applied oldest first with fmaf), so
+// either way the result is the serial recurrence over chunk aggregates.
+__device__ __forceinline__ bool lb_from_slot(const char *slot, int n, int k, float h_before_first,
+                                             uint32_t tag, float &out)
+{
+    auto word = [&](int arr) { return *(const uint64_t *)(slot + arr * 256 + n * 8); };
+    const uint64_t i1 = word(0);
+    if (tagged(i1, tag)) {
+        out = word_val(i1);
+        return true;
+    }
+    const uint64_t a1 = word(1), x1 = word(2);
+    if (!tagged(a1, tag) || !tagged(x1, tag)) return false;
+    float s;
+    if (k == 0) {
+        s = h_before_first;
+    } else {
+        const uint64_t i2 = word(3);
+        if (tagged(i2, tag)) {
+            s = word_val(i2);
+        } else {
+            const uint64_t a2 = word(4), x2 = word(5);
+            if (!tagged(a2, tag) || !tagged(x2, tag)) return false;
+            float s2;
+            if (k == 1) {
+                s2 = h_before_first;
+            } else {
+                const uint64_t i3 = word(6);
+                if (!tagged(i3, tag)) return false;
+                s2 = word_val(i3);
+            }
+            s = fmaf(word_val(a2), s2, word_val(x2));
+        }
+    }
+    out = fmaf(word_val(a1), s, word_val(x1));
+    return true;
+}
 
 // Mode C: the x, r and i values of a lane's 16 tokens of unit q, as stored
 // (requested one unit ahead and kept in registers until used); tokens past the
@@ -157,16 +242,21 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
     constexpr bool WREG = (sizeof(T) == 2) && MODE != 2;   // weights held in registers
     constexpr bool STAGE = (sizeof(T) == 2) && CONV;        // input tile prefetched into LDS
     constexpr bool GTILE = STAGE && MERGE;                   // branch-2 tile staged too
+    constexpr bool LBP = STAGE && MODE == 0;                 // look-back words prefetched
     extern __shared__ __attribute__((aligned(16))) char smem[];
     T *Xs = (T *)smem;
     float *pslot_base = (float *)(smem + (MODE == 2 ? 0 : 32 * S * sizeof(T)));
     char *stage_base = (char *)pslot_base + 512 * PSTRIDE * sizeof(float);
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // mode A takes the wave index as a scalar: wave-derived addresses then
+    // live in scalar registers (fewer vector registers held across the loop)
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = LBP ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
     const int n = lane & 31, half = lane >> 5;
     const int g = blockIdx.x % p.G;
     char *gt_base = stage_base + (STAGE ? 2 * ST_BYTES : 0);   // mode 4: two branch-2 tiles
-    uint32_t *s_unit = (uint32_t *)(gt_base + (GTILE ? 2 * GT_BYTES : 0));   // 2 claim slots, flag
+    char *lbp_base = gt_base + (GTILE ? 2 * GT_BYTES : 0);   // look-back prefetch slots
+    uint32_t *s_unit = (uint32_t *)(lbp_base + (LBP ? 8 * LBP_BYTES : 0));   // 2 claim slots, flag
     uint32_t *claim = p.claim + g;
     if (tid == 0) {
         s_unit[0] = claim_next(claim);
@@ -217,6 +307,10 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
     // wave-uniform: some half-1 lane of this wave has a channel, so the wave
     // runs the back half's branch (and its wait for the tile requests)
     const bool half1_live = g * 256 + wave * 32 < p.D;
+    // wave-uniform: the wave's 32 channels exist and their words are 16-byte
+    // aligned, so the look-back words can be prefetched
+    const bool lbp_ok = LBP && p.lbp && (p.D & 1) == 0 && g * 256 + wave * 32 + 32 <= p.D;
+    char *lbp_slot = lbp_base + wave * LBP_BYTES;
     bool tile_waited = false;
     // Unit u_m of this workgroup travels through claim slot m & 1: thread 0
     // claims u_{n+2} at the start of iteration n and stores it later in the
@@ -232,7 +326,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
         if (j < units) {
             const int c0 = (int)(j / p.B), b0 = (int)(j % p.B);
             if (stageable(c0, p.T))
-                stage_issue<ST_BLOCKS, MERGE>((const bf16 *)in, (long)b0 * p.T + (long)c0 * CHUNK - 4, p.D,
+                stage_issue<ST_BLOCKS, MERGE || LBP>((const bf16 *)in, (long)b0 * p.T + (long)c0 * CHUNK - 4, p.D,
                                               g, stage_base, wave, lane);
         }
     }
@@ -254,6 +348,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
 
         float hl[16], P[16];
         Pend cur = {0, 0, 0.f, 0.f, 0.f, 0.f};
+        bool lbp_pend = false;   // the pending chunk's look-back words were requested
         auto publish_agg = [&](const Pend &u) {   // half-1 lanes with a channel
             const long widx = ((long)u.b * p.NC + u.c) * p.D + d;
             put_word(p.aggA + widx, u.Ach, tag);
@@ -289,7 +384,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
                     if (jn < units) {   // prefetch the next unit's tile
                         const int cn = (int)(jn / p.B), bn = (int)(jn % p.B);
                         if (stageable(cn, p.T))
-                            stage_issue<ST_BLOCKS, MERGE>((const bf16 *)in, (long)bn * p.T + (long)cn * CHUNK - 4,
+                            stage_issue<ST_BLOCKS, MERGE || LBP>((const bf16 *)in, (long)bn * p.T + (long)cn * CHUNK - 4,
                                                           p.D, g, stage_base + ((it + 1) & 1) * ST_BYTES, wave,
                                                           lane);
                     }
@@ -352,6 +447,10 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
                 // the other stage buffer) and the last back half's stores stay
                 // in flight
                 ds_barrier();
+                if constexpr (LBP) {
+                    lbp_pend = lbp_ok && have_pend && pd.c > 0;
+                    if (lbp_pend) lb_prefetch(p, pd.b, pd.c, g, wave, lane, lbp_slot);
+                }
                 if constexpr (WREG) {
                     const int r = lane & 31, kg = lane >> 5;
                     const bf16 *xrow = (const bf16 *)Xs + tile_row_token(r) * S + 8 * kg;
@@ -477,9 +576,17 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
                 const long base = (long)b * p.NC * p.D + d;
                 const long widx = base + (long)c * p.D;
                 const float hbefore = p.h0 ? p.h0[(long)b * p.D + d] : 0.0f;
-                hchunk = c == 0 ? hbefore
-                                : look_back(p.aggA + base, p.aggX + base, p.incl + base, c - 1, p.D,
-                                            hbefore, tag, p.hdr);
+                bool got = c == 0;
+                hchunk = hbefore;
+                if constexpr (LBP) {
+                    if (!got && lbp_pend) {
+                        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));   // the slot has landed
+                        got = lb_from_slot(lbp_slot, n, c - 1, hbefore, tag, hchunk);
+                    }
+                }
+                if (!got)
+                    hchunk = look_back(p.aggA + base, p.aggX + base, p.incl + base, c - 1, p.D, hbefore, tag,
+                                       p.hdr);
                 // the tile requests of this iteration's front were issued before
                 // the look-back's loads, so this wait costs little
                 if constexpr (STAGE) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
@@ -585,8 +692,9 @@ size_t fwd_lds_bytes()
 {
     const bool stage = sizeof(T) == 2 && (MODE == 0 || MODE == 3 || MODE == 4);
     const bool gtile = sizeof(T) == 2 && MODE == 4;
+    const bool lbp = stage && MODE == 0;
     return (MODE == 2 ? 0 : 32 * XTile<T>::STRIDE * sizeof(T)) + 512 * PSTRIDE * sizeof(float) +
-           (stage ? 2 * ST_BYTES : 0) + (gtile ? 2 * GT_BYTES : 0) + 16;
+           (stage ? 2 * ST_BYTES : 0) + (gtile ? 2 * GT_BYTES : 0) + (lbp ? 8 * LBP_BYTES : 0) + 16;
 }
 
 // Per device: CU count and resident workgroups per CU of one kernel, looked
@@ -624,7 +732,9 @@ void launch_mode(FwdParams p, hipStream_t s)
 {
     static_assert(32 * 260 * 4 + 512 * PSTRIDE * 4 + 16 <= 160 * 1024, "LDS budget (fp32)");
     static_assert(32 * 264 * 2 + 512 * PSTRIDE * 4 + 2 * ST_BYTES + 2 * GT_BYTES + 16 <= 160 * 1024,
-                  "LDS budget (bf16)");
+                  "LDS budget (bf16, mode 4)");
+    static_assert(32 * 264 * 2 + 512 * PSTRIDE * 4 + 2 * ST_BYTES + 8 * LBP_BYTES + 16 <= 160 * 1024,
+                  "LDS budget (bf16, mode A)");
     const LaunchShape ls = fwd_shape<T, MODE>();
     // workgroups per block: fill the resident slots, never more than the units;
     // RGLRU_FWD_GROUP_WORKGROUPS (a positive integer) caps the count, which
@@ -638,6 +748,11 @@ void launch_mode(FwdParams p, hipStream_t s)
     if (wpg > p.units) wpg = p.units;
     const long grid = (long)p.G * wpg;
     const size_t shmem = fwd_lds_bytes<T, MODE>();
+    // A block's workgroups hold about wpg consecutive units, wpg / B chunks of
+    // each stream; the prefetch reaches 3 chunks back, so it pays only when
+    // few chunks of a stream are in flight together (a lone 32k-token stream
+    // has ~25 in flight and its walks are long)
+    p.lbp = wpg <= 4L * p.B;
     fwd_kernel<T, MODE><<<dim3((unsigned)grid), dim3(512), shmem, s>>>(p);
 }
 
