@@ -76,16 +76,23 @@ constexpr int GT_BLOCKS = 16, GT_BYTES = GT_BLOCKS * ST_BLK;
 __device__ __forceinline__ bool stageable(int c, int T) { return c > 0 && (c + 1) * CHUNK <= T; }
 
 // OPQ: the lane's part of the address is rebuilt at every call instead of
-// being kept live (as a 64-bit pointer) across the caller's loop -- fewer
-// spilled registers in modes A and 4, a little slower where registers suffice
-template <int NBLK = ST_BLOCKS, bool OPQ = false>
+// being computed once and kept live (as a 64-bit value) across the caller's
+// loop, where it was spilled and its reload, waited for with every request in
+// flight, stalled the issue of the next tile.  OPQ 1 hides the offset from
+// the compiler, OPQ 2 the lane index it is computed from (modes 3 and 4,
+// where the offset itself was still hoisted and spilled; there the block
+// index also starts at the wave index taken as a scalar, so that the LDS
+// addresses are scalar).
+template <int NBLK = ST_BLOCKS, int OPQ = 0>
 __device__ __forceinline__ void stage_issue(const bf16 *in, long row0, int D, int g, char *dst,
                                             int wave, int lane)
 {
-    int loff = (lane >> 5) * D + (lane & 31) * 8;
-    if constexpr (OPQ) asm volatile("" : "+v"(loff));
-    for (int i = wave; i < NBLK; i += 8) {
-        const bf16 *src = OPQ ? in + (row0 + 2 * i) * D + g * 256 + loff
+    int ln = lane;
+    if constexpr (OPQ == 2) asm volatile("" : "+v"(ln));
+    int loff = (ln >> 5) * D + (ln & 31) * 8;
+    if constexpr (OPQ == 1) asm volatile("" : "+v"(loff));
+    for (int i = OPQ == 2 ? __builtin_amdgcn_readfirstlane(wave) : wave; i < NBLK; i += 8) {
+        const bf16 *src = OPQ != 0 ? in + (row0 + 2 * i) * D + g * 256 + loff
                               : in + (row0 + 2 * i + (lane >> 5)) * D + g * 256 + (lane & 31) * 8;
         __builtin_amdgcn_global_load_lds((const void *)src,
                                          (__attribute__((address_space(3))) void *)(dst + i * ST_BLK),
@@ -326,7 +333,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
         if (j < units) {
             const int c0 = (int)(j / p.B), b0 = (int)(j % p.B);
             if (stageable(c0, p.T))
-                stage_issue<ST_BLOCKS, MERGE || LBP>((const bf16 *)in, (long)b0 * p.T + (long)c0 * CHUNK - 4, p.D,
+                stage_issue<ST_BLOCKS, LBP ? 1 : 2>((const bf16 *)in, (long)b0 * p.T + (long)c0 * CHUNK - 4, p.D,
                                               g, stage_base, wave, lane);
         }
     }
@@ -384,13 +391,13 @@ __global__ __launch_bounds__(512) void fwd_kernel(FwdParams p)
                     if (jn < units) {   // prefetch the next unit's tile
                         const int cn = (int)(jn / p.B), bn = (int)(jn % p.B);
                         if (stageable(cn, p.T))
-                            stage_issue<ST_BLOCKS, MERGE || LBP>((const bf16 *)in, (long)bn * p.T + (long)cn * CHUNK - 4,
+                            stage_issue<ST_BLOCKS, LBP ? 1 : 2>((const bf16 *)in, (long)bn * p.T + (long)cn * CHUNK - 4,
                                                           p.D, g, stage_base + ((it + 1) & 1) * ST_BYTES, wave,
                                                           lane);
                     }
                     // this unit's branch-2 tile, read by its back half in the next iteration
                     if (GTILE && full)
-                        stage_issue<GT_BLOCKS, true>((const bf16 *)p.gate_in, row_b + (long)c * CHUNK, p.D, g,
+                        stage_issue<GT_BLOCKS, 2>((const bf16 *)p.gate_in, row_b + (long)c * CHUNK, p.D, g,
                                                      gt_base + (it & 1) * GT_BYTES, wave, lane);
                 }
                 if (staged) {
