@@ -303,7 +303,10 @@ def test_repeatable():
 def test_results_independent_of_grid(mode, monkeypatch):
     # the persistent forward claims its units at run time; one workgroup per
     # 256-channel group (every wait then on the same workgroup's earlier
-    # units) and three must give the same bits as the full grid
+    # units) and three must give the same bits as the full grid.  In mode A
+    # the full grid here (25 workgroups per group, 4 streams) runs without the
+    # look-back prefetch and the capped grids with it, so this also compares
+    # the two look-back paths bit for bit
     prob = make_problem(1, B=4, T=700, with_state=True)
     w = prob.weights(DEV)
     u = to_dev(prob.u, DEV)
