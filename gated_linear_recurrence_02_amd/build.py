@@ -9,6 +9,7 @@ atomic optimizer (see FILE_FLAGS).
 from __future__ import annotations
 
 import concurrent.futures as cf
+import ctypes
 import glob
 import os
 import subprocess
@@ -52,6 +53,12 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # every symbol resolves (a host stub missing from an object would only
+    # surface when the library is loaded); loading needs no GPU
+    try:
+        ctypes.CDLL(os.path.abspath(tmp))
+    except OSError as e:
+        raise RuntimeError(f"the linked library does not load: {e}")
     os.replace(tmp, OUT)
     # the microbenchmarks bench.py --micro runs: a library of their own
     msrc = os.path.join(HERE, "micro", "micro.hip")

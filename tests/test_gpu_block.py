@@ -123,6 +123,26 @@ def test_block_bf16_ragged_projection_shapes(T, d_model):
     _cmp("hist_out", ho, rhist, TOL["bf16"])
 
 
+@pytest.mark.parametrize("T,d_model", [(33, 320), (300, 576)])
+def test_block_gemm_tile_widths_agree(T, d_model, monkeypatch):
+    # the projections' two matrix-core tile widths (256 and 128 output
+    # columns) accumulate every output in the same order over K, so forced
+    # either way (partial row and column tiles included) the block gives the
+    # same bits, and the oracle's values
+    prob, bp, x = _block_setup(1, 2, T, d_model, with_state=True)
+    runs = {}
+    for width in ("256", "128"):
+        monkeypatch.setenv("RGLRU_GEMM_TILE_N", width)
+        _say(f"block bf16: B=2 T={T} d_model={d_model}, GEMM tiles {width} wide")
+        runs[width] = _run(prob, bp, x, True)
+    monkeypatch.delenv("RGLRU_GEMM_TILE_N")
+    for k, name in enumerate(("out", "h_last", "hist_out")):
+        assert np.array_equal(runs["256"][k], runs["128"][k]), f"{name} depends on the GEMM tile width"
+    ro, rh, _ = _oracle_block_stored(prob, bp, x, 0, 2, with_state=True)
+    _cmp("out", runs["256"][0], ro, TOL["bf16"])
+    _cmp("h_last", runs["256"][1], rh, TOL["bf16"])
+
+
 def test_block_prefill_split_equals_whole():
     # two calls that hand over (h_last, hist_out) equal one call over the whole
     # sequence, and both equal the oracle
