@@ -133,13 +133,19 @@ struct FwdParams {
 // 2 KB slot while the products and the elementwise work run, so that the back
 // half usually finds the start state there instead of paying a round trip to
 // memory; a word not yet published when it was copied sends the lane to
-// look_back.  Slot layout: array k (0 incl c-1, 1 aggA c-1, 2 aggX c-1,
-// 3 incl c-2, 4 aggA c-2, 5 aggX c-2, 6 incl c-3) at k * 256 bytes, channel n
-// of the wave at n * 8 within it.
+// look_back.  Slot layout: array k at k * 256 bytes, channel n of the wave at
+// n * 8 within it; k = 0..3 the inclusive states of chunks c-1 .. c-4 (c-4
+// unused), k = 4, 5 the aggregate halves A, X of chunk c-1, k = 6, 7 those of
+// chunk c-2.
 constexpr int LBP_BYTES = 2048;
 
 // Two DMA instructions of 16 bytes per lane (two channels' words): lanes
-// 16q .. 16q+15 fill array q of the instruction's half of the slot.  Chunks
+// 16q .. 16q+15 fill array q of the instruction's half of the slot.  The
+// three word arrays sit one after another in the workspace (aggA, aggX,
+// incl; see run_fwd), so both instructions read at one scalar base (stream b, the wave's channels) plus a
+// 32-bit lane offset that is affine in q: q chunks back in the inclusive
+// array, and aggregate half q & 1 of chunk c-1-(q >> 1).  The host enables
+// the prefetch only when the three arrays span less than 2^31 bytes.  Chunks
 // before the first read chunk 0 (in bounds; never used).  The words are read
 // at agent coherence (sc1), as look_back reads them.
 __device__ __forceinline__ void lb_prefetch(const FwdParams &p, int b, int c, int g, int wave, int lane,
@@ -150,20 +156,15 @@ __device__ __forceinline__ void lb_prefetch(const FwdParams &p, int b, int c, in
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int q = ln >> 4;
-    const long ch0 = (long)g * 256 + wave * 32 + 2 * (ln & 15);
-    const long row = (long)b * p.NC;
-    // the three arrays sit one after another in the workspace (aggA, aggX,
-    // incl; see run_fwd), so a lane picks its array by an offset from one
-    // scalar base rather than by selecting a pointer per lane
-    const long nw = (long)p.B * p.NC * p.D;
-    const int k1 = q == 0 ? 2 : q == 1 ? 0 : q == 2 ? 1 : 2;   // incl, aggA, aggX, incl
-    const int c1 = q == 3 ? c - 2 : c - 1;
-    const int k2 = q == 0 ? 0 : q == 1 ? 1 : 2;                 // aggA, aggX, incl, incl
-    const int c2 = q < 2 ? c - 2 : c - 3;
-    const uint64_t *s1 = p.aggA + k1 * nw, *s2 = p.aggA + k2 * nw;
-    __builtin_amdgcn_global_load_lds((const void *)(s1 + (row + max(c1, 0)) * p.D + ch0),
-                                     (__attribute__((address_space(3))) void *)slot, 16, 0, 16);
-    __builtin_amdgcn_global_load_lds((const void *)(s2 + (row + max(c2, 0)) * p.D + ch0),
+    const uint32_t Db = (uint32_t)p.D * 8u;             // bytes per chunk row of one array
+    const uint32_t nwb = (uint32_t)p.NC * (uint32_t)p.B * Db;   // bytes per array (aggA, aggX, incl)
+    const uint32_t lo = (uint32_t)(ln & 15) * 16u;
+    const uint32_t v1 = 2u * nwb + (uint32_t)max(c - 1 - q, 0) * Db + lo;
+    const uint32_t v2 = (uint32_t)(q & 1) * nwb + (uint32_t)max(c - 1 - (q >> 1), 0) * Db + lo;
+    const char *base = (const char *)(p.aggA + (long)b * p.NC * p.D + g * 256 + wave * 32);
+    __builtin_amdgcn_global_load_lds((const void *)(base + v1), (__attribute__((address_space(3))) void *)slot, 16,
+                                     0, 16);
+    __builtin_amdgcn_global_load_lds((const void *)(base + v2),
                                      (__attribute__((address_space(3))) void *)(slot + 1024), 16, 0, 16);
 }
 
@@ -181,23 +182,23 @@ __device__ __forceinline__ bool lb_from_slot(const char *slot, int n, int k, flo
         out = word_val(i1);
         return true;
     }
-    const uint64_t a1 = word(1), x1 = word(2);
+    const uint64_t a1 = word(4), x1 = word(5);
     if (!tagged(a1, tag) || !tagged(x1, tag)) return false;
     float s;
     if (k == 0) {
         s = h_before_first;
     } else {
-        const uint64_t i2 = word(3);
+        const uint64_t i2 = word(1);
         if (tagged(i2, tag)) {
             s = word_val(i2);
         } else {
-            const uint64_t a2 = word(4), x2 = word(5);
+            const uint64_t a2 = word(6), x2 = word(7);
             if (!tagged(a2, tag) || !tagged(x2, tag)) return false;
             float s2;
             if (k == 1) {
                 s2 = h_before_first;
             } else {
-                const uint64_t i3 = word(6);
+                const uint64_t i3 = word(2);
                 if (!tagged(i3, tag)) return false;
                 s2 = word_val(i3);
             }
@@ -758,8 +759,9 @@ void launch_mode(FwdParams p, hipStream_t s)
     // A block's workgroups hold about wpg consecutive units, wpg / B chunks of
     // each stream; the prefetch reaches 3 chunks back, so it pays only when
     // few chunks of a stream are in flight together (a lone 32k-token stream
-    // has ~25 in flight and its walks are long)
-    p.lbp = wpg <= 4L * p.B;
+    // has ~25 in flight and its walks are long); it addresses the three word
+    // arrays by 32-bit offsets, so they must span less than 2^31 bytes
+    p.lbp = wpg <= 4L * p.B && 3 * (size_t)p.B * p.NC * p.D * sizeof(uint64_t) < ((size_t)1 << 31);
     fwd_kernel<T, MODE><<<dim3((unsigned)grid), dim3(512), shmem, s>>>(p);
 }
 
